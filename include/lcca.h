@@ -1,0 +1,238 @@
+/*
+ * lcca.h -- compressed-KV attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of liblcca.so: the four stages of decode and chunked-prefill
+ * attention over a compressed, paged KV cache plus a sliding window.
+ *
+ * Sources for what each call computes:
+ *   [P1] page "vLLM uveo DeepSeek V4 s 8,7x manjim KV cacheom: milijun
+ *        tokena konteksta na standardnom GPU hardveru" (24-ai.news; the
+ *        German page "vLLM integriert DeepSeek V4 mit 8,7x kleinerem
+ *        KV-Cache" is its translation).
+ *   [P3] page "DeepSeek-V4.1-Flash ve vLLM: kde se vzala 5,3x vyssi
+ *        propustnost" (aidevelopers.cz).
+ *
+ * Conventions common to every call
+ *   - Every buffer pointer is a DEVICE pointer owned by the caller, except
+ *     the descriptor structs themselves, which live in host memory and are
+ *     read during the call only.  The library never allocates, frees or
+ *     synchronises.  Every call is asynchronous on `stream` (a hipStream_t;
+ *     NULL is the null stream).
+ *   - The library keeps no state between calls: positions and lengths are
+ *     explicit, so a call repeated at the same positions rewrites the same
+ *     bytes.
+ *   - Arguments are validated on the host before any launch; a failing call
+ *     launches nothing and returns a negative lcca_status, with details in
+ *     lcca_last_error() (thread-local).  Device-side indices (block table,
+ *     top-k indices, positions) are trusted: the host cannot see them.
+ *
+ * Data layout
+ *   dtype codes: LCCA_F32 (4 B), LCCA_BF16 (2 B), LCCA_FP8_E4M3 (1 B, OCP
+ *   E4M3 "fn": bias 7, max 448, no infinities), LCCA_MXFP4 (OCP MX: E2M1
+ *   codes, two per byte with element 2i in the low nibble, and one E8M0
+ *   scale byte per 32 elements in a separate array).
+ *
+ *   Paged pool (lcca_paged_cache): a block covers 256 logical token
+ *   positions, so it holds E = 256 / ratio_m compressed entries [P1 "Sto je
+ *   vLLM morao rijesiti u integraciji?": fixed logical blocks of 256 token
+ *   positions, with a logical->physical mapping that depends on the layer's
+ *   compression ratio].  data is [num_blocks][E][row] with row = dim
+ *   elements of `dtype`; scale is [num_blocks][E][dim/32] E8M0 bytes for
+ *   MXFP4, or [num_blocks][E] float (per-entry scale; NULL means 1) for FP8.
+ *   Entry g of sequence b is at physical block block_table[b][g / E], slot
+ *   g % E.
+ *
+ *   Window ring (lcca_window_cache): data [batch][capacity][dim]; token at
+ *   position t of sequence b lives in slot t % capacity.  FP8 windows carry
+ *   a float scale per slot [batch][capacity]: code = RNE(x / s) with
+ *   s = max|x| / 448 (1 if the token is zero).  A window of full vectors of
+ *   the most recent positions sits beside the compressed entries [P1 "Kako
+ *   funkcionira optimizacija KV cachea?"; FP8, 128 positions: P3 "Proc je
+ *   obnova sliding-window cache draha"].
+ *
+ *   Remainder ring (lcca_remainder): tokens of a sequence's incomplete last
+ *   group, in the token dtype, [batch][ratio_m][dim], slot t % ratio_m, with
+ *   float logits [batch][ratio_m]; the compressor's remainder is carried as
+ *   window-like state [P1 "Sto je vLLM morao rijesiti u integraciji?"].
+ *
+ *   Query rows (lcca_rows): one row is one (sequence, position) with all its
+ *   query heads.  A row at position p sees compressed entries
+ *   g < n = floor((p + 1) / ratio_m) (an entry is visible once its last
+ *   token is) and window tokens max(0, p - window + 1) .. p.
+ */
+#ifndef LCCA_H
+#define LCCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t lcca_status;
+#define LCCA_OK               0
+#define LCCA_ERR_INVALID_ARG (-1)   /* NULL/negative/inconsistent argument          */
+#define LCCA_ERR_UNSUPPORTED (-2)   /* dtype or shape combination not built          */
+#define LCCA_ERR_WORKSPACE   (-3)   /* workspace missing or smaller than required    */
+#define LCCA_ERR_HIP         (-4)   /* a HIP runtime call or kernel launch failed    */
+
+typedef enum { LCCA_F32 = 0, LCCA_BF16 = 1, LCCA_FP8_E4M3 = 2, LCCA_MXFP4 = 3 } lcca_dtype;
+
+typedef struct {
+    int32_t dtype;        /* lcca_dtype of the stored entries                    */
+    int32_t dim;          /* elements per entry                                  */
+    int32_t ratio_m;      /* tokens per entry; 256 % ratio_m == 0                */
+    int32_t num_blocks;   /* physical blocks in the pool                         */
+    void*   data;         /* device [num_blocks][256/ratio_m][row bytes]          */
+    void*   scale;        /* device: MXFP4 u8 [..][dim/32]; FP8 float [..] or NULL */
+} lcca_paged_cache;
+
+typedef struct {
+    int32_t dtype;        /* LCCA_F32, LCCA_BF16 or LCCA_FP8_E4M3                */
+    int32_t dim;          /* elements per token (= the pool's dim)               */
+    int32_t capacity;     /* slots per sequence (>= window)                      */
+    int32_t window;       /* positions attended: max(0, p-window+1) .. p          */
+    void*   data;         /* device [batch][capacity][row bytes]                 */
+    float*  scale;        /* device [batch][capacity]; FP8 only                  */
+} lcca_window_cache;
+
+typedef struct {
+    int32_t batch;              /* sequences                                     */
+    int32_t max_blocks_per_seq; /* row stride of block_table                     */
+    const int32_t* block_table; /* device [batch][max_blocks_per_seq]            */
+} lcca_pages;
+
+typedef struct {
+    int32_t num_rows;           /* query rows                                    */
+    int32_t max_pos;            /* host: upper bound of every row_pos (sizes grids) */
+    const int32_t* row_seq;     /* device [num_rows] sequence of each row        */
+    const int32_t* row_pos;     /* device [num_rows] position of each row        */
+} lcca_rows;
+
+typedef struct {
+    int32_t tok_dtype;          /* LCCA_F32 or LCCA_BF16 (the token dtype)       */
+    void*   kv;                 /* device [batch][ratio_m][kv dim]               */
+    void*   ik;                 /* device [batch][ratio_m][indexer dim] or NULL  */
+    float*  kv_logit;           /* device [batch][ratio_m]                       */
+    float*  ik_logit;           /* device [batch][ratio_m] or NULL               */
+} lcca_remainder;
+
+/*
+ * lcca_compress_append -- fold new tokens into compressed entries and append.
+ *
+ * [P1 "Kako funkcionira optimizacija KV cachea?": the cache is compressed by
+ * weighted summation of tokens, 4x (CSA) to 128x (HCA); P1 "Sto je vLLM morao
+ * rijesiti u integraciji?": paged 256-position blocks, remainder as window
+ * state.]  Sequence b receives n_b = cu_new[b+1] - cu_new[b] tokens at
+ * positions start_pos[b] .. start_pos[b]+n_b-1 (rows cu_new[b].. of the token
+ * arrays).  For each group g of ratio_m tokens completed by the chunk, and for
+ * each stream (shared-KV vectors; indexer keys if `ik` is given):
+ *     w_i = softmax_i(a_{g m + i})  over the group's per-token logits a,
+ *     C_g = sum_i w_i x_{g m + i}   (fp32),
+ * encoded to the pool dtype and stored as entry g.  Group tokens older than
+ * the chunk are read from the remainder ring; new tokens of a still
+ * incomplete group are stored into it.  The last min(n_b, capacity) new
+ * tokens are encoded into the window ring.
+ *   cu_new     device int32 [batch+1], cu_new[0] = 0, nondecreasing
+ *   start_pos  device int32 [batch]
+ *   total_new  host: cu_new[batch] (the grid has one block per new token)
+ *   kv_tok     device [total_new][kv->dim] of tok_dtype (F32 or BF16)
+ *   kv_logit   device float [total_new]
+ *   ik_tok, ik_logit   device, as above with ik->dim; both NULL iff ik NULL
+ *   kv         pool of dtype F32, BF16 or MXFP4 (dim % 32 == 0 for MXFP4)
+ *   ik         pool of dtype F32, BF16 or FP8 (raw E4M3, scale NULL), or NULL
+ *   win        window ring of the kv stream (dim = kv->dim), or NULL
+ *   rem        remainder ring (tok_dtype must match)
+ * Stored codes: bf16 and E4M3 round to nearest even (E4M3 saturates at
+ * +-448); MXFP4 uses the OCP rule: X = floor(log2(max|x|)) - 2 per 32
+ * elements, elements RNE to E2M1 after division by 2^X, saturating at +-6.
+ * Chunks of one sequence must be appended in position order; calls for
+ * distinct sequences may be combined freely.
+ */
+lcca_status lcca_compress_append(void* stream, const lcca_pages* pages,
+                                 const int32_t* cu_new, const int32_t* start_pos, int32_t total_new,
+                                 int32_t tok_dtype, const void* kv_tok, const float* kv_logit,
+                                 const void* ik_tok, const float* ik_logit,
+                                 const lcca_paged_cache* kv, const lcca_paged_cache* ik,
+                                 const lcca_window_cache* win, const lcca_remainder* rem);
+
+/*
+ * lcca_index_logits -- sparse MQA logits of the indexer.
+ *
+ * [P3 "Vykon neprinesl jeden kernel": the indexer scores only candidate
+ * positions.]  For row r (sequence b, position p) and every visible entry
+ * g < n_r = floor((p+1)/m):
+ *     logits[r*ld + g] = s_I * sum_h w_idx[r][h] * max(0, q_idx[r][h] . K_g)
+ * with K_g the dequantised indexer key of entry g.  Entries g >= n_r are not
+ * written.  fp32 accumulation; bf16 queries and bf16/FP8 keys use MFMA on
+ * exactly upconverted keys.
+ *   q_idx   device [num_rows][HI][ik->dim] of q_dtype (F32 with F32 keys;
+ *           BF16 with BF16 or FP8 keys)
+ *   w_idx   device float [num_rows][HI]
+ *   logits  device float [num_rows][ld], ld >= max visible entries
+ * BF16 path: HI % 32 == 0 and ik->dim % 64 == 0 (HI <= 128, dim <= 256).
+ */
+lcca_status lcca_index_logits(void* stream, const lcca_pages* pages, const lcca_rows* rows,
+                              int32_t q_dtype, const void* q_idx, int32_t HI, const float* w_idx, float s_I,
+                              const lcca_paged_cache* ik, float* logits, int64_t ld);
+
+/*
+ * lcca_topk_select -- the entries each row attends to.
+ *
+ * [P1 "Kako funkcionira optimizacija KV cachea?": attention is restricted to
+ * the top-k compressed tokens.]  topk_idx[r][0..] receives the min(k, n_r)
+ * entries with the largest logits[r][g], g < n_r; equal logits rank the
+ * smaller entry first (-0.0 equals +0.0).  The set is written in ascending
+ * entry order and padded with -1 up to k.  NaN logits give an unspecified
+ * selection.
+ *   logits    device float [num_rows][ld]
+ *   topk_idx  device int32 [num_rows][k]
+ *   ws        unused (may be NULL); ws_bytes ignored
+ */
+lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_m,
+                             const float* logits, int64_t ld, int32_t k, int32_t* topk_idx,
+                             void* ws, size_t ws_bytes);
+
+/*
+ * lcca_sparse_attn_fwd -- attention over selected entries plus the window.
+ *
+ * [P1 "Kako funkcionira optimizacija KV cachea?": shared KV vectors, top-k
+ * sparse attention over compressed tokens, and a local window of full
+ * vectors.]  For row r (sequence b, position p) the keys are the dequantised
+ * entries listed in topk_idx[r][0..k) (entries < 0 or >= n_r are skipped;
+ * topk_idx NULL means every visible entry g < n_r), followed by the window
+ * tokens max(0, p - win->window + 1) .. p.  One vector is key and value
+ * (value = its first d_v elements).  For each head h:
+ *     s_j = sm_scale * q[r][h] . k_j,
+ *     out[r][h] = sum_j softmax(s)_j v_j,    lse[r][h] = ln sum_j exp(s_j)
+ * with all keys in ONE softmax.  Keys are split across workgroups and the
+ * partial softmax states are merged exactly (max, rescaled sums).
+ *   q        device [num_rows][H][kv->dim] of q_dtype (F32 with F32 cache;
+ *            BF16 otherwise)
+ *   out      device [num_rows][H][d_v] of out_dtype (F32 or BF16)
+ *   lse      device float [num_rows][H] or NULL
+ *   ws       device workspace of at least lcca_sparse_attn_workspace_size()
+ *            bytes for the same arguments (may be NULL if that size is 0)
+ * BF16 path: kv dtype BF16 or MXFP4, window BF16 or FP8, H % 16 == 0 (<= 64
+ * per workgroup), kv->dim % 32 == 0, d_v <= kv->dim.
+ */
+lcca_status lcca_sparse_attn_fwd(void* stream, const lcca_pages* pages, const lcca_rows* rows,
+                                 int32_t q_dtype, const void* q, int32_t H, int32_t d_v, float sm_scale,
+                                 const lcca_paged_cache* kv, const int32_t* topk_idx, int32_t k,
+                                 const lcca_window_cache* win, int32_t out_dtype, void* out, float* lse,
+                                 void* ws, size_t ws_bytes);
+
+/* Workspace bytes lcca_sparse_attn_fwd needs for these arguments
+ * (partial softmax states of the key splits). */
+size_t lcca_sparse_attn_workspace_size(const lcca_rows* rows, int32_t ratio_m, int32_t H, int32_t dim,
+                                       int32_t d_v, int32_t k, int32_t topk_given, int32_t window);
+
+const char* lcca_status_string(lcca_status s);
+const char* lcca_last_error(void);
+const char* lcca_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LCCA_H */

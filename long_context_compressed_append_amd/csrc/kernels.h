@@ -1,0 +1,62 @@
+// Internal interface between the host entry points (lcca_api.cpp) and the
+// gfx950 kernels.  Plain structs of device pointers and sizes, validated by
+// the host before a launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lcca {
+
+struct CompressArgs {
+    const int32_t* block_table; int32_t max_blocks;
+    const int32_t* cu_new; const int32_t* start_pos; int32_t batch;
+    int32_t tok_dtype;
+    const void* kv_tok; const float* kv_logit; const void* ik_tok; const float* ik_logit;
+    int32_t m, D, dI;
+    int32_t kv_dtype; void* kv_data; void* kv_scale;
+    int32_t ik_dtype; void* ik_data; void* ik_scale;     // ik_data == nullptr: no indexer stream
+    int32_t win_dtype; int32_t win_cap; void* win_data; float* win_scale;   // win_data == nullptr: no window
+    void* rem_kv; void* rem_ik; float* rem_kv_logit; float* rem_ik_logit;
+};
+
+struct IndexArgs {
+    const int32_t* block_table; int32_t max_blocks;
+    const int32_t* row_seq; const int32_t* row_pos; int32_t num_rows;
+    const void* q; const float* w; float s_I;
+    int32_t HI, dI, m;
+    int32_t key_dtype; const void* keys;
+    float* logits; int64_t ld;
+    // launch plan
+    int32_t tiles_per_wave;      // 32-entry tiles per wave (decode) / per workgroup (prefill)
+};
+
+struct TopkArgs {
+    const int32_t* row_pos; int32_t num_rows; int32_t m;
+    const float* logits; int64_t ld; int32_t k;
+    int32_t* idx;
+};
+
+struct AttnArgs {
+    const int32_t* block_table; int32_t max_blocks;
+    const int32_t* row_seq; const int32_t* row_pos; int32_t num_rows;
+    const void* q; int32_t H, D, d_v; float scale_log2;     // sm_scale * log2(e)
+    int32_t m; int32_t kv_dtype; const void* kv_data; const void* kv_scale;
+    const int32_t* topk; int32_t k;                         // topk == nullptr: dense over visible entries
+    int32_t win_dtype; const void* win_data; const float* win_scale; int32_t win_cap, window;
+    int32_t out_dtype; void* out; float* lse;
+    // split plan
+    int32_t nsplit, split_keys;
+    float* part_o;     // [rows][nsplit][H][d_v]   (nsplit > 1)
+    float* part_ml;    // [rows][nsplit][2][H]
+};
+
+hipError_t launch_compress_append(const CompressArgs& a, int total_new, hipStream_t stream);
+hipError_t launch_index_logits(const IndexArgs& a, int max_entries, hipStream_t stream);
+hipError_t launch_topk_select(const TopkArgs& a, int max_entries, hipStream_t stream);
+hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
+
+// which (dtype, shape) combinations the kernels are built for
+bool index_supported(int q_dtype, int key_dtype, int HI, int dI);
+bool attn_supported(int q_dtype, int kv_dtype, int win_dtype, int H, int D, int d_v);
+
+}  // namespace lcca

@@ -1,0 +1,274 @@
+// Host side of liblcca: argument validation, launch planning and dispatch of
+// the gfx950 kernels.  Every check runs before any launch; a failed check
+// returns an error code and launches nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/lcca.h"
+#include "device.h"
+#include "kernels.h"
+
+namespace lcca {
+int attn_f32_max_keys();
+}
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+lcca_status fail(lcca_status code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+lcca_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return LCCA_OK;
+    return fail(LCCA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_m(int m) { return m >= 1 && m <= 256 && 256 % m == 0; }
+
+bool valid_dtype(int d) { return d >= LCCA_F32 && d <= LCCA_MXFP4; }
+
+lcca_status check_pages(const lcca_pages* pg) {
+    if (!pg) return fail(LCCA_ERR_INVALID_ARG, "pages is NULL");
+    if (pg->batch < 1 || pg->max_blocks_per_seq < 1 || !pg->block_table)
+        return fail(LCCA_ERR_INVALID_ARG, "pages: batch=%d max_blocks_per_seq=%d block_table=%p", pg->batch,
+                    pg->max_blocks_per_seq, (const void*)pg->block_table);
+    return LCCA_OK;
+}
+
+lcca_status check_rows(const lcca_rows* rw, int ratio_m, int max_blocks) {
+    if (!rw) return fail(LCCA_ERR_INVALID_ARG, "rows is NULL");
+    if (rw->num_rows < 0) return fail(LCCA_ERR_INVALID_ARG, "rows: num_rows=%d", rw->num_rows);
+    if (rw->num_rows > 0 && (!rw->row_seq || !rw->row_pos))
+        return fail(LCCA_ERR_INVALID_ARG, "rows: row_seq/row_pos NULL");
+    if (rw->max_pos < 0) return fail(LCCA_ERR_INVALID_ARG, "rows: max_pos=%d", rw->max_pos);
+    if (max_blocks > 0 && (int64_t)rw->max_pos >= (int64_t)max_blocks * 256)
+        return fail(LCCA_ERR_INVALID_ARG, "rows: max_pos=%d beyond the block table (%d blocks of 256)", rw->max_pos,
+                    max_blocks);
+    (void)ratio_m;
+    return LCCA_OK;
+}
+
+lcca_status check_pool(const lcca_paged_cache* c, const char* name) {
+    if (!c) return fail(LCCA_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!valid_dtype(c->dtype) || c->dim < 1 || !valid_m(c->ratio_m) || c->num_blocks < 1 || !c->data)
+        return fail(LCCA_ERR_INVALID_ARG, "%s: dtype=%d dim=%d ratio_m=%d num_blocks=%d data=%p", name, c->dtype,
+                    c->dim, c->ratio_m, c->num_blocks, c->data);
+    if (c->dtype == LCCA_MXFP4 && (c->dim % 32 != 0 || !c->scale))
+        return fail(LCCA_ERR_INVALID_ARG, "%s: MXFP4 needs dim %% 32 == 0 and a scale array", name);
+    return LCCA_OK;
+}
+
+lcca_status check_window(const lcca_window_cache* w, int dim) {
+    if (!w) return fail(LCCA_ERR_INVALID_ARG, "window is NULL");
+    if (w->dtype != LCCA_F32 && w->dtype != LCCA_BF16 && w->dtype != LCCA_FP8_E4M3)
+        return fail(LCCA_ERR_UNSUPPORTED, "window dtype %d (F32, BF16 or FP8_E4M3)", w->dtype);
+    if (w->dim != dim || w->capacity < 1 || w->window < 1 || w->window > w->capacity || !w->data)
+        return fail(LCCA_ERR_INVALID_ARG, "window: dim=%d (want %d) capacity=%d window=%d data=%p", w->dim, dim,
+                    w->capacity, w->window, w->data);
+    if (w->dtype == LCCA_FP8_E4M3 && !w->scale) return fail(LCCA_ERR_INVALID_ARG, "FP8 window needs a scale array");
+    return LCCA_OK;
+}
+
+struct AttnPlan {
+    int nsplit, split_keys;
+    size_t ws_bytes;
+};
+
+// Split the keys of each row across workgroups only when the rows alone
+// cannot fill the 256 compute units; tiles of 32 keys.
+AttnPlan attn_plan(int rows, int max_pos, int m, int H, int d_v, int k, bool topk_given, int window) {
+    AttnPlan p{1, 32, 0};
+    if (rows <= 0) return p;
+    const int64_t nvis = (int64_t)(max_pos + 1) / m;
+    const int64_t L = (topk_given ? (int64_t)k : nvis) + std::min<int64_t>(window, (int64_t)max_pos + 1);
+    const int64_t tiles = std::max<int64_t>(1, (L + 31) / 32);
+    constexpr int kTargetWorkgroups = 256;
+    if (rows >= kTargetWorkgroups / 2) {
+        p.nsplit = 1;
+        p.split_keys = (int)(tiles * 32);
+        return p;
+    }
+    int64_t tps = (tiles * rows + kTargetWorkgroups - 1) / kTargetWorkgroups;
+    if (tps < 1) tps = 1;
+    p.split_keys = (int)(tps * 32);
+    p.nsplit = (int)((tiles + tps - 1) / tps);
+    if (p.nsplit > 1) {
+        size_t po = (size_t)rows * p.nsplit * H * d_v * sizeof(float);
+        po = (po + 255) & ~(size_t)255;
+        p.ws_bytes = po + (size_t)rows * p.nsplit * 2 * H * sizeof(float);
+    }
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lcca_last_error(void) { return g_err; }
+
+const char* lcca_version(void) { return "lcca 0.1.0 (gfx950)"; }
+
+const char* lcca_status_string(lcca_status s) {
+    switch (s) {
+    case LCCA_OK: return "ok";
+    case LCCA_ERR_INVALID_ARG: return "invalid argument";
+    case LCCA_ERR_UNSUPPORTED: return "unsupported dtype/shape combination";
+    case LCCA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LCCA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+lcca_status lcca_compress_append(void* stream, const lcca_pages* pages, const int32_t* cu_new,
+                                 const int32_t* start_pos, int32_t total_new, int32_t tok_dtype, const void* kv_tok,
+                                 const float* kv_logit, const void* ik_tok, const float* ik_logit,
+                                 const lcca_paged_cache* kv, const lcca_paged_cache* ik,
+                                 const lcca_window_cache* win, const lcca_remainder* rem) {
+    g_err[0] = 0;
+    lcca_status s;
+    if ((s = check_pages(pages))) return s;
+    if ((s = check_pool(kv, "kv"))) return s;
+    if (ik && (s = check_pool(ik, "ik"))) return s;
+    if (win && (s = check_window(win, kv->dim))) return s;
+    if (total_new < 0) return fail(LCCA_ERR_INVALID_ARG, "total_new=%d", total_new);
+    if (!cu_new || !start_pos) return fail(LCCA_ERR_INVALID_ARG, "cu_new/start_pos NULL");
+    if (tok_dtype != LCCA_F32 && tok_dtype != LCCA_BF16)
+        return fail(LCCA_ERR_UNSUPPORTED, "token dtype %d (F32 or BF16)", tok_dtype);
+    if (total_new > 0 && (!kv_tok || !kv_logit)) return fail(LCCA_ERR_INVALID_ARG, "kv_tok/kv_logit NULL");
+    if (ik && total_new > 0 && (!ik_tok || !ik_logit)) return fail(LCCA_ERR_INVALID_ARG, "ik_tok/ik_logit NULL");
+    if (!ik && (ik_tok || ik_logit)) return fail(LCCA_ERR_INVALID_ARG, "ik_tok given without an ik pool");
+    if (kv->dtype == LCCA_FP8_E4M3) return fail(LCCA_ERR_UNSUPPORTED, "kv pool dtype FP8 (F32, BF16 or MXFP4)");
+    if (ik && ik->dtype == LCCA_MXFP4) return fail(LCCA_ERR_UNSUPPORTED, "ik pool dtype MXFP4 (F32, BF16 or FP8)");
+    if (ik && ik->dtype == LCCA_FP8_E4M3 && ik->scale)
+        return fail(LCCA_ERR_UNSUPPORTED, "FP8 ik pool with a scale array (raw E4M3 only)");
+    if (ik && ik->ratio_m != kv->ratio_m) return fail(LCCA_ERR_INVALID_ARG, "kv and ik ratio_m differ");
+    if (kv->dim % 2 || (ik && ik->dim % 2)) return fail(LCCA_ERR_UNSUPPORTED, "odd dims");
+    if (kv->dim > 2048) return fail(LCCA_ERR_UNSUPPORTED, "kv dim %d > 2048", kv->dim);
+    if (!rem || rem->tok_dtype != tok_dtype || !rem->kv || !rem->kv_logit || (ik && (!rem->ik || !rem->ik_logit)))
+        return fail(LCCA_ERR_INVALID_ARG, "remainder ring missing or of another token dtype");
+    lcca::CompressArgs a{};
+    a.block_table = pages->block_table; a.max_blocks = pages->max_blocks_per_seq;
+    a.cu_new = cu_new; a.start_pos = start_pos; a.batch = pages->batch;
+    a.tok_dtype = tok_dtype;
+    a.kv_tok = kv_tok; a.kv_logit = kv_logit; a.ik_tok = ik ? ik_tok : nullptr; a.ik_logit = ik ? ik_logit : nullptr;
+    a.m = kv->ratio_m; a.D = kv->dim; a.dI = ik ? ik->dim : 0;
+    a.kv_dtype = kv->dtype; a.kv_data = kv->data; a.kv_scale = kv->scale;
+    a.ik_dtype = ik ? ik->dtype : lcca::DT_NONE; a.ik_data = ik ? ik->data : nullptr; a.ik_scale = ik ? ik->scale : nullptr;
+    a.win_dtype = win ? win->dtype : lcca::DT_NONE; a.win_cap = win ? win->capacity : 1;
+    a.win_data = win ? win->data : nullptr; a.win_scale = win ? win->scale : nullptr;
+    a.rem_kv = rem->kv; a.rem_ik = rem->ik; a.rem_kv_logit = rem->kv_logit; a.rem_ik_logit = rem->ik_logit;
+    return hip_status(lcca::launch_compress_append(a, total_new, (hipStream_t)stream), "compress_append launch");
+}
+
+lcca_status lcca_index_logits(void* stream, const lcca_pages* pages, const lcca_rows* rows, int32_t q_dtype,
+                              const void* q_idx, int32_t HI, const float* w_idx, float s_I,
+                              const lcca_paged_cache* ik, float* logits, int64_t ld) {
+    g_err[0] = 0;
+    lcca_status s;
+    if ((s = check_pages(pages))) return s;
+    if ((s = check_pool(ik, "ik"))) return s;
+    if ((s = check_rows(rows, ik->ratio_m, pages->max_blocks_per_seq))) return s;
+    if (rows->num_rows == 0) return LCCA_OK;
+    if (!q_idx || !w_idx || !logits) return fail(LCCA_ERR_INVALID_ARG, "q_idx/w_idx/logits NULL");
+    if (HI < 1) return fail(LCCA_ERR_INVALID_ARG, "HI=%d", HI);
+    if (ik->dtype == LCCA_FP8_E4M3 && ik->scale)
+        return fail(LCCA_ERR_UNSUPPORTED, "FP8 indexer keys with a scale array (raw E4M3 only)");
+    if (!lcca::index_supported(q_dtype, ik->dtype, HI, ik->dim))
+        return fail(LCCA_ERR_UNSUPPORTED, "index_logits: q dtype %d, key dtype %d, HI=%d, dim=%d not built", q_dtype,
+                    ik->dtype, HI, ik->dim);
+    const int max_entries = (rows->max_pos + 1) / ik->ratio_m;
+    if (ld < max_entries) return fail(LCCA_ERR_INVALID_ARG, "ld=%lld < max visible entries %d", (long long)ld, max_entries);
+    lcca::IndexArgs a{};
+    a.block_table = pages->block_table; a.max_blocks = pages->max_blocks_per_seq;
+    a.row_seq = rows->row_seq; a.row_pos = rows->row_pos; a.num_rows = rows->num_rows;
+    a.q = q_idx; a.w = w_idx; a.s_I = s_I; a.HI = HI; a.dI = ik->dim; a.m = ik->ratio_m;
+    a.key_dtype = ik->dtype; a.keys = ik->data; a.logits = logits; a.ld = ld;
+    return hip_status(lcca::launch_index_logits(a, max_entries, (hipStream_t)stream), "index_logits launch");
+}
+
+lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_m, const float* logits, int64_t ld,
+                             int32_t k, int32_t* topk_idx, void* ws, size_t ws_bytes) {
+    (void)ws; (void)ws_bytes;
+    g_err[0] = 0;
+    lcca_status s;
+    if (!valid_m(ratio_m)) return fail(LCCA_ERR_INVALID_ARG, "ratio_m=%d", ratio_m);
+    if ((s = check_rows(rows, ratio_m, 0))) return s;
+    if (k < 1) return fail(LCCA_ERR_INVALID_ARG, "k=%d", k);
+    if (rows->num_rows == 0) return LCCA_OK;
+    if (!logits || !topk_idx) return fail(LCCA_ERR_INVALID_ARG, "logits/topk_idx NULL");
+    const int max_entries = (rows->max_pos + 1) / ratio_m;
+    if (ld < max_entries) return fail(LCCA_ERR_INVALID_ARG, "ld=%lld < max visible entries %d", (long long)ld, max_entries);
+    lcca::TopkArgs a{rows->row_pos, rows->num_rows, ratio_m, logits, ld, k, topk_idx};
+    return hip_status(lcca::launch_topk_select(a, max_entries, (hipStream_t)stream), "topk_select launch");
+}
+
+size_t lcca_sparse_attn_workspace_size(const lcca_rows* rows, int32_t ratio_m, int32_t H, int32_t dim, int32_t d_v,
+                                       int32_t k, int32_t topk_given, int32_t window) {
+    (void)dim;
+    if (!rows || !valid_m(ratio_m) || rows->num_rows <= 0) return 0;
+    return attn_plan(rows->num_rows, rows->max_pos, ratio_m, H, d_v, k, topk_given != 0, window).ws_bytes;
+}
+
+lcca_status lcca_sparse_attn_fwd(void* stream, const lcca_pages* pages, const lcca_rows* rows, int32_t q_dtype,
+                                 const void* q, int32_t H, int32_t d_v, float sm_scale, const lcca_paged_cache* kv,
+                                 const int32_t* topk_idx, int32_t k, const lcca_window_cache* win, int32_t out_dtype,
+                                 void* out, float* lse, void* ws, size_t ws_bytes) {
+    g_err[0] = 0;
+    lcca_status s;
+    if ((s = check_pages(pages))) return s;
+    if ((s = check_pool(kv, "kv"))) return s;
+    if ((s = check_rows(rows, kv->ratio_m, pages->max_blocks_per_seq))) return s;
+    if ((s = check_window(win, kv->dim))) return s;
+    if (rows->num_rows == 0) return LCCA_OK;
+    if (!q || !out) return fail(LCCA_ERR_INVALID_ARG, "q/out NULL");
+    if (H < 1 || d_v < 1 || d_v > kv->dim) return fail(LCCA_ERR_INVALID_ARG, "H=%d d_v=%d dim=%d", H, d_v, kv->dim);
+    if (topk_idx && k < 1) return fail(LCCA_ERR_INVALID_ARG, "k=%d with a top-k index array", k);
+    if (!std::isfinite(sm_scale)) return fail(LCCA_ERR_INVALID_ARG, "sm_scale not finite");
+    if (out_dtype != LCCA_F32 && out_dtype != LCCA_BF16) return fail(LCCA_ERR_UNSUPPORTED, "out dtype %d", out_dtype);
+    if (kv->dtype == LCCA_FP8_E4M3) return fail(LCCA_ERR_UNSUPPORTED, "FP8 kv pool (BF16, MXFP4 or F32)");
+    if (!lcca::attn_supported(q_dtype, kv->dtype, win->dtype, H, kv->dim, d_v))
+        return fail(LCCA_ERR_UNSUPPORTED, "sparse_attn: q %d, kv %d, window %d, H=%d, dim=%d, d_v=%d not built", q_dtype,
+                    kv->dtype, win->dtype, H, kv->dim, d_v);
+    const int m = kv->ratio_m;
+    const bool f32 = q_dtype == LCCA_F32;
+    AttnPlan plan = attn_plan(rows->num_rows, rows->max_pos, m, H, d_v, k, topk_idx != nullptr, win->window);
+    if (f32) {
+        const int64_t L = (topk_idx ? (int64_t)k : (int64_t)(rows->max_pos + 1) / m) +
+                          std::min<int64_t>(win->window, (int64_t)rows->max_pos + 1);
+        if (L > lcca::attn_f32_max_keys())
+            return fail(LCCA_ERR_UNSUPPORTED, "fp32 attention: %lld keys per row > %d", (long long)L,
+                        lcca::attn_f32_max_keys());
+        plan = AttnPlan{1, (int)L, 0};
+    }
+    if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes))
+        return fail(LCCA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, plan.ws_bytes);
+    lcca::AttnArgs a{};
+    a.block_table = pages->block_table; a.max_blocks = pages->max_blocks_per_seq;
+    a.row_seq = rows->row_seq; a.row_pos = rows->row_pos; a.num_rows = rows->num_rows;
+    a.q = q; a.H = H; a.D = kv->dim; a.d_v = d_v; a.scale_log2 = sm_scale * 1.4426950408889634f;
+    a.m = m; a.kv_dtype = kv->dtype; a.kv_data = kv->data; a.kv_scale = kv->scale;
+    a.topk = topk_idx; a.k = topk_idx ? k : 0;
+    a.win_dtype = win->dtype; a.win_data = win->data; a.win_scale = win->scale; a.win_cap = win->capacity;
+    a.window = win->window;
+    a.out_dtype = out_dtype; a.out = out; a.lse = lse;
+    a.nsplit = plan.nsplit; a.split_keys = plan.split_keys;
+    if (plan.nsplit > 1) {
+        size_t po = (size_t)rows->num_rows * plan.nsplit * H * d_v * sizeof(float);
+        po = (po + 255) & ~(size_t)255;
+        a.part_o = reinterpret_cast<float*>(ws);
+        a.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + po);
+    }
+    return hip_status(lcca::launch_sparse_attn(a, (hipStream_t)stream), "sparse_attn launch");
+}
+
+}  // extern "C"

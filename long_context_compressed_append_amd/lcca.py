@@ -1,0 +1,207 @@
+"""ctypes binding of liblcca.so (declared in include/lcca.h).
+
+Argument marshalling only: torch tensors supply device pointers, the current
+torch stream supplies the hipStream_t, and every computation runs in the
+library's gfx950 kernels.  There is no fallback: if the library cannot be
+loaded, every call raises.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblcca.so")
+
+EXPORTED = ("lcca_compress_append", "lcca_index_logits", "lcca_topk_select", "lcca_sparse_attn_fwd",
+            "lcca_sparse_attn_workspace_size", "lcca_status_string", "lcca_last_error", "lcca_version")
+
+
+class LccaError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__("lcca status %d: %s" % (status, detail))
+        self.status = status
+
+
+class _Pages(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32), ("block_table", ctypes.c_void_p)]
+
+
+class _Rows(ctypes.Structure):
+    _fields_ = [("num_rows", ctypes.c_int32), ("max_pos", ctypes.c_int32), ("row_seq", ctypes.c_void_p),
+                ("row_pos", ctypes.c_void_p)]
+
+
+class _PagedCache(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("dim", ctypes.c_int32), ("ratio_m", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("data", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+
+
+class _WindowCache(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("dim", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("data", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+
+
+class _Remainder(ctypes.Structure):
+    _fields_ = [("tok_dtype", ctypes.c_int32), ("kv", ctypes.c_void_p), ("ik", ctypes.c_void_p),
+                ("kv_logit", ctypes.c_void_p), ("ik_logit", ctypes.c_void_p)]
+
+
+_LIB = None
+
+
+def lib():
+    """Load liblcca.so (built in-tree; compiled first only if absent)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        PP, PR, PC, PW, PM = (ctypes.POINTER(_Pages), ctypes.POINTER(_Rows), ctypes.POINTER(_PagedCache),
+                              ctypes.POINTER(_WindowCache), ctypes.POINTER(_Remainder))
+        L.lcca_compress_append.argtypes = [P, PP, P, P, i32, i32, P, P, P, P, PC, PC, PW, PM]
+        L.lcca_index_logits.argtypes = [P, PP, PR, i32, P, i32, P, f32, PC, P, i64]
+        L.lcca_topk_select.argtypes = [P, PR, i32, P, i64, i32, P, P, sz]
+        L.lcca_sparse_attn_fwd.argtypes = [P, PP, PR, i32, P, i32, i32, f32, PC, P, i32, PW, i32, P, P, P, sz]
+        L.lcca_sparse_attn_workspace_size.argtypes = [PR, i32, i32, i32, i32, i32, i32, i32]
+        L.lcca_sparse_attn_workspace_size.restype = sz
+        for n in ("lcca_compress_append", "lcca_index_logits", "lcca_topk_select", "lcca_sparse_attn_fwd"):
+            getattr(L, n).restype = i32
+        L.lcca_status_string.argtypes = [i32]
+        for n in ("lcca_status_string", "lcca_last_error", "lcca_version"):
+            getattr(L, n).restype = ctypes.c_char_p
+        _LIB = L
+    return _LIB
+
+
+def version():
+    return lib().lcca_version().decode()
+
+
+def _check(status):
+    if status != OK:
+        raise LccaError(status, lib().lcca_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    assert t.is_contiguous(), "lcca tensors must be contiguous"
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+# --------------------------------------------------------------------------
+# descriptors
+# --------------------------------------------------------------------------
+
+@dataclass
+class Pages:
+    block_table: torch.Tensor            # int32 [batch][max_blocks_per_seq]
+
+    def c(self):
+        b, mb = self.block_table.shape
+        return _Pages(b, mb, _ptr(self.block_table))
+
+
+@dataclass
+class Rows:
+    row_seq: torch.Tensor                # int32 [num_rows]
+    row_pos: torch.Tensor                # int32 [num_rows]
+    max_pos: int                         # host upper bound of row_pos
+
+    def c(self):
+        return _Rows(self.row_seq.numel(), int(self.max_pos), _ptr(self.row_seq), _ptr(self.row_pos))
+
+
+@dataclass
+class PagedCache:
+    dtype: int
+    dim: int
+    ratio_m: int
+    num_blocks: int
+    data: torch.Tensor                   # uint8 [num_blocks * E * row_bytes]
+    scale: Optional[torch.Tensor] = None
+
+    def c(self):
+        return _PagedCache(self.dtype, self.dim, self.ratio_m, self.num_blocks, _ptr(self.data), _ptr(self.scale))
+
+
+@dataclass
+class WindowCache:
+    dtype: int
+    dim: int
+    capacity: int
+    window: int
+    data: torch.Tensor                   # uint8 [batch * capacity * row_bytes]
+    scale: Optional[torch.Tensor] = None # float32 [batch * capacity] (FP8)
+
+    def c(self):
+        return _WindowCache(self.dtype, self.dim, self.capacity, self.window, _ptr(self.data), _ptr(self.scale))
+
+
+@dataclass
+class Remainder:
+    tok_dtype: int
+    kv: torch.Tensor
+    kv_logit: torch.Tensor
+    ik: Optional[torch.Tensor] = None
+    ik_logit: Optional[torch.Tensor] = None
+
+    def c(self):
+        return _Remainder(self.tok_dtype, _ptr(self.kv), _ptr(self.ik), _ptr(self.kv_logit), _ptr(self.ik_logit))
+
+
+def _ref(x):
+    return ctypes.byref(x) if x is not None else None
+
+
+# --------------------------------------------------------------------------
+# the four calls
+# --------------------------------------------------------------------------
+
+def compress_append(pages: Pages, cu_new, start_pos, total_new: int, tok_dtype: int, kv_tok, kv_logit,
+                    ik_tok, ik_logit, kv: PagedCache, ik: Optional[PagedCache], win: Optional[WindowCache],
+                    rem: Remainder, stream=None):
+    _check(lib().lcca_compress_append(
+        _stream(stream), ctypes.byref(pages.c()), _ptr(cu_new), _ptr(start_pos), int(total_new), tok_dtype,
+        _ptr(kv_tok), _ptr(kv_logit), _ptr(ik_tok), _ptr(ik_logit), ctypes.byref(kv.c()),
+        _ref(ik.c() if ik else None), _ref(win.c() if win else None), ctypes.byref(rem.c())))
+
+
+def index_logits(pages: Pages, rows: Rows, q_dtype: int, q_idx, HI: int, w_idx, s_I: float, ik: PagedCache,
+                 logits, ld: int, stream=None):
+    _check(lib().lcca_index_logits(_stream(stream), ctypes.byref(pages.c()), ctypes.byref(rows.c()), q_dtype,
+                                   _ptr(q_idx), HI, _ptr(w_idx), float(s_I), ctypes.byref(ik.c()), _ptr(logits),
+                                   int(ld)))
+
+
+def topk_select(rows: Rows, ratio_m: int, logits, ld: int, k: int, topk_idx, stream=None):
+    _check(lib().lcca_topk_select(_stream(stream), ctypes.byref(rows.c()), ratio_m, _ptr(logits), int(ld), k,
+                                  _ptr(topk_idx), None, 0))
+
+
+def sparse_attn_workspace_size(rows: Rows, ratio_m: int, H: int, dim: int, d_v: int, k: int, topk_given: bool,
+                               window: int) -> int:
+    return lib().lcca_sparse_attn_workspace_size(ctypes.byref(rows.c()), ratio_m, H, dim, d_v, k,
+                                                 1 if topk_given else 0, window)
+
+
+def sparse_attn_fwd(pages: Pages, rows: Rows, q_dtype: int, q, H: int, d_v: int, sm_scale: float, kv: PagedCache,
+                    topk_idx, k: int, win: WindowCache, out_dtype: int, out, lse=None, ws=None, stream=None):
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().lcca_sparse_attn_fwd(_stream(stream), ctypes.byref(pages.c()), ctypes.byref(rows.c()), q_dtype,
+                                      _ptr(q), H, d_v, float(sm_scale), ctypes.byref(kv.c()), _ptr(topk_idx), k,
+                                      ctypes.byref(win.c()), out_dtype, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes))

@@ -1,0 +1,94 @@
+"""The C ABI: the library loads, exports every function include/lcca.h
+declares, and rejects invalid arguments on the host before any launch
+(these calls return before touching the GPU, so they run anywhere)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_compressed_append_amd import lcca
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "lcca.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lcca_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = lcca.lib()
+    names = _declared()
+    assert set(names) == set(lcca.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+    assert "gfx950" in lcca.version()
+
+
+def test_status_strings():
+    L = lcca.lib()
+    for s in (0, -1, -2, -3, -4):
+        assert L.lcca_status_string(s)
+
+
+def _pool(dtype=lcca.BF16, dim=576, m=4, blocks=4, data=1):
+    return lcca._PagedCache(dtype, dim, m, blocks, data, None)
+
+
+def test_invalid_arguments_rejected_before_launch():
+    L = lcca.lib()
+    pages = lcca._Pages(1, 4, 1)
+    rows = lcca._Rows(1, 100, 1, 1)
+    ik = _pool(lcca.BF16, 128)
+    by = ctypes.byref
+    # NULL pages
+    assert L.lcca_index_logits(None, None, by(rows), lcca.BF16, 1, 64, 1, 1.0, by(ik), 1, 64) == lcca.ERR_INVALID_ARG
+    assert b"pages" in L.lcca_last_error()
+    # ld too small for the visible entries
+    assert L.lcca_index_logits(None, by(pages), by(rows), lcca.BF16, 1, 64, 1, 1.0, by(ik), 1, 10) == lcca.ERR_INVALID_ARG
+    # unsupported head count for the MFMA path
+    assert L.lcca_index_logits(None, by(pages), by(rows), lcca.BF16, 1, 48, 1, 1.0, by(ik), 1, 64) == lcca.ERR_UNSUPPORTED
+    # max_pos beyond the block table
+    far = lcca._Rows(1, 4 * 256, 1, 1)
+    assert L.lcca_index_logits(None, by(pages), by(far), lcca.BF16, 1, 64, 1, 1.0, by(ik), 1, 4096) == lcca.ERR_INVALID_ARG
+    # bad ratio
+    bad = _pool(lcca.BF16, 128, m=3)
+    assert L.lcca_index_logits(None, by(pages), by(rows), lcca.BF16, 1, 64, 1, 1.0, by(bad), 1, 64) == lcca.ERR_INVALID_ARG
+    # top-k: k < 1
+    assert L.lcca_topk_select(None, by(rows), 4, 1, 64, 0, 1, None, 0) == lcca.ERR_INVALID_ARG
+    # attention: workspace too small (16 rows of 64K context need key splits)
+    kv = _pool(lcca.BF16, 576, blocks=4096)
+    win = lcca._WindowCache(lcca.FP8_E4M3, 576, 128, 128, 1, 1)
+    pg = lcca._Pages(16, 256, 1)
+    rw = lcca._Rows(16, 65535, 1, 1)
+    need = L.lcca_sparse_attn_workspace_size(by(rw), 4, 64, 576, 576, 2048, 1, 128)
+    assert need > 0
+    st = L.lcca_sparse_attn_fwd(None, by(pg), by(rw), lcca.BF16, 1, 64, 576, 0.04, by(kv), 1, 2048, by(win),
+                                lcca.F32, 1, None, 1, need - 1)
+    assert st == lcca.ERR_WORKSPACE
+    # FP8 window without its scale array
+    win_ns = lcca._WindowCache(lcca.FP8_E4M3, 576, 128, 128, 1, None)
+    st = L.lcca_sparse_attn_fwd(None, by(pg), by(rw), lcca.BF16, 1, 64, 576, 0.04, by(kv), 1, 2048, by(win_ns),
+                                lcca.F32, 1, None, 1, need)
+    assert st == lcca.ERR_INVALID_ARG
+    # MXFP4 indexer pool is not a supported combination
+    rem = lcca._Remainder(lcca.BF16, 1, 1, 1, 1)
+    mx = _pool(lcca.MXFP4, 128)
+    mx.scale = 1
+    st = L.lcca_compress_append(None, by(pages), 1, 1, 1, lcca.BF16, 1, 1, 1, 1, by(kv), by(mx), None, by(rem))
+    assert st == lcca.ERR_UNSUPPORTED
+    # token dtype must match the remainder ring
+    rem32 = lcca._Remainder(lcca.F32, 1, 1, 1, 1)
+    st = L.lcca_compress_append(None, by(pages), 1, 1, 1, lcca.BF16, 1, 1, 1, 1, by(kv), by(ik), None, by(rem32))
+    assert st == lcca.ERR_INVALID_ARG
+
+
+def test_binding_raises_on_error():
+    import torch
+    t = torch.zeros(4, dtype=torch.int32)
+    rows = lcca.Rows(t, t, 100)
+    with pytest.raises(lcca.LccaError) as e:
+        lcca.topk_select(rows, 4, t, 10, 64, t, stream=0)
+    assert e.value.status == lcca.ERR_INVALID_ARG
