@@ -191,8 +191,11 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
         const bool none = m_new == -INFINITY;
         const float alpha = none ? 1.0f : exp2f(m_run - m_new);
         m_run = m_new;
+        // P for the value product as an unevaluated sum of two bf16 values
+        // (hi + lo carries 16 significant bits): a single bf16 P would put a
+        // relative error of 2^-9 on every value it weights.
         float psum = 0.0f;
-        uint32_t pk[4];
+        uint32_t pk[4], pl[4];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -201,30 +204,34 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
                 float p0 = none ? 0.0f : exp2f(x[kt][v] - m_new);
                 float p1 = none ? 0.0f : exp2f(x[kt][v + 1] - m_new);
                 psum += p0 + p1;
-                pk[kt * 2 + v / 2] = pack_bf16x2(p0 * kscale[kk], p1 * kscale[kk + 1]);
+                const float w0 = p0 * kscale[kk], w1 = p1 * kscale[kk + 1];
+                const uint32_t h = pack_bf16x2(w0, w1);
+                pk[kt * 2 + v / 2] = h;
+                pl[kt * 2 + v / 2] = pack_bf16x2(w0 - bf16_to_f32(h & 0xffffu), w1 - bf16_to_f32(h >> 16));
             }
         l_run = l_run * alpha + psum;
         const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+        const bf16x8 pbl = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
 
-        // 4. O^T += V^T P^T; lane (dim dt*16 + c16, g) needs keys 4g..4g+3 and 16+4g..16+4g+3
+        // 4. O^T += V^T P^T; lane (dim dt*16 + c16, g) needs keys 4g..4g+3 and 16+4g..16+4g+3.
+        // ds_read_b64_tr_b16 within each 16-lane block hands lane i element (i & 3) of
+        // the 8-byte chunk addressed by lane (i >> 2) + 4e, for e = 0..3: lane s of the
+        // block addresses key 4g + (s >> 2), dims dt*16 + 4(s & 3) .. +3, so lane i
+        // receives keys 4g + e at dim dt*16 + i.
+        const uint8_t* vbase = lds + (4 * g + (c16 >> 2)) * T::ROWB + 8 * (c16 & 3);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const uint8_t* col = lds + (dt * 16 + c16) * 2;
-            uint32_t vv[4];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int k0 = 16 * h + 4 * g;
-                uint32_t e0 = *reinterpret_cast<const uint16_t*>(col + (k0 + 0) * T::ROWB);
-                uint32_t e1 = *reinterpret_cast<const uint16_t*>(col + (k0 + 1) * T::ROWB);
-                uint32_t e2 = *reinterpret_cast<const uint16_t*>(col + (k0 + 2) * T::ROWB);
-                uint32_t e3 = *reinterpret_cast<const uint16_t*>(col + (k0 + 3) * T::ROWB);
-                vv[2 * h] = e0 | (e1 << 16);
-                vv[2 * h + 1] = e2 | (e3 << 16);
-            }
-            const bf16x8 vA = __builtin_bit_cast(bf16x8, u32x4{vv[0], vv[1], vv[2], vv[3]});
+            const uint8_t* p0 = vbase + dt * 32;
+            i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0));
+            i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(p0 + 16 * T::ROWB));
+            const bf16x8 vA = __builtin_bit_cast(
+                bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                              __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
             o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pb, o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pbl, o[dt], 0, 0, 0);
         }
         __syncthreads();
     }
