@@ -214,8 +214,11 @@ lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_
  *   lse      device float [num_rows][H] or NULL
  *   ws       device workspace of at least lcca_sparse_attn_workspace_size()
  *            bytes for the same arguments (may be NULL if that size is 0)
- * BF16 path: kv dtype BF16 or MXFP4, window BF16 or FP8, H % 16 == 0 (<= 64
- * per workgroup), kv->dim % 32 == 0, d_v <= kv->dim.
+ * BF16 path: kv dtype BF16 or MXFP4, window BF16 or FP8, H a multiple of 64
+ * (64 heads per workgroup), (dim, d_v) in {(576, 576), (576, 512), (128, 128)};
+ * with top-k indices, positions below 2^20 (the block-table range a
+ * workgroup caches); an FP8 window's scale array must be given.  Other
+ * combinations return LCCA_ERR_UNSUPPORTED.
  */
 lcca_status lcca_sparse_attn_fwd(void* stream, const lcca_pages* pages, const lcca_rows* rows,
                                  int32_t q_dtype, const void* q, int32_t H, int32_t d_v, float sm_scale,

@@ -24,6 +24,12 @@ DEVICE = ["-x", "hip", "--offload-arch=" + ARCH, "-Xclang", "-target-feature", "
           "-fno-gpu-rdc"]
 
 
+# Per-file device flags.  The attention kernels keep their MFMA accumulators
+# in architectural VGPRs (the online-softmax rescale is VALU work on them);
+# AGPRs then serve as spill space instead of scratch memory.
+EXTRA = {"sparse_attn.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"]}
+
+
 def sources():
     out = []
     for f in sorted(os.listdir(CSRC)):
@@ -37,7 +43,7 @@ def sources():
 def _compile(item, verbose):
     src, device = item
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + (DEVICE if device else []) + COMMON + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + (DEVICE if device else []) + EXTRA.get(os.path.basename(src), []) + COMMON + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

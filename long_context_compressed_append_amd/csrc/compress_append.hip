@@ -2,21 +2,27 @@
 // softmax-weighted sum (one scalar logit per token), encode it into the paged
 // pool, write new tokens into the window ring and the remainder ring.
 //
-// [P1 = page "vLLM uveo DeepSeek V4 s 8,7x manjim KV cacheom", section
-//  "Kako funkcionira optimizacija KV cachea?": tokens are aggregated by
-//  weighted summation (4x to 128x); section "Sto je vLLM morao rijesiti u
+// [Page "vLLM uveo DeepSeek V4 s 8,7x manjim KV cacheom", section "Kako
+//  funkcionira optimizacija KV cachea?": tokens are aggregated by weighted
+//  summation (4x to 128x); section "Sto je vLLM morao rijesiti u
 //  integraciji?": 256-position logical blocks per layer, remainder of the
 //  compressor kept as sliding-window state.]
 //
-// One workgroup per new token (HBM/latency bound, no reuse to exploit):
-//   * if the token is among the last `capacity` of its sequence's chunk, it is
-//     encoded into the window ring;
-//   * if it completes a group (pos+1 multiple of m), the block aggregates the
-//     group (tokens older than the chunk come from the remainder ring) for the
-//     KV stream and the indexer-key stream and stores both entries;
-//   * exactly one block per sequence writes the chunk's incomplete tail into
-//     the remainder ring: the block that read the ring (if any), after its
-//     reads, so no other block can observe a half-updated ring.
+// Grid: (new token t, slice s).  Slices 0 .. SK-1 cover 64-dimension blocks
+// of the shared-KV stream, SK .. SK+SI-1 those of the indexer-key stream.
+//   * A token that completes group g makes each of its slices aggregate the
+//     slice's 64 dimensions of the group: 256 threads = 32 token lanes x 8
+//     dimension chunks of 8, every lane loading its tokens with 16-byte loads
+//     (all in flight together), then a reduction over the token lanes in LDS,
+//     the encode (bf16 / MXFP4 / FP8 / fp32) and the store into the pool.
+//   * Slice 0 of every token writes it into the window ring if it is among
+//     the last `capacity` tokens of its chunk (FP8 with a per-token scale).
+//   * Remainder ring: each token of the chunk's incomplete tail is written by
+//     its own slice 0.  One case needs ordering: a chunk that starts inside a
+//     group, completes that group and ends inside a later group reads ring
+//     slots it also rewrites.  Then slice 0 of the token completing the first
+//     group aggregates that whole group (all slices, both streams) and writes
+//     the tail after its reads.
 #include "device.h"
 #include "kernels.h"
 
@@ -25,7 +31,10 @@ namespace lcca {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxPairsPerThread = 4;        // dim <= 2048
+constexpr int kSliceDims = 64;               // dimensions per slice
+constexpr int kChunk = 8;                    // dimensions per thread
+constexpr int kLanes = kThreads / (kSliceDims / kChunk);   // token lanes = 32
+constexpr int kMaxPairsPerThread = 4;        // window encode: dim <= 2048
 
 template <int TOK>
 __device__ inline void load_pair(const void* base, int64_t elem, float& x0, float& x1) {
@@ -35,6 +44,21 @@ __device__ inline void load_pair(const void* base, int64_t elem, float& x0, floa
     } else {
         uint32_t v = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(base) + elem);
         x0 = bf16_to_f32(v & 0xffffu); x1 = bf16_to_f32(v >> 16);
+    }
+}
+
+// Eight consecutive token values starting at element `elem` (multiple of 8).
+template <int TOK>
+__device__ inline void load8(const void* base, int64_t elem, float (&x)[kChunk]) {
+    if (TOK == DT_F32) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + elem);
+        const f32x4 a = p[0], b = p[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+    } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[2 * i] = bf16_to_f32(v[i] & 0xffffu); x[2 * i + 1] = bf16_to_f32(v[i] >> 16); }
     }
 }
 
@@ -50,109 +74,160 @@ __device__ inline float block_max(float v, float* red) {
     return r;
 }
 
-// Store one (even, odd) channel pair of row `row` in pool/ring dtype `dt`.
-// MXFP4 needs the 16 threads of a 32-channel block to be active together;
-// `amax32` is their shared block maximum.
-__device__ inline void store_pair(int dt, uint8_t* data, uint8_t* scale_mx, int64_t row, int dim, int pair,
-                                  float x0, float x1) {
-    switch (dt) {
-    case DT_F32:
-        *reinterpret_cast<float2*>(data + row * 4LL * dim + 8LL * pair) = make_float2(x0, x1);
-        break;
-    case DT_BF16:
-        *reinterpret_cast<uint32_t*>(data + row * 2LL * dim + 4LL * pair) = pack_bf16x2(x0, x1);
-        break;
-    case DT_FP8:
-        *reinterpret_cast<uint16_t*>(data + row * (int64_t)dim + 2LL * pair) =
-            (uint16_t)(f32_to_fp8(x0) | (f32_to_fp8(x1) << 8));
-        break;
-    case DT_MXFP4: {
-        float a = fmaxf(fabsf(x0), fabsf(x1));
-        for (int o = 8; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));   // 16 lanes = 32 channels
-        int X = mx_scale_exp(a);
-        uint32_t c0 = fp4_code(ldexpf(x0, -X)), c1 = fp4_code(ldexpf(x1, -X));
-        data[row * (int64_t)(dim / 2) + pair] = (uint8_t)(c0 | (c1 << 4));
-        if ((pair & 15) == 0) scale_mx[row * (int64_t)(dim / 32) + pair / 16] = (uint8_t)(X + 127);
-        break;
-    }
-    }
+// Store one (even, odd) channel pair of row `row` in window dtype `dt`
+// (F32 or BF16).
+__device__ inline void store_pair(int dt, uint8_t* data, int64_t row, int dim, int pair, float x0, float x1) {
+    if (dt == DT_F32) *reinterpret_cast<float2*>(data + row * 4LL * dim + 8LL * pair) = make_float2(x0, x1);
+    else *reinterpret_cast<uint32_t*>(data + row * 2LL * dim + 4LL * pair) = pack_bf16x2(x0, x1);
 }
 
+struct SeqChunk {
+    int b, start, end, n;
+    int64_t c0;
+};
+
+__device__ inline SeqChunk seq_of(const CompressArgs& p, int t) {
+    // sequence of token t: the largest b with cu_new[b] <= t
+    int lo = 0, hi = p.batch - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.cu_new[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    SeqChunk q;
+    q.b = lo;
+    q.c0 = p.cu_new[lo];
+    q.n = p.cu_new[lo + 1] - (int)q.c0;
+    q.start = p.start_pos[lo];
+    q.end = q.start + q.n;
+    return q;
+}
+
+// Aggregate dimensions [d0, d0 + 64) of group g of one stream and store them.
+// w_lds must already hold the group's softmax weights.
 template <int TOK>
-__device__ void compress_group(const CompressArgs& p, int b, int64_t c0, int start, int g, bool ik_stream,
-                               float* w_lds) {
+__device__ void compress_slice(const CompressArgs& p, const SeqChunk& q, int g, bool ik_stream, int d0,
+                               const float* w_lds, float* red) {
     const int m = p.m;
     const int dim = ik_stream ? p.dI : p.D;
     const void* tok = ik_stream ? p.ik_tok : p.kv_tok;
-    const float* lg = ik_stream ? p.ik_logit : p.kv_logit;
     const void* rtok = ik_stream ? p.rem_ik : p.rem_kv;
-    const float* rlg = ik_stream ? p.rem_ik_logit : p.rem_kv_logit;
     const int tid = threadIdx.x;
+    const int lane = tid / (kSliceDims / kChunk), ch = tid % (kSliceDims / kChunk);
+    const int d = d0 + ch * kChunk;
+    const bool active = d < dim;
 
-    // softmax weights of the group's m logits (m <= 256)
-    __syncthreads();
-    if (tid < m) {
-        int t = g * m + tid;
-        w_lds[tid] = t >= start ? lg[c0 + (t - start)] : rlg[(int64_t)b * m + t % m];
+    float acc[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) acc[i] = 0.0f;
+    if (active) {
+        for (int i = lane; i < m; i += kLanes) {
+            const int t = g * m + i;
+            float x[kChunk];
+            if (t >= q.start) load8<TOK>(tok, (q.c0 + (t - q.start)) * dim + d, x);
+            else load8<TOK>(rtok, ((int64_t)q.b * m + t % m) * dim + d, x);
+            const float w = w_lds[i];
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+        }
     }
+    // reduce over the token lanes: red[lane][64]
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) red[lane * kSliceDims + ch * kChunk + e] = acc[e];
     __syncthreads();
-    if (tid < 64) {
-        float mx = -INFINITY;
-        for (int i = tid; i < m; i += 64) mx = fmaxf(mx, w_lds[i]);
-        mx = wave_max(mx);
-        float s = 0.0f;
-        for (int i = tid; i < m; i += 64) s += expf(w_lds[i] - mx);
-        s = wave_sum(s);
-        for (int i = tid; i < m; i += 64) w_lds[i] = expf(w_lds[i] - mx) / s;
+    float v = 0.0f;
+    const int dd = tid;                                        // dimension d0 + dd, threads < 64
+    if (tid < kSliceDims) {
+        for (int l = 0; l < kLanes; ++l) v += red[l * kSliceDims + dd];
     }
-    __syncthreads();
-
-    const int pairs = dim / 2;
+    // encode and store (threads < 64 hold one dimension each)
     const int E = 256 / m;
-    const int64_t blk = p.block_table[(int64_t)b * p.max_blocks + g / E];
-    const int64_t row = blk * E + g % E;
+    const int64_t row = (int64_t)p.block_table[(int64_t)q.b * p.max_blocks + g / E] * E + g % E;
     const int dt = ik_stream ? p.ik_dtype : p.kv_dtype;
     uint8_t* data = reinterpret_cast<uint8_t*>(ik_stream ? p.ik_data : p.kv_data);
-    uint8_t* scale = reinterpret_cast<uint8_t*>(ik_stream ? p.ik_scale : p.kv_scale);
-    for (int pr = tid; pr < pairs; pr += kThreads) {
-        float a0 = 0.0f, a1 = 0.0f;
-        for (int i = 0; i < m; ++i) {
-            int t = g * m + i;
-            float x0, x1;
-            if (t >= start) load_pair<TOK>(tok, (c0 + (t - start)) * dim + 2 * pr, x0, x1);
-            else load_pair<TOK>(rtok, ((int64_t)b * m + t % m) * dim + 2 * pr, x0, x1);
-            const float w = w_lds[i];
-            a0 = fmaf(w, x0, a0);
-            a1 = fmaf(w, x1, a1);
+    if (tid < kSliceDims) {
+        const int dim_i = d0 + dd;
+        const bool in = dim_i < dim;
+        if (dt == DT_MXFP4) {
+            // blocks of 32 dimensions = the two half-waves of wave 0
+            float a = in ? fabsf(v) : 0.0f;
+            for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+            const int X = mx_scale_exp(a);
+            const uint32_t c = fp4_code(ldexpf(v, -X));
+            const uint32_t c_hi = __shfl_down(c, 1);
+            if (in && (dim_i & 1) == 0) data[row * (int64_t)(dim / 2) + dim_i / 2] = (uint8_t)(c | (c_hi << 4));
+            if (in && (dim_i & 31) == 0)
+                reinterpret_cast<uint8_t*>(p.kv_scale)[row * (int64_t)(dim / 32) + dim_i / 32] = (uint8_t)(X + 127);
+        } else if (in) {
+            if (dt == DT_F32) reinterpret_cast<float*>(data)[row * dim + dim_i] = v;
+            else if (dt == DT_BF16) reinterpret_cast<uint16_t*>(data)[row * dim + dim_i] = (uint16_t)f32_to_bf16(v);
+            else data[row * (int64_t)dim + dim_i] = (uint8_t)f32_to_fp8(v);
         }
-        store_pair(dt, data, scale, row, dim, pr, a0, a1);
+    }
+    __syncthreads();                                           // red is reused by the next slice
+}
+
+// Softmax weights of group g of one stream into w_lds (m <= 256).
+__device__ void group_weights(const CompressArgs& p, const SeqChunk& q, int g, bool ik_stream, float* w_lds,
+                              float* red) {
+    const int m = p.m;
+    const float* lg = ik_stream ? p.ik_logit : p.kv_logit;
+    const float* rlg = ik_stream ? p.rem_ik_logit : p.rem_kv_logit;
+    const int tid = threadIdx.x;
+    float a = -INFINITY;
+    if (tid < m) {
+        const int t = g * m + tid;
+        a = t >= q.start ? lg[q.c0 + (t - q.start)] : rlg[(int64_t)q.b * m + t % m];
+    }
+    float mx = wave_max(a);
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float e = tid < m ? expf(a - mx) : 0.0f;
+    float s = wave_sum(e);
+    __syncthreads();
+    if ((tid & 63) == 0) red[4 + (tid >> 6)] = s;
+    __syncthreads();
+    s = red[4] + red[5] + red[6] + red[7];
+    if (tid < m) w_lds[tid] = e / s;
+    __syncthreads();
+}
+
+template <int TOK>
+__device__ void write_ring(const CompressArgs& p, const SeqChunk& q, int tt) {
+    const int m = p.m;
+    const int esz = TOK == DT_F32 ? 4 : 2;
+    const int64_t src = q.c0 + (tt - q.start);
+    const int64_t slot = (int64_t)q.b * m + tt % m;
+    const uint8_t* s8 = reinterpret_cast<const uint8_t*>(p.kv_tok) + src * p.D * esz;
+    uint8_t* d8 = reinterpret_cast<uint8_t*>(p.rem_kv) + slot * p.D * esz;
+    for (int i = threadIdx.x; i < p.D * esz / 4; i += kThreads)
+        reinterpret_cast<uint32_t*>(d8)[i] = reinterpret_cast<const uint32_t*>(s8)[i];
+    if (threadIdx.x == 0) p.rem_kv_logit[slot] = p.kv_logit[src];
+    if (p.ik_data != nullptr) {
+        const uint8_t* si = reinterpret_cast<const uint8_t*>(p.ik_tok) + src * p.dI * esz;
+        uint8_t* di = reinterpret_cast<uint8_t*>(p.rem_ik) + slot * p.dI * esz;
+        for (int i = threadIdx.x; i < p.dI * esz / 4; i += kThreads)
+            reinterpret_cast<uint32_t*>(di)[i] = reinterpret_cast<const uint32_t*>(si)[i];
+        if (threadIdx.x == 0) p.rem_ik_logit[slot] = p.ik_logit[src];
     }
 }
 
 template <int TOK>
 __global__ __launch_bounds__(kThreads) void compress_append_kernel(CompressArgs p) {
     __shared__ float w_lds[256];
-    __shared__ float red[kThreads / 64];
-    const int t = blockIdx.x;
+    __shared__ float red[kLanes * kSliceDims];
+    const int t = blockIdx.x, s = blockIdx.y;
     const int tid = threadIdx.x;
-    // sequence of this token: the largest b with cu_new[b] <= t
-    int lo = 0, hi = p.batch - 1;
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (p.cu_new[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int b = lo;
-    const int64_t c0 = p.cu_new[b];
-    const int n = p.cu_new[b + 1] - (int)c0;
-    const int start = p.start_pos[b];
-    const int end = start + n;
-    const int pos = start + (t - (int)c0);
-    const int m = p.m;
-    const int D = p.D;
+    const SeqChunk q = seq_of(p, t);
+    const int pos = q.start + (t - (int)q.c0);
+    const int m = p.m, D = p.D;
+    const int SK = (D + kSliceDims - 1) / kSliceDims;
+    const int SI = p.ik_data != nullptr ? (p.dI + kSliceDims - 1) / kSliceDims : 0;
 
     // (1) window ring
-    if (p.win_data != nullptr && pos >= end - p.win_cap) {
-        const int64_t slot = (int64_t)b * p.win_cap + pos % p.win_cap;
+    if (s == 0 && p.win_data != nullptr && pos >= q.end - p.win_cap) {
+        const int64_t slot = (int64_t)q.b * p.win_cap + pos % p.win_cap;
         uint8_t* wd = reinterpret_cast<uint8_t*>(p.win_data);
         const int pairs = D / 2;
         if (p.win_dtype == DT_FP8) {
@@ -160,19 +235,19 @@ __global__ __launch_bounds__(kThreads) void compress_append_kernel(CompressArgs 
             float amax = 0.0f;
 #pragma unroll
             for (int i = 0; i < kMaxPairsPerThread; ++i) {
-                int pr = tid + i * kThreads;
+                const int pr = tid + i * kThreads;
                 x0[i] = x1[i] = 0.0f;
                 if (pr < pairs) load_pair<TOK>(p.kv_tok, (int64_t)t * D + 2 * pr, x0[i], x1[i]);
                 amax = fmaxf(amax, fmaxf(fabsf(x0[i]), fabsf(x1[i])));
             }
             amax = block_max(amax, red);
-            const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-            if (tid == 0) p.win_scale[slot] = s;
+            const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+            if (tid == 0) p.win_scale[slot] = sc;
 #pragma unroll
             for (int i = 0; i < kMaxPairsPerThread; ++i) {
-                int pr = tid + i * kThreads;
+                const int pr = tid + i * kThreads;
                 if (pr < pairs) {
-                    uint32_t c = f32_to_fp8(x0[i] / s) | (f32_to_fp8(x1[i] / s) << 8);
+                    const uint32_t c = f32_to_fp8(x0[i] / sc) | (f32_to_fp8(x1[i] / sc) << 8);
                     *reinterpret_cast<uint16_t*>(wd + slot * D + 2 * pr) = (uint16_t)c;
                 }
             }
@@ -180,53 +255,51 @@ __global__ __launch_bounds__(kThreads) void compress_append_kernel(CompressArgs 
             for (int pr = tid; pr < pairs; pr += kThreads) {
                 float x0, x1;
                 load_pair<TOK>(p.kv_tok, (int64_t)t * D + 2 * pr, x0, x1);
-                store_pair(p.win_dtype, wd, nullptr, slot, D, pr, x0, x1);
+                store_pair(p.win_dtype, wd, slot, D, pr, x0, x1);
             }
         }
     }
 
-    // (2) group completed by this token
+    // (2) the group this token completes
+    const int g0 = q.start / m;                                // group holding `start`
+    const bool race = (q.start % m) != 0 && (q.end % m) != 0 && q.end >= (g0 + 1) * m;
+    const int tail0 = max((q.end / m) * m, q.start);
     if ((pos + 1) % m == 0) {
         const int g = pos / m;
-        compress_group<TOK>(p, b, c0, start, g, false, w_lds);
-        if (p.ik_data != nullptr) compress_group<TOK>(p, b, c0, start, g, true, w_lds);
-    }
-
-    // (3) remainder ring: the incomplete tail of the chunk
-    const int g0_end = (start / m + 1) * m;                    // end of the group holding `start`
-    const int writer = (start % m != 0 && end >= g0_end) ? g0_end - 1 : start;
-    if (pos == writer) {
-        __syncthreads();                                       // ring reads of step (2) are done
-        int tail0 = (end / m) * m;
-        if (tail0 < start) tail0 = start;
-        const int esz = TOK == DT_F32 ? 4 : 2;
-        for (int tt = tail0; tt < end; ++tt) {
-            const int64_t src = c0 + (tt - start);
-            const int64_t slot = (int64_t)b * m + tt % m;
-            const uint8_t* s8 = reinterpret_cast<const uint8_t*>(p.kv_tok) + src * D * esz;
-            uint8_t* d8 = reinterpret_cast<uint8_t*>(p.rem_kv) + slot * D * esz;
-            for (int i = tid; i < D * esz / 4; i += kThreads)
-                reinterpret_cast<uint32_t*>(d8)[i] = reinterpret_cast<const uint32_t*>(s8)[i];
-            if (tid == 0) p.rem_kv_logit[slot] = p.kv_logit[src];
-            if (p.ik_data != nullptr) {
-                const uint8_t* si = reinterpret_cast<const uint8_t*>(p.ik_tok) + src * p.dI * esz;
-                uint8_t* di = reinterpret_cast<uint8_t*>(p.rem_ik) + slot * p.dI * esz;
-                for (int i = tid; i < p.dI * esz / 4; i += kThreads)
-                    reinterpret_cast<uint32_t*>(di)[i] = reinterpret_cast<const uint32_t*>(si)[i];
-                if (tid == 0) p.rem_ik_logit[slot] = p.ik_logit[src];
+        if (race && g == g0) {
+            // whole first group here, then the tail of the chunk into the ring
+            if (s == 0) {
+                group_weights(p, q, g, false, w_lds, red);
+                for (int k = 0; k < SK; ++k) compress_slice<TOK>(p, q, g, false, k * kSliceDims, w_lds, red);
+                if (SI) {
+                    group_weights(p, q, g, true, w_lds, red);
+                    for (int k = 0; k < SI; ++k) compress_slice<TOK>(p, q, g, true, k * kSliceDims, w_lds, red);
+                }
+                __syncthreads();
+                for (int tt = tail0; tt < q.end; ++tt) write_ring<TOK>(p, q, tt);
             }
+        } else if (s < SK + SI) {
+            const bool ik = s >= SK;
+            group_weights(p, q, g, ik, w_lds, red);
+            compress_slice<TOK>(p, q, g, ik, (ik ? s - SK : s) * kSliceDims, w_lds, red);
         }
     }
+
+    // (3) remainder ring: each tail token writes itself (see the header comment for `race`)
+    if (s == 0 && !race && pos >= tail0) write_ring<TOK>(p, q, pos);
 }
 
 }  // namespace
 
 hipError_t launch_compress_append(const CompressArgs& a, int total_new, hipStream_t stream) {
     if (total_new <= 0) return hipSuccess;
+    const int SK = (a.D + kSliceDims - 1) / kSliceDims;
+    const int SI = a.ik_data != nullptr ? (a.dI + kSliceDims - 1) / kSliceDims : 0;
+    dim3 grid(total_new, SK + SI);
     if (a.tok_dtype == DT_F32)
-        hipLaunchKernelGGL(compress_append_kernel<DT_F32>, dim3(total_new), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(compress_append_kernel<DT_F32>, grid, dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL(compress_append_kernel<DT_BF16>, dim3(total_new), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(compress_append_kernel<DT_BF16>, grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

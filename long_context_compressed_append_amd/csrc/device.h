@@ -57,12 +57,14 @@ __device__ inline uint32_t f32_to_fp8(float x) {
     return sign | ((uint32_t)(e + 7) << 3) | m3;
 }
 
-// E4M3 code -> bf16 bits (exact: 3 mantissa bits fit in bf16's 7).
+// E4M3 code -> bf16 bits (exact: 3 mantissa bits fit in bf16's 7).  Branch
+// free: subnormal codes (exponent field 0) are m * 2^-9, formed in fp32.
 __device__ inline uint32_t fp8_to_bf16(uint32_t c) {
-    uint32_t s = (c & 0x80u) << 8;
-    uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    if (e == 0) return s | (__float_as_uint((float)m * 0.001953125f) >> 16);   // m * 2^-9
-    return s | ((e + 120u) << 7) | (m << 4);
+    const uint32_t s = (c & 0x80u) << 8;
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const uint32_t normal = ((e + 120u) << 7) | (m << 4);
+    const uint32_t sub = __float_as_uint((float)m * 0.001953125f) >> 16;
+    return s | (e == 0 ? sub : normal);
 }
 
 __device__ inline float fp8_to_f32(uint32_t c) { return bf16_to_f32(fp8_to_bf16(c)); }
@@ -97,16 +99,38 @@ __device__ inline int mx_scale_exp(float amax) {
     return X < -127 ? -127 : (X > 127 ? 127 : X);
 }
 
-// E2M1 code -> bf16 bits of code * 2^X (exact while the result is a normal
-// bf16; the tiny/huge scale range goes through fp32 ldexp).
+// E2M1 code -> bf16 bits of code * 2^X.  The E2M1 magnitude (two significant
+// bits) is formed in fp32, scaled by v_ldexp_f32 (exact for every E8M0 scale
+// of fp32 data, subnormal results included) and truncated to bf16, which
+// drops only zero bits.  Branch free.
 __device__ inline uint32_t fp4_to_bf16(uint32_t nib, int X) {
-    // bf16 of the E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6
     const uint32_t mag = nib & 7u;
-    uint32_t b = mag == 0 ? 0u : mag == 1 ? 0x3f00u : (((mag >> 1) + 126u) << 7) | ((mag & 1u) << 6);
-    uint32_t s = (nib & 8u) << 12;
-    if (b == 0) return s;
-    if (X >= -125 && X <= 125) return s | (b + ((uint32_t)X << 7));
-    return s | (__float_as_uint(ldexpf(__uint_as_float(b << 16), X)) >> 16);
+    const uint32_t e = mag >> 1, mb = mag & 1u;
+    uint32_t fb = ((126u + e) << 23) | (mb << 22);             // (1 + mb/2) * 2^(e-1), e >= 1
+    fb = mag == 1u ? 0x3f000000u : fb;                         // 0.5
+    fb = mag == 0u ? 0u : fb;
+    const float v = ldexpf(__uint_as_float(fb), X);
+    return ((nib & 8u) << 12) | (__float_as_uint(v) >> 16);
+}
+
+// Eight E4M3 codes (two words) -> eight bf16 (four words).
+__device__ inline u32x4 fp8x8_to_bf16(uint32_t a, uint32_t b) {
+    return u32x4{fp8_to_bf16(a & 0xffu) | (fp8_to_bf16((a >> 8) & 0xffu) << 16),
+                 fp8_to_bf16((a >> 16) & 0xffu) | (fp8_to_bf16(a >> 24) << 16),
+                 fp8_to_bf16(b & 0xffu) | (fp8_to_bf16((b >> 8) & 0xffu) << 16),
+                 fp8_to_bf16((b >> 16) & 0xffu) | (fp8_to_bf16(b >> 24) << 16)};
+}
+
+// Eight E2M1 codes (one word, element 2i in the low nibble of byte i) with
+// shared exponent X -> eight bf16 (four words).
+__device__ inline u32x4 fp4x8_to_bf16(uint32_t w, int X) {
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t bb = w >> (8 * q);
+        o[q] = fp4_to_bf16(bb & 15u, X) | (fp4_to_bf16((bb >> 4) & 15u, X) << 16);
+    }
+    return o;
 }
 
 // ---------------------------------------------------------------------------

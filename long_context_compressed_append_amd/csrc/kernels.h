@@ -45,7 +45,7 @@ struct AttnArgs {
     int32_t win_dtype; const void* win_data; const float* win_scale; int32_t win_cap, window;
     int32_t out_dtype; void* out; float* lse;
     // split plan
-    int32_t nsplit, split_keys;
+    int32_t nsplit, split_tiles;       // key splits per row, 32-key tiles per split
     float* part_o;     // [rows][nsplit][H][d_v]   (nsplit > 1)
     float* part_ml;    // [rows][nsplit][2][H]
 };

@@ -14,6 +14,10 @@
 
 namespace lcca {
 int attn_f32_max_keys();
+int attn_max_split_tiles();
+int attn_max_splits();
+int attn_tile_keys();
+int attn_max_table_blocks();
 }
 
 namespace {
@@ -80,28 +84,35 @@ lcca_status check_window(const lcca_window_cache* w, int dim) {
 }
 
 struct AttnPlan {
-    int nsplit, split_keys;
+    int nsplit, split_tiles;
     size_t ws_bytes;
 };
 
-// Split the keys of each row across workgroups only when the rows alone
-// cannot fill the 256 compute units; tiles of 32 keys.
+// Split plan of the bf16 attention kernels.  A row's key list is its
+// selected part padded to whole 32-key tiles, then the window tiles.  Rows
+// are split into ranges of whole tiles across workgroups only when the rows
+// alone cannot fill the 256 compute units (and a split never exceeds the
+// kernel's per-split index cache); partial softmax states then go to the
+// workspace for the merge kernel.
 AttnPlan attn_plan(int rows, int max_pos, int m, int H, int d_v, int k, bool topk_given, int window) {
-    AttnPlan p{1, 32, 0};
+    AttnPlan p{1, 1, 0};
     if (rows <= 0) return p;
     const int64_t nvis = (int64_t)(max_pos + 1) / m;
-    const int64_t L = (topk_given ? (int64_t)k : nvis) + std::min<int64_t>(window, (int64_t)max_pos + 1);
-    const int64_t tiles = std::max<int64_t>(1, (L + 31) / 32);
+    const int64_t nsel = topk_given ? (int64_t)k : nvis;
+    const int64_t nwin = std::min<int64_t>(window, (int64_t)max_pos + 1);
+    const int64_t key_tiles = lcca::attn_tile_keys();
+    const int64_t tiles = std::max<int64_t>(1, (nsel + key_tiles - 1) / key_tiles + (nwin + key_tiles - 1) / key_tiles);
+    const int64_t max_tps = lcca::attn_max_split_tiles();
     constexpr int kTargetWorkgroups = 256;
-    if (rows >= kTargetWorkgroups / 2) {
-        p.nsplit = 1;
-        p.split_keys = (int)(tiles * 32);
-        return p;
+    int64_t tps = rows >= kTargetWorkgroups / 2 ? tiles : (tiles * rows + kTargetWorkgroups - 1) / kTargetWorkgroups;
+    tps = std::max<int64_t>(1, std::min<int64_t>(tps, max_tps));
+    int64_t nsplit = (tiles + tps - 1) / tps;
+    if (nsplit > lcca::attn_max_splits()) {
+        tps = (tiles + lcca::attn_max_splits() - 1) / lcca::attn_max_splits();
+        nsplit = (tiles + tps - 1) / tps;
     }
-    int64_t tps = (tiles * rows + kTargetWorkgroups - 1) / kTargetWorkgroups;
-    if (tps < 1) tps = 1;
-    p.split_keys = (int)(tps * 32);
-    p.nsplit = (int)((tiles + tps - 1) / tps);
+    p.nsplit = (int)nsplit;
+    p.split_tiles = (int)tps;
     if (p.nsplit > 1) {
         size_t po = (size_t)rows * p.nsplit * H * d_v * sizeof(float);
         po = (po + 255) & ~(size_t)255;
@@ -152,7 +163,7 @@ lcca_status lcca_compress_append(void* stream, const lcca_pages* pages, const in
     if (ik && ik->dtype == LCCA_FP8_E4M3 && ik->scale)
         return fail(LCCA_ERR_UNSUPPORTED, "FP8 ik pool with a scale array (raw E4M3 only)");
     if (ik && ik->ratio_m != kv->ratio_m) return fail(LCCA_ERR_INVALID_ARG, "kv and ik ratio_m differ");
-    if (kv->dim % 2 || (ik && ik->dim % 2)) return fail(LCCA_ERR_UNSUPPORTED, "odd dims");
+    if (kv->dim % 8 || (ik && ik->dim % 8)) return fail(LCCA_ERR_UNSUPPORTED, "dims must be multiples of 8");
     if (kv->dim > 2048) return fail(LCCA_ERR_UNSUPPORTED, "kv dim %d > 2048", kv->dim);
     if (!rem || rem->tok_dtype != tok_dtype || !rem->kv || !rem->kv_logit || (ik && (!rem->ik || !rem->ik_logit)))
         return fail(LCCA_ERR_INVALID_ARG, "remainder ring missing or of another token dtype");
@@ -242,13 +253,19 @@ lcca_status lcca_sparse_attn_fwd(void* stream, const lcca_pages* pages, const lc
     const int m = kv->ratio_m;
     const bool f32 = q_dtype == LCCA_F32;
     AttnPlan plan = attn_plan(rows->num_rows, rows->max_pos, m, H, d_v, k, topk_idx != nullptr, win->window);
+    if (!f32 && topk_idx && ((int64_t)rows->max_pos + 1) / 256 + 1 > lcca::attn_max_table_blocks())
+        return fail(LCCA_ERR_UNSUPPORTED, "sparse_attn: positions up to %d need more than %d block-table entries",
+                    rows->max_pos, lcca::attn_max_table_blocks());
+    if (!f32 && plan.split_tiles > lcca::attn_max_split_tiles())
+        return fail(LCCA_ERR_UNSUPPORTED, "sparse_attn: %d key tiles per split needed (> %d)", plan.split_tiles,
+                    lcca::attn_max_split_tiles());
     if (f32) {
         const int64_t L = (topk_idx ? (int64_t)k : (int64_t)(rows->max_pos + 1) / m) +
                           std::min<int64_t>(win->window, (int64_t)rows->max_pos + 1);
         if (L > lcca::attn_f32_max_keys())
             return fail(LCCA_ERR_UNSUPPORTED, "fp32 attention: %lld keys per row > %d", (long long)L,
                         lcca::attn_f32_max_keys());
-        plan = AttnPlan{1, (int)L, 0};
+        plan = AttnPlan{1, 1, 0};
     }
     if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes))
         return fail(LCCA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, plan.ws_bytes);
@@ -261,7 +278,7 @@ lcca_status lcca_sparse_attn_fwd(void* stream, const lcca_pages* pages, const lc
     a.win_dtype = win->dtype; a.win_data = win->data; a.win_scale = win->scale; a.win_cap = win->capacity;
     a.window = win->window;
     a.out_dtype = out_dtype; a.out = out; a.lse = lse;
-    a.nsplit = plan.nsplit; a.split_keys = plan.split_keys;
+    a.nsplit = plan.nsplit; a.split_tiles = plan.split_tiles;
     if (plan.nsplit > 1) {
         size_t po = (size_t)rows->num_rows * plan.nsplit * H * d_v * sizeof(float);
         po = (po + 255) & ~(size_t)255;

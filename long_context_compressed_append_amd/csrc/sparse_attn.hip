@@ -1,32 +1,36 @@
 // sparse_attn_fwd: single-KV-head attention of H query heads over the
 // selected compressed entries plus the sliding window, one joint softmax.
 //
-// [P1 = page "vLLM uveo DeepSeek V4 s 8,7x manjim KV cacheom", section
-//  "Kako funkcionira optimizacija KV cachea?": shared KV vectors (one vector
-//  is key and value), attention restricted to the top-k compressed tokens,
-//  and a local window of full vectors for recent context.  P3 = page
-//  "DeepSeek-V4.1-Flash ve vLLM: kde se vzala 5,3x vyssi propustnost",
-//  section "Vykon neprinesl jeden kernel": the fused attention reads a 4-bit
-//  compressed cache; here MXFP4 (OCP) or bf16 entries and an FP8 or bf16
-//  window are dequantised while staging into LDS.]
+// [Page "vLLM uveo DeepSeek V4 s 8,7x manjim KV cacheom", section "Kako
+//  funkcionira optimizacija KV cachea?": shared KV vectors (one vector is key
+//  and value), attention restricted to the top-k compressed tokens, and a
+//  local window of full vectors for recent context.  Page "DeepSeek-V4.1-Flash
+//  ve vLLM: kde se vzala 5,3x vyssi propustnost", section "Vykon neprinesl
+//  jeden kernel": the fused attention reads a 4-bit compressed cache; here
+//  MXFP4 (OCP) or bf16 entries and an FP8 or bf16 window are upconverted
+//  exactly to bf16 on their way into LDS.]
 //
-// bf16/MFMA path.  A workgroup = (row, key split) with one wave per 16 query
-// heads.  Per 32-key tile:
-//   1. the workgroup gathers the tile (block table / window ring), converts
-//      it exactly to bf16 and stages it in LDS ([32][D] + pad);
-//   2. each wave computes S^T = K Q^T with MFMA 16x16x32 (A = keys from LDS,
-//      B = its heads' queries, resident in VGPRs), so every lane owns one
-//      head and 8 keys;
-//   3. online softmax in the exp2 domain, entirely per lane plus two
-//      cross-lane max/sum steps; FP8 window scales multiply the scores and
-//      are folded into P for the value product;
-//   4. O^T += V^T P^T with MFMA 16x16x32: the P operand is the softmax
-//      result already in the right registers, V^T is read from the same LDS
-//      tile (K = V) transposed; O^T stays in registers with one head per
-//      lane, so the softmax rescale is a per-lane multiply.
-// Keys are split across workgroups when there are too few rows to fill the
-// GPU; partial (max, sum, unnormalised O) states go to the workspace and a
-// merge kernel combines them exactly.
+// Key list of a row: the selected entries (topk slots, or every visible
+// entry), padded with masked slots to a multiple of 32, then the window
+// tokens.  So every 32-key tile holds either pool entries or window tokens.
+//
+// bf16/MFMA path.  A workgroup = (row, range of tiles, group of 64 heads)
+// with one wave per 16 query heads.  Pipeline per workgroup:
+//   prologue: the block-table range and the top-k indices the split needs are
+//     copied to LDS, so resolving a key to its storage row is two LDS reads;
+//   loads:    each tile's raw bytes (bf16, FP8 or MXFP4 + E8M0 scales) are
+//     loaded into registers P tiles ahead of their use (static register sets,
+//     loop unrolled by P), converted exactly to bf16 and written to one of two
+//     padded LDS stages; one barrier per tile;
+//   compute:  S^T = K Q^T with MFMA 16x16x32 (A = keys from LDS, B = the
+//     wave's queries, resident in VGPRs); online softmax per lane in the exp2
+//     domain; O^T += V^T P^T with V^T read from the same LDS tile by
+//     ds_read_b64_tr_b16 (K = V); P enters as bf16 hi + lo so the value
+//     weights keep 16 significant bits; FP8 window scales multiply the scores
+//     and are folded into P.
+// Keys are split across workgroups when the rows alone cannot fill the GPU;
+// the partial (max, sum, unnormalised O) states go to the workspace and a
+// merge kernel (one workgroup per row and head) combines them exactly.
 #include "device.h"
 #include "kernels.h"
 
@@ -35,18 +39,35 @@ namespace lcca {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kKeys = 32;              // keys per tile
 
-template <int D>
-struct Tile {
-    static constexpr int ROWB = D * 2 + 16;          // padded row: conflict-free 16-B reads across 16 rows
-    static constexpr int KEYS = 32;
-    static constexpr int CPK = D / 8;                // 16-byte bf16 chunks per key
+// LDS-typed pointers: stage addresses are formed in address space 3 so no
+// generic-to-LDS conversion is ever needed on a run-time selected pointer.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+
+template <int N>
+struct IntC {
+    static constexpr int value = N;
 };
 
-// Key list of a row: [selected entries (k slots, or every visible entry)] ++
-// [window tokens max(0, p-window+1) .. p].
+template <int D>
+struct Geo {
+    static constexpr int ROWB = D * 2 + 16;          // padded bf16 row: conflict-free 16-B reads over 16 rows
+    static constexpr int STAGE = kKeys * ROWB;
+    static constexpr int U16 = D / 8;                // 16-B bf16 units per key
+};
+
+// Row-level key geometry.
 struct RowKeys {
-    int b, p, n, nsel, t0, L;
+    int b, p, n;          // sequence, position, visible entries
+    int nsel;             // selected (or visible) entries in the list
+    int sel_tiles;        // tiles of the selected part (padded to 32)
+    int t0, nwin;         // first window position, window tokens
+    int tiles;            // total tiles of the row
 };
 
 __device__ inline RowKeys row_keys(const AttnArgs& a, int r) {
@@ -55,248 +76,390 @@ __device__ inline RowKeys row_keys(const AttnArgs& a, int r) {
     k.p = a.row_pos[r];
     k.n = visible_entries(k.p, a.m);
     k.nsel = a.topk ? a.k : k.n;
+    k.sel_tiles = (k.nsel + kKeys - 1) / kKeys;
     k.t0 = max(0, k.p - a.window + 1);
-    k.L = k.nsel + (k.p - k.t0 + 1);
+    k.nwin = k.p - k.t0 + 1;
+    k.tiles = k.sel_tiles + (k.nwin + kKeys - 1) / kKeys;
     return k;
 }
 
-// Resolve list position j to a storage row.  kind: 0 = invalid, 1 = pool
-// entry (row in the pool), 2 = window slot (row = b*cap + t % cap).
-__device__ inline void resolve_key(const AttnArgs& a, const RowKeys& rk, int r, int j, int j_end, int& kind,
-                                   int64_t& row) {
-    kind = 0;
-    row = 0;
-    if (j >= j_end) return;
-    if (j < rk.nsel) {
-        int g = a.topk ? a.topk[(int64_t)r * a.k + j] : j;
-        if (g < 0 || g >= rk.n) return;
-        const int E = 256 / a.m;
-        row = (int64_t)a.block_table[(int64_t)rk.b * a.max_blocks + g / E] * E + g % E;
-        kind = 1;
-    } else {
-        int t = rk.t0 + (j - rk.nsel);
-        row = (int64_t)rk.b * a.win_cap + t % a.win_cap;
-        kind = 2;
-    }
+// Storage row of slot j of the selected part (-1: masked).  The block-table
+// range of the split is in LDS.
+__device__ __forceinline__ int64_t pool_row(const AttnArgs& a, const RowKeys& rk, int j, const lds_i32* idx_lds, int idx0,
+                                            const lds_i32* bt_lds, int blk0) {
+    const int g = a.topk ? idx_lds[j - idx0] : j;
+    const bool ok = j < rk.nsel && g >= 0 && g < rk.n;
+    const int sh = __builtin_ctz(256 / a.m);                  // E = 256/m entries per block, a power of two
+    const int gc = ok ? g : blk0 << sh;
+    const int lb = gc >> sh;
+    const int pb = bt_lds[lb - blk0];
+    return ok ? ((int64_t)pb << sh) + (gc & ((1 << sh) - 1)) : -1;
 }
 
-template <int KVD, int WD, int D, int DV, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
-    using T = Tile<D>;
-    constexpr int NT = NW * 64;
-    constexpr int KS = D / 32;          // k-steps of S^T
-    constexpr int NDT = DV / 16;        // 16-dim tiles of O^T
-    __shared__ __attribute__((aligned(16))) uint8_t lds[T::KEYS * T::ROWB];
-    __shared__ int64_t src_row[T::KEYS];
-    __shared__ int src_kind[T::KEYS];
-    __shared__ float kscale[T::KEYS];
+// Tile staging.  Eight threads share a key: thread t stages key t / 8 (of
+// the 32 keys of a tile), 16-byte parts (t % 8) + 8i of its row, so each
+// thread resolves one storage row per tile and its loads and LDS writes
+// differ only by immediate offsets.  Raw bytes are loaded into registers
+// ahead of use and converted exactly to bf16 when they are written to LDS;
+// loaded values are consumed only then, so the loads stay in flight.
+constexpr int kThreadsPerKey = 8;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, c16 = lane & 15;
-    const int split = blockIdx.x, r = blockIdx.y;
-    const RowKeys rk = row_keys(a, r);
-    const int j_begin = split * a.split_keys;
-    if (j_begin >= rk.L) return;                                  // empty split (merge skips it)
-    const int j_end = min(j_begin + a.split_keys, rk.L);
-    const int head = wave * 16 + c16;
+template <int NU>
+struct TileRegs {
+    u32x4 v[NU];
+    uint32_t sc[NU];      // E8M0 scale of each MXFP4 part
+    float kscale;         // FP8 window scale of this thread's key (1 otherwise)
+    bool valid;           // this thread's key is not masked
+};
 
-    // Q^T as B operands: lane (head, g) holds dims [32s + 8g, +8)
+template <int KVD, int WD, int D, int NT>
+struct Tiler {
+    static_assert(NT == kKeys * kThreadsPerKey, "one workgroup stages one tile");
+    // 16-byte source parts per key: bf16 rows, FP8 rows, MXFP4 rows
+    static constexpr int UB = D / 8, UF8 = D / 16, UF4 = D / 32;
+    static constexpr int UPK_W = WD == DT_BF16 ? UB : UF8;
+    static constexpr int UPK_P = KVD == DT_BF16 ? UB : UF4;
+    static constexpr int NU_W = (UPK_W + kThreadsPerKey - 1) / kThreadsPerKey;
+    static constexpr int NU_P = (UPK_P + kThreadsPerKey - 1) / kThreadsPerKey;
+    static constexpr int NU = NU_W > NU_P ? NU_W : NU_P;
+
+    // Issue the loads of tile `tile` (row-local tile index).  `live` false (a
+    // tile past the split): the loads read row 0 and nothing is used; issuing
+    // them anyway keeps the number of loads per step fixed, so the compiler's
+    // wait counts stay exact.  Masked keys also read row 0 and are zeroed
+    // when stored.
+    __device__ __forceinline__ static void load(const AttnArgs& a, const RowKeys& rk, int tile, bool live,
+                                                const lds_i32* idx_lds, int idx0, const lds_i32* bt_lds, int blk0,
+                                                TileRegs<NU>& R) {
+        const int tid = threadIdx.x;
+        const int key = tid / kThreadsPerKey, sub = tid % kThreadsPerKey;
+        const bool win = live && tile >= rk.sel_tiles;              // uniform over the workgroup
+        if (win) {
+            const int w = (tile - rk.sel_tiles) * kKeys + key;
+            const bool ok = w < rk.nwin;
+            const int64_t row = (int64_t)rk.b * a.win_cap + (rk.t0 + (ok ? w : 0)) % a.win_cap;
+            const uint8_t* src = reinterpret_cast<const uint8_t*>(a.win_data) + row * (WD == DT_BF16 ? 2 * D : D);
+#pragma unroll
+            for (int i = 0; i < NU_W; ++i) {
+                const int part = sub + kThreadsPerKey * i;
+                const int pc = part < UPK_W ? part : 0;
+                R.v[i] = *reinterpret_cast<const u32x4*>(src + pc * 16);
+                R.sc[i] = 127u;
+            }
+            R.kscale = WD == DT_FP8 ? a.win_scale[row] : 1.0f;
+            R.valid = ok;
+        } else {
+            const int64_t prow = pool_row(a, rk, (live ? tile * kKeys : idx0) + key, idx_lds, idx0, bt_lds, blk0);
+            const bool ok = live && prow >= 0;
+            const int64_t row = ok ? prow : 0;
+            const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv_data) + row * (KVD == DT_BF16 ? 2 * D : D / 2);
+            const uint8_t* scs = reinterpret_cast<const uint8_t*>(a.kv_scale) + row * (D / 32);
+#pragma unroll
+            for (int i = 0; i < NU_P; ++i) {
+                const int part = sub + kThreadsPerKey * i;
+                const int pc = part < UPK_P ? part : 0;
+                R.v[i] = *reinterpret_cast<const u32x4*>(src + pc * 16);
+                R.sc[i] = KVD == DT_MXFP4 ? (uint32_t)scs[pc] : 127u;
+            }
+            R.kscale = 1.0f;
+            R.valid = ok;
+        }
+    }
+
+    // Convert the registers of tile `tile` to bf16 and write them to an LDS stage.
+    __device__ __forceinline__ static void store(const RowKeys& rk, int tile, const TileRegs<NU>& R, lds_u8* stage,
+                                                 lds_f32* kmeta) {
+        const int tid = threadIdx.x;
+        const int key = tid / kThreadsPerKey, sub = tid % kThreadsPerKey;
+        if (sub == 0) kmeta[key] = R.valid ? R.kscale : -1.0f;
+        lds_u8* dst = stage + key * Geo<D>::ROWB;
+        if (tile >= rk.sel_tiles) store_parts<WD, UPK_W, NU_W>(R, dst, sub);
+        else store_parts<KVD, UPK_P, NU_P>(R, dst, sub);
+    }
+
+    template <int SRC, int UPK, int NUS>
+    __device__ __forceinline__ static void store_parts(const TileRegs<NU>& R, lds_u8* dst, int sub) {
+        const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < NUS; ++i) {
+            const int part = sub + kThreadsPerKey * i;
+            const bool in = (i + 1) * kThreadsPerKey <= UPK || part < UPK;
+            const u32x4 v = R.valid ? R.v[i] : zero;
+            if (SRC == DT_BF16) {
+                if (in) *reinterpret_cast<lds_u32x4*>(dst + part * 16) = v;
+            } else if (SRC == DT_FP8) {
+                // 16 E4M3 codes -> 16 bf16 (exact)
+                const u32x4 o0 = fp8x8_to_bf16(v[0], v[1]);
+                const u32x4 o1 = fp8x8_to_bf16(v[2], v[3]);
+                if (in) {
+                    *reinterpret_cast<lds_u32x4*>(dst + part * 32) = o0;
+                    *reinterpret_cast<lds_u32x4*>(dst + part * 32 + 16) = o1;
+                }
+            } else {
+                // 32 E2M1 codes with one E8M0 scale -> 32 bf16 (exact)
+                const int X = R.valid ? (int)R.sc[i] - 127 : 0;
+                const u32x4 o0 = fp4x8_to_bf16(v[0], X), o1 = fp4x8_to_bf16(v[1], X);
+                const u32x4 o2 = fp4x8_to_bf16(v[2], X), o3 = fp4x8_to_bf16(v[3], X);
+                if (in) {
+                    *reinterpret_cast<lds_u32x4*>(dst + part * 64) = o0;
+                    *reinterpret_cast<lds_u32x4*>(dst + part * 64 + 16) = o1;
+                    *reinterpret_cast<lds_u32x4*>(dst + part * 64 + 32) = o2;
+                    *reinterpret_cast<lds_u32x4*>(dst + part * 64 + 48) = o3;
+                }
+            }
+        }
+    }
+};
+
+// Per-wave softmax/PV state and the tile computation.
+template <int D, int DV>
+struct WaveAttn {
+    static constexpr int KS = D / 32;          // k-steps of S^T
+    static constexpr int NDT = DV / 16;        // 16-dim tiles of O^T
     bf16x8 qb[KS];
-    {
+    f32x4 o[NDT];
+    float m_run, l_run;
+
+    __device__ __forceinline__ void init(const AttnArgs& a, int r, int head, int g) {
         const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + head) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) qb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + 32 * s + 8 * g));
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_run = 0.0f;
     }
-    f32x4 o[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;
 
-    const uint8_t* kvd = reinterpret_cast<const uint8_t*>(a.kv_data);
-    const uint8_t* kvs = reinterpret_cast<const uint8_t*>(a.kv_scale);
-    const uint8_t* wdat = reinterpret_cast<const uint8_t*>(a.win_data);
-
-    for (int j0 = j_begin; j0 < j_end; j0 += T::KEYS) {
-        // 1a. resolve the tile's keys
-        if (tid < T::KEYS) {
-            int kind; int64_t row;
-            resolve_key(a, rk, r, j0 + tid, j_end, kind, row);
-            src_row[tid] = row;
-            src_kind[tid] = kind;
-            kscale[tid] = (kind == 2 && WD == DT_FP8) ? a.win_scale[row] : 1.0f;
-        }
-        __syncthreads();
-        // 1b. gather + dequantise into LDS (16-byte bf16 chunks)
-        for (int c = tid; c < T::KEYS * T::CPK; c += NT) {
-            const int kk = c / T::CPK, part = c - kk * T::CPK;
-            const int kind = src_kind[kk];
-            const int64_t row = src_row[kk];
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (kind == 1) {
-                if (KVD == DT_BF16) {
-                    v = *reinterpret_cast<const u32x4*>(kvd + row * (2 * D) + part * 16);
-                } else {   // MXFP4: 8 nibbles + the block's E8M0 scale
-                    uint32_t w = *reinterpret_cast<const uint32_t*>(kvd + row * (D / 2) + part * 4);
-                    int X = (int)kvs[row * (D / 32) + part / 4] - 127;
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        uint32_t bb = w >> (8 * h);
-                        v[h] = fp4_to_bf16(bb & 15u, X) | (fp4_to_bf16((bb >> 4) & 15u, X) << 16);
-                    }
-                }
-            } else if (kind == 2) {
-                if (WD == DT_BF16) {
-                    v = *reinterpret_cast<const u32x4*>(wdat + row * (2 * D) + part * 16);
-                } else {   // FP8 codes; the per-token scale is applied to scores and P
-                    u32x2 w = *reinterpret_cast<const u32x2*>(wdat + row * D + part * 8);
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        uint32_t x = w[h];
-                        v[2 * h] = fp8_to_bf16(x & 0xffu) | (fp8_to_bf16((x >> 8) & 0xffu) << 16);
-                        v[2 * h + 1] = fp8_to_bf16((x >> 16) & 0xffu) | (fp8_to_bf16(x >> 24) << 16);
-                    }
-                }
-            }
-            *reinterpret_cast<u32x4*>(lds + kk * T::ROWB + part * 16) = v;
-        }
-        __syncthreads();
-
-        // 2. S^T = K Q^T: two 16-key sub-tiles
+    __device__ __forceinline__ void tile(const lds_u8* lds, const lds_f32* kmeta, float scale_log2, int g, int c16) {
+        constexpr int ROWB = Geo<D>::ROWB;
+        // S^T = K Q^T over two 16-key sub-tiles; lane holds keys kt*16 + 4g + v of its head
         f32x4 sacc[2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint8_t* rowp = lds + (kt * 16 + c16) * T::ROWB + 16 * g;
+            const lds_u8* rowp = lds + (kt * 16 + c16) * ROWB + 16 * g;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                bf16x8 kA = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(rowp + 64 * s));
+                bf16x8 kA = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(rowp + 64 * s));
                 sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, qb[s], sacc[kt], 0, 0, 0);
             }
         }
-        // 3. online softmax (log2 domain); lane holds keys kt*16 + 4g + v of head `head`
-        float x[2][4];
+        float x[2][4], ks[2][4];
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int kk = kt * 16 + 4 * g + v;
-                float sc = sacc[kt][v] * a.scale_log2 * kscale[kk];
-                x[kt][v] = src_kind[kk] ? sc : -INFINITY;
+                const float km = kmeta[kt * 16 + 4 * g + v];
+                ks[kt][v] = km;
+                x[kt][v] = km >= 0.0f ? sacc[kt][v] * scale_log2 * km : -INFINITY;
                 mx = fmaxf(mx, x[kt][v]);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const bool none = m_new == -INFINITY;
-        const float alpha = none ? 1.0f : exp2f(m_run - m_new);
-        m_run = m_new;
-        // P for the value product as an unevaluated sum of two bf16 values
-        // (hi + lo carries 16 significant bits): a single bf16 P would put a
-        // relative error of 2^-9 on every value it weights.
+        // Lazy rescaling: the reference max m_run moves only when the tile's max
+        // exceeds it by more than 8 (log2 units), so most tiles leave the O
+        // accumulators untouched; probabilities relative to m_run stay <= 2^8.
+        if (mx > m_run + 8.0f) {
+            const float alpha = exp2f(m_run - mx);             // 0 while m_run = -inf
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+            m_run = mx;
+        }
+        const bool none = m_run == -INFINITY;
         float psum = 0.0f;
         uint32_t pk[4], pl[4];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int v = 0; v < 4; v += 2) {
-                const int kk = kt * 16 + 4 * g + v;
-                float p0 = none ? 0.0f : exp2f(x[kt][v] - m_new);
-                float p1 = none ? 0.0f : exp2f(x[kt][v + 1] - m_new);
+                const float p0 = none ? 0.0f : exp2f(x[kt][v] - m_run);
+                const float p1 = none ? 0.0f : exp2f(x[kt][v + 1] - m_run);
                 psum += p0 + p1;
-                const float w0 = p0 * kscale[kk], w1 = p1 * kscale[kk + 1];
+                const float w0 = p0 * fmaxf(ks[kt][v], 0.0f), w1 = p1 * fmaxf(ks[kt][v + 1], 0.0f);
                 const uint32_t h = pack_bf16x2(w0, w1);
                 pk[kt * 2 + v / 2] = h;
                 pl[kt * 2 + v / 2] = pack_bf16x2(w0 - bf16_to_f32(h & 0xffffu), w1 - bf16_to_f32(h >> 16));
             }
-        l_run = l_run * alpha + psum;
+        l_run += psum;
         const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
         const bf16x8 pbl = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-
-        // 4. O^T += V^T P^T; lane (dim dt*16 + c16, g) needs keys 4g..4g+3 and 16+4g..16+4g+3.
-        // ds_read_b64_tr_b16 within each 16-lane block hands lane i element (i & 3) of
-        // the 8-byte chunk addressed by lane (i >> 2) + 4e, for e = 0..3: lane s of the
-        // block addresses key 4g + (s >> 2), dims dt*16 + 4(s & 3) .. +3, so lane i
+        // O^T += V^T P^T.  Within each 16-lane block, ds_read_b64_tr_b16 hands lane i
+        // element (i & 3) of the 8-byte chunk addressed by lane (i >> 2) + 4e, e = 0..3:
+        // lane s addresses key 4g + (s >> 2), dims dt*16 + 4(s & 3) .. +3, so lane i
         // receives keys 4g + e at dim dt*16 + i.
-        const uint8_t* vbase = lds + (4 * g + (c16 >> 2)) * T::ROWB + 8 * (c16 & 3);
+        const lds_u8* vbase = lds + (4 * g + (c16 >> 2)) * ROWB + 8 * (c16 & 3);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const uint8_t* p0 = vbase + dt * 32;
-            i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0));
-            i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(p0 + 16 * T::ROWB));
+            const lds_u8* p0 = vbase + dt * 32;
+            i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+            i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 16 * ROWB));
             const bf16x8 vA = __builtin_bit_cast(
                 bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                               __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
             o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pb, o[dt], 0, 0, 0);
             o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pbl, o[dt], 0, 0, 0);
         }
+    }
+};
+
+constexpr int kBtLds = 4096;           // block-table entries cached in LDS
+constexpr int kIdxLds = 2560;          // top-k slots cached in LDS (= max keys per split)
+
+template <int KVD, int WD, int D, int DV, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_mfma_kernel(AttnArgs a) {
+    using G = Geo<D>;
+    constexpr int NT = NW * 64;
+    using TL = Tiler<KVD, WD, D, NT>;
+    constexpr int NU = TL::NU;
+    // tiles held in registers ahead of the LDS stage
+    constexpr int kPrefetch = NU <= 12 ? 2 : 1;
+    static_assert(kPrefetch == 1 || kPrefetch == 2, "prefetch depth");
+    __shared__ __attribute__((aligned(16))) uint8_t stage[2][G::STAGE];
+    __shared__ float kmeta[2][kKeys];
+    __shared__ int32_t bt_mem[kBtLds];
+    __shared__ int32_t idx_mem[kIdxLds];
+    lds_i32* const bt_lds = (lds_i32*)&bt_mem[0];
+    lds_i32* const idx_lds = (lds_i32*)&idx_mem[0];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int split = blockIdx.x, r = blockIdx.y;
+    const RowKeys rk = row_keys(a, r);
+    const int tb = split * a.split_tiles;
+    if (tb >= rk.tiles) return;                                   // empty split (the merge skips it)
+    const int te = min(tb + a.split_tiles, rk.tiles);
+    const int head = (int)blockIdx.z * (NW * 16) + wave * 16 + c16;
+
+    // prologue: top-k slots and block-table range of this split into LDS
+    const int sel_end = min(te, rk.sel_tiles) * kKeys;            // selected slots [tb*32, sel_end)
+    const int idx0 = tb * kKeys;
+    int blk0 = 0, nblk = 0;
+    if (sel_end > idx0) {
+        const int E = 256 / a.m;
+        if (a.topk) {
+            nblk = (rk.n + E - 1) / E;
+            for (int i = tid; i < sel_end - idx0; i += NT)
+                idx_lds[i] = idx0 + i < rk.nsel ? a.topk[(int64_t)r * a.k + idx0 + i] : -1;
+        } else {
+            const int g1 = min(sel_end, rk.nsel);
+            if (g1 > idx0) {
+                blk0 = idx0 / E;
+                nblk = (g1 - 1) / E - blk0 + 1;
+            }
+        }
+    }
+    for (int i = tid; i < min(nblk, kBtLds); i += NT) bt_lds[i] = a.block_table[(int64_t)rk.b * a.max_blocks + blk0 + i];
+    __syncthreads();
+
+    WaveAttn<D, DV> W;
+    W.init(a, r, head, g);
+
+    TileRegs<NU> R[kPrefetch];
+    const int ntl = te - tb;
+    TL::load(a, rk, tb, true, idx_lds, idx0, bt_lds, blk0, R[0]);
+    if constexpr (kPrefetch > 1) TL::load(a, rk, tb + 1, 1 < ntl, idx_lds, idx0, bt_lds, blk0, R[1]);
+    lds_u8* const st = (lds_u8*)&stage[0][0];
+    lds_f32* const km = (lds_f32*)&kmeta[0][0];
+    TL::store(rk, tb, R[0], st, km);
+    TL::load(a, rk, tb + kPrefetch, kPrefetch < ntl, idx_lds, idx0, bt_lds, blk0, R[0]);
+    __syncthreads();
+
+    // tile u sits in register set (u - tb) % P until it is stored to stage
+    // (u - tb) % 2; the steps of one round are spelled out so that every
+    // register set is addressed statically
+    auto step = [&](auto J, int t) __attribute__((always_inline)) {
+        constexpr int nxt = (decltype(J)::value + 1) % kPrefetch;
+        if (t + 1 < ntl) TL::store(rk, tb + t + 1, R[nxt], st + ((t + 1) & 1) * G::STAGE, km + ((t + 1) & 1) * kKeys);
+        TL::load(a, rk, tb + t + 1 + kPrefetch, t + 1 + kPrefetch < ntl, idx_lds, idx0, bt_lds, blk0, R[nxt]);
+        W.tile(st + (t & 1) * G::STAGE, km + (t & 1) * kKeys, a.scale_log2, g, c16);
         __syncthreads();
+    };
+    for (int t0 = 0; t0 < ntl; t0 += kPrefetch) {
+        step(IntC<0>{}, t0);
+        if constexpr (kPrefetch > 1)
+            if (t0 + 1 < ntl) step(IntC<1>{}, t0 + 1);
     }
 
     // finish: total row sum of this head over the 4 lane groups
-    float l_tot = l_run + __shfl_xor(l_run, 16);
+    float l_tot = W.l_run + __shfl_xor(W.l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
+    constexpr int NDT = DV / 16;
     if (a.nsplit == 1) {
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         const int64_t base = ((int64_t)r * a.H + head) * DV + 4 * g;
         if (a.out_dtype == DT_F32) {
             float* out = reinterpret_cast<float*>(a.out) + base;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(out + dt * 16) = o[dt] * inv;
+            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(out + dt * 16) = W.o[dt] * inv;
         } else {
             uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + base;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-                f32x4 t = o[dt] * inv;
+                f32x4 t = W.o[dt] * inv;
                 *reinterpret_cast<u32x2*>(out + dt * 16) = u32x2{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
             }
         }
-        if (a.lse && g == 0) a.lse[(int64_t)r * a.H + head] = (m_run + log2f(l_tot)) * kLn2;
+        if (a.lse && g == 0) a.lse[(int64_t)r * a.H + head] = (W.m_run + log2f(l_tot)) * kLn2;
     } else {
         float* po = a.part_o + (((int64_t)r * a.nsplit + split) * a.H + head) * DV + 4 * g;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
+        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = W.o[dt];
         if (g == 0) {
             float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H;
-            ml[head] = m_run;
+            ml[head] = W.m_run;
             ml[a.H + head] = l_tot;
         }
     }
 }
 
-// Merge the key splits of each row: m* = max m_s, w_s = 2^(m_s - m*),
+// Merge the key splits of one (row, head): m* = max m_s, w_s = 2^(m_s - m*),
 // out = sum_s w_s O_s / sum_s w_s l_s, lse = (m* + log2 sum_s w_s l_s) ln 2.
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-    extern __shared__ float wts[];                  // [nsplit][H]
-    const int r = blockIdx.x, tid = threadIdx.x;
+constexpr int kMergeThreads = 128;
+constexpr int kMaxSplits = 256;
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
+    __shared__ float wts[kMaxSplits];
+    __shared__ float red[2][kMergeThreads / 64];
+    const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
     const RowKeys rk = row_keys(a, r);
-    const int ns = (rk.L + a.split_keys - 1) / a.split_keys;
+    const int ns = (rk.tiles + a.split_tiles - 1) / a.split_tiles;
     const int H = a.H, DV = a.d_v;
     const float* ml = a.part_ml + (int64_t)r * a.nsplit * 2 * H;
-    for (int h = tid; h < H; h += 256) {
-        float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s * 2 * H + h]);
-        float Lsum = 0.0f;
-        for (int s = 0; s < ns; ++s) {
-            float w = ml[s * 2 * H + h] == -INFINITY ? 0.0f : exp2f(ml[s * 2 * H + h] - M);
-            wts[s * H + h] = w;
-            Lsum += w * ml[s * 2 * H + H + h];
-        }
-        const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
-        for (int s = 0; s < ns; ++s) wts[s * H + h] *= inv;
-        if (a.lse) a.lse[(int64_t)r * H + h] = (M + log2f(Lsum)) * kLn2;
-    }
+    float M = -INFINITY;
+    for (int s = tid; s < ns; s += kMergeThreads) M = fmaxf(M, ml[s * 2 * H + h]);
+    M = wave_max(M);
+    if ((tid & 63) == 0) red[0][tid >> 6] = M;
     __syncthreads();
-    const float* po = a.part_o + (int64_t)r * a.nsplit * H * DV;
-    for (int e = tid; e < H * DV; e += 256) {
-        const int h = e / DV;
-        float acc = 0.0f;
-        for (int s = 0; s < ns; ++s) acc = fmaf(wts[s * H + h], po[(int64_t)s * H * DV + e], acc);
-        if (a.out_dtype == DT_F32) reinterpret_cast<float*>(a.out)[(int64_t)r * H * DV + e] = acc;
-        else reinterpret_cast<uint16_t*>(a.out)[(int64_t)r * H * DV + e] = (uint16_t)f32_to_bf16(acc);
+    M = red[0][0];
+    for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[0][i]);
+    float Ls = 0.0f;
+    for (int s = tid; s < ns; s += kMergeThreads) {
+        const float ms = ml[s * 2 * H + h];
+        const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+        wts[s] = w;
+        Ls += w * ml[s * 2 * H + H + h];
+    }
+    Ls = wave_sum(Ls);
+    if ((tid & 63) == 0) red[1][tid >> 6] = Ls;
+    __syncthreads();
+    Ls = 0.0f;
+    for (int i = 0; i < kMergeThreads / 64; ++i) Ls += red[1][i];
+    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    if (a.lse && tid == 0) a.lse[(int64_t)r * H + h] = (M + log2f(Ls)) * kLn2;
+    const float* po = a.part_o + ((int64_t)r * a.nsplit * H + h) * DV;
+    const int64_t sstride = (int64_t)H * DV;
+    for (int d = tid * 4; d < DV; d += kMergeThreads * 4) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < ns; ++s) acc += wts[s] * *reinterpret_cast<const f32x4*>(po + s * sstride + d);
+        acc *= inv;
+        const int64_t oi = ((int64_t)r * H + h) * DV + d;
+        if (a.out_dtype == DT_F32) {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + oi) = acc;
+        } else {
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + oi) =
+                u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+        }
     }
 }
 
@@ -306,19 +469,30 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     __shared__ float sc[kF32MaxKeys];
     __shared__ float red[4];
     const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
-    const RowKeys rk = row_keys(a, r);
+    const int b = a.row_seq[r], p = a.row_pos[r];
+    const int n = visible_entries(p, a.m);
+    const int nsel = a.topk ? a.k : n;
+    const int t0 = max(0, p - a.window + 1);
+    const int L = nsel + (p - t0 + 1);
+    const int E = 256 / a.m;
     const int D = a.D;
     const float* q = reinterpret_cast<const float*>(a.q) + ((int64_t)r * a.H + h) * D;
     const float* kvd = reinterpret_cast<const float*>(a.kv_data);
     const float* wd = reinterpret_cast<const float*>(a.win_data);
     const float scale = a.scale_log2 * kLn2;
+    auto key_ptr = [&](int j) -> const float* {
+        if (j < nsel) {
+            const int g = a.topk ? a.topk[(int64_t)r * a.k + j] : j;
+            if (g < 0 || g >= n) return nullptr;
+            return kvd + ((int64_t)a.block_table[(int64_t)b * a.max_blocks + g / E] * E + g % E) * D;
+        }
+        return wd + ((int64_t)b * a.win_cap + (t0 + j - nsel) % a.win_cap) * D;
+    };
     float mx = -INFINITY;
-    for (int j = tid; j < rk.L; j += 256) {
-        int kind; int64_t row;
-        resolve_key(a, rk, r, j, rk.L, kind, row);
+    for (int j = tid; j < L; j += 256) {
+        const float* kp = key_ptr(j);
         float s = -INFINITY;
-        if (kind) {
-            const float* kp = (kind == 1 ? kvd : wd) + row * D;
+        if (kp) {
             float dot = 0.0f;
             for (int d = 0; d < D; ++d) dot = fmaf(q[d], kp[d], dot);
             s = scale * dot;
@@ -332,7 +506,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();
     float sum = 0.0f;
-    for (int j = tid; j < rk.L; j += 256) {
+    for (int j = tid; j < L; j += 256) {
         float e = sc[j] == -INFINITY ? 0.0f : expf(sc[j] - mx);
         sc[j] = e;
         sum += e;
@@ -344,11 +518,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
     for (int d = tid; d < a.d_v; d += 256) {
         float acc = 0.0f;
-        for (int j = 0; j < rk.L; ++j) {
+        for (int j = 0; j < L; ++j) {
             if (sc[j] == 0.0f) continue;
-            int kind; int64_t row;
-            resolve_key(a, rk, r, j, rk.L, kind, row);
-            acc = fmaf(sc[j], (kind == 1 ? kvd : wd)[row * D + d], acc);
+            acc = fmaf(sc[j], key_ptr(j)[d], acc);
         }
         const int64_t oi = ((int64_t)r * a.H + h) * a.d_v + d;
         if (a.out_dtype == DT_F32) reinterpret_cast<float*>(a.out)[oi] = acc * inv;
@@ -359,22 +531,19 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
 template <int KVD, int WD, int D, int DV, int NW>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
-    dim3 grid(a.nsplit, a.num_rows);
+    dim3 grid(a.nsplit, a.num_rows, a.H / (NW * 16));
     hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, NW>), grid, dim3(NW * 64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.num_rows), dim3(256), a.nsplit * a.H * sizeof(float), stream, a);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.H, a.num_rows), dim3(kMergeThreads), 0, stream, a);
     return hipGetLastError();
 }
 
+// Workgroups of four waves cover 64 heads; more heads add head groups to the grid.
 template <int KVD, int WD, int D, int DV>
 hipError_t launch_heads(const AttnArgs& a, hipStream_t stream) {
-    switch (a.H) {
-    case 16: return launch_mfma<KVD, WD, D, DV, 1>(a, stream);
-    case 32: return launch_mfma<KVD, WD, D, DV, 2>(a, stream);
-    case 64: return launch_mfma<KVD, WD, D, DV, 4>(a, stream);
-    }
-    return hipErrorInvalidValue;
+    if (a.H % 64 != 0) return hipErrorInvalidValue;
+    return launch_mfma<KVD, WD, D, DV, 4>(a, stream);
 }
 
 template <int KVD, int WD>
@@ -388,6 +557,10 @@ hipError_t launch_dims(const AttnArgs& a, hipStream_t stream) {
 }  // namespace
 
 int attn_f32_max_keys() { return kF32MaxKeys; }
+int attn_max_split_tiles() { return kIdxLds / kKeys; }
+int attn_max_splits() { return kMaxSplits; }
+int attn_tile_keys() { return kKeys; }
+int attn_max_table_blocks() { return kBtLds; }
 
 bool attn_supported(int q_dtype, int kv_dtype, int win_dtype, int H, int D, int d_v) {
     if (q_dtype == DT_F32)
@@ -395,7 +568,7 @@ bool attn_supported(int q_dtype, int kv_dtype, int win_dtype, int H, int D, int 
     if (q_dtype != DT_BF16) return false;
     if (kv_dtype != DT_BF16 && kv_dtype != DT_MXFP4) return false;
     if (win_dtype != DT_BF16 && win_dtype != DT_FP8) return false;
-    if (H != 16 && H != 32 && H != 64) return false;
+    if (H < 64 || H % 64 != 0) return false;
     return (D == 576 && (d_v == 576 || d_v == 512)) || (D == 128 && d_v == 128);
 }
 

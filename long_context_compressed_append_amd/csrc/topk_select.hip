@@ -1,15 +1,22 @@
 // topk_select: for each query row, the k visible entries with the largest
 // indexer logits (equal logits: smaller entry first), written in ascending
-// entry order and padded with -1.  [P1 = page "vLLM uveo DeepSeek V4 s 8,7x
-// manjim KV cacheom", section "Kako funkcionira optimizacija KV cachea?":
-// attention is limited to the top-k compressed tokens.]
+// entry order and padded with -1.  [Page "vLLM uveo DeepSeek V4 s 8,7x manjim
+// KV cacheom", section "Kako funkcionira optimizacija KV cachea?": attention is
+// limited to the top-k compressed tokens.]
 //
-// One 1024-thread workgroup per row.  Logits map to order-preserving u32
-// keys (-0.0 folded onto +0.0); four 8-bit radix passes with LDS histograms
-// find the k-th largest key T and how many keys equal to T are still
-// needed; a final pass in index order keeps every key > T and the first
-// `need` keys == T, with block-wide exclusive scans giving each kept entry
-// its output slot, so the result is deterministic and sorted by entry.
+// One 1024-thread workgroup per row; thread i owns the contiguous entries
+// [i*C, (i+1)*C).  Logits map to order-preserving u32 keys (-0.0 folded onto
+// +0.0).  Rows of up to 32K entries are held in registers; longer rows are
+// re-read from memory on every pass.
+//   1. A block min/max of the keys gives their common leading bits, so the
+//      radix digits start at the first bit in which the keys differ.
+//   2. Radix passes of up to 8 bits find the k-th largest key T and how many
+//      keys equal to T are still needed.  Histograms live in LDS as 16 copies
+//      selected by lane, so lanes holding the same digit rarely hit the same
+//      counter.
+//   3. A final pass in entry order keeps every key > T and the first `need`
+//      keys == T; block-wide exclusive scans give each kept entry its output
+//      slot, so the result is deterministic and sorted by entry.
 #include "device.h"
 #include "kernels.h"
 
@@ -19,6 +26,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kCopies = 16;
 
 __device__ inline uint32_t order_key(float x) {
     uint32_t u = __float_as_uint(x);
@@ -48,12 +56,43 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint
     return before + inc - v;
 }
 
+// Keys of this thread's chunk: resident in registers (R > 0) or streamed.
+template <int R>
+struct Chunk {
+    uint32_t u[R > 0 ? R : 1];
+    int c0, c1;                 // entry range [c0, c1)
+    const float* L;
+
+    __device__ void init(const float* logits, int n, int per_thread) {
+        L = logits;
+        c0 = min((int)threadIdx.x * per_thread, n);
+        c1 = min(c0 + per_thread, n);
+        if (R > 0) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) u[i] = c0 + i < c1 ? order_key(L[c0 + i]) : 0u;
+        }
+    }
+    template <class F>
+    __device__ void each(F f) const {
+        if (R > 0) {
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+                if (c0 + i < c1) f(c0 + i, u[i]);
+        } else {
+            for (int i = c0; i < c1; ++i) f(i, order_key(L[i]));
+        }
+    }
+};
+
+template <int R>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
-    __shared__ uint32_t hist[256];
+    __shared__ uint32_t hist[kCopies][256];
+    __shared__ uint32_t tot[256];
     __shared__ uint32_t wsum[kWaves];
+    __shared__ uint32_t red[2][kWaves];
     __shared__ uint32_t sel_digit, sel_above;
     const int r = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = visible_entries(p.row_pos[r], p.m);
     const int k = p.k;
     int32_t* out = p.idx + (int64_t)r * k;
@@ -61,24 +100,51 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
         for (int i = tid; i < k; i += kThreads) out[i] = i < n ? i : -1;
         return;
     }
-    const float* L = p.logits + (int64_t)r * p.ld;
+    const int per_thread = (n + kThreads - 1) / kThreads;
+    Chunk<R> C;
+    C.init(p.logits + (int64_t)r * p.ld, n, per_thread);
 
-    uint32_t prefix = 0, mask = 0;
-    uint32_t need = (uint32_t)k;            // keys still to take among those matching prefix
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        if (tid < 256) hist[tid] = 0;
+    // 1. common leading bits of all keys
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    C.each([&](int, uint32_t u) { kmin = min(kmin, u); kmax = max(kmax, u); });
+    for (int o = 32; o > 0; o >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    }
+    if (lane == 0) { red[0][wave] = kmin; red[1][wave] = kmax; }
+    __syncthreads();
+    kmin = red[0][0]; kmax = red[1][0];
+    for (int i = 1; i < kWaves; ++i) { kmin = min(kmin, red[0][i]); kmax = max(kmax, red[1][i]); }
+    const uint32_t diff = kmin ^ kmax;
+    int top = diff ? 31 - __builtin_clz(diff) : -1;            // highest differing bit
+    uint32_t mask = diff == 0 ? 0xffffffffu : top >= 31 ? 0u : ~((2u << top) - 1u);   // the common bits
+    uint32_t prefix = kmax & mask;
+    uint32_t need = (uint32_t)k;                                // keys still to take among those matching
+
+    // 2. radix passes from the highest differing bit down
+    while (top >= 0) {
+        const int w = min(8, top + 1);
+        const int shift = top - w + 1;
+        const uint32_t bins = 1u << w;
+        for (int i = tid; i < kCopies * 256; i += kThreads) (&hist[0][0])[i] = 0u;
         __syncthreads();
-        for (int i = tid; i < n; i += kThreads) {
-            uint32_t u = order_key(L[i]);
-            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+        uint32_t* h = hist[lane & (kCopies - 1)];
+        C.each([&](int, uint32_t u) {
+            if ((u & mask) == prefix) atomicAdd(&h[(u >> shift) & (bins - 1)], 1u);
+        });
+        __syncthreads();
+        if (tid < 256) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int cp = 0; cp < kCopies; ++cp) c += hist[cp][tid];
+            tot[tid] = c;
         }
         __syncthreads();
         if (tid < 64) {
             // lane l owns bins 4l..4l+3; suffix sums from the top digit down
             uint32_t c[4], s = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { c[i] = hist[4 * tid + i]; s += c[i]; }
+            for (int i = 0; i < 4; ++i) { c[i] = tot[4 * tid + i]; s += c[i]; }
             uint32_t suf = s;
             for (int o = 1; o < 64; o <<= 1) {
                 uint32_t t = __shfl_down(suf, o);
@@ -93,41 +159,39 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
         }
         __syncthreads();
         prefix |= sel_digit << shift;
-        mask |= 255u << shift;
+        mask |= (bins - 1u) << shift;
         need -= sel_above;
+        top = shift - 1;
         __syncthreads();
     }
     const uint32_t T = prefix;
 
-    // final pass: contiguous chunk per thread, in entry order
-    const int chunk = (n + kThreads - 1) / kThreads;
-    const int c0 = min(tid * chunk, n), c1 = min(c0 + chunk, n);
+    // 3. ordered output
     uint32_t gt = 0, eq = 0;
-    for (int i = c0; i < c1; ++i) {
-        uint32_t u = order_key(L[i]);
-        gt += u > T;
-        eq += u == T;
-    }
-    uint32_t tot;
-    const uint32_t gt_before = block_exclusive_scan(gt, wsum, &tot);
-    const uint32_t eq_before = block_exclusive_scan(eq, wsum, &tot);
+    C.each([&](int, uint32_t u) { gt += u > T; eq += u == T; });
+    uint32_t total;
+    const uint32_t gt_before = block_exclusive_scan(gt, wsum, &total);
+    const uint32_t eq_before = block_exclusive_scan(eq, wsum, &total);
     uint32_t pos = gt_before + min(eq_before, need);
     uint32_t eq_seen = eq_before;
-    for (int i = c0; i < c1; ++i) {
-        uint32_t u = order_key(L[i]);
+    C.each([&](int i, uint32_t u) {
         if (u > T) out[pos++] = i;
         else if (u == T) {
             if (eq_seen < need) out[pos++] = i;
             ++eq_seen;
         }
-    }
+    });
 }
 
 }  // namespace
 
-hipError_t launch_topk_select(const TopkArgs& a, int /*max_entries*/, hipStream_t stream) {
+hipError_t launch_topk_select(const TopkArgs& a, int max_entries, hipStream_t stream) {
     if (a.num_rows <= 0 || a.k <= 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_kernel, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
+    const int per_thread = (max_entries + kThreads - 1) / kThreads;
+    if (per_thread <= 8) hipLaunchKernelGGL(topk_kernel<8>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
+    else if (per_thread <= 16) hipLaunchKernelGGL(topk_kernel<16>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
+    else if (per_thread <= 32) hipLaunchKernelGGL(topk_kernel<32>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL(topk_kernel<0>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
