@@ -96,14 +96,12 @@ __device__ __forceinline__ int64_t pool_row(const AttnArgs& a, const RowKeys& rk
     return ok ? ((int64_t)pb << sh) + (gc & ((1 << sh) - 1)) : -1;
 }
 
-// Tile staging.  Eight threads share a key: thread t stages key t / 8 (of
-// the 32 keys of a tile), 16-byte parts (t % 8) + 8i of its row, so each
+// Tile staging.  NT / 32 threads share a key: thread t stages key t / (NT/32)
+// of the 32 keys of a tile, 16-byte parts (t % (NT/32)) + (NT/32) i, so each
 // thread resolves one storage row per tile and its loads and LDS writes
 // differ only by immediate offsets.  Raw bytes are loaded into registers
 // ahead of use and converted exactly to bf16 when they are written to LDS;
 // loaded values are consumed only then, so the loads stay in flight.
-constexpr int kThreadsPerKey = 8;
-
 template <int NU>
 struct TileRegs {
     u32x4 v[NU];
@@ -114,7 +112,8 @@ struct TileRegs {
 
 template <int KVD, int WD, int D, int NT>
 struct Tiler {
-    static_assert(NT == kKeys * kThreadsPerKey, "one workgroup stages one tile");
+    static constexpr int kThreadsPerKey = NT / kKeys;
+    static_assert(NT % kKeys == 0, "whole keys per workgroup");
     // 16-byte source parts per key: bf16 rows, FP8 rows, MXFP4 rows
     static constexpr int UB = D / 8, UF8 = D / 16, UF4 = D / 32;
     static constexpr int UPK_W = WD == DT_BF16 ? UB : UF8;
@@ -211,17 +210,21 @@ struct Tiler {
     }
 };
 
-// Per-wave softmax/PV state and the tile computation.
+// Per-wave softmax/PV state and the tile computation.  A pair of waves
+// shares 16 heads and splits the shared-KV dimension: each wave computes the
+// partial scores over its half of D (its half of every query stays in
+// VGPRs), the pair swaps partial scores through LDS, and each wave then runs
+// the same softmax and accumulates P V for its half of the value dims.
 template <int D, int DV>
-struct WaveAttn {
-    static constexpr int KS = D / 32;          // k-steps of S^T
-    static constexpr int NDT = DV / 16;        // 16-dim tiles of O^T
+struct HalfWave {
+    static constexpr int KS = D / 64;          // k-steps of S^T per half
+    static constexpr int NDT = DV / 32;        // 16-dim tiles of O^T per half
     bf16x8 qb[KS];
     f32x4 o[NDT];
     float m_run, l_run;
 
-    __device__ __forceinline__ void init(const AttnArgs& a, int r, int head, int g) {
-        const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + head) * D;
+    __device__ __forceinline__ void init(const AttnArgs& a, int r, int head, int g, int half) {
+        const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + head) * D + half * (D / 2);
 #pragma unroll
         for (int s = 0; s < KS; ++s) qb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + 32 * s + 8 * g));
 #pragma unroll
@@ -230,29 +233,41 @@ struct WaveAttn {
         l_run = 0.0f;
     }
 
-    __device__ __forceinline__ void tile(const lds_u8* lds, const lds_f32* kmeta, float scale_log2, int g, int c16) {
+    // xs_mine / xs_pair: this wave's and the partner wave's score exchange
+    // slots, [8][64] floats each.
+    __device__ __forceinline__ void tile(const lds_u8* lds, const lds_f32* kmeta, lds_f32* xs_mine,
+                                         const lds_f32* xs_pair, float scale_log2, int g, int c16, int lane, int half) {
         constexpr int ROWB = Geo<D>::ROWB;
-        // S^T = K Q^T over two 16-key sub-tiles; lane holds keys kt*16 + 4g + v of its head
+        // partial S^T = K Q^T over this half's dims, two 16-key sub-tiles, two
+        // accumulators each so consecutive MFMAs are independent
         f32x4 sacc[2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-            sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const lds_u8* rowp = lds + (kt * 16 + c16) * ROWB + 16 * g;
+            f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+            const lds_u8* rowp = lds + (kt * 16 + c16) * ROWB + half * D + 16 * g;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 bf16x8 kA = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(rowp + 64 * s));
-                sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, qb[s], sacc[kt], 0, 0, 0);
+                if (s & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, qb[s], acc1, 0, 0, 0);
+                else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, qb[s], acc0, 0, 0, 0);
             }
+            sacc[kt] = acc0 + acc1;
         }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) xs_mine[(kt * 4 + v) * 64 + lane] = sacc[kt][v];
+        __syncthreads();
         float x[2][4], ks[2][4];
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
+                const float full = sacc[kt][v] + xs_pair[(kt * 4 + v) * 64 + lane];
                 const float km = kmeta[kt * 16 + 4 * g + v];
                 ks[kt][v] = km;
-                x[kt][v] = km >= 0.0f ? sacc[kt][v] * scale_log2 * km : -INFINITY;
+                x[kt][v] = km >= 0.0f ? full * scale_log2 * km : -INFINITY;
                 mx = fmaxf(mx, x[kt][v]);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -285,21 +300,34 @@ struct WaveAttn {
         l_run += psum;
         const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
         const bf16x8 pbl = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
-        // O^T += V^T P^T.  Within each 16-lane block, ds_read_b64_tr_b16 hands lane i
-        // element (i & 3) of the 8-byte chunk addressed by lane (i >> 2) + 4e, e = 0..3:
-        // lane s addresses key 4g + (s >> 2), dims dt*16 + 4(s & 3) .. +3, so lane i
-        // receives keys 4g + e at dim dt*16 + i.
-        const lds_u8* vbase = lds + (4 * g + (c16 >> 2)) * ROWB + 8 * (c16 & 3);
+        // O^T += V^T P^T over this half's value dims.  Within each 16-lane block,
+        // ds_read_b64_tr_b16 hands lane i element (i & 3) of the 8-byte chunk
+        // addressed by lane (i >> 2) + 4e, e = 0..3: lane s addresses key
+        // 4g + (s >> 2), dims dt*16 + 4(s & 3) .. +3, so lane i receives keys
+        // 4g + e at dim dt*16 + i.  The hi and lo products of a dim tile are
+        // issued four tiles apart so they do not wait on each other.
+        const lds_u8* vbase = lds + (4 * g + (c16 >> 2)) * ROWB + half * (DV / 2) * 2 + 8 * (c16 & 3);
+        constexpr int G4 = 4;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const lds_u8* p0 = vbase + dt * 32;
-            i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-            i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 16 * ROWB));
-            const bf16x8 vA = __builtin_bit_cast(
-                bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                              __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pb, o[dt], 0, 0, 0);
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pbl, o[dt], 0, 0, 0);
+        for (int d0 = 0; d0 < NDT; d0 += G4) {
+            bf16x8 vA[G4];
+#pragma unroll
+            for (int j = 0; j < G4; ++j) {
+                if (d0 + j < NDT) {
+                    const lds_u8* p0 = vbase + (d0 + j) * 32;
+                    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+                    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 16 * ROWB));
+                    vA[j] = __builtin_bit_cast(
+                        bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                                      __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < G4; ++j)
+                if (d0 + j < NDT) o[d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA[j], pb, o[d0 + j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < G4; ++j)
+                if (d0 + j < NDT) o[d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA[j], pbl, o[d0 + j], 0, 0, 0);
         }
     }
 };
@@ -308,7 +336,7 @@ constexpr int kBtLds = 4096;           // block-table entries cached in LDS
 constexpr int kIdxLds = 2560;          // top-k slots cached in LDS (= max keys per split)
 
 template <int KVD, int WD, int D, int DV, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(AttnArgs a) {
     using G = Geo<D>;
     constexpr int NT = NW * 64;
     using TL = Tiler<KVD, WD, D, NT>;
@@ -320,6 +348,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     __shared__ float kmeta[2][kKeys];
     __shared__ int32_t bt_mem[kBtLds];
     __shared__ int32_t idx_mem[kIdxLds];
+    __shared__ float xs_mem[NW][8 * 64];                          // partial-score exchange
     lds_i32* const bt_lds = (lds_i32*)&bt_mem[0];
     lds_i32* const idx_lds = (lds_i32*)&idx_mem[0];
 
@@ -330,7 +359,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const int tb = split * a.split_tiles;
     if (tb >= rk.tiles) return;                                   // empty split (the merge skips it)
     const int te = min(tb + a.split_tiles, rk.tiles);
-    const int head = (int)blockIdx.z * (NW * 16) + wave * 16 + c16;
+    // waves w and w + NW/2 share 16 heads and split the dimensions
+    const int hg = wave % (NW / 2), half = wave / (NW / 2);
+    const int head = (int)blockIdx.z * (NW * 8) + hg * 16 + c16;
 
     // prologue: top-k slots and block-table range of this split into LDS
     const int sel_end = min(te, rk.sel_tiles) * kKeys;            // selected slots [tb*32, sel_end)
@@ -353,8 +384,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     for (int i = tid; i < min(nblk, kBtLds); i += NT) bt_lds[i] = a.block_table[(int64_t)rk.b * a.max_blocks + blk0 + i];
     __syncthreads();
 
-    WaveAttn<D, DV> W;
-    W.init(a, r, head, g);
+    HalfWave<D, DV> W;
+    W.init(a, r, head, g, half);
+    lds_f32* const xs_mine = (lds_f32*)&xs_mem[wave][0];
+    const lds_f32* const xs_pair = (lds_f32*)&xs_mem[wave ^ (NW / 2)][0];
 
     TileRegs<NU> R[kPrefetch];
     const int ntl = te - tb;
@@ -373,7 +406,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
         constexpr int nxt = (decltype(J)::value + 1) % kPrefetch;
         if (t + 1 < ntl) TL::store(rk, tb + t + 1, R[nxt], st + ((t + 1) & 1) * G::STAGE, km + ((t + 1) & 1) * kKeys);
         TL::load(a, rk, tb + t + 1 + kPrefetch, t + 1 + kPrefetch < ntl, idx_lds, idx0, bt_lds, blk0, R[nxt]);
-        W.tile(st + (t & 1) * G::STAGE, km + (t & 1) * kKeys, a.scale_log2, g, c16);
+        W.tile(st + (t & 1) * G::STAGE, km + (t & 1) * kKeys, xs_mine, xs_pair, a.scale_log2, g, c16, lane, half);
         __syncthreads();
     };
     for (int t0 = 0; t0 < ntl; t0 += kPrefetch) {
@@ -385,10 +418,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     // finish: total row sum of this head over the 4 lane groups
     float l_tot = W.l_run + __shfl_xor(W.l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
-    constexpr int NDT = DV / 16;
+    constexpr int NDT = HalfWave<D, DV>::NDT;
+    const int dv0 = half * (DV / 2) + 4 * g;
     if (a.nsplit == 1) {
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        const int64_t base = ((int64_t)r * a.H + head) * DV + 4 * g;
+        const int64_t base = ((int64_t)r * a.H + head) * DV + dv0;
         if (a.out_dtype == DT_F32) {
             float* out = reinterpret_cast<float*>(a.out) + base;
 #pragma unroll
@@ -401,12 +435,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
                 *reinterpret_cast<u32x2*>(out + dt * 16) = u32x2{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
             }
         }
-        if (a.lse && g == 0) a.lse[(int64_t)r * a.H + head] = (W.m_run + log2f(l_tot)) * kLn2;
+        if (a.lse && g == 0 && half == 0) a.lse[(int64_t)r * a.H + head] = (W.m_run + log2f(l_tot)) * kLn2;
     } else {
-        float* po = a.part_o + (((int64_t)r * a.nsplit + split) * a.H + head) * DV + 4 * g;
+        float* po = a.part_o + (((int64_t)r * a.nsplit + split) * a.H + head) * DV + dv0;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = W.o[dt];
-        if (g == 0) {
+        if (g == 0 && half == 0) {
             float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H;
             ml[head] = W.m_run;
             ml[a.H + head] = l_tot;
@@ -531,7 +565,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
 template <int KVD, int WD, int D, int DV, int NW>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
-    dim3 grid(a.nsplit, a.num_rows, a.H / (NW * 16));
+    dim3 grid(a.nsplit, a.num_rows, a.H / (NW * 8));
     hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, NW>), grid, dim3(NW * 64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
@@ -539,11 +573,11 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Workgroups of four waves cover 64 heads; more heads add head groups to the grid.
+// Workgroups of eight waves cover 64 heads; more heads add head groups to the grid.
 template <int KVD, int WD, int D, int DV>
 hipError_t launch_heads(const AttnArgs& a, hipStream_t stream) {
     if (a.H % 64 != 0) return hipErrorInvalidValue;
-    return launch_mfma<KVD, WD, D, DV, 4>(a, stream);
+    return launch_mfma<KVD, WD, D, DV, 8>(a, stream);
 }
 
 template <int KVD, int WD>
