@@ -86,18 +86,31 @@ struct SeqChunk {
     int64_t c0;
 };
 
-__device__ inline SeqChunk seq_of(const CompressArgs& p, int t) {
-    // sequence of token t: the largest b with cu_new[b] <= t
+constexpr int kSeqLds = 1024;                 // batches up to this size search in LDS
+
+// Sequence of token t: the largest b with cu_new[b] <= t.  For batches of up
+// to kSeqLds sequences, cu_new and start_pos are first copied to LDS in one
+// round of loads, so the search costs no dependent global loads.
+__device__ inline SeqChunk seq_of(const CompressArgs& p, int t, int* cu_lds, int* sp_lds) {
+    const bool in_lds = p.batch <= kSeqLds;
+    if (in_lds) {
+        for (int i = threadIdx.x; i <= p.batch; i += blockDim.x) {
+            cu_lds[i] = p.cu_new[i];
+            if (i < p.batch) sp_lds[i] = p.start_pos[i];
+        }
+        __syncthreads();
+    }
+    auto cu = [&](int i) { return in_lds ? cu_lds[i] : p.cu_new[i]; };
     int lo = 0, hi = p.batch - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (p.cu_new[mid] <= t) lo = mid; else hi = mid - 1;
+        if (cu(mid) <= t) lo = mid; else hi = mid - 1;
     }
     SeqChunk q;
     q.b = lo;
-    q.c0 = p.cu_new[lo];
-    q.n = p.cu_new[lo + 1] - (int)q.c0;
-    q.start = p.start_pos[lo];
+    q.c0 = cu(lo);
+    q.n = cu(lo + 1) - (int)q.c0;
+    q.start = in_lds ? sp_lds[lo] : p.start_pos[lo];
     q.end = q.start + q.n;
     return q;
 }
@@ -217,9 +230,10 @@ template <int TOK>
 __global__ __launch_bounds__(kThreads) void compress_append_kernel(CompressArgs p) {
     __shared__ float w_lds[256];
     __shared__ float red[kLanes * kSliceDims];
+    __shared__ int cu_lds[kSeqLds + 1], sp_lds[kSeqLds];
     const int t = blockIdx.x, s = blockIdx.y;
     const int tid = threadIdx.x;
-    const SeqChunk q = seq_of(p, t);
+    const SeqChunk q = seq_of(p, t, cu_lds, sp_lds);
     const int pos = q.start + (t - (int)q.c0);
     const int m = p.m, D = p.D;
     const int SK = (D + kSliceDims - 1) / kSliceDims;

@@ -20,6 +20,8 @@
 // tile ranges.  Prefill (many rows): a workgroup covers 4 consecutive rows
 // (one per wave) that share the same tile range, so the keys are fetched
 // from HBM once and re-read from L1/L2 by the other waves.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -29,30 +31,35 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Raw key registers of one lane: its half of one entry's key, loaded as
+// stored (bf16, or E4M3 converted to bf16 right before the MFMA), so a tile
+// in flight costs 32 (bf16) or 16 (FP8) VGPRs.
 template <int KD, int KS>
-__device__ inline void load_keys(const uint8_t* keys, int64_t row, int g, bf16x8 (&kb)[KS]) {
+struct RawKey {
+    typedef typename std::conditional<KD == DT_BF16, u32x4, u32x2>::type word;
+    word w[KS];
+};
+
+template <int KD, int KS>
+__device__ __forceinline__ void load_key(const uint8_t* keys, int64_t row, int g, RawKey<KD, KS>& k) {
     constexpr int DI = KS * 16, HALF = DI / 2;
-    if (KD == DT_BF16) {
+    if constexpr (KD == DT_BF16) {
         const u32x4* src = reinterpret_cast<const u32x4*>(keys + (row * DI + g * HALF) * 2);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            u32x4 v = src[s];
-            kb[s] = __builtin_bit_cast(bf16x8, v);
-        }
+        for (int s = 0; s < KS; ++s) k.w[s] = src[s];
     } else {
         const u32x2* src = reinterpret_cast<const u32x2*>(keys + row * DI + g * HALF);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            u32x2 v = src[s];
-            u32x4 o;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                uint32_t w = v[h];
-                o[2 * h] = fp8_to_bf16(w & 0xffu) | (fp8_to_bf16((w >> 8) & 0xffu) << 16);
-                o[2 * h + 1] = fp8_to_bf16((w >> 16) & 0xffu) | (fp8_to_bf16(w >> 24) << 16);
-            }
-            kb[s] = __builtin_bit_cast(bf16x8, o);
-        }
+        for (int s = 0; s < KS; ++s) k.w[s] = src[s];
+    }
+}
+
+template <int KD, int KS>
+__device__ inline bf16x8 key_operand(const RawKey<KD, KS>& k, int s) {
+    if constexpr (KD == DT_BF16) {
+        return __builtin_bit_cast(bf16x8, k.w[s]);
+    } else {
+        return __builtin_bit_cast(bf16x8, fp8x8_to_bf16(k.w[s][0], k.w[s][1]));
     }
 }
 
@@ -61,53 +68,86 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(IndexArgs p) {
     constexpr int KS = DI / 16, HALF = DI / 2;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, j = lane & 31;
-    const int r = ROWS == 1 ? (int)blockIdx.y : (int)blockIdx.y * 4 + wave;
-    if (r >= p.num_rows) return;
+    const int r_raw = ROWS == 1 ? (int)blockIdx.y : (int)blockIdx.y * 4 + wave;
+    const bool row_ok = r_raw < p.num_rows;
+    const int r = row_ok ? r_raw : p.num_rows - 1;
     const int tpw = p.tiles_per_wave;
     int t_begin = ROWS == 1 ? ((int)blockIdx.x * 4 + wave) * tpw : (int)blockIdx.x * tpw;
     const int b = p.row_seq[r];
     const int n = visible_entries(p.row_pos[r], p.m);
     const int ntiles = (n + 31) >> 5;
     const int t_end = min(t_begin + tpw, ntiles);
-    if (t_begin >= t_end) return;
-    const int E = 256 / p.m;
+    const bool work = row_ok && t_begin < t_end;
+    const int sh = __builtin_ctz(256 / p.m);                    // E = 256/m entries per block, a power of two
     const int32_t* bt = p.block_table + (int64_t)b * p.max_blocks;
     const uint8_t* keys = reinterpret_cast<const uint8_t*>(p.keys);
 
+    // Loads are issued unconditionally (tile indices clamped to the wave's
+    // range) so the compiler's wait counts stay exact.  The block-table entry
+    // of a tile is fetched one tile ahead of its keys, the keys one tile
+    // ahead of their MFMAs.
+    auto entry = [&](int tile) { return min(min(tile, t_end - 1) * 32 + j, n - 1); };
+    auto table = [&](int tile) { return bt[entry(tile) >> sh]; };
+    auto row = [&](int tile, int pb) -> int64_t {
+        return ((int64_t)pb << sh) + (entry(tile) & ((1 << sh) - 1));
+    };
+    int pb_next = 0;
+    RawKey<KD, KS> kcur;
+    if (work) {
+        pb_next = table(t_begin + 1);
+        load_key<KD, KS>(keys, row(t_begin, table(t_begin)), g, kcur);
+    }
+
+    // The query (HI x DI bf16) and head weights of the workgroup's row(s) are
+    // staged in LDS once (rows padded by 16 bytes against bank conflicts);
+    // every wave then reads its A operands from there instead of from L2.
+    constexpr int QROWB = DI * 2 + 16;
+    constexpr int NQ = ROWS == 1 ? 1 : 4;
+    __shared__ __attribute__((aligned(16))) uint8_t q_lds[NQ][NHT * 32 * QROWB];
+    __shared__ float w_lds[NQ][NHT * 32];
+    {
+        const int slot = ROWS == 1 ? 0 : wave;
+        const int nthr = ROWS == 1 ? kThreads : 64;
+        const int t0 = ROWS == 1 ? (int)threadIdx.x : lane;
+        const uint8_t* qg = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)r * p.HI * DI * 2;
+        constexpr int UPR = DI * 2 / 16;                         // 16-byte units per head
+        for (int u = t0; u < NHT * 32 * UPR; u += nthr) {
+            const int h = u / UPR, part = u % UPR;
+            *reinterpret_cast<u32x4*>(&q_lds[slot][h * QROWB + part * 16]) =
+                *reinterpret_cast<const u32x4*>(qg + (int64_t)h * DI * 2 + part * 16);
+        }
+        for (int h = t0; h < NHT * 32; h += nthr) w_lds[slot][h] = p.w[(int64_t)r * p.HI + h] * p.s_I;
+    }
+    __syncthreads();
+    const int slot = ROWS == 1 ? 0 : wave;
     // query as A operands: head 32t + j, dims [g*HALF + 8s, +8)
     bf16x8 qa[NHT][KS];
-    const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)r * p.HI * DI;
 #pragma unroll
     for (int t = 0; t < NHT; ++t)
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-            qa[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + (32 * t + j) * DI + g * HALF + 8 * s));
+            qa[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                      &q_lds[slot][(32 * t + j) * QROWB + (g * HALF + 8 * s) * 2]));
     // head weights in C-layout order: head 32t + 8(v/4) + 4g + v%4
     float wv[NHT][16];
 #pragma unroll
     for (int t = 0; t < NHT; ++t)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            wv[t][v] = p.w[(int64_t)r * p.HI + 32 * t + 8 * (v >> 2) + 4 * g + (v & 3)] * p.s_I;
+        for (int v = 0; v < 16; ++v) wv[t][v] = w_lds[slot][32 * t + 8 * (v >> 2) + 4 * g + (v & 3)];
 
-    auto key_row = [&](int tile) -> int64_t {
-        int e = min(tile * 32 + j, n - 1);
-        return (int64_t)bt[e / E] * E + e % E;
-    };
-
-    bf16x8 kb[KS];
-    load_keys<KD, KS>(keys, key_row(t_begin), g, kb);
     float* out = p.logits + (int64_t)r * p.ld;
-    for (int tile = t_begin; tile < t_end; ++tile) {
-        bf16x8 kn[KS];
-        if (tile + 1 < t_end) load_keys<KD, KS>(keys, key_row(tile + 1), g, kn);
+    auto step = [&](int tile, RawKey<KD, KS>& kc, RawKey<KD, KS>& kn) __attribute__((always_inline)) {
+        const int pb2 = table(tile + 2);
+        load_key<KD, KS>(keys, row(tile + 1, pb_next), g, kn);
+        pb_next = pb2;
         f32x16 acc[NHT];
 #pragma unroll
-        for (int t = 0; t < NHT; ++t) {
-            acc[t] = f32x16{};
+        for (int t = 0; t < NHT; ++t) acc[t] = f32x16{};
 #pragma unroll
-            for (int s = 0; s < KS; ++s) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t][s], kb[s], acc[t], 0, 0, 0);
-        }
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int t = 0; t < NHT; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t][s], key_operand<KD, KS>(kc, s), acc[t], 0, 0, 0);
         float l = 0.0f;
 #pragma unroll
         for (int t = 0; t < NHT; ++t)
@@ -116,8 +156,12 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(IndexArgs p) {
         l += __shfl_xor(l, 32);
         const int e = tile * 32 + j;
         if (g == 0 && e < n) out[e] = l;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kb[s] = kn[s];
+    };
+    RawKey<KD, KS> kalt;
+    if (!work) return;
+    for (int tile = t_begin; tile < t_end; tile += 2) {
+        step(tile, kcur, kalt);
+        if (tile + 1 < t_end) step(tile + 1, kalt, kcur);
     }
 }
 

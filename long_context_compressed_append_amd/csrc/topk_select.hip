@@ -63,13 +63,29 @@ struct Chunk {
     int c0, c1;                 // entry range [c0, c1)
     const float* L;
 
-    __device__ void init(const float* logits, int n, int per_thread) {
+    // per_thread is a multiple of 4; with `vec` the row is 16-byte aligned and
+    // the chunk is read with 16-byte loads.
+    __device__ void init(const float* logits, int n, int per_thread, bool vec) {
         L = logits;
         c0 = min((int)threadIdx.x * per_thread, n);
         c1 = min(c0 + per_thread, n);
         if (R > 0) {
+            if (vec) {
 #pragma unroll
-            for (int i = 0; i < R; ++i) u[i] = c0 + i < c1 ? order_key(L[c0 + i]) : 0u;
+                for (int i = 0; i < R; i += 4) {
+                    if (c0 + i < c1) {
+                        const f32x4 v = *reinterpret_cast<const f32x4*>(L + c0 + i);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) u[i + e] = c0 + i + e < c1 ? order_key(v[e]) : 0u;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) u[i + e] = 0u;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < R; ++i) u[i] = c0 + i < c1 ? order_key(L[c0 + i]) : 0u;
+            }
         }
     }
     template <class F>
@@ -86,8 +102,7 @@ struct Chunk {
 
 template <int R>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
-    __shared__ uint32_t hist[kCopies][256];
-    __shared__ uint32_t tot[256];
+    __shared__ uint32_t hist[2][kCopies][256];
     __shared__ uint32_t wsum[kWaves];
     __shared__ uint32_t red[2][kWaves];
     __shared__ uint32_t sel_digit, sel_above;
@@ -100,9 +115,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
         for (int i = tid; i < k; i += kThreads) out[i] = i < n ? i : -1;
         return;
     }
-    const int per_thread = (n + kThreads - 1) / kThreads;
+    const int per_thread = ((n + kThreads - 1) / kThreads + 3) & ~3;
     Chunk<R> C;
-    C.init(p.logits + (int64_t)r * p.ld, n, per_thread);
+    const float* row = p.logits + (int64_t)r * p.ld;
+    C.init(row, n, per_thread, (reinterpret_cast<uintptr_t>(row) & 15) == 0);
 
     // 1. common leading bits of all keys
     uint32_t kmin = 0xffffffffu, kmax = 0u;
@@ -121,30 +137,32 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
     uint32_t prefix = kmax & mask;
     uint32_t need = (uint32_t)k;                                // keys still to take among those matching
 
-    // 2. radix passes from the highest differing bit down
+    // 2. radix passes from the highest differing bit down.  Two histogram
+    // buffers: while wave 0 sums the copies of this pass's buffer and scans
+    // it, the other waves clear the buffer of the next pass.
+    for (int i = tid; i < kCopies * 256; i += kThreads) (&hist[0][0][0])[i] = 0u;
+    __syncthreads();
+    int cur = 0;
     while (top >= 0) {
         const int w = min(8, top + 1);
         const int shift = top - w + 1;
         const uint32_t bins = 1u << w;
-        for (int i = tid; i < kCopies * 256; i += kThreads) (&hist[0][0])[i] = 0u;
-        __syncthreads();
-        uint32_t* h = hist[lane & (kCopies - 1)];
+        uint32_t* h = hist[cur][lane & (kCopies - 1)];
         C.each([&](int, uint32_t u) {
             if ((u & mask) == prefix) atomicAdd(&h[(u >> shift) & (bins - 1)], 1u);
         });
-        __syncthreads();
-        if (tid < 256) {
-            uint32_t c = 0;
-#pragma unroll
-            for (int cp = 0; cp < kCopies; ++cp) c += hist[cp][tid];
-            tot[tid] = c;
-        }
         __syncthreads();
         if (tid < 64) {
             // lane l owns bins 4l..4l+3; suffix sums from the top digit down
             uint32_t c[4], s = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { c[i] = tot[4 * tid + i]; s += c[i]; }
+            for (int i = 0; i < 4; ++i) {
+                uint32_t t = 0;
+#pragma unroll
+                for (int cp = 0; cp < kCopies; ++cp) t += hist[cur][cp][4 * tid + i];
+                c[i] = t;
+                s += t;
+            }
             uint32_t suf = s;
             for (int o = 1; o < 64; o <<= 1) {
                 uint32_t t = __shfl_down(suf, o);
@@ -156,13 +174,15 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
                 if (above < need && above + c[i] >= need) { sel_digit = 4 * tid + i; sel_above = above; }
                 above += c[i];
             }
+        } else {
+            for (int i = tid - 64; i < kCopies * 256; i += kThreads - 64) (&hist[cur ^ 1][0][0])[i] = 0u;
         }
         __syncthreads();
         prefix |= sel_digit << shift;
         mask |= (bins - 1u) << shift;
         need -= sel_above;
         top = shift - 1;
-        __syncthreads();
+        cur ^= 1;
     }
     const uint32_t T = prefix;
 
@@ -187,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
 
 hipError_t launch_topk_select(const TopkArgs& a, int max_entries, hipStream_t stream) {
     if (a.num_rows <= 0 || a.k <= 0) return hipSuccess;
-    const int per_thread = (max_entries + kThreads - 1) / kThreads;
+    const int per_thread = ((max_entries + kThreads - 1) / kThreads + 3) & ~3;
     if (per_thread <= 8) hipLaunchKernelGGL(topk_kernel<8>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
     else if (per_thread <= 16) hipLaunchKernelGGL(topk_kernel<16>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
     else if (per_thread <= 32) hipLaunchKernelGGL(topk_kernel<32>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
