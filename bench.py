@@ -1,20 +1,26 @@
 #!/usr/bin/env python3
-"""Decode-step benchmark of compressed-KV attention on one MI355X.
+"""Decode and chunked-prefill benchmark of compressed-KV attention on one MI355X.
 
-One step is the whole hot path for one batch of decode query rows:
-compress_append (one new token per sequence, completing one entry) ->
-index_logits -> topk_select -> sparse_attn_fwd, all launched back to back on
-one HIP stream through liblcca's C ABI.  Inputs are seeded synthetic tensors
-generated on the device with torch (N(0,1), 1% outlier channels x8 where the
-workload has them, bf16 entries, FP8 E4M3 window with a per-token scale) and
+One step is the whole hot path for one batch of query rows:
+compress_append -> index_logits -> topk_select -> sparse_attn_fwd (+ the
+split merge), all launched back to back on one HIP stream through liblcca's
+C ABI.  Inputs are seeded synthetic tensors generated on the device with
+torch (N(0,1) values, 1% outlier channels x8 where the workload has them,
+caches encoded by torch casts: bf16 RNE, FP8 E4M3 RNE with a per-token
+scale for windows, raw E4M3 for FP8 indexer keys, OCP MXFP4 with RNE) and
 resident in HBM before the timed region starts.
 
-Workloads timed:
-  csa_64k  16 sequences x 65,536 tokens, m=4 (16,384 entries each), 64 query
-           heads, dim 576, indexer 64 x 128, top-k 2,048, 128-token FP8 window.
-           This is the line's `value`.
-  hca_1m   4 sequences x 1,048,576 tokens, m=128 (8,192 entries each), dense
-           attention over every entry plus the window (no indexer / top-k).
+Workloads (one attention layer each):
+  csa_64k     16 sequences x 65,536 tokens, m=4 (16,384 bf16 entries each),
+              64 query heads, dim 576, indexer 64 x 128, top-k 2,048,
+              128-token FP8 window.  This is the line's `value`.
+  hca_1m      4 sequences x 1,048,576 tokens, m=128 (8,192 entries each),
+              dense attention over every entry plus the window.
+  lp_512k     32 sequences x 524,288 tokens, m=4, MXFP4 entries, FP8 indexer
+              keys, FP8 window, top-k 2,048.
+  prefill_8k  1 sequence: 122,880 prior tokens + an 8,192-token chunk
+              compressed and appended; one query row per new token; bf16
+              window.
 
 Cold-cache rule: the caches are replicated R times so that R copies exceed
 1 GiB (four times the 256 MiB Infinity Cache) and step i reads copy i % R;
@@ -22,11 +28,12 @@ Cold-cache rule: the caches are replicated R times so that R copies exceed
 
 Per-stage times come from HIP events recorded between the launches on the
 stream they run on.  Algorithmic bytes count the unique bytes each stage must
-move (see the formulas in `stage_bytes`).  The CPU baseline is the oracle
-(plain fp64 C, OpenMP over rows) timed on the host on a sample of the same
-step, on the same bytes copied to the host before the first device step.
+move (`Workload.stage_work`).  The CPU baseline is the oracle (plain fp64 C,
+OpenMP over rows) timed on the host on a sample of the headline step, on the
+same bytes copied to the host before the first device step; every workload's
+sampled rows are also compared with the oracle (`parity`).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads a,b]
 """
 import argparse
 import hashlib
@@ -44,6 +51,7 @@ METRIC = "decode query-rows/s + achieved HBM GB/s (% peak) at 64K/1M ctx, 1 MI35
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 COLD_BYTES = 1 << 30
+CHUNK_ELEMS = 1 << 25                   # device temporaries while encoding large pools
 
 
 def log(*a):
@@ -51,24 +59,103 @@ def log(*a):
 
 
 # --------------------------------------------------------------------------
+# device-side encoders (input construction only; the oracle checks them)
+# --------------------------------------------------------------------------
+
+def enc_bf16(torch, x):
+    return x.to(torch.bfloat16).contiguous().view(torch.uint8).reshape(-1)
+
+
+def enc_fp8_scaled(torch, x):
+    """Per-row scale s = amax/448 (1 for a zero row), codes = RNE(x/s) in E4M3."""
+    amax = x.abs().amax(-1, keepdim=True)
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    codes = (x / s).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return codes.contiguous().view(torch.uint8).reshape(-1), s.reshape(-1).contiguous()
+
+
+def enc_fp8_raw(torch, x):
+    return x.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).contiguous().view(torch.uint8).reshape(-1)
+
+
+def enc_mxfp4(torch, x):
+    """OCP MX: per 32 elements X = floor(log2 amax) - 2 (amax 0 -> -127), E2M1
+    codes of x / 2^X rounded to nearest even, saturating at 6; element 2i in
+    the low nibble.  Returns (codes uint8 [rows*dim/2], scales uint8 [rows*dim/32])."""
+    rows, dim = x.shape
+    xb = x.reshape(rows, dim // 32, 32)
+    amax = xb.abs().amax(-1)
+    _, e = torch.frexp(amax)
+    X = torch.where(amax > 0, e - 3, torch.full_like(e, -127)).clamp(-127, 127)
+    a = torch.ldexp(xb.abs(), -X.unsqueeze(-1).to(torch.float32))
+    code = ((a > 0.25).int() + (a >= 0.75).int() + (a > 1.25).int() + (a >= 1.75).int() + (a > 2.5).int()
+            + (a >= 3.5).int() + (a > 5.0).int())
+    nib = (code | (torch.signbit(xb).int() << 3)).reshape(rows, dim // 2, 2)
+    data = (nib[..., 0] | (nib[..., 1] << 4)).to(torch.uint8).reshape(-1)
+    scale = (X + 127).to(torch.uint8).reshape(-1)
+    return data, scale
+
+
+# --------------------------------------------------------------------------
 # workload construction (device-side, seeded)
 # --------------------------------------------------------------------------
 
+def stage_work(c):
+    """Algorithmic (bytes, flops) per stage: the unique bytes each stage
+    must read and write (every cache row counted once per step, however
+    many rows or heads use it) and the multiply-adds it must do."""
+    import numpy as np
+    m, D, H, HI, dI, k, w = c.m, c.D, c.H, c.HI, c.dI, c.k, c.window
+    kv_row = {"bf16": 2 * D, "mxfp4": D // 2 + D // 32}[c.kv_dtype]
+    ik_row = {"bf16": 2 * dI, "fp8": dI}[c.ik_dtype] if HI else 0
+    win_row = {"fp8": D + 4, "bf16": 2 * D}[c.win_dtype]
+    tok_row = 2 * D + 4 + ((2 * dI + 4) if HI else 0)      # bf16 token + its logit, both streams
+    seq, pos = c.rows_of()
+    pos = pos.astype(np.int64)
+    n_r = (pos + 1) // m
+    nwin = np.minimum(pos + 1, w)
+    nsel = np.minimum(n_r, k) if HI else n_r
+    comp = idx_b = topk_b = attn_b = 0
+    for b in range(c.batch):
+        P, T, nn = c.prior_len[b], c.total_len(b), c.n_new[b]
+        groups = T // m - P // m
+        ring_in = (P % m) if groups else 0                  # earlier tokens of the first completed group
+        tail = min(nn, T % m)                               # new tokens left in the remainder ring
+        comp += nn * (tok_row + win_row) + ring_in * tok_row + tail * tok_row + groups * (kv_row + ik_row)
+        sel = seq == b
+        if not sel.any():
+            continue
+        nb = c.blocks_per_seq(b)
+        keys = int(n_r[sel].max())                          # every visible key of the sequence, once
+        if HI:
+            idx_b += keys * ik_row + nb * 4 + int(sel.sum()) * (HI * dI * 2 + 4 * HI) + 4 * int(n_r[sel].sum())
+            topk_b += 4 * int(n_r[sel].sum()) + 4 * k * int(sel.sum())
+        span = int(pos[sel].max() - max(0, pos[sel].min() - w + 1) + 1)
+        attn_b += (min(int(nsel[sel].sum()), keys) * kv_row + (4 * k * int(sel.sum()) if HI else 0)
+                   + min(int(nwin[sel].sum()), span) * win_row)
+    nrows = len(pos)
+    attn_b += nrows * (H * D * 2 + H * c.dv * 2 + 4 * H)
+    idx_f = int(2 * HI * dI * n_r.sum()) if HI else 0
+    attn_f = int(2 * H * (D + c.dv) * (nsel + nwin).sum())
+    return {"compress_append": (int(comp), 0), "index_logits": (int(idx_b), idx_f),
+            "topk_select": (int(topk_b), 0), "sparse_attn_fwd": (int(attn_b), attn_f)}
+
+
 class Workload:
-    """Device tensors of one decode step and R rotated cache copies."""
+    """Device tensors of one step of a workload and R rotated cache copies."""
 
     def __init__(self, name, torch, lcca, synth, cold=True):
         self.name = name
         self.cfg = c = synth.CONFIGS[name]
         self.torch, self.lcca = torch, lcca
         dev = "cuda"
-        assert c.rows == "last" and all(n == 1 for n in c.n_new), "decode workloads only"
         B, m, D, H, HI, dI = c.batch, c.m, c.D, c.H, c.HI, c.dI
         self.B = B
         E = c.E
         nb = c.max_blocks
         nblk = c.num_blocks
         self.seed_base = (0x1CCA << 16) | (c.cfg_id << 8)
+        assert c.tok_dtype == synth.BF16 and c.q_dtype == synth.BF16
 
         def gen(tid):
             g = torch.Generator(device=dev)
@@ -77,81 +164,106 @@ class Workload:
 
         def outliers(dim, stream):
             n = int(round(c.outlier_frac * dim))
-            if n == 0:
+            if n == 0 or dim == 0:
                 return None
             g = torch.Generator()
             g.manual_seed(self.seed_base + 100 + stream)
             return torch.randperm(dim, generator=g)[:n].to(dev)
 
-        och = {0: outliers(D, 0), 1: outliers(dI, 1) if HI else None}
+        och = {0: outliers(D, 0), 1: outliers(dI, 1)}
 
-        def values(tid, shape, stream):
-            x = torch.randn(shape, generator=gen(tid), device=dev, dtype=torch.float32)
+        def values(g, shape, stream):
+            x = torch.randn(shape, generator=g, device=dev, dtype=torch.float32)
             ch = och[stream]
             if ch is not None:
                 x[..., ch] *= c.outlier_mult
             return x
 
-        def bf16_bytes(x):
-            return x.to(torch.bfloat16).contiguous().view(torch.uint8).reshape(-1)
+        def rows_of(tid, nrows, dim, stream, enc):
+            """nrows x dim values of one stream, encoded chunk by chunk."""
+            g = gen(tid)
+            step = max(1, CHUNK_ELEMS // dim)
+            parts, scales = [], []
+            for r0 in range(0, nrows, step):
+                x = values(g, (min(step, nrows - r0), dim), stream)
+                out = enc(x)
+                if isinstance(out, tuple):
+                    parts.append(out[0]); scales.append(out[1])
+                else:
+                    parts.append(out)
+                del x
+            data = torch.cat(parts) if len(parts) > 1 else parts[0]
+            sc = (torch.cat(scales) if len(scales) > 1 else scales[0]) if scales else None
+            return data, sc
 
-        def fp8_rows_scaled(x):
-            amax = x.abs().amax(-1, keepdim=True)
-            s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
-            codes = (x / s).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
-            return codes.contiguous().view(torch.uint8).reshape(-1), s.reshape(-1).contiguous()
+        bf16 = lambda x: enc_bf16(torch, x)
+        kv_enc = {synth.BF16: bf16, synth.MXFP4: lambda x: enc_mxfp4(torch, x)}[c.kv_dtype]
+        ik_enc = {synth.BF16: bf16, synth.FP8: lambda x: enc_fp8_raw(torch, x)}[c.ik_dtype] if HI else None
+        win_enc = {synth.FP8: lambda x: enc_fp8_scaled(torch, x), synth.BF16: bf16}[c.win_dtype]
+        LDT = {synth.BF16: lcca.BF16, synth.FP8: lcca.FP8_E4M3, synth.MXFP4: lcca.MXFP4}
+        self.kv_dt, self.win_dt = LDT[c.kv_dtype], LDT[c.win_dtype]
+        self.ik_dt = LDT[c.ik_dtype] if HI else None
 
-        assert c.kv_dtype == synth.BF16 and c.win_dtype == synth.FP8 and c.tok_dtype == synth.BF16
         g = torch.Generator()
         g.manual_seed(self.seed_base + 15)
         perm = torch.randperm(nblk, generator=g).to(torch.int32)
-        self.block_table = perm.reshape(B, nb).contiguous().to(dev)
+        bt = torch.zeros((B, nb), dtype=torch.int32)
+        o = 0
+        for b in range(B):
+            k = c.blocks_per_seq(b)
+            bt[b, :k] = perm[o:o + k]
+            o += k
+        self.block_table = bt.contiguous().to(dev)
 
-        kv_data = bf16_bytes(values(1, (nblk * E, D), 0))
-        ik_data = bf16_bytes(values(2, (nblk * E, dI), 1)) if HI else None
-        win_data, win_scale = fp8_rows_scaled(values(3, (B * c.win_cap, D), 0))
-        # remainder ring: the m-1 tokens before the new one (positions T-m .. T-2)
-        rem_kv = bf16_bytes(values(4, (B * m, D), 0))
-        rem_ik = bf16_bytes(values(5, (B * m, dI), 1)) if HI else None
+        kv_data, kv_scale = rows_of(1, nblk * E, D, 0, kv_enc)
+        ik_data = rows_of(2, nblk * E, dI, 1, ik_enc)[0] if HI else None
+        win_data, win_scale = rows_of(3, B * c.win_cap, D, 0, win_enc)
+        rem_kv = rows_of(4, B * m, D, 0, bf16)[0]
+        rem_ik = rows_of(5, B * m, dI, 1, bf16)[0] if HI else None
         rem_kv_logit = torch.randn(B * m, generator=gen(6), device=dev)
         rem_ik_logit = torch.randn(B * m, generator=gen(7), device=dev) if HI else None
-        self.new_kv = bf16_bytes(values(8, (B, D), 0))
-        self.new_ik = bf16_bytes(values(9, (B, dI), 1)) if HI else None
-        self.new_kv_logit = torch.randn(B, generator=gen(10), device=dev)
-        self.new_ik_logit = torch.randn(B, generator=gen(11), device=dev) if HI else None
-        self.q = bf16_bytes(values(12, (B, H, D), 0))
-        self.q_idx = bf16_bytes(values(13, (B, HI, dI), 1)) if HI else None
-        self.w_idx = torch.rand((B, HI), generator=gen(14), device=dev) if HI else None
+        total_new = sum(c.n_new)
+        self.total_new = total_new
+        self.new_kv = rows_of(8, total_new, D, 0, bf16)[0]
+        self.new_ik = rows_of(9, total_new, dI, 1, bf16)[0] if HI else None
+        self.new_kv_logit = torch.randn(total_new, generator=gen(10), device=dev)
+        self.new_ik_logit = torch.randn(total_new, generator=gen(11), device=dev) if HI else None
 
-        self.cu_new = torch.arange(B + 1, dtype=torch.int32, device=dev)
-        self.start_pos = torch.tensor([c.prior_len[b] for b in range(B)], dtype=torch.int32, device=dev)
-        self.row_seq = torch.arange(B, dtype=torch.int32, device=dev)
-        self.row_pos = torch.tensor([c.total_len(b) - 1 for b in range(B)], dtype=torch.int32, device=dev)
-        self.max_pos = max(c.total_len(b) for b in range(B)) - 1
+        rs, rp = c.rows_of()
+        self.nrows = len(rs)
+        self.row_seq = torch.from_numpy(rs).to(dev)
+        self.row_pos = torch.from_numpy(rp).to(dev)
+        self.row_pos_host = rp
+        self.max_pos = int(rp.max())
+        self.q = rows_of(12, self.nrows * H, D, 0, bf16)[0]
+        self.q_idx = rows_of(13, self.nrows * HI, dI, 1, bf16)[0] if HI else None
+        self.w_idx = torch.rand((self.nrows, HI), generator=gen(14), device=dev) if HI else None
+
+        self.cu_new = torch.tensor([0] + list(torch.tensor(c.n_new).cumsum(0).tolist()), dtype=torch.int32,
+                                   device=dev)
+        self.start_pos = torch.tensor(list(c.prior_len), dtype=torch.int32, device=dev)
         self.ld = c.max_entries
         self.pages = lcca.Pages(self.block_table)
         self.rows = lcca.Rows(self.row_seq, self.row_pos, self.max_pos)
 
-        # host copy of the initial state for the oracle (taken before any device step)
         self.host = None
-        self._init = dict(kv_data=kv_data, ik_data=ik_data, win_data=win_data, win_scale=win_scale, rem_kv=rem_kv,
-                          rem_ik=rem_ik, rem_kv_logit=rem_kv_logit, rem_ik_logit=rem_ik_logit)
-
-        footprint = sum(t.numel() * t.element_size() for t in self._init.values() if t is not None)
-        self.footprint = footprint
-        self.R = max(1, math.ceil(COLD_BYTES / footprint)) if cold else 1
+        self._init = dict(kv_data=kv_data, kv_scale=kv_scale, ik_data=ik_data, win_data=win_data,
+                          win_scale=win_scale, rem_kv=rem_kv, rem_ik=rem_ik, rem_kv_logit=rem_kv_logit,
+                          rem_ik_logit=rem_ik_logit)
+        self.footprint = sum(t.numel() * t.element_size() for t in self._init.values() if t is not None)
+        self.R = max(1, math.ceil(COLD_BYTES / self.footprint)) if cold else 1
         self.copies = []
         for i in range(self.R):
-            t = {k: (v.clone() if v is not None else None) for k, v in self._init.items()}
-            kv = lcca.PagedCache(lcca.BF16, D, m, nblk, t["kv_data"])
-            ik = lcca.PagedCache(lcca.BF16, dI, m, nblk, t["ik_data"]) if HI else None
-            win = lcca.WindowCache(lcca.FP8_E4M3, D, c.win_cap, c.window, t["win_data"], t["win_scale"])
+            t = self._init if i == 0 else {k: (v.clone() if v is not None else None) for k, v in self._init.items()}
+            kv = lcca.PagedCache(self.kv_dt, D, m, nblk, t["kv_data"], t["kv_scale"])
+            ik = lcca.PagedCache(self.ik_dt, dI, m, nblk, t["ik_data"]) if HI else None
+            win = lcca.WindowCache(self.win_dt, D, c.win_cap, c.window, t["win_data"], t["win_scale"])
             rem = lcca.Remainder(lcca.BF16, t["rem_kv"], t["rem_kv_logit"], t["rem_ik"], t["rem_ik_logit"])
             self.copies.append((kv, ik, win, rem))
-        self.logits = torch.empty((B, max(self.ld, 1)), dtype=torch.float32, device=dev) if HI else None
-        self.topk = torch.empty((B, max(c.k, 1)), dtype=torch.int32, device=dev) if HI else None
-        self.out = torch.empty((B, H, c.dv), dtype=torch.bfloat16, device=dev)
-        self.lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        self.logits = torch.empty((self.nrows, max(self.ld, 1)), dtype=torch.float32, device=dev) if HI else None
+        self.topk = torch.empty((self.nrows, max(c.k, 1)), dtype=torch.int32, device=dev) if HI else None
+        self.out = torch.empty((self.nrows, H, c.dv), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((self.nrows, H), dtype=torch.float32, device=dev)
         wsb = lcca.sparse_attn_workspace_size(self.rows, m, H, D, c.dv, c.k, bool(HI), c.window)
         self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
 
@@ -163,7 +275,6 @@ class Workload:
             v = getattr(self, k)
             h[k] = v.cpu().numpy() if v is not None else None
         self.host = h
-        del self._init
 
     # one step on copy i; `ev` (optional) gets an event after each stage
     def step(self, i, ev=None):
@@ -171,8 +282,8 @@ class Workload:
         kv, ik, win, rem = self.copies[i % self.R]
         if ev is not None:
             ev[0].record()
-        L.compress_append(self.pages, self.cu_new, self.start_pos, self.B, L.BF16, self.new_kv, self.new_kv_logit,
-                          self.new_ik, self.new_ik_logit, kv, ik, win, rem)
+        L.compress_append(self.pages, self.cu_new, self.start_pos, self.total_new, L.BF16, self.new_kv,
+                          self.new_kv_logit, self.new_ik, self.new_ik_logit, kv, ik, win, rem)
         if ev is not None:
             ev[1].record()
         idx = None
@@ -191,27 +302,6 @@ class Workload:
                           c.k if idx is not None else 0, win, L.BF16, self.out, self.lse, self.ws)
         if ev is not None:
             ev[4].record()
-
-    # algorithmic bytes and flops per step, by stage
-    def stage_work(self):
-        c = self.cfg
-        B, m, D, H, HI, dI, k, w = c.batch, c.m, c.D, c.H, c.HI, c.dI, c.k, c.window
-        N = c.max_entries
-        E = c.E
-        b_kv, b_ik, b_q, b_out, b_win = 2 * D, 2 * dI, 2, 2, D + 4
-        # compress: the group's m tokens (m-1 from the remainder ring, one new) and
-        # logits read; one entry per stream and one window slot written
-        comp = B * (m * (2 * D + 4) + b_kv + b_win + ((m * (2 * dI + 4) + b_ik) if HI else 0))
-        idx_b = B * (N * b_ik + HI * dI * b_q + 4 * HI + 4 * N // E + 4 * N) if HI else 0
-        topk_b = B * (4 * N + 4 * k) if HI else 0
-        nsel = k if HI else N
-        attn_b = B * (nsel * b_kv + (4 * nsel if HI else 4 * N // E) + w * b_win + H * D * b_q + H * c.dv * b_out
-                      + 4 * H)
-        idx_f = B * 2 * HI * dI * N if HI else 0
-        attn_f = B * 2 * H * (D + c.dv) * (nsel + w)
-        return {"compress_append": (comp, 0), "index_logits": (idx_b, idx_f), "topk_select": (topk_b, 0),
-                "sparse_attn_fwd": (attn_b, attn_f)}
-
 
 def time_steps(torch, wl, steps, warmup):
     """Mean step time and per-stage mean times (ms) over `steps` timed steps."""
@@ -252,57 +342,77 @@ def plain_steps(torch, wl, steps):
 
 
 # --------------------------------------------------------------------------
-# CPU baseline: the oracle on a sample of the same step
+# the oracle on sampled rows of the same step
 # --------------------------------------------------------------------------
 
-def cpu_baseline(wl, sample_rows):
+def sample_rows(wl, max_rows=16):
+    n = wl.nrows
+    if n <= max_rows:
+        return list(range(n))
+    half = max_rows // 2
+    return list(range(half)) + list(range(n - half, n))
+
+
+def oracle_rows(wl, rows):
+    """Oracle outputs (out [rows][H][dv] fp64, top-k [rows][k] or None) for the
+    given row indices, from the host snapshot; returns them with the wall time."""
     import numpy as np
     import oracle as O
     h, c = wl.host, wl.cfg
-    S = min(sample_rows, c.batch)
     m, D, dI = c.m, c.D, c.dI
-    bt = np.ascontiguousarray(h["block_table"][:S])
-    kv = {"dtype": O.BF16, "data": h["kv_data"], "scale": None}
-    ik = {"dtype": O.BF16, "data": h["ik_data"], "scale": None} if c.HI else None
-    win = {"dtype": O.FP8, "cap": c.win_cap, "data": h["win_data"], "scale": h["win_scale"]}
-    rem = {"kv": h["rem_kv"], "ik": h["rem_ik"], "kv_logit": h["rem_kv_logit"], "ik_logit": h["rem_ik_logit"]}
-    new_kv = h["new_kv"].view(np.uint16).reshape(c.batch, D)[:S]
-    new_ik = h["new_ik"].view(np.uint16).reshape(c.batch, dI)[:S] if c.HI else None
-    q = h["q"].view(np.uint16).reshape(c.batch, c.H, D)[:S]
-    rs, rp = h["row_seq"][:S], h["row_pos"][:S]
+    ODT = {"bf16": O.BF16, "fp8": O.FP8, "mxfp4": O.MXFP4}
+    kv = {"dtype": ODT[c.kv_dtype], "data": h["kv_data"].copy(),
+          "scale": h["kv_scale"].copy() if h["kv_scale"] is not None else None}
+    ik = {"dtype": ODT[c.ik_dtype], "data": h["ik_data"].copy(), "scale": None} if c.HI else None
+    win = {"dtype": ODT[c.win_dtype], "cap": c.win_cap, "data": h["win_data"].copy(),
+           "scale": h["win_scale"].copy() if h["win_scale"] is not None else None}
+    rem = {"kv": h["rem_kv"].copy(), "ik": h["rem_ik"].copy() if c.HI else None,
+           "kv_logit": h["rem_kv_logit"].copy(), "ik_logit": h["rem_ik_logit"].copy() if c.HI else None}
+    bt = np.ascontiguousarray(h["block_table"])
+    rows = np.asarray(rows)
     t0 = time.perf_counter()
-    O.compress_append(bt, h["cu_new"][:S + 1], h["start_pos"][:S], O.BF16, new_kv, h["new_kv_logit"][:S],
-                      new_ik, h["new_ik_logit"][:S] if c.HI else None, m, D, dI, kv, ik, win, rem)
+    O.compress_append(bt, h["cu_new"], h["start_pos"], O.BF16, h["new_kv"].view(np.uint16),
+                      h["new_kv_logit"], h["new_ik"].view(np.uint16) if c.HI else None,
+                      h["new_ik_logit"] if c.HI else None, m, D, dI, kv, ik, win, rem)
+    rs, rp = h["row_seq"][rows], h["row_pos"][rows]
+    q = h["q"].view(np.uint16).reshape(wl.nrows, c.H, D)[rows]
     idx = None
     if c.HI:
-        qi = h["q_idx"].view(np.uint16).reshape(c.batch, c.HI, dI)[:S]
-        lg = O.index_logits(rs, rp, m, bt, O.BF16, qi, c.HI, dI, h["w_idx"][:S], 1.0, ik, wl.ld)
+        qi = h["q_idx"].view(np.uint16).reshape(wl.nrows, c.HI, dI)[rows]
+        lg = O.index_logits(rs, rp, m, bt, O.BF16, qi, c.HI, dI, h["w_idx"][rows], 1.0, ik, wl.ld)
         idx = O.topk(rp, m, lg, c.k)
+    else:
+        lg = None
     out, lse = O.sparse_attn(rs, rp, m, bt, O.BF16, q, c.H, D, c.dv, c.scale, kv, idx, c.k if c.HI else 0, win,
                              c.window)
-    dt = time.perf_counter() - t0
-    threads = min(O.num_threads(), S)
-    return {"value": S / dt, "unit": "query-rows/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d decode rows of %s (compress_append + index_logits + topk_select + sparse_attn, "
-                      "fp64, OpenMP over rows), %.1f s wall" % (S, c.batch, wl.name, dt)}, out, idx
+    return out, idx, lg, time.perf_counter() - t0
 
 
-def parity_summary(torch, wl, out_ref, idx_ref):
+def cpu_baseline(wl, rows, dt):
+    import oracle as O
+    return {"value": len(rows) / dt, "unit": "query-rows/s", "cores": min(O.num_threads(), len(rows)),
+            "kind": "oracle",
+            "sample": "%d of %d rows of %s (compress_append of the whole step + index_logits + topk_select + "
+                      "sparse_attn for the sampled rows, fp64, OpenMP over rows), %.1f s wall" % (
+                          len(rows), wl.nrows, wl.name, dt)}
+
+
+def parity_summary(wl, rows, out_ref, idx_ref):
     """Device output (bf16) against the oracle's fp64 output on the sampled
     rows; `max_abs_excess` discounts the output's own bf16 rounding (half an
     ulp of the oracle's value), which the tests also allow."""
     import numpy as np
-    S = out_ref.shape[0]
-    got = wl.out[:S].float().cpu().numpy().astype(np.float64)
+    got = wl.out[rows].float().cpu().numpy().astype(np.float64)
     d = np.abs(got - out_ref)
     a = np.abs(out_ref)
     half_ulp = 0.5 * 2.0 ** (np.floor(np.log2(np.where(a > 0, a, 1.0))).clip(-126) - 7)
-    res = {"rows": int(S), "max_abs": float(d.max()), "mean_abs": float(d.mean()),
+    res = {"rows": len(rows), "max_abs": float(d.max()), "mean_abs": float(d.mean()),
            "max_abs_excess": float(np.maximum(d - half_ulp, 0).max()),
            "rel_l2": float(np.linalg.norm(got - out_ref) / max(np.linalg.norm(out_ref), 1e-30))}
     if idx_ref is not None:
-        gi = wl.topk[:S].cpu().numpy()
-        res["topk_set_diff"] = int(sum(len(set(gi[r].tolist()) ^ set(idx_ref[r].tolist())) // 2 for r in range(S)))
+        gi = wl.topk[rows].cpu().numpy()
+        res["topk_set_diff"] = int(sum(len(set(gi[i].tolist()) ^ set(idx_ref[i].tolist())) // 2
+                                       for i in range(len(rows))))
     return res
 
 
@@ -329,13 +439,66 @@ def measured_traffic(workload, kernel, source):
     return None
 
 
+def run_workload(torch, lcca, synth, name, args, with_oracle):
+    log("workload", name, "building")
+    wl = Workload(name, torch, lcca, synth, cold=True)
+    torch.cuda.synchronize()
+    if with_oracle:
+        wl.snapshot_host()
+    log("workload", name, "R=%d copies of %.1f MiB, %d rows" % (wl.R, wl.footprint / 2 ** 20, wl.nrows))
+    steps = args.steps if wl.nrows <= 1024 else max(1, min(args.steps, args.prefill_steps))
+    total, stage, wall = time_steps(torch, wl, steps, args.warmup)
+    plain = plain_steps(torch, wl, steps)
+    hot_total = None
+    if not args.no_hot and wl.R > 1:
+        saved = wl.R
+        wl.R = 1
+        for i in range(args.warmup):
+            wl.step(0)
+        hot_total = plain_steps(torch, wl, steps)
+        wl.R = saved
+    work = stage_work(wl.cfg)
+    step_bytes = sum(b for b, _ in work.values())
+    step_flops = sum(f for _, f in work.values())
+    per = {}
+    for n, (b, f) in work.items():
+        t = stage[n]
+        if b == 0 and f == 0:
+            continue
+        e = {"ms": round(t, 5), "GB/s": round(b / t / 1e6, 1) if t > 0 else None,
+             "hbm_frac": round(b / t / 1e6 / HBM_PEAK_GBS, 4) if t > 0 else None, "bytes": b}
+        if f:
+            e["TFLOP/s"] = round(f / t / 1e9, 2)
+            e["mfma_frac"] = round(f / t / 1e9 / BF16_PEAK_TFLOPS, 4)
+        per[n] = e
+    res = {"rows_per_s": wl.nrows / (plain / 1e3), "ms_per_step": plain, "ms_per_step_events": total,
+           "wall_ms_per_step": wall, "hot_ms_per_step": hot_total,
+           "hot_rows_per_s": wl.nrows / (hot_total / 1e3) if hot_total else None,
+           "step_GB/s": step_bytes / plain / 1e6, "step_hbm_frac": step_bytes / plain / 1e6 / HBM_PEAK_GBS,
+           "step_TFLOP/s": step_flops / plain / 1e9, "step_bytes": step_bytes, "step_flops": step_flops,
+           "stages": per, "R": wl.R, "steps": steps, "rows": wl.nrows}
+    baseline = None
+    if with_oracle:
+        torch.cuda.synchronize()
+        rows = sample_rows(wl, args.cpu_sample_rows)
+        out_ref, idx_ref, _, dt = oracle_rows(wl, rows)
+        res["parity"] = parity_summary(wl, rows, out_ref, idx_ref)
+        baseline = cpu_baseline(wl, rows, dt)
+        log(name, "oracle %.1f s; parity %s" % (dt, json.dumps(res["parity"])))
+    log(name, json.dumps({k: v for k, v in res.items() if k != "stages"}))
+    del wl
+    torch.cuda.empty_cache()
+    return res, baseline
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workloads", default="csa_64k,hca_1m")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prefill-steps", type=int, default=20, help="timed steps of workloads with > 1024 rows")
+    ap.add_argument("--workloads", default="csa_64k,hca_1m,lp_512k,prefill_8k")
+    ap.add_argument("--no-oracle", action="store_true", help="skip the oracle baseline and parity samples")
     ap.add_argument("--cpu-sample-rows", type=int, default=16)
     ap.add_argument("--no-hot", action="store_true")
     args = ap.parse_args()
@@ -354,84 +517,40 @@ def main():
 
     stream = torch.cuda.Stream()
     names = [n for n in args.workloads.split(",") if n]
-    results = {}
-    baseline = None
+    results, baselines = {}, {}
     with torch.cuda.stream(stream):
-        for wi, name in enumerate(names):
-            log("workload", name, "building")
-            wl = Workload(name, torch, lcca, synth, cold=True)
-            torch.cuda.synchronize()
-            if wi == 0 and not args.no_cpu_baseline:
-                wl.snapshot_host()
-            log("workload", name, "R=%d copies of %.1f MiB" % (wl.R, wl.footprint / 2 ** 20))
-            total, stage, wall = time_steps(torch, wl, args.steps, args.warmup)
-            plain = plain_steps(torch, wl, args.steps)
-            hot_total = None
-            if not args.no_hot:
-                saved = wl.R
-                wl.R = 1
-                for i in range(args.warmup):
-                    wl.step(0)
-                hot_total = plain_steps(torch, wl, args.steps)
-                wl.R = saved
-            work = wl.stage_work()
-            step_bytes = sum(b for b, _ in work.values())
-            step_flops = sum(f for _, f in work.values())
-            per = {}
-            for n, (b, f) in work.items():
-                t = stage[n]
-                if b == 0 and f == 0:
-                    continue
-                e = {"ms": round(t, 5), "GB/s": round(b / t / 1e6, 1) if t > 0 else None,
-                     "hbm_frac": round(b / t / 1e6 / HBM_PEAK_GBS, 4) if t > 0 else None, "bytes": b}
-                if f:
-                    e["TFLOP/s"] = round(f / t / 1e9, 2)
-                    e["mfma_frac"] = round(f / t / 1e9 / BF16_PEAK_TFLOPS, 4)
-                per[n] = e
-            rows = wl.cfg.batch
-            results[name] = {"rows_per_s": rows / (plain / 1e3), "ms_per_step": plain, "ms_per_step_events": total,
-                             "wall_ms_per_step": wall, "hot_ms_per_step": hot_total,
-                             "hot_rows_per_s": rows / (hot_total / 1e3) if hot_total else None,
-                             "step_GB/s": step_bytes / plain / 1e6, "step_hbm_frac": step_bytes / plain / 1e6 / HBM_PEAK_GBS,
-                             "step_bytes": step_bytes, "step_flops": step_flops, "stages": per, "R": wl.R}
-            log(name, json.dumps(results[name]))
-            if wi == 0 and not args.no_cpu_baseline:
-                torch.cuda.synchronize()
-                baseline, out_ref, idx_ref = cpu_baseline(wl, args.cpu_sample_rows)
-                results[name]["parity_sample"] = parity_summary(torch, wl, out_ref, idx_ref)
-                log("cpu baseline", json.dumps(baseline), "parity", json.dumps(results[name]["parity_sample"]))
-            del wl
-            torch.cuda.empty_cache()
+        for name in names:
+            results[name], baselines[name] = run_workload(torch, lcca, synth, name, args, not args.no_oracle)
 
     head = names[0]
     r = results[head]
     # the dominant kernel of the headline workload: the stage with the most time
-    dom = max(r["stages"].items(), key=lambda kv: kv[1]["ms"])
-    dname, d = dom
+    dname, d = max(r["stages"].items(), key=lambda kv: kv[1]["ms"])
     src = {"index_logits": "index_logits.hip", "sparse_attn_fwd": "sparse_attn.hip",
            "topk_select": "topk_select.hip", "compress_append": "compress_append.hip"}[dname]
     traffic = measured_traffic(head, dname, src)
     roof = {"kernel": dname, "bound": "hbm", "achieved": d["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": d["hbm_frac"], "traffic": traffic, "algorithmic_bytes": d["bytes"]}
+    cfg = synth.CONFIGS[head]
     line = {
         "metric": METRIC, "value": round(r["rows_per_s"], 1), "unit": "query-rows/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
+        "steps": r["steps"], "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": head, "batch": synth.CONFIGS[head].batch,
-                   "context": synth.CONFIGS[head].total_len(0), "ratio_m": synth.CONFIGS[head].m,
-                   "top_k": synth.CONFIGS[head].k, "window": synth.CONFIGS[head].window, "kv": "bf16",
-                   "window_cache": "fp8_e4m3", "heads": synth.CONFIGS[head].H, "dim": synth.CONFIGS[head].D,
-                   "cold_cache_copies": r["R"]},
+        "config": {"workload": head, "batch": cfg.batch, "context": cfg.total_len(0), "ratio_m": cfg.m,
+                   "top_k": cfg.k, "window": cfg.window, "kv": cfg.kv_dtype, "window_cache": cfg.win_dtype,
+                   "heads": cfg.H, "dim": cfg.D, "cold_cache_copies": r["R"]},
         "step_hbm_GB/s": round(r["step_GB/s"], 1), "step_hbm_frac": round(r["step_hbm_frac"], 4),
         "roofline": roof,
-        "cpu_baseline": baseline,
+        "cpu_baseline": baselines.get(head),
         "stages": r["stages"],
         "hot_rows_per_s": round(r["hot_rows_per_s"], 1) if r["hot_rows_per_s"] else None,
-        "parity_sample": r.get("parity_sample"),
+        "parity": r.get("parity"),
         "also": {n: {"rows_per_s": round(v["rows_per_s"], 1), "ms_per_step": round(v["ms_per_step"], 5),
-                     "step_hbm_GB/s": round(v["step_GB/s"], 1), "step_hbm_frac": round(v["step_hbm_frac"], 4),
+                     "rows": v["rows"], "step_hbm_GB/s": round(v["step_GB/s"], 1),
+                     "step_hbm_frac": round(v["step_hbm_frac"], 4), "step_TFLOP/s": round(v["step_TFLOP/s"], 2),
                      "hot_rows_per_s": round(v["hot_rows_per_s"], 1) if v["hot_rows_per_s"] else None,
-                     "stages": v["stages"], "cold_cache_copies": v["R"]}
+                     "stages": v["stages"], "cold_cache_copies": v["R"], "steps": v["steps"],
+                     "parity": v.get("parity")}
                  for n, v in results.items() if n != head},
     }
     print(json.dumps(line), flush=True)
