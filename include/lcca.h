@@ -189,6 +189,8 @@ lcca_status lcca_index_logits(void* stream, const lcca_pages* pages, const lcca_
  *   logits    device float [num_rows][ld]
  *   topk_idx  device int32 [num_rows][k]
  *   ws        unused (may be NULL); ws_bytes ignored
+ * Rows of more than 2^18 visible entries ((max_pos + 1) / ratio_m) return
+ * LCCA_ERR_UNSUPPORTED (the selection keeps a bitmap of the row in LDS).
  */
 lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_m,
                              const float* logits, int64_t ld, int32_t k, int32_t* topk_idx,

@@ -30,6 +30,9 @@ struct IndexArgs {
     int32_t tiles_per_wave;      // 32-entry tiles per wave (decode) / per workgroup (prefill)
 };
 
+// top-k rows hold at most this many visible entries (bitmaps of the row in LDS)
+constexpr int kTopkMaxEntries = 1 << 18;
+
 struct TopkArgs {
     const int32_t* row_pos; int32_t num_rows; int32_t m;
     const float* logits; int64_t ld; int32_t k;

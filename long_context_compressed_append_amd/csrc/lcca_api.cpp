@@ -219,6 +219,8 @@ lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_
     if (!logits || !topk_idx) return fail(LCCA_ERR_INVALID_ARG, "logits/topk_idx NULL");
     const int max_entries = (rows->max_pos + 1) / ratio_m;
     if (ld < max_entries) return fail(LCCA_ERR_INVALID_ARG, "ld=%lld < max visible entries %d", (long long)ld, max_entries);
+    if (max_entries > lcca::kTopkMaxEntries)
+        return fail(LCCA_ERR_UNSUPPORTED, "%d visible entries > %d", max_entries, lcca::kTopkMaxEntries);
     lcca::TopkArgs a{rows->row_pos, rows->num_rows, ratio_m, logits, ld, k, topk_idx};
     return hip_status(lcca::launch_topk_select(a, max_entries, (hipStream_t)stream), "topk_select launch");
 }

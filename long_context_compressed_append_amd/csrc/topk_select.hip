@@ -4,19 +4,31 @@
 // KV cacheom", section "Kako funkcionira optimizacija KV cachea?": attention is
 // limited to the top-k compressed tokens.]
 //
-// One 1024-thread workgroup per row; thread i owns the contiguous entries
-// [i*C, (i+1)*C).  Logits map to order-preserving u32 keys (-0.0 folded onto
-// +0.0).  Rows of up to 32K entries are held in registers; longer rows are
-// re-read from memory on every pass.
-//   1. A block min/max of the keys gives their common leading bits, so the
-//      radix digits start at the first bit in which the keys differ.
-//   2. Radix passes of up to 8 bits find the k-th largest key T and how many
-//      keys equal to T are still needed.  Histograms live in LDS as 16 copies
-//      selected by lane, so lanes holding the same digit rarely hit the same
-//      counter.
-//   3. A final pass in entry order keeps every key > T and the first `need`
-//      keys == T; block-wide exclusive scans give each kept entry its output
-//      slot, so the result is deterministic and sorted by entry.
+// One 1024-thread workgroup per row.  Logits map to order-preserving u32 keys
+// (-0.0 folded onto +0.0).  Thread t owns the 4-entry groups t, t + 1024,
+// t + 2048, ... of the row, so every load is a coalesced 16-byte access.
+// Rows of up to 32K entries are held in registers as full keys, rows of up
+// to 128K as their leading 16 bits (two per register); longer rows are read
+// again for each pass over them.
+//   1. Histogram of the leading 12 key bits (sign, exponent, 3 mantissa
+//      bits) in LDS; a block scan from the top bin finds the bin holding the
+//      k-th largest key and how many keys lie above it.
+//   2. One pass marks every key of a higher bin in a bitmap of the row
+//      (each 8-lane group assembles its 32-bit word with DPP moves and
+//      stores it, no atomics) and collects the keys of the boundary bin,
+//      with their entries, in LDS.
+//   3. Radix passes over those candidates alone (bits 19..12, 11..4, 3..0)
+//      give the k-th largest key T and how many keys equal to T are needed.
+//      If the boundary bin overflows the candidate buffer, the same passes
+//      run over the whole row instead.
+//   4. Candidates above T join the bitmap; candidates equal to T go to a
+//      second bitmap.  A block scan of the bitmaps' popcounts gives every
+//      thread its output offset, so the result comes out sorted by entry and
+//      the first `need` equal keys (smallest entries) are the ones kept.
+// The leading-digit histogram keeps 8 copies of every bin side by side
+// ([bin][copy], the copy picked by lane), so lanes that hit the same bin land
+// in different banks; the copies are summed into one count per bin before the
+// scan, which then reads 4 consecutive bins per thread.
 #include "device.h"
 #include "kernels.h"
 
@@ -26,7 +38,28 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kCopies = 16;
+constexpr int kGroup = 4 * kThreads;            // entries per load round
+constexpr int kLeadBits = 12;
+constexpr int kLeadShift = 32 - kLeadBits;
+constexpr int kLeadBins = 1 << kLeadBits;
+constexpr int kLeadCopies = 8;                  // lane & 7 picks the copy
+constexpr int kCandCap = 4096;
+constexpr int kWords = kTopkMaxEntries / 32;
+
+struct alignas(16) Smem {
+    union alignas(16) {
+        uint32_t lead[kLeadBins * kLeadCopies];       // step 1: [bin][copy]
+        struct {
+            uint32_t bits[2][kWords];                 // [0] keys above T, [1] keys equal to T
+            uint32_t cand_key[kCandCap];
+            int32_t cand_idx[kCandCap];
+            uint32_t fine[2][256];                    // refinement histograms, double-buffered
+        } b;
+    } u;
+    alignas(16) uint32_t cnt[kLeadBins];              // step 1: copies summed
+    uint32_t wsum[2][kWaves];
+    uint32_t cand_n, sel_digit, sel_above;
+};
 
 __device__ inline uint32_t order_key(float x) {
     uint32_t u = __float_as_uint(x);
@@ -34,80 +67,218 @@ __device__ inline uint32_t order_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive scan over the block (thread order); returns this thread's prefix
-// and writes the block total to *total.
-__device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint32_t inc = v;
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t t = __shfl_up(inc, o);
-        if (lane >= o) inc += t;
-    }
-    __syncthreads();
-    if (lane == 63) wsum[w] = inc;
-    __syncthreads();
-    uint32_t before = 0, tot = 0;
-    for (int i = 0; i < kWaves; ++i) {
-        uint32_t s = wsum[i];
-        if (i < w) before += s;
-        tot += s;
-    }
-    *total = tot;
-    return before + inc - v;
+// OR of x over each aligned group of 8 lanes (DPP: swap within pairs, within
+// quads, then mirror the two quads of the group).
+__device__ inline uint32_t or8(uint32_t x) {
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false);   // row_half_mirror
+    return x;
 }
 
-// Keys of this thread's chunk: resident in registers (R > 0) or streamed.
-template <int R>
-struct Chunk {
-    uint32_t u[R > 0 ? R : 1];
-    int c0, c1;                 // entry range [c0, c1)
-    const float* L;
+// Inclusive prefix sum over the wave (DPP: shifts within rows of 16 lanes,
+// then row broadcasts of lanes 15 and 31).
+__device__ inline uint32_t wave_incl_sum(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return x;
+}
 
-    // per_thread is a multiple of 4; with `vec` the row is 16-byte aligned and
-    // the chunk is read with 16-byte loads.
-    __device__ void init(const float* logits, int n, int per_thread, bool vec) {
-        L = logits;
-        c0 = min((int)threadIdx.x * per_thread, n);
-        c1 = min(c0 + per_thread, n);
-        if (R > 0) {
-            if (vec) {
+// Exclusive scans of a and b over the block, in thread order.
+__device__ inline void block_exclusive_scan2(uint32_t& a, uint32_t& b, uint32_t (*wsum)[kWaves]) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint32_t ia = wave_incl_sum(a), ib = wave_incl_sum(b);
+    __syncthreads();
+    if (lane == 63) { wsum[0][w] = ia; wsum[1][w] = ib; }
+    __syncthreads();
+    uint32_t ba = 0, bb = 0;
+    for (int i = 0; i < w; ++i) { ba += wsum[0][i]; bb += wsum[1][i]; }
+    a = ba + ia - a;
+    b = bb + ib - b;
+}
+
+// The row's keys.  R > 0: R keys per thread in registers, full (Half false)
+// or their leading 16 bits (Half true, two per register); R == 0: read from
+// memory on every pass.  Vec: every row starts 16-byte aligned, so a 4-entry
+// group is one 16-byte load (the row holds ld >= n floats, and the last
+// group's load is clamped to the last group that starts below n).  Loads
+// are branch-free: addresses are clamped into the row and entries >= n
+// masked.
+template <int R, bool Half, bool Vec>
+struct Keys {
+    static constexpr int kRounds = R / 4;
+    static constexpr bool kFull = R > 0 && !Half;      // full keys without memory reads
+    uint32_t u[R == 0 ? 1 : (Half ? R / 2 : R)];
+    const float* L;
+    int n, rounds;
+
+    __device__ __forceinline__ void load4(int e, uint32_t* o) const {
+        if constexpr (Vec) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(L + min(e, (n - 1) & ~3));
 #pragma unroll
-                for (int i = 0; i < R; i += 4) {
-                    if (c0 + i < c1) {
-                        const f32x4 v = *reinterpret_cast<const f32x4*>(L + c0 + i);
+            for (int i = 0; i < 4; ++i) o[i] = e + i < n ? order_key(v[i]) : 0u;
+        } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) u[i + e] = c0 + i + e < c1 ? order_key(v[e]) : 0u;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) u[i + e] = 0u;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < R; ++i) u[i] = c0 + i < c1 ? order_key(L[c0 + i]) : 0u;
+            for (int i = 0; i < 4; ++i) {
+                const float x = L[min(e + i, n - 1)];
+                o[i] = e + i < n ? order_key(x) : 0u;
             }
         }
     }
-    template <class F>
-    __device__ void each(F f) const {
-        if (R > 0) {
+    // First entry of the thread's group in round j.  Every pass takes its
+    // own opaque copy of the thread index, so entry offsets are recomputed
+    // per pass rather than kept live (or spilled) across the whole kernel.
+    __device__ __forceinline__ static int tid_copy() {
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        return t;
+    }
+    __device__ __forceinline__ static int first(int t, int j) { return 4 * (t + kThreads * j); }
+
+    __device__ __forceinline__ void init(const float* row, int n_) {
+        L = row; n = n_;
+        rounds = (n + kGroup - 1) / kGroup;
+        if constexpr (R > 0) {
+            const int t = tid_copy();
+            constexpr int kBatch = kRounds < (Half ? 4 : 8) ? kRounds : (Half ? 4 : 8);
 #pragma unroll
-            for (int i = 0; i < R; ++i)
-                if (c0 + i < c1) f(c0 + i, u[i]);
-        } else {
-            for (int i = c0; i < c1; ++i) f(i, order_key(L[i]));
+            for (int j0 = 0; j0 < kRounds; j0 += kBatch) {
+                uint32_t v[kBatch][4];
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b) load4(first(t, j0 + b), v[b]);
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b) {
+                    if constexpr (Half) {
+                        u[2 * (j0 + b)] = (v[b][0] >> 16) | (v[b][1] & 0xffff0000u);
+                        u[2 * (j0 + b) + 1] = (v[b][2] >> 16) | (v[b][3] & 0xffff0000u);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) u[4 * (j0 + b) + i] = v[b][i];
+                    }
+                }
+                // at most one batch of loads in flight per thread
+                if constexpr (Half) __builtin_amdgcn_sched_barrier(0);
+            }
         }
+    }
+    // f(first entry of the thread's group, its 4 keys) once per round, the
+    // same number of calls in every thread; entries >= n must be skipped by
+    // f.  With Half the keys carry their leading 16 bits only.
+    template <class F>
+    __device__ __forceinline__ void rounds_each(F f) const {
+        if constexpr (R > 0) {
+            const int t = tid_copy();
+#pragma unroll
+            for (int j = 0; j < kRounds; ++j) {
+                if (j < rounds) {
+                    uint32_t k[4];
+                    if constexpr (Half) {
+                        k[0] = u[2 * j] << 16; k[1] = u[2 * j] & 0xffff0000u;
+                        k[2] = u[2 * j + 1] << 16; k[3] = u[2 * j + 1] & 0xffff0000u;
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) k[i] = u[4 * j + i];
+                    }
+                    f(first(t, j), k);
+                    // keep the scheduler from hoisting later rounds' work
+                    // (and their registers) above this one
+                    if constexpr (Half) __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else {
+            stream_rounds(f);
+        }
+    }
+    template <class F>
+    __device__ __forceinline__ void stream_rounds(F f) const {
+        const int t = tid_copy();
+        for (int j = 0; j < rounds; j += 2) {
+            uint32_t t0[4], t1[4];
+            const int e0 = first(t, j), e1 = e0 + kGroup;
+            load4(e0, t0);
+            if (j + 1 < rounds) load4(e1, t1);
+            f(e0, t0);
+            if (j + 1 < rounds) f(e1, t1);
+        }
+    }
+    // f(entry, full key) for every entry < n
+    template <class F>
+    __device__ __forceinline__ void each_full(F f) const {
+        auto g = [&](int e, const uint32_t* k) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (e + i < n) f(e + i, k[i]);
+        };
+        if constexpr (kFull) rounds_each(g);
+        else stream_rounds(g);
+    }
+    __device__ __forceinline__ uint32_t full_key(int e, uint32_t k) const {
+        if constexpr (kFull) return k;
+        else return order_key(L[e]);
     }
 };
 
-template <int R>
+// Wave 0 reads the 256-bin histogram `h` (lane l: bins 4l .. 4l+3) and finds
+// the digit holding the need-th largest key among those counted.
+__device__ __forceinline__ void pick_digit(const uint32_t* h, uint32_t need, uint32_t* sel_digit, uint32_t* sel_above) {
+    const int lane = threadIdx.x;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(h + 4 * lane);
+    uint32_t c[4] = {v[0], v[1], v[2], v[3]};
+    const uint32_t s = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_incl_sum(s);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    uint32_t above = total - incl;            // keys in the bins of higher lanes
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+        if (above < need && above + c[i] >= need) { *sel_digit = 4 * lane + i; *sel_above = above; }
+        above += c[i];
+    }
+}
+
+// Radix passes over the keys `each` enumerates that match `prefix` under
+// `mask`, from bit `top` down; leaves the need-th largest key in *prefix and
+// the number of keys equal to it still needed in *need.  fine[0] must be
+// zero on entry.
+template <class Each>
+__device__ __forceinline__ void refine(Smem& sm, Each each, int top, uint32_t* prefix_io, uint32_t* mask_io, uint32_t* need_io) {
+    const int tid = threadIdx.x;
+    uint32_t prefix = *prefix_io, mask = *mask_io, need = *need_io;
+    int cur = 0;
+    while (top >= 0) {
+        const int w = min(8, top + 1);
+        const int shift = top - w + 1;
+        const uint32_t bins = 1u << w;
+        uint32_t* h = sm.u.b.fine[cur];
+        each([&](int, uint32_t key) __attribute__((always_inline)) {
+            if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & (bins - 1)], 1u);
+        });
+        __syncthreads();
+        if (tid < 64) {
+            pick_digit(h, need, &sm.sel_digit, &sm.sel_above);
+        } else {
+            if (tid < 128) reinterpret_cast<u32x4*>(sm.u.b.fine[cur ^ 1])[tid - 64] = u32x4{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
+        prefix |= sm.sel_digit << shift;
+        mask |= (bins - 1u) << shift;
+        need -= sm.sel_above;
+        top = shift - 1;
+        cur ^= 1;
+        // sel_digit is rewritten only after the next pass's first barrier,
+        // which every thread reaches after reading it here
+    }
+    *prefix_io = prefix; *mask_io = mask; *need_io = need;
+}
+
+template <int R, bool Half, bool Vec>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
-    __shared__ uint32_t hist[2][kCopies][256];
-    __shared__ uint32_t wsum[kWaves];
-    __shared__ uint32_t red[2][kWaves];
-    __shared__ uint32_t sel_digit, sel_above;
+    __shared__ Smem sm;
     const int r = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int n = visible_entries(p.row_pos[r], p.m);
     const int k = p.k;
     int32_t* out = p.idx + (int64_t)r * k;
@@ -115,103 +286,178 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
         for (int i = tid; i < k; i += kThreads) out[i] = i < n ? i : -1;
         return;
     }
-    const int per_thread = ((n + kThreads - 1) / kThreads + 3) & ~3;
-    Chunk<R> C;
-    const float* row = p.logits + (int64_t)r * p.ld;
-    C.init(row, n, per_thread, (reinterpret_cast<uintptr_t>(row) & 15) == 0);
+    Keys<R, Half, Vec> K;
+    K.init(p.logits + (int64_t)r * p.ld, n);
 
-    // 1. common leading bits of all keys
-    uint32_t kmin = 0xffffffffu, kmax = 0u;
-    C.each([&](int, uint32_t u) { kmin = min(kmin, u); kmax = max(kmax, u); });
-    for (int o = 32; o > 0; o >>= 1) {
-        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    {
+        u32x4* z = reinterpret_cast<u32x4*>(sm.u.lead);
+        for (int i = tid; i < kLeadBins * kLeadCopies / 4; i += kThreads) z[i] = u32x4{0u, 0u, 0u, 0u};
     }
-    if (lane == 0) { red[0][wave] = kmin; red[1][wave] = kmax; }
+    if (tid == 0) sm.cand_n = 0;
     __syncthreads();
-    kmin = red[0][0]; kmax = red[1][0];
-    for (int i = 1; i < kWaves; ++i) { kmin = min(kmin, red[0][i]); kmax = max(kmax, red[1][i]); }
-    const uint32_t diff = kmin ^ kmax;
-    int top = diff ? 31 - __builtin_clz(diff) : -1;            // highest differing bit
-    uint32_t mask = diff == 0 ? 0xffffffffu : top >= 31 ? 0u : ~((2u << top) - 1u);   // the common bits
-    uint32_t prefix = kmax & mask;
-    uint32_t need = (uint32_t)k;                                // keys still to take among those matching
 
-    // 2. radix passes from the highest differing bit down.  Two histogram
-    // buffers: while wave 0 sums the copies of this pass's buffer and scans
-    // it, the other waves clear the buffer of the next pass.
-    for (int i = tid; i < kCopies * 256; i += kThreads) (&hist[0][0][0])[i] = 0u;
-    __syncthreads();
-    int cur = 0;
-    while (top >= 0) {
-        const int w = min(8, top + 1);
-        const int shift = top - w + 1;
-        const uint32_t bins = 1u << w;
-        uint32_t* h = hist[cur][lane & (kCopies - 1)];
-        C.each([&](int, uint32_t u) {
-            if ((u & mask) == prefix) atomicAdd(&h[(u >> shift) & (bins - 1)], 1u);
+    // 1. leading-digit histogram and the boundary bin
+    {
+        const int copy = lane & (kLeadCopies - 1);
+        K.rounds_each([&](int e, const uint32_t* key) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                atomicAdd(&sm.u.lead[(key[i] >> kLeadShift) * kLeadCopies + copy], e + i < n ? 1u : 0u);
         });
-        __syncthreads();
-        if (tid < 64) {
-            // lane l owns bins 4l..4l+3; suffix sums from the top digit down
-            uint32_t c[4], s = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t t = 0;
-#pragma unroll
-                for (int cp = 0; cp < kCopies; ++cp) t += hist[cur][cp][4 * tid + i];
-                c[i] = t;
-                s += t;
-            }
-            uint32_t suf = s;
-            for (int o = 1; o < 64; o <<= 1) {
-                uint32_t t = __shfl_down(suf, o);
-                if (tid + o < 64) suf += t;
-            }
-            uint32_t above = suf - s;        // keys in bins of higher lanes
-#pragma unroll
-            for (int i = 3; i >= 0; --i) {
-                if (above < need && above + c[i] >= need) { sel_digit = 4 * tid + i; sel_above = above; }
-                above += c[i];
-            }
-        } else {
-            for (int i = tid - 64; i < kCopies * 256; i += kThreads - 64) (&hist[cur ^ 1][0][0])[i] = 0u;
-        }
-        __syncthreads();
-        prefix |= sel_digit << shift;
-        mask |= (bins - 1u) << shift;
-        need -= sel_above;
-        top = shift - 1;
-        cur ^= 1;
     }
-    const uint32_t T = prefix;
-
-    // 3. ordered output
-    uint32_t gt = 0, eq = 0;
-    C.each([&](int, uint32_t u) { gt += u > T; eq += u == T; });
-    uint32_t total;
-    const uint32_t gt_before = block_exclusive_scan(gt, wsum, &total);
-    const uint32_t eq_before = block_exclusive_scan(eq, wsum, &total);
-    uint32_t pos = gt_before + min(eq_before, need);
-    uint32_t eq_seen = eq_before;
-    C.each([&](int i, uint32_t u) {
-        if (u > T) out[pos++] = i;
-        else if (u == T) {
-            if (eq_seen < need) out[pos++] = i;
-            ++eq_seen;
+    __syncthreads();
+    // sum the copies: lane pairs read one bin's 8 copies as two consecutive
+    // 16-byte chunks and add them across the pair
+#pragma unroll
+    for (int i = 0; i < kLeadBins * kLeadCopies / 4 / kThreads; ++i) {
+        const int chunk = tid + kThreads * i;
+        const u32x4 x = reinterpret_cast<const u32x4*>(sm.u.lead)[chunk];
+        uint32_t c = x[0] + x[1] + x[2] + x[3];
+        c += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)c, 0xB1, 0xF, 0xF, false);     // quad_perm [1,0,3,2]
+        if ((chunk & 1) == 0) sm.cnt[chunk >> 1] = c;
+    }
+    __syncthreads();
+    {
+        // thread t owns bins 4095-4t .. 4092-4t, so thread order is descending bins
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.cnt[kLeadBins - 4 - 4 * tid]);
+        const uint32_t c[4] = {v[3], v[2], v[1], v[0]};
+        const uint32_t s = c[0] + c[1] + c[2] + c[3];
+        uint32_t above = s, unused = 0;
+        block_exclusive_scan2(above, unused, sm.wsum);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (above < (uint32_t)k && above + c[i] >= (uint32_t)k) {
+                sm.sel_digit = kLeadBins - 1 - 4 * tid - i;
+                sm.sel_above = above;
+            }
+            above += c[i];
         }
-    });
+    }
+    __syncthreads();
+    const uint32_t lead = sm.sel_digit;
+    uint32_t need = (uint32_t)k - sm.sel_above;
+    __syncthreads();                          // the histogram's LDS is reused from here on
+
+    // 2. bitmap of the keys above the boundary bin; candidates of the bin
+    const int W = (n + 31) / 32;
+    if (tid < 64) reinterpret_cast<u32x4*>(sm.u.b.fine[0])[tid] = u32x4{0u, 0u, 0u, 0u};
+    auto words = [&](int e, const uint32_t* key, uint32_t& ncand) __attribute__((always_inline)) {
+        uint32_t above = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t d = key[i] >> kLeadShift;
+            above |= (d > lead && e + i < n ? 1u : 0u) << i;
+            ncand += d == lead && e + i < n ? 1u : 0u;
+        }
+        const uint32_t word = or8(above << (4 * (lane & 7)));
+        const int wi = e >> 5;
+        if ((lane & 7) == 0 && wi < W) { sm.u.b.bits[0][wi] = word; sm.u.b.bits[1][wi] = 0u; }
+    };
+    auto put = [&](uint32_t c, int e, uint32_t key) __attribute__((always_inline)) {
+        if (c < (uint32_t)kCandCap) {
+            if constexpr (Keys<R, Half, Vec>::kFull) sm.u.b.cand_key[c] = key;
+            sm.u.b.cand_idx[c] = e;
+        }
+    };
+    if constexpr (R > 0) {
+        // count this thread's candidates, reserve their slots with one LDS
+        // atomic per wave, then write them
+        uint32_t mine = 0;
+        K.rounds_each([&](int e, const uint32_t* key) __attribute__((always_inline)) { words(e, key, mine); });
+        const uint32_t incl = wave_incl_sum(mine);
+        uint32_t base = 0;
+        if (lane == 63 && incl > 0) base = atomicAdd(&sm.cand_n, incl);
+        uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)base, 63) + incl - mine;
+        if (mine > 0) {
+            K.rounds_each([&](int e, const uint32_t* key) __attribute__((always_inline)) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if ((key[i] >> kLeadShift) == lead && e + i < n) put(c++, e + i, key[i]);
+            });
+        }
+    } else {
+        K.rounds_each([&](int e, const uint32_t* key) __attribute__((always_inline)) {
+            uint32_t unused = 0;
+            words(e, key, unused);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if ((key[i] >> kLeadShift) == lead && e + i < n) put(atomicAdd(&sm.cand_n, 1u), e + i, key[i]);
+        });
+    }
+    __syncthreads();
+
+    // 3. the k-th largest key within the boundary bin
+    const uint32_t nc = sm.cand_n;
+    uint32_t T = lead << kLeadShift, mask = ~0u << kLeadShift;
+    const bool fits = nc <= (uint32_t)kCandCap;
+    if constexpr (!Keys<R, Half, Vec>::kFull) {
+        if (fits) {
+            for (int c = tid; c < (int)nc; c += kThreads) sm.u.b.cand_key[c] = K.full_key(sm.u.b.cand_idx[c], 0u);
+            __syncthreads();
+        }
+    }
+    auto cands = [&](auto f) __attribute__((always_inline)) {
+        for (int c = tid; c < (int)nc; c += kThreads) f(sm.u.b.cand_idx[c], sm.u.b.cand_key[c]);
+    };
+    auto row_bin = [&](auto f) __attribute__((always_inline)) {
+        K.each_full([&](int e, uint32_t key) __attribute__((always_inline)) {
+            if ((key >> kLeadShift) == lead) f(e, key);
+        });
+    };
+    if (fits) refine(sm, cands, kLeadShift - 1, &T, &mask, &need);
+    else refine(sm, row_bin, kLeadShift - 1, &T, &mask, &need);
+
+    // 4. keys of the bin above T or equal to it join the bitmaps
+    auto mark = [&](int e, uint32_t key) __attribute__((always_inline)) {
+        if (key > T) atomicOr(&sm.u.b.bits[0][e >> 5], 1u << (e & 31));
+        else if (key == T) atomicOr(&sm.u.b.bits[1][e >> 5], 1u << (e & 31));
+    };
+    if (fits) cands(mark);
+    else row_bin(mark);
+    __syncthreads();
+
+    const int wpt = (W + kThreads - 1) / kThreads;
+    const int w0 = min(W, tid * wpt), w1 = min(W, w0 + wpt);
+    uint32_t gt = 0, eq = 0;
+    for (int w = w0; w < w1; ++w) { gt += __popc(sm.u.b.bits[0][w]); eq += __popc(sm.u.b.bits[1][w]); }
+    block_exclusive_scan2(gt, eq, sm.wsum);
+    uint32_t pos = gt + min(eq, need);
+    uint32_t eq_seen = eq;
+    for (int w = w0; w < w1; ++w) {
+        const uint32_t g = sm.u.b.bits[0][w], q = sm.u.b.bits[1][w];
+        uint32_t any = g | q;
+        while (any) {
+            const int b = __builtin_ctz(any);
+            any &= any - 1;
+            const int e = 32 * w + b;
+            const bool take = ((g >> b) & 1u) || eq_seen < need;
+            eq_seen += (g >> b) & 1u ? 0u : 1u;
+            if (take) {
+                if (pos < (uint32_t)k) out[pos] = e;           // always true; keeps every store in the row
+                ++pos;
+            }
+        }
+    }
 }
 
 }  // namespace
 
+template <bool Vec>
+void launch_rows(const TopkArgs& a, int rounds, hipStream_t stream) {
+    const dim3 grid(a.num_rows), block(kThreads);
+    if (rounds <= 2) hipLaunchKernelGGL((topk_kernel<8, false, Vec>), grid, block, 0, stream, a);
+    else if (rounds <= 4) hipLaunchKernelGGL((topk_kernel<16, false, Vec>), grid, block, 0, stream, a);
+    else if (rounds <= 8) hipLaunchKernelGGL((topk_kernel<32, false, Vec>), grid, block, 0, stream, a);
+    else if (rounds <= 32) hipLaunchKernelGGL((topk_kernel<128, true, Vec>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((topk_kernel<0, false, Vec>), grid, block, 0, stream, a);
+}
+
 hipError_t launch_topk_select(const TopkArgs& a, int max_entries, hipStream_t stream) {
     if (a.num_rows <= 0 || a.k <= 0) return hipSuccess;
-    const int per_thread = ((max_entries + kThreads - 1) / kThreads + 3) & ~3;
-    if (per_thread <= 8) hipLaunchKernelGGL(topk_kernel<8>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
-    else if (per_thread <= 16) hipLaunchKernelGGL(topk_kernel<16>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
-    else if (per_thread <= 32) hipLaunchKernelGGL(topk_kernel<32>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL(topk_kernel<0>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
+    const int rounds = (max_entries + kGroup - 1) / kGroup;
+    const bool vec = (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 && a.ld % 4 == 0;
+    if (vec) launch_rows<true>(a, rounds, stream);
+    else launch_rows<false>(a, rounds, stream);
     return hipGetLastError();
 }
 

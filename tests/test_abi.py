@@ -58,6 +58,11 @@ def test_invalid_arguments_rejected_before_launch():
     assert L.lcca_index_logits(None, by(pages), by(rows), lcca.BF16, 1, 64, 1, 1.0, by(bad), 1, 64) == lcca.ERR_INVALID_ARG
     # top-k: k < 1
     assert L.lcca_topk_select(None, by(rows), 4, 1, 64, 0, 1, None, 0) == lcca.ERR_INVALID_ARG
+    # top-k: more visible entries than the selection's row bitmaps hold (2^18)
+    huge = lcca._Rows(1, 4 * (1 << 18) + 3, 1, 1)
+    assert L.lcca_topk_select(None, by(huge), 4, 1, (1 << 18) + 1, 64, 1, None, 0) == lcca.ERR_UNSUPPORTED
+    ok = lcca._Rows(1, 4 * (1 << 18) - 1, 1, 1)
+    assert L.lcca_topk_select(None, by(ok), 4, 1, 1 << 18, 0, 1, None, 0) == lcca.ERR_INVALID_ARG   # k < 1 only
     # attention: workspace too small (16 rows of 64K context need key splits)
     kv = _pool(lcca.BF16, 576, blocks=4096)
     win = lcca._WindowCache(lcca.FP8_E4M3, 576, 128, 128, 1, 1)
