@@ -9,20 +9,23 @@
 //  compressor kept as sliding-window state.]
 //
 // Grid: (new token t, slice s).  Slices 0 .. SK-1 cover 64-dimension blocks
-// of the shared-KV stream, SK .. SK+SI-1 those of the indexer-key stream.
-//   * A token that completes group g makes each of its slices aggregate the
-//     slice's 64 dimensions of the group: 256 threads = 32 token lanes x 8
-//     dimension chunks of 8, every lane loading its tokens with 16-byte loads
-//     (all in flight together), then a reduction over the token lanes in LDS,
-//     the encode (bf16 / MXFP4 / FP8 / fp32) and the store into the pool.
-//   * Slice 0 of every token writes it into the window ring if it is among
-//     the last `capacity` tokens of its chunk (FP8 with a per-token scale).
-//   * Remainder ring: each token of the chunk's incomplete tail is written by
-//     its own slice 0.  One case needs ordering: a chunk that starts inside a
-//     group, completes that group and ends inside a later group reads ring
-//     slots it also rewrites.  Then slice 0 of the token completing the first
-//     group aggregates that whole group (all slices, both streams) and writes
-//     the tail after its reads.
+// of the shared-KV stream, SK .. SK+SI-1 those of the indexer-key stream,
+// slice SK+SI the token's ring writes.
+//   * A token that completes group g makes each of its compression slices
+//     aggregate the slice's 64 dimensions of the group: 256 threads = 32
+//     token lanes x 8 dimension chunks of 8.  The group's token bytes, its
+//     logits and the pool row's block-table entry are all requested first,
+//     so they travel together; the softmax weights, the weighted sum (token
+//     lanes reduced in LDS), the encode (bf16 / MXFP4 / FP8 / fp32) and the
+//     store into the pool follow.
+//   * The ring slice writes the token into the window ring if it is among
+//     the last `capacity` tokens of its chunk (FP8 with a per-token scale)
+//     and, if it belongs to the chunk's incomplete tail, into the remainder
+//     ring.  One case needs ordering: a chunk that starts inside a group,
+//     completes that group and ends inside a later group reads ring slots it
+//     also rewrites.  Then slice 0 of the token completing the first group
+//     aggregates that whole group (all slices, both streams) and writes the
+//     tail after its reads.
 #include "device.h"
 #include "kernels.h"
 
@@ -44,21 +47,6 @@ __device__ inline void load_pair(const void* base, int64_t elem, float& x0, floa
     } else {
         uint32_t v = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(base) + elem);
         x0 = bf16_to_f32(v & 0xffffu); x1 = bf16_to_f32(v >> 16);
-    }
-}
-
-// Eight consecutive token values starting at element `elem` (multiple of 8).
-template <int TOK>
-__device__ inline void load8(const void* base, int64_t elem, float (&x)[kChunk]) {
-    if (TOK == DT_F32) {
-        const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + elem);
-        const f32x4 a = p[0], b = p[1];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
-    } else {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { x[2 * i] = bf16_to_f32(v[i] & 0xffffu); x[2 * i + 1] = bf16_to_f32(v[i] >> 16); }
     }
 }
 
@@ -115,15 +103,105 @@ __device__ inline SeqChunk seq_of(const CompressArgs& p, int t, int* cu_lds, int
     return q;
 }
 
-// Aggregate dimensions [d0, d0 + 64) of group g of one stream and store them.
-// w_lds must already hold the group's softmax weights.
+constexpr int kMaxTokPerLane = 256 / kLanes;   // m <= 256
+
+// Raw bytes of one token's 8-dimension chunk: one 16-byte load for bf16,
+// two for fp32.
 template <int TOK>
-__device__ void compress_slice(const CompressArgs& p, const SeqChunk& q, int g, bool ik_stream, int d0,
-                               const float* w_lds, float* red) {
+struct RawChunk {
+    u32x4 v[TOK == DT_F32 ? 2 : 1];
+};
+
+template <int TOK>
+__device__ __forceinline__ void load_chunk(const void* base, int64_t elem, RawChunk<TOK>& r) {
+    if constexpr (TOK == DT_F32) {
+        const u32x4* q = reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(base) + elem);
+        r.v[0] = q[0];
+        r.v[1] = q[1];
+    } else {
+        r.v[0] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+    }
+}
+
+template <int TOK>
+__device__ __forceinline__ void unpack_chunk(const RawChunk<TOK>& r, float (&x)[kChunk]) {
+    if constexpr (TOK == DT_F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[i] = __uint_as_float(r.v[0][i]); x[4 + i] = __uint_as_float(r.v[1][i]); }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_to_f32(r.v[0][i] & 0xffffu);
+            x[2 * i + 1] = bf16_to_f32(r.v[0][i] >> 16);
+        }
+    }
+}
+
+// Everything one slice of group g reads from memory, requested up front.
+template <int TOK>
+struct SliceLoads {
+    RawChunk<TOK> tok[kMaxTokPerLane];   // token lane's chunks, tokens lane + 32 j
+    float logit;                         // logit of token `tid` of the group (threads < m)
+    int64_t row;                         // pool row of the entry
+};
+
+template <int TOK>
+__device__ __forceinline__ void issue_slice(const CompressArgs& p, const SeqChunk& q, int g, bool ik_stream, int d0,
+                                            SliceLoads<TOK>& L) {
     const int m = p.m;
     const int dim = ik_stream ? p.dI : p.D;
     const void* tok = ik_stream ? p.ik_tok : p.kv_tok;
     const void* rtok = ik_stream ? p.rem_ik : p.rem_kv;
+    const float* lg = ik_stream ? p.ik_logit : p.kv_logit;
+    const float* rlg = ik_stream ? p.rem_ik_logit : p.rem_kv_logit;
+    const int tid = threadIdx.x;
+    const int lane = tid / (kSliceDims / kChunk), ch = tid % (kSliceDims / kChunk);
+    const int d = d0 + ch * kChunk;
+    const bool active = d < dim;
+#pragma unroll
+    for (int j = 0; j < kMaxTokPerLane; ++j) {
+        const int i = lane + kLanes * j;
+        if (active && i < m) {
+            const int t = g * m + i;
+            if (t >= q.start) load_chunk<TOK>(tok, (q.c0 + (t - q.start)) * dim + d, L.tok[j]);
+            else load_chunk<TOK>(rtok, ((int64_t)q.b * m + t % m) * dim + d, L.tok[j]);
+        }
+    }
+    L.logit = -INFINITY;
+    if (tid < m) {
+        const int t = g * m + tid;
+        L.logit = t >= q.start ? lg[q.c0 + (t - q.start)] : rlg[(int64_t)q.b * m + t % m];
+    }
+    const int E = 256 / m;
+    L.row = (int64_t)p.block_table[(int64_t)q.b * p.max_blocks + g / E] * E + g % E;
+}
+
+// Softmax weights of the group's logits (thread i < m holds logit i) into
+// w_lds (m <= 256).
+__device__ void group_weights(int m, float a, float* w_lds, float* red) {
+    const int tid = threadIdx.x;
+    float mx = wave_max(a);
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float e = tid < m ? expf(a - mx) : 0.0f;
+    float s = wave_sum(e);
+    __syncthreads();
+    if ((tid & 63) == 0) red[4 + (tid >> 6)] = s;
+    __syncthreads();
+    s = red[4] + red[5] + red[6] + red[7];
+    if (tid < m) w_lds[tid] = e / s;
+    __syncthreads();
+}
+
+// Weighted sum of dimensions [d0, d0 + 64) of the group over its tokens
+// (loaded by issue_slice, weights in w_lds), encoded into the pool.
+template <int TOK>
+__device__ void reduce_slice(const CompressArgs& p, bool ik_stream, int d0, const SliceLoads<TOK>& L,
+                             const float* w_lds, float* red) {
+    const int m = p.m;
+    const int dim = ik_stream ? p.dI : p.D;
     const int tid = threadIdx.x;
     const int lane = tid / (kSliceDims / kChunk), ch = tid % (kSliceDims / kChunk);
     const int d = d0 + ch * kChunk;
@@ -132,12 +210,12 @@ __device__ void compress_slice(const CompressArgs& p, const SeqChunk& q, int g, 
     float acc[kChunk];
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) acc[i] = 0.0f;
-    if (active) {
-        for (int i = lane; i < m; i += kLanes) {
-            const int t = g * m + i;
+#pragma unroll
+    for (int j = 0; j < kMaxTokPerLane; ++j) {
+        const int i = lane + kLanes * j;
+        if (active && i < m) {
             float x[kChunk];
-            if (t >= q.start) load8<TOK>(tok, (q.c0 + (t - q.start)) * dim + d, x);
-            else load8<TOK>(rtok, ((int64_t)q.b * m + t % m) * dim + d, x);
+            unpack_chunk<TOK>(L.tok[j], x);
             const float w = w_lds[i];
 #pragma unroll
             for (int e = 0; e < kChunk; ++e) acc[e] = fmaf(w, x[e], acc[e]);
@@ -153,8 +231,7 @@ __device__ void compress_slice(const CompressArgs& p, const SeqChunk& q, int g, 
         for (int l = 0; l < kLanes; ++l) v += red[l * kSliceDims + dd];
     }
     // encode and store (threads < 64 hold one dimension each)
-    const int E = 256 / m;
-    const int64_t row = (int64_t)p.block_table[(int64_t)q.b * p.max_blocks + g / E] * E + g % E;
+    const int64_t row = L.row;
     const int dt = ik_stream ? p.ik_dtype : p.kv_dtype;
     uint8_t* data = reinterpret_cast<uint8_t*>(ik_stream ? p.ik_data : p.kv_data);
     if (tid < kSliceDims) {
@@ -179,31 +256,14 @@ __device__ void compress_slice(const CompressArgs& p, const SeqChunk& q, int g, 
     __syncthreads();                                           // red is reused by the next slice
 }
 
-// Softmax weights of group g of one stream into w_lds (m <= 256).
-__device__ void group_weights(const CompressArgs& p, const SeqChunk& q, int g, bool ik_stream, float* w_lds,
-                              float* red) {
-    const int m = p.m;
-    const float* lg = ik_stream ? p.ik_logit : p.kv_logit;
-    const float* rlg = ik_stream ? p.rem_ik_logit : p.rem_kv_logit;
-    const int tid = threadIdx.x;
-    float a = -INFINITY;
-    if (tid < m) {
-        const int t = g * m + tid;
-        a = t >= q.start ? lg[q.c0 + (t - q.start)] : rlg[(int64_t)q.b * m + t % m];
-    }
-    float mx = wave_max(a);
-    __syncthreads();
-    if ((tid & 63) == 0) red[tid >> 6] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float e = tid < m ? expf(a - mx) : 0.0f;
-    float s = wave_sum(e);
-    __syncthreads();
-    if ((tid & 63) == 0) red[4 + (tid >> 6)] = s;
-    __syncthreads();
-    s = red[4] + red[5] + red[6] + red[7];
-    if (tid < m) w_lds[tid] = e / s;
-    __syncthreads();
+// One slice of group g, start to finish.
+template <int TOK>
+__device__ void compress_slice(const CompressArgs& p, const SeqChunk& q, int g, bool ik_stream, int d0, float* w_lds,
+                               float* red) {
+    SliceLoads<TOK> L;
+    issue_slice<TOK>(p, q, g, ik_stream, d0, L);
+    group_weights(p.m, L.logit, w_lds, red);
+    reduce_slice<TOK>(p, ik_stream, d0, L, w_lds, red);
 }
 
 template <int TOK>
@@ -238,69 +298,67 @@ __global__ __launch_bounds__(kThreads) void compress_append_kernel(CompressArgs 
     const int m = p.m, D = p.D;
     const int SK = (D + kSliceDims - 1) / kSliceDims;
     const int SI = p.ik_data != nullptr ? (p.dI + kSliceDims - 1) / kSliceDims : 0;
-
-    // (1) window ring
-    if (s == 0 && p.win_data != nullptr && pos >= q.end - p.win_cap) {
-        const int64_t slot = (int64_t)q.b * p.win_cap + pos % p.win_cap;
-        uint8_t* wd = reinterpret_cast<uint8_t*>(p.win_data);
-        const int pairs = D / 2;
-        if (p.win_dtype == DT_FP8) {
-            float x0[kMaxPairsPerThread], x1[kMaxPairsPerThread];
-            float amax = 0.0f;
-#pragma unroll
-            for (int i = 0; i < kMaxPairsPerThread; ++i) {
-                const int pr = tid + i * kThreads;
-                x0[i] = x1[i] = 0.0f;
-                if (pr < pairs) load_pair<TOK>(p.kv_tok, (int64_t)t * D + 2 * pr, x0[i], x1[i]);
-                amax = fmaxf(amax, fmaxf(fabsf(x0[i]), fabsf(x1[i])));
-            }
-            amax = block_max(amax, red);
-            const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
-            if (tid == 0) p.win_scale[slot] = sc;
-#pragma unroll
-            for (int i = 0; i < kMaxPairsPerThread; ++i) {
-                const int pr = tid + i * kThreads;
-                if (pr < pairs) {
-                    const uint32_t c = f32_to_fp8(x0[i] / sc) | (f32_to_fp8(x1[i] / sc) << 8);
-                    *reinterpret_cast<uint16_t*>(wd + slot * D + 2 * pr) = (uint16_t)c;
-                }
-            }
-        } else {
-            for (int pr = tid; pr < pairs; pr += kThreads) {
-                float x0, x1;
-                load_pair<TOK>(p.kv_tok, (int64_t)t * D + 2 * pr, x0, x1);
-                store_pair(p.win_dtype, wd, slot, D, pr, x0, x1);
-            }
-        }
-    }
-
-    // (2) the group this token completes
     const int g0 = q.start / m;                                // group holding `start`
     const bool race = (q.start % m) != 0 && (q.end % m) != 0 && q.end >= (g0 + 1) * m;
     const int tail0 = max((q.end / m) * m, q.start);
+
+    if (s == SK + SI) {
+        // (1) window ring
+        if (p.win_data != nullptr && pos >= q.end - p.win_cap) {
+            const int64_t slot = (int64_t)q.b * p.win_cap + pos % p.win_cap;
+            uint8_t* wd = reinterpret_cast<uint8_t*>(p.win_data);
+            const int pairs = D / 2;
+            if (p.win_dtype == DT_FP8) {
+                float x0[kMaxPairsPerThread], x1[kMaxPairsPerThread];
+                float amax = 0.0f;
+#pragma unroll
+                for (int i = 0; i < kMaxPairsPerThread; ++i) {
+                    const int pr = tid + i * kThreads;
+                    x0[i] = x1[i] = 0.0f;
+                    if (pr < pairs) load_pair<TOK>(p.kv_tok, (int64_t)t * D + 2 * pr, x0[i], x1[i]);
+                    amax = fmaxf(amax, fmaxf(fabsf(x0[i]), fabsf(x1[i])));
+                }
+                amax = block_max(amax, red);
+                const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+                if (tid == 0) p.win_scale[slot] = sc;
+#pragma unroll
+                for (int i = 0; i < kMaxPairsPerThread; ++i) {
+                    const int pr = tid + i * kThreads;
+                    if (pr < pairs) {
+                        const uint32_t c = f32_to_fp8(x0[i] / sc) | (f32_to_fp8(x1[i] / sc) << 8);
+                        *reinterpret_cast<uint16_t*>(wd + slot * D + 2 * pr) = (uint16_t)c;
+                    }
+                }
+            } else {
+                for (int pr = tid; pr < pairs; pr += kThreads) {
+                    float x0, x1;
+                    load_pair<TOK>(p.kv_tok, (int64_t)t * D + 2 * pr, x0, x1);
+                    store_pair(p.win_dtype, wd, slot, D, pr, x0, x1);
+                }
+            }
+        }
+        // (3) remainder ring: each tail token writes itself (see the header
+        // comment for `race`)
+        if (!race && pos >= tail0) write_ring<TOK>(p, q, pos);
+        return;
+    }
+
+    // (2) the group this token completes
     if ((pos + 1) % m == 0) {
         const int g = pos / m;
         if (race && g == g0) {
             // whole first group here, then the tail of the chunk into the ring
             if (s == 0) {
-                group_weights(p, q, g, false, w_lds, red);
                 for (int k = 0; k < SK; ++k) compress_slice<TOK>(p, q, g, false, k * kSliceDims, w_lds, red);
-                if (SI) {
-                    group_weights(p, q, g, true, w_lds, red);
-                    for (int k = 0; k < SI; ++k) compress_slice<TOK>(p, q, g, true, k * kSliceDims, w_lds, red);
-                }
+                for (int k = 0; k < SI; ++k) compress_slice<TOK>(p, q, g, true, k * kSliceDims, w_lds, red);
                 __syncthreads();
                 for (int tt = tail0; tt < q.end; ++tt) write_ring<TOK>(p, q, tt);
             }
-        } else if (s < SK + SI) {
+        } else {
             const bool ik = s >= SK;
-            group_weights(p, q, g, ik, w_lds, red);
             compress_slice<TOK>(p, q, g, ik, (ik ? s - SK : s) * kSliceDims, w_lds, red);
         }
     }
-
-    // (3) remainder ring: each tail token writes itself (see the header comment for `race`)
-    if (s == 0 && !race && pos >= tail0) write_ring<TOK>(p, q, pos);
 }
 
 }  // namespace
@@ -309,7 +367,7 @@ hipError_t launch_compress_append(const CompressArgs& a, int total_new, hipStrea
     if (total_new <= 0) return hipSuccess;
     const int SK = (a.D + kSliceDims - 1) / kSliceDims;
     const int SI = a.ik_data != nullptr ? (a.dI + kSliceDims - 1) / kSliceDims : 0;
-    dim3 grid(total_new, SK + SI);
+    dim3 grid(total_new, SK + SI + 1);
     if (a.tok_dtype == DT_F32)
         hipLaunchKernelGGL(compress_append_kernel<DT_F32>, grid, dim3(kThreads), 0, stream, a);
     else

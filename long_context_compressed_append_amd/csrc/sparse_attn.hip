@@ -357,7 +357,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int split = blockIdx.x, r = blockIdx.y;
     const RowKeys rk = row_keys(a, r);
     const int tb = split * a.split_tiles;
-    if (tb >= rk.tiles) return;                                   // empty split (the merge skips it)
+    if (tb >= rk.tiles) {
+        // empty split (a row with fewer tiles than the longest): a zero state
+        if (a.nsplit > 1 && tid < NW * 8) {
+            float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H + (int)blockIdx.z * (NW * 8) + tid;
+            ml[0] = -INFINITY;
+            ml[a.H] = 0.0f;
+        }
+        return;
+    }
     const int te = min(tb + a.split_tiles, rk.tiles);
     // waves w and w + NW/2 share 16 heads and split the dimensions
     const int hg = wave % (NW / 2), half = wave / (NW / 2);
@@ -450,50 +458,73 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
 // Merge the key splits of one (row, head): m* = max m_s, w_s = 2^(m_s - m*),
 // out = sum_s w_s O_s / sum_s w_s l_s, lse = (m* + log2 sum_s w_s l_s) ln 2.
-constexpr int kMergeThreads = 128;
-constexpr int kMaxSplits = 256;
+// Each thread owns 4 value dims.  The partial outputs of the first
+// kMergeBatch splits are requested before anything else, so they are in
+// flight while the block forms the weights (thread s owns split s and
+// s + kMergeThreads).  Empty splits carry m = -inf, weight 0, and their
+// workspace bytes are never used.
+constexpr int kMergeThreads = 192;     // >= 576 / 4
+constexpr int kMaxSplits = 256;        // <= 2 * kMergeThreads
+constexpr int kMergeBatch = 16;
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     __shared__ float wts[kMaxSplits];
     __shared__ float red[2][kMergeThreads / 64];
     const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
-    const RowKeys rk = row_keys(a, r);
-    const int ns = (rk.tiles + a.split_tiles - 1) / a.split_tiles;
-    const int H = a.H, DV = a.d_v;
-    const float* ml = a.part_ml + (int64_t)r * a.nsplit * 2 * H;
-    float M = -INFINITY;
-    for (int s = tid; s < ns; s += kMergeThreads) M = fmaxf(M, ml[s * 2 * H + h]);
-    M = wave_max(M);
+    const int H = a.H, DV = a.d_v, ns = a.nsplit;
+    const float* ml = a.part_ml + (int64_t)r * ns * 2 * H + h;
+    const int d = 4 * tid;
+    const bool mine = d < DV;
+    const float* po = a.part_o + ((int64_t)r * ns * H + h) * DV + (mine ? d : 0);
+    const int64_t sstride = (int64_t)H * DV;
+    f32x4 os[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) os[j] = *reinterpret_cast<const f32x4*>(po + min(j, ns - 1) * sstride);
+    const int s1 = tid + kMergeThreads;
+    const float m0 = tid < ns ? ml[(int64_t)tid * 2 * H] : -INFINITY;
+    const float l0 = tid < ns ? ml[(int64_t)tid * 2 * H + H] : 0.0f;
+    const float m1 = s1 < ns ? ml[(int64_t)s1 * 2 * H] : -INFINITY;
+    const float l1 = s1 < ns ? ml[(int64_t)s1 * 2 * H + H] : 0.0f;
+    float M = wave_max(fmaxf(m0, m1));
     if ((tid & 63) == 0) red[0][tid >> 6] = M;
     __syncthreads();
     M = red[0][0];
+#pragma unroll
     for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[0][i]);
-    float Ls = 0.0f;
-    for (int s = tid; s < ns; s += kMergeThreads) {
-        const float ms = ml[s * 2 * H + h];
-        const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-        wts[s] = w;
-        Ls += w * ml[s * 2 * H + H + h];
-    }
-    Ls = wave_sum(Ls);
-    if ((tid & 63) == 0) red[1][tid >> 6] = Ls;
+    const float w0 = m0 == -INFINITY ? 0.0f : exp2f(m0 - M);
+    const float w1 = m1 == -INFINITY ? 0.0f : exp2f(m1 - M);
+    if (tid < ns) wts[tid] = w0;
+    if (s1 < ns) wts[s1] = w1;
+    float L = wave_sum(w0 * l0 + w1 * l1);
+    if ((tid & 63) == 0) red[1][tid >> 6] = L;
     __syncthreads();
-    Ls = 0.0f;
-    for (int i = 0; i < kMergeThreads / 64; ++i) Ls += red[1][i];
-    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-    if (a.lse && tid == 0) a.lse[(int64_t)r * H + h] = (M + log2f(Ls)) * kLn2;
-    const float* po = a.part_o + ((int64_t)r * a.nsplit * H + h) * DV;
-    const int64_t sstride = (int64_t)H * DV;
-    for (int d = tid * 4; d < DV; d += kMergeThreads * 4) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < ns; ++s) acc += wts[s] * *reinterpret_cast<const f32x4*>(po + s * sstride + d);
-        acc *= inv;
-        const int64_t oi = ((int64_t)r * H + h) * DV + d;
-        if (a.out_dtype == DT_F32) {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + oi) = acc;
-        } else {
-            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + oi) =
-                u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    L = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMergeThreads / 64; ++i) L += red[1][i];
+    if (a.lse && tid == 0) a.lse[(int64_t)r * H + h] = (M + log2f(L)) * kLn2;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+        const float w = j < ns ? wts[j] : 0.0f;
+        acc = w > 0.0f ? acc + w * os[j] : acc;
+    }
+    for (int s0 = kMergeBatch; s0 < ns; s0 += kMergeBatch) {
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) os[j] = *reinterpret_cast<const f32x4*>(po + min(s0 + j, ns - 1) * sstride);
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+            const float w = s0 + j < ns ? wts[s0 + j] : 0.0f;
+            acc = w > 0.0f ? acc + w * os[j] : acc;
         }
+    }
+    if (!mine) return;
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    acc *= inv;
+    const int64_t oi = ((int64_t)r * H + h) * DV + d;
+    if (a.out_dtype == DT_F32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + oi) = acc;
+    } else {
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + oi) =
+            u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
     }
 }
 
