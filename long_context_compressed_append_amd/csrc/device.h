@@ -34,6 +34,15 @@ __device__ inline uint32_t f32_to_bf16(float x) {
 
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) { return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// The same rounding in one instruction (v_cvt_pk_bf16_f32, round to nearest
+// even) for finite values: attention probabilities and outputs.
+__device__ inline uint32_t cvt_pk_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 // ---------------------------------------------------------------------------
 // OCP E4M3 ("fn": bias 7, max 448, S.1111.111 = NaN)
 // ---------------------------------------------------------------------------
@@ -56,18 +65,6 @@ __device__ inline uint32_t f32_to_fp8(float x) {
     if (e > 8 || (e == 8 && m3 == 7u)) return sign | 0x7eu;    // rounded past 448
     return sign | ((uint32_t)(e + 7) << 3) | m3;
 }
-
-// E4M3 code -> bf16 bits (exact: 3 mantissa bits fit in bf16's 7).  Branch
-// free: subnormal codes (exponent field 0) are m * 2^-9, formed in fp32.
-__device__ inline uint32_t fp8_to_bf16(uint32_t c) {
-    const uint32_t s = (c & 0x80u) << 8;
-    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    const uint32_t normal = ((e + 120u) << 7) | (m << 4);
-    const uint32_t sub = __float_as_uint((float)m * 0.001953125f) >> 16;
-    return s | (e == 0 ? sub : normal);
-}
-
-__device__ inline float fp8_to_f32(uint32_t c) { return bf16_to_f32(fp8_to_bf16(c)); }
 
 // ---------------------------------------------------------------------------
 // OCP MXFP4: E2M1 elements, one E8M0 scale per 32 elements
@@ -99,38 +96,29 @@ __device__ inline int mx_scale_exp(float amax) {
     return X < -127 ? -127 : (X > 127 ? 127 : X);
 }
 
-// E2M1 code -> bf16 bits of code * 2^X.  The E2M1 magnitude (two significant
-// bits) is formed in fp32, scaled by v_ldexp_f32 (exact for every E8M0 scale
-// of fp32 data, subnormal results included) and truncated to bf16, which
-// drops only zero bits.  Branch free.
-__device__ inline uint32_t fp4_to_bf16(uint32_t nib, int X) {
-    const uint32_t mag = nib & 7u;
-    const uint32_t e = mag >> 1, mb = mag & 1u;
-    uint32_t fb = ((126u + e) << 23) | (mb << 22);             // (1 + mb/2) * 2^(e-1), e >= 1
-    fb = mag == 1u ? 0x3f000000u : fb;                         // 0.5
-    fb = mag == 0u ? 0u : fb;
-    const float v = ldexpf(__uint_as_float(fb), X);
-    return ((nib & 8u) << 12) | (__float_as_uint(v) >> 16);
-}
+// Decoding uses gfx950's scaled conversions (v_cvt_scalef32_pk_bf16_fp8 /
+// _fp4: two OCP codes -> two bf16, times a float scale).  Every E4M3 value
+// and every E2M1 value times a power-of-two scale 2^X, X >= -126, is a bf16
+// value, so the conversion is exact; for X = -127 (the scale of an all-zero
+// block, or of a block below 2^-125) the scale operand 2^-127 is a float
+// subnormal and the block decodes to zeros, an absolute error below 2^-124.
 
-// Eight E4M3 codes (two words) -> eight bf16 (four words).
+// Eight E4M3 codes (two words, code i in byte i) -> eight bf16 (four words).
 __device__ inline u32x4 fp8x8_to_bf16(uint32_t a, uint32_t b) {
-    return u32x4{fp8_to_bf16(a & 0xffu) | (fp8_to_bf16((a >> 8) & 0xffu) << 16),
-                 fp8_to_bf16((a >> 16) & 0xffu) | (fp8_to_bf16(a >> 24) << 16),
-                 fp8_to_bf16(b & 0xffu) | (fp8_to_bf16((b >> 8) & 0xffu) << 16),
-                 fp8_to_bf16((b >> 16) & 0xffu) | (fp8_to_bf16(b >> 24) << 16)};
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.0f, true))};
 }
 
 // Eight E2M1 codes (one word, element 2i in the low nibble of byte i) with
 // shared exponent X -> eight bf16 (four words).
 __device__ inline u32x4 fp4x8_to_bf16(uint32_t w, int X) {
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t bb = w >> (8 * q);
-        o[q] = fp4_to_bf16(bb & 15u, X) | (fp4_to_bf16((bb >> 4) & 15u, X) << 16);
-    }
-    return o;
+    const float sc = __uint_as_float(X > -127 ? (uint32_t)(X + 127) << 23 : 0u);
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3))};
 }
 
 // ---------------------------------------------------------------------------

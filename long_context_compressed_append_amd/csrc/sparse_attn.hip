@@ -45,6 +45,7 @@ constexpr int kKeys = 32;              // keys per tile
 // generic-to-LDS conversion is ever needed on a run-time selected pointer.
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
@@ -122,22 +123,37 @@ struct Tiler {
     static constexpr int NU_P = (UPK_P + kThreadsPerKey - 1) / kThreadsPerKey;
     static constexpr int NU = NU_W > NU_P ? NU_W : NU_P;
 
-    // Issue the loads of tile `tile` (row-local tile index).  `live` false (a
-    // tile past the split): the loads read row 0 and nothing is used; issuing
-    // them anyway keeps the number of loads per step fixed, so the compiler's
-    // wait counts stay exact.  Masked keys also read row 0 and are zeroed
-    // when stored.
-    __device__ __forceinline__ static void load(const AttnArgs& a, const RowKeys& rk, int tile, bool live,
-                                                const lds_i32* idx_lds, int idx0, const lds_i32* bt_lds, int blk0,
-                                                TileRegs<NU>& R) {
-        const int tid = threadIdx.x;
-        const int key = tid / kThreadsPerKey, sub = tid % kThreadsPerKey;
-        const bool win = live && tile >= rk.sel_tiles;              // uniform over the workgroup
-        if (win) {
+    // Where this thread's key of tile `tile` (row-local tile index) is
+    // stored.  `live` false (a tile past the split): row 0 is read and
+    // nothing is used; issuing those loads anyway keeps the number of loads
+    // per step fixed, so the compiler's wait counts stay exact.  Masked keys
+    // also read row 0 and are zeroed when stored.
+    struct Src {
+        int64_t row;
+        bool ok, win;
+    };
+    __device__ __forceinline__ static Src resolve(const AttnArgs& a, const RowKeys& rk, int tile, bool live,
+                                                  const lds_i32* idx_lds, int idx0, const lds_i32* bt_lds, int blk0) {
+        const int key = (int)threadIdx.x / kThreadsPerKey;
+        Src s;
+        s.win = live && tile >= rk.sel_tiles;                       // uniform over the workgroup
+        if (s.win) {
             const int w = (tile - rk.sel_tiles) * kKeys + key;
-            const bool ok = w < rk.nwin;
-            const int64_t row = (int64_t)rk.b * a.win_cap + (rk.t0 + (ok ? w : 0)) % a.win_cap;
-            const uint8_t* src = reinterpret_cast<const uint8_t*>(a.win_data) + row * (WD == DT_BF16 ? 2 * D : D);
+            s.ok = w < rk.nwin;
+            s.row = (int64_t)rk.b * a.win_cap + (rk.t0 + (s.ok ? w : 0)) % a.win_cap;
+        } else {
+            const int64_t prow = pool_row(a, rk, (live ? tile * kKeys : idx0) + key, idx_lds, idx0, bt_lds, blk0);
+            s.ok = live && prow >= 0;
+            s.row = s.ok ? prow : 0;
+        }
+        return s;
+    }
+
+    // Issue the loads of a resolved key into registers.
+    __device__ __forceinline__ static void issue(const AttnArgs& a, const Src& s, TileRegs<NU>& R) {
+        const int sub = (int)threadIdx.x % kThreadsPerKey;
+        if (s.win) {
+            const uint8_t* src = reinterpret_cast<const uint8_t*>(a.win_data) + s.row * (WD == DT_BF16 ? 2 * D : D);
 #pragma unroll
             for (int i = 0; i < NU_W; ++i) {
                 const int part = sub + kThreadsPerKey * i;
@@ -145,14 +161,10 @@ struct Tiler {
                 R.v[i] = *reinterpret_cast<const u32x4*>(src + pc * 16);
                 R.sc[i] = 127u;
             }
-            R.kscale = WD == DT_FP8 ? a.win_scale[row] : 1.0f;
-            R.valid = ok;
+            R.kscale = WD == DT_FP8 ? a.win_scale[s.row] : 1.0f;
         } else {
-            const int64_t prow = pool_row(a, rk, (live ? tile * kKeys : idx0) + key, idx_lds, idx0, bt_lds, blk0);
-            const bool ok = live && prow >= 0;
-            const int64_t row = ok ? prow : 0;
-            const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv_data) + row * (KVD == DT_BF16 ? 2 * D : D / 2);
-            const uint8_t* scs = reinterpret_cast<const uint8_t*>(a.kv_scale) + row * (D / 32);
+            const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv_data) + s.row * (KVD == DT_BF16 ? 2 * D : D / 2);
+            const uint8_t* scs = reinterpret_cast<const uint8_t*>(a.kv_scale) + s.row * (D / 32);
 #pragma unroll
             for (int i = 0; i < NU_P; ++i) {
                 const int part = sub + kThreadsPerKey * i;
@@ -161,16 +173,21 @@ struct Tiler {
                 R.sc[i] = KVD == DT_MXFP4 ? (uint32_t)scs[pc] : 127u;
             }
             R.kscale = 1.0f;
-            R.valid = ok;
         }
+        R.valid = s.ok;
     }
 
     // Convert the registers of tile `tile` to bf16 and write them to an LDS stage.
+    // kmeta[0..31]: each key's value scale (FP8 window scale, 1, or -1 for
+    // a masked key); kmeta[32..63]: its score factor scale_log2 * scale.
     __device__ __forceinline__ static void store(const RowKeys& rk, int tile, const TileRegs<NU>& R, lds_u8* stage,
-                                                 lds_f32* kmeta) {
+                                                 lds_f32* kmeta, float scale_log2) {
         const int tid = threadIdx.x;
         const int key = tid / kThreadsPerKey, sub = tid % kThreadsPerKey;
-        if (sub == 0) kmeta[key] = R.valid ? R.kscale : -1.0f;
+        if (sub == 0) {
+            kmeta[key] = R.valid ? R.kscale : -1.0f;
+            kmeta[kKeys + key] = scale_log2 * R.kscale;
+        }
         lds_u8* dst = stage + key * Geo<D>::ROWB;
         if (tile >= rk.sel_tiles) store_parts<WD, UPK_W, NU_W>(R, dst, sub);
         else store_parts<KVD, UPK_P, NU_P>(R, dst, sub);
@@ -211,103 +228,136 @@ struct Tiler {
 };
 
 // Per-wave softmax/PV state and the tile computation.  A pair of waves
-// shares 16 heads and splits the shared-KV dimension: each wave computes the
-// partial scores over its half of D (its half of every query stays in
-// VGPRs), the pair swaps partial scores through LDS, and each wave then runs
-// the same softmax and accumulates P V for its half of the value dims.
-template <int D, int DV>
+// shares HB blocks of 16 heads and splits the shared-KV dimension: each wave
+// computes the partial scores over its half of D (its half of every query
+// stays in VGPRs), the pair swaps partial scores through LDS, and each wave
+// then runs the same softmax and accumulates P V for its half of the value
+// dims.  Every key or value fragment read from LDS feeds HB head blocks.
+template <int D, int DV, int HB>
 struct HalfWave {
     static constexpr int KS = D / 64;          // k-steps of S^T per half
     static constexpr int NDT = DV / 32;        // 16-dim tiles of O^T per half
-    bf16x8 qb[KS];
-    f32x4 o[NDT];
-    float m_run, l_run;
+    static constexpr int NACC = HB == 1 ? 2 : 1;   // accumulators per score sub-tile
+    static constexpr int XS = HB * 8 * 64;     // floats of one wave's score exchange slot
+    bf16x8 qb[HB][KS];
+    f32x4 o[HB][NDT];
+    float m_run[HB], l_run[HB];
 
-    __device__ __forceinline__ void init(const AttnArgs& a, int r, int head, int g, int half) {
-        const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + head) * D + half * (D / 2);
+    __device__ __forceinline__ void init(const AttnArgs& a, int r, int head0, int g, int half) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) qb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + 32 * s + 8 * g));
+        for (int hb = 0; hb < HB; ++hb) {
+            const uint16_t* q =
+                reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + head0 + 16 * hb) * D + half * (D / 2);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_run = -INFINITY;
-        l_run = 0.0f;
+            for (int s = 0; s < KS; ++s)
+                qb[hb][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + 32 * s + 8 * g));
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) o[hb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            m_run[hb] = -INFINITY;
+            l_run[hb] = 0.0f;
+        }
     }
 
     // xs_mine / xs_pair: this wave's and the partner wave's score exchange
-    // slots, [8][64] floats each.
+    // slots, [HB][64 lanes][8] floats each.
     __device__ __forceinline__ void tile(const lds_u8* lds, const lds_f32* kmeta, lds_f32* xs_mine,
-                                         const lds_f32* xs_pair, float scale_log2, int g, int c16, int lane, int half) {
+                                         const lds_f32* xs_pair, int g, int c16, int lane, int half) {
         constexpr int ROWB = Geo<D>::ROWB;
-        // partial S^T = K Q^T over this half's dims, two 16-key sub-tiles, two
-        // accumulators each so consecutive MFMAs are independent
-        f32x4 sacc[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-            const lds_u8* rowp = lds + (kt * 16 + c16) * ROWB + half * D + 16 * g;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                bf16x8 kA = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(rowp + 64 * s));
-                if (s & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, qb[s], acc1, 0, 0, 0);
-                else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, qb[s], acc0, 0, 0, 0);
-            }
-            sacc[kt] = acc0 + acc1;
-        }
+        // partial S^T = K Q^T over this half's dims: two 16-key sub-tiles per
+        // head block; each key fragment serves every head block
+        f32x4 sacc[2][HB][NACC];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) xs_mine[(kt * 4 + v) * 64 + lane] = sacc[kt][v];
+            for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                for (int c = 0; c < NACC; ++c) sacc[kt][hb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            bf16x8 kA[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+                kA[kt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(
+                                                        lds + (kt * 16 + c16) * ROWB + half * D + 16 * g + 64 * s));
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb)
+                    sacc[kt][hb][s % NACC] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[kt], qb[hb][s], sacc[kt][hb][s % NACC], 0, 0, 0);
+        }
+        f32x4 sp[2][HB];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
+                sp[kt][hb] = sacc[kt][hb][0];
+                if constexpr (NACC > 1) sp[kt][hb] += sacc[kt][hb][1];
+                *reinterpret_cast<lds_f32x4*>(xs_mine + (hb * 64 + lane) * 8 + 4 * kt) = sp[kt][hb];
+            }
         __syncthreads();
-        float x[2][4], ks[2][4];
-        float mx = -INFINITY;
+        bf16x8 pb[HB], pbl[HB];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int hb = 0; hb < HB; ++hb) {
+            float x[2][4], ks[2][4];
+            float mx = -INFINITY;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float full = sacc[kt][v] + xs_pair[(kt * 4 + v) * 64 + lane];
-                const float km = kmeta[kt * 16 + 4 * g + v];
-                ks[kt][v] = km;
-                x[kt][v] = km >= 0.0f ? full * scale_log2 * km : -INFINITY;
-                mx = fmaxf(mx, x[kt][v]);
+            for (int kt = 0; kt < 2; ++kt) {
+                const f32x4 pair = *reinterpret_cast<const lds_f32x4*>(xs_pair + (hb * 64 + lane) * 8 + 4 * kt);
+                const f32x4 km = *reinterpret_cast<const lds_f32x4*>(kmeta + kt * 16 + 4 * g);
+                const f32x4 kx = *reinterpret_cast<const lds_f32x4*>(kmeta + kKeys + kt * 16 + 4 * g);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    ks[kt][v] = km[v];
+                    x[kt][v] = km[v] >= 0.0f ? (sp[kt][hb][v] + pair[v]) * kx[v] : -INFINITY;
+                    mx = fmaxf(mx, x[kt][v]);
+                }
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // Lazy rescaling: the reference max m_run moves only when the tile's max
-        // exceeds it by more than 8 (log2 units), so most tiles leave the O
-        // accumulators untouched; probabilities relative to m_run stay <= 2^8.
-        if (mx > m_run + 8.0f) {
-            const float alpha = exp2f(m_run - mx);             // 0 while m_run = -inf
-            l_run *= alpha;
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            // Lazy rescaling: the reference max m_run moves only when the tile's
+            // max exceeds it by more than 8 (log2 units), so most tiles leave the
+            // O accumulators untouched; probabilities relative to m_run stay <= 2^8.
+            if (mx > m_run[hb] + 8.0f) {
+                const float alpha = exp2f(m_run[hb] - mx);     // 0 while m_run = -inf
+                l_run[hb] *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-            m_run = mx;
+                for (int dt = 0; dt < NDT; ++dt) o[hb][dt] *= alpha;
+                m_run[hb] = mx;
+            }
+            // reference for the exponent: m_run, or 0 while every key so far is
+            // masked (then every x is -inf and every p is 0)
+            const float mref = m_run[hb] == -INFINITY ? 0.0f : m_run[hb];
+            float psum = 0.0f;
+            uint32_t pk[4], pl[4];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int v = 0; v < 4; v += 2) {
+                    // x - mref <= 8: v_exp_f32 directly (results below 2^-126
+                    // may flush to zero, far below the sum's precision)
+                    const float p0 = __builtin_amdgcn_exp2f(x[kt][v] - mref);
+                    const float p1 = __builtin_amdgcn_exp2f(x[kt][v + 1] - mref);
+                    psum += p0 + p1;
+                    // masked keys have p = 0; FP8 window keys carry their scale
+                    const float w0 = p0 * ks[kt][v], w1 = p1 * ks[kt][v + 1];
+                    const uint32_t h = cvt_pk_bf16(w0, w1);
+                    pk[kt * 2 + v / 2] = h;
+                    pl[kt * 2 + v / 2] = cvt_pk_bf16(w0 - __uint_as_float(h << 16), w1 - __uint_as_float(h & 0xffff0000u));
+                }
+            l_run[hb] += psum;
+            pb[hb] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+            pbl[hb] = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
         }
-        const bool none = m_run == -INFINITY;
-        float psum = 0.0f;
-        uint32_t pk[4], pl[4];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int v = 0; v < 4; v += 2) {
-                const float p0 = none ? 0.0f : exp2f(x[kt][v] - m_run);
-                const float p1 = none ? 0.0f : exp2f(x[kt][v + 1] - m_run);
-                psum += p0 + p1;
-                const float w0 = p0 * fmaxf(ks[kt][v], 0.0f), w1 = p1 * fmaxf(ks[kt][v + 1], 0.0f);
-                const uint32_t h = pack_bf16x2(w0, w1);
-                pk[kt * 2 + v / 2] = h;
-                pl[kt * 2 + v / 2] = pack_bf16x2(w0 - bf16_to_f32(h & 0xffffu), w1 - bf16_to_f32(h >> 16));
-            }
-        l_run += psum;
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-        const bf16x8 pbl = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
         // O^T += V^T P^T over this half's value dims.  Within each 16-lane block,
         // ds_read_b64_tr_b16 hands lane i element (i & 3) of the 8-byte chunk
         // addressed by lane (i >> 2) + 4e, e = 0..3: lane s addresses key
         // 4g + (s >> 2), dims dt*16 + 4(s & 3) .. +3, so lane i receives keys
-        // 4g + e at dim dt*16 + i.  The hi and lo products of a dim tile are
-        // issued four tiles apart so they do not wait on each other.
+        // 4g + e at dim dt*16 + i.  Each value fragment serves every head
+        // block, hi and lo; the hi and lo products of a dim tile are issued
+        // apart so they do not wait on each other.
         const lds_u8* vbase = lds + (4 * g + (c16 >> 2)) * ROWB + half * (DV / 2) * 2 + 8 * (c16 & 3);
-        constexpr int G4 = 4;
+        constexpr int G4 = HB == 1 ? 4 : 2;
 #pragma unroll
         for (int d0 = 0; d0 < NDT; d0 += G4) {
             bf16x8 vA[G4];
@@ -324,19 +374,28 @@ struct HalfWave {
             }
 #pragma unroll
             for (int j = 0; j < G4; ++j)
-                if (d0 + j < NDT) o[d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA[j], pb, o[d0 + j], 0, 0, 0);
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb)
+                    if (d0 + j < NDT)
+                        o[hb][d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA[j], pb[hb], o[hb][d0 + j], 0, 0, 0);
 #pragma unroll
             for (int j = 0; j < G4; ++j)
-                if (d0 + j < NDT) o[d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA[j], pbl, o[d0 + j], 0, 0, 0);
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb)
+                    if (d0 + j < NDT)
+                        o[hb][d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA[j], pbl[hb], o[hb][d0 + j], 0, 0, 0);
         }
     }
 };
 
+constexpr int kHeadBlocks = 1;         // 16-head blocks per wave
 constexpr int kBtLds = 4096;           // block-table entries cached in LDS
 constexpr int kIdxLds = 2560;          // top-k slots cached in LDS (= max keys per split)
 
-template <int KVD, int WD, int D, int DV, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(AttnArgs a) {
+template <int KVD, int WD, int D, int DV, int HB>
+__global__ __launch_bounds__(8 / HB * 64) __attribute__((amdgpu_waves_per_eu(2 / HB, 2 / HB))) void attn_mfma_kernel(
+    AttnArgs a) {
+    constexpr int NW = 8 / HB;                                    // waves: NW/2 head groups x 2 halves of D
     using G = Geo<D>;
     constexpr int NT = NW * 64;
     using TL = Tiler<KVD, WD, D, NT>;
@@ -345,10 +404,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     constexpr int kPrefetch = NU <= 12 ? 2 : 1;
     static_assert(kPrefetch == 1 || kPrefetch == 2, "prefetch depth");
     __shared__ __attribute__((aligned(16))) uint8_t stage[2][G::STAGE];
-    __shared__ float kmeta[2][kKeys];
+    __shared__ __attribute__((aligned(16))) float kmeta[2][2 * kKeys];
     __shared__ int32_t bt_mem[kBtLds];
     __shared__ int32_t idx_mem[kIdxLds];
-    __shared__ float xs_mem[NW][8 * 64];                          // partial-score exchange
+    __shared__ __attribute__((aligned(16))) float xs_mem[NW][HalfWave<D, DV, HB>::XS];   // partial-score exchange
     lds_i32* const bt_lds = (lds_i32*)&bt_mem[0];
     lds_i32* const idx_lds = (lds_i32*)&idx_mem[0];
 
@@ -359,17 +418,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int tb = split * a.split_tiles;
     if (tb >= rk.tiles) {
         // empty split (a row with fewer tiles than the longest): a zero state
-        if (a.nsplit > 1 && tid < NW * 8) {
-            float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H + (int)blockIdx.z * (NW * 8) + tid;
+        if (a.nsplit > 1 && tid < 64) {
+            float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H + (int)blockIdx.z * 64 + tid;
             ml[0] = -INFINITY;
             ml[a.H] = 0.0f;
         }
         return;
     }
     const int te = min(tb + a.split_tiles, rk.tiles);
-    // waves w and w + NW/2 share 16 heads and split the dimensions
+    // waves w and w + NW/2 share 16 HB heads and split the dimensions
     const int hg = wave % (NW / 2), half = wave / (NW / 2);
-    const int head = (int)blockIdx.z * (NW * 8) + hg * 16 + c16;
+    const int head = (int)blockIdx.z * 64 + hg * 16 * HB + c16;   // this lane's head of head block 0
 
     // prologue: top-k slots and block-table range of this split into LDS
     const int sel_end = min(te, rk.sel_tiles) * kKeys;            // selected slots [tb*32, sel_end)
@@ -392,19 +451,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int i = tid; i < min(nblk, kBtLds); i += NT) bt_lds[i] = a.block_table[(int64_t)rk.b * a.max_blocks + blk0 + i];
     __syncthreads();
 
-    HalfWave<D, DV> W;
+    HalfWave<D, DV, HB> W;
     W.init(a, r, head, g, half);
     lds_f32* const xs_mine = (lds_f32*)&xs_mem[wave][0];
     const lds_f32* const xs_pair = (lds_f32*)&xs_mem[wave ^ (NW / 2)][0];
 
     TileRegs<NU> R[kPrefetch];
     const int ntl = te - tb;
-    TL::load(a, rk, tb, true, idx_lds, idx0, bt_lds, blk0, R[0]);
-    if constexpr (kPrefetch > 1) TL::load(a, rk, tb + 1, 1 < ntl, idx_lds, idx0, bt_lds, blk0, R[1]);
+    TL::issue(a, TL::resolve(a, rk, tb, true, idx_lds, idx0, bt_lds, blk0), R[0]);
+    if constexpr (kPrefetch > 1) TL::issue(a, TL::resolve(a, rk, tb + 1, 1 < ntl, idx_lds, idx0, bt_lds, blk0), R[1]);
     lds_u8* const st = (lds_u8*)&stage[0][0];
     lds_f32* const km = (lds_f32*)&kmeta[0][0];
-    TL::store(rk, tb, R[0], st, km);
-    TL::load(a, rk, tb + kPrefetch, kPrefetch < ntl, idx_lds, idx0, bt_lds, blk0, R[0]);
+    TL::store(rk, tb, R[0], st, km, a.scale_log2);
+    TL::issue(a, TL::resolve(a, rk, tb + kPrefetch, kPrefetch < ntl, idx_lds, idx0, bt_lds, blk0), R[0]);
     __syncthreads();
 
     // tile u sits in register set (u - tb) % P until it is stored to stage
@@ -412,9 +471,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // register set is addressed statically
     auto step = [&](auto J, int t) __attribute__((always_inline)) {
         constexpr int nxt = (decltype(J)::value + 1) % kPrefetch;
-        if (t + 1 < ntl) TL::store(rk, tb + t + 1, R[nxt], st + ((t + 1) & 1) * G::STAGE, km + ((t + 1) & 1) * kKeys);
-        TL::load(a, rk, tb + t + 1 + kPrefetch, t + 1 + kPrefetch < ntl, idx_lds, idx0, bt_lds, blk0, R[nxt]);
-        W.tile(st + (t & 1) * G::STAGE, km + (t & 1) * kKeys, xs_mine, xs_pair, a.scale_log2, g, c16, lane, half);
+        // the next loads' storage rows come from LDS before this step's stores
+        const typename TL::Src nsrc =
+            TL::resolve(a, rk, tb + t + 1 + kPrefetch, t + 1 + kPrefetch < ntl, idx_lds, idx0, bt_lds, blk0);
+        if (t + 1 < ntl)
+            TL::store(rk, tb + t + 1, R[nxt], st + ((t + 1) & 1) * G::STAGE, km + ((t + 1) & 1) * 2 * kKeys, a.scale_log2);
+        TL::issue(a, nsrc, R[nxt]);
+        W.tile(st + (t & 1) * G::STAGE, km + (t & 1) * 2 * kKeys, xs_mine, xs_pair, g, c16, lane, half);
         __syncthreads();
     };
     for (int t0 = 0; t0 < ntl; t0 += kPrefetch) {
@@ -423,35 +486,39 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             if (t0 + 1 < ntl) step(IntC<1>{}, t0 + 1);
     }
 
-    // finish: total row sum of this head over the 4 lane groups
-    float l_tot = W.l_run + __shfl_xor(W.l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    constexpr int NDT = HalfWave<D, DV>::NDT;
+    // finish: total row sum of each head over the 4 lane groups
+    constexpr int NDT = HalfWave<D, DV, HB>::NDT;
     const int dv0 = half * (DV / 2) + 4 * g;
-    if (a.nsplit == 1) {
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        const int64_t base = ((int64_t)r * a.H + head) * DV + dv0;
-        if (a.out_dtype == DT_F32) {
-            float* out = reinterpret_cast<float*>(a.out) + base;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(out + dt * 16) = W.o[dt] * inv;
-        } else {
-            uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + base;
+    for (int hb = 0; hb < HB; ++hb) {
+        const int hd = head + 16 * hb;
+        float l_tot = W.l_run[hb] + __shfl_xor(W.l_run[hb], 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        if (a.nsplit == 1) {
+            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            const int64_t base = ((int64_t)r * a.H + hd) * DV + dv0;
+            if (a.out_dtype == DT_F32) {
+                float* out = reinterpret_cast<float*>(a.out) + base;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                f32x4 t = W.o[dt] * inv;
-                *reinterpret_cast<u32x2*>(out + dt * 16) = u32x2{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
+                for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(out + dt * 16) = W.o[hb][dt] * inv;
+            } else {
+                uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + base;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    f32x4 t = W.o[hb][dt] * inv;
+                    *reinterpret_cast<u32x2*>(out + dt * 16) = u32x2{cvt_pk_bf16(t[0], t[1]), cvt_pk_bf16(t[2], t[3])};
+                }
             }
-        }
-        if (a.lse && g == 0 && half == 0) a.lse[(int64_t)r * a.H + head] = (W.m_run + log2f(l_tot)) * kLn2;
-    } else {
-        float* po = a.part_o + (((int64_t)r * a.nsplit + split) * a.H + head) * DV + dv0;
+            if (a.lse && g == 0 && half == 0) a.lse[(int64_t)r * a.H + hd] = (W.m_run[hb] + log2f(l_tot)) * kLn2;
+        } else {
+            float* po = a.part_o + (((int64_t)r * a.nsplit + split) * a.H + hd) * DV + dv0;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = W.o[dt];
-        if (g == 0 && half == 0) {
-            float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H;
-            ml[head] = W.m_run;
-            ml[a.H + head] = l_tot;
+            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = W.o[hb][dt];
+            if (g == 0 && half == 0) {
+                float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H;
+                ml[hd] = W.m_run[hb];
+                ml[a.H + hd] = l_tot;
+            }
         }
     }
 }
@@ -524,7 +591,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + oi) = acc;
     } else {
         *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + oi) =
-            u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+            u32x2{cvt_pk_bf16(acc[0], acc[1]), cvt_pk_bf16(acc[2], acc[3])};
     }
 }
 
@@ -594,21 +661,22 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     if (a.lse && tid == 0) a.lse[(int64_t)r * a.H + h] = mx + logf(sum);
 }
 
-template <int KVD, int WD, int D, int DV, int NW>
+template <int KVD, int WD, int D, int DV, int HB>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
-    dim3 grid(a.nsplit, a.num_rows, a.H / (NW * 8));
-    hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, NW>), grid, dim3(NW * 64), 0, stream, a);
+    dim3 grid(a.nsplit, a.num_rows, a.H / 64);
+    hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, HB>), grid, dim3(8 / HB * 64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     hipLaunchKernelGGL(attn_merge_kernel, dim3(a.H, a.num_rows), dim3(kMergeThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-// Workgroups of eight waves cover 64 heads; more heads add head groups to the grid.
+// Workgroups cover 64 heads (eight waves of 16 heads each); more heads add
+// head groups to the grid.
 template <int KVD, int WD, int D, int DV>
 hipError_t launch_heads(const AttnArgs& a, hipStream_t stream) {
     if (a.H % 64 != 0) return hipErrorInvalidValue;
-    return launch_mfma<KVD, WD, D, DV, 8>(a, stream);
+    return launch_mfma<KVD, WD, D, DV, kHeadBlocks>(a, stream);
 }
 
 template <int KVD, int WD>
