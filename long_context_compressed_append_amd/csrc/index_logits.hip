@@ -63,9 +63,42 @@ __device__ inline bf16x8 key_operand(const RawKey<KD, KS>& k, int s) {
     }
 }
 
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
+
+// Register sets of keys per wave (PF - 1 tiles in flight) at two waves per
+// SIMD (the head weights are read from LDS per tile to make room).  Decode
+// streams keys from HBM: FP8 waves (half the registers per tile) keep three
+// tiles in flight; bf16 waves keep one (two measured no faster).  Prefill
+// waves re-read keys their neighbours fetched and keep one.
+template <int KD, int ROWS>
+constexpr int key_depth() {
+    return ROWS == 1 && KD == DT_FP8 ? 4 : 2;
+}
+template <int KD, int ROWS>
+constexpr int waves_per_simd() {
+    return 2;
+}
+
+// Calls f(IntC<J>, tile + J) for J = 0 .. PF-1 while tile + J < t_end.
+template <int J, int PF, class F>
+__device__ __forceinline__ void unroll_steps(F& f, int tile, int t_end) {
+    if constexpr (J < PF) {
+        if (tile + J < t_end) {
+            f(IntC<J>{}, tile + J);
+            unroll_steps<J + 1, PF>(f, tile, t_end);
+        }
+    }
+}
+
 template <int KD, int NHT, int DI, int ROWS>
-__global__ __launch_bounds__(kThreads) void index_mfma_kernel(IndexArgs p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KD, ROWS>(),
+                                                                           waves_per_simd<KD, ROWS>()))) void
+index_mfma_kernel(IndexArgs p) {
     constexpr int KS = DI / 16, HALF = DI / 2;
+    constexpr int PF = key_depth<KD, ROWS>();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, j = lane & 31;
     const int r_raw = ROWS == 1 ? (int)blockIdx.y : (int)blockIdx.y * 4 + wave;
@@ -84,18 +117,20 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(IndexArgs p) {
 
     // Loads are issued unconditionally (tile indices clamped to the wave's
     // range) so the compiler's wait counts stay exact.  The block-table entry
-    // of a tile is fetched one tile ahead of its keys, the keys one tile
-    // ahead of their MFMAs.
+    // of a tile is fetched one step ahead of its keys, the keys PF - 1 tiles
+    // ahead of their MFMAs, in a ring of PF register sets addressed
+    // statically (the tile loop is unrolled by PF).
     auto entry = [&](int tile) { return min(min(tile, t_end - 1) * 32 + j, n - 1); };
     auto table = [&](int tile) { return bt[entry(tile) >> sh]; };
     auto row = [&](int tile, int pb) -> int64_t {
         return ((int64_t)pb << sh) + (entry(tile) & ((1 << sh) - 1));
     };
     int pb_next = 0;
-    RawKey<KD, KS> kcur;
+    RawKey<KD, KS> kr[PF];
     if (work) {
-        pb_next = table(t_begin + 1);
-        load_key<KD, KS>(keys, row(t_begin, table(t_begin)), g, kcur);
+#pragma unroll
+        for (int i = 0; i < PF - 1; ++i) load_key<KD, KS>(keys, row(t_begin + i, table(t_begin + i)), g, kr[i]);
+        pb_next = table(t_begin + PF - 1);
     }
 
     // The query (HI x DI bf16) and head weights of the workgroup's row(s) are
@@ -104,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(IndexArgs p) {
     constexpr int QROWB = DI * 2 + 16;
     constexpr int NQ = ROWS == 1 ? 1 : 4;
     __shared__ __attribute__((aligned(16))) uint8_t q_lds[NQ][NHT * 32 * QROWB];
-    __shared__ float w_lds[NQ][NHT * 32];
+    __shared__ __attribute__((aligned(16))) float w_lds[NQ][NHT * 32];
     {
         const int slot = ROWS == 1 ? 0 : wave;
         const int nthr = ROWS == 1 ? kThreads : 64;
@@ -128,17 +163,16 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(IndexArgs p) {
         for (int s = 0; s < KS; ++s)
             qa[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                                       &q_lds[slot][(32 * t + j) * QROWB + (g * HALF + 8 * s) * 2]));
-    // head weights in C-layout order: head 32t + 8(v/4) + 4g + v%4
-    float wv[NHT][16];
-#pragma unroll
-    for (int t = 0; t < NHT; ++t)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) wv[t][v] = w_lds[slot][32 * t + 8 * (v >> 2) + 4 * g + (v & 3)];
+    // head weights are read from LDS per tile, in C-layout order: head
+    // 32t + 8(v/4) + 4g + v%4, four consecutive heads per 16-byte read
+    const float* wrow = &w_lds[slot][4 * g];
 
     float* out = p.logits + (int64_t)r * p.ld;
-    auto step = [&](int tile, RawKey<KD, KS>& kc, RawKey<KD, KS>& kn) __attribute__((always_inline)) {
-        const int pb2 = table(tile + 2);
-        load_key<KD, KS>(keys, row(tile + 1, pb_next), g, kn);
+    auto step = [&](auto J, int tile) __attribute__((always_inline)) {
+        constexpr int cur = decltype(J)::value, ld = (cur + PF - 1) % PF;
+        RawKey<KD, KS>& kc = kr[cur];
+        const int pb2 = table(tile + PF);
+        load_key<KD, KS>(keys, row(tile + PF - 1, pb_next), g, kr[ld]);
         pb_next = pb2;
         f32x16 acc[NHT];
 #pragma unroll
@@ -152,17 +186,17 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(IndexArgs p) {
 #pragma unroll
         for (int t = 0; t < NHT; ++t)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) l = fmaf(wv[t][v], fmaxf(acc[t][v], 0.0f), l);
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 32 * t + 8 * q);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) l = fmaf(w4[i], fmaxf(acc[t][4 * q + i], 0.0f), l);
+            }
         l += __shfl_xor(l, 32);
         const int e = tile * 32 + j;
         if (g == 0 && e < n) out[e] = l;
     };
-    RawKey<KD, KS> kalt;
     if (!work) return;
-    for (int tile = t_begin; tile < t_end; tile += 2) {
-        step(tile, kcur, kalt);
-        if (tile + 1 < t_end) step(tile + 1, kalt, kcur);
-    }
+    for (int tile = t_begin; tile < t_end; tile += PF) unroll_steps<0, PF>(step, tile, t_end);
 }
 
 // fp32 path (tiny workloads): one thread per (row, entry), plain FMAs.
@@ -193,9 +227,11 @@ hipError_t launch_mfma(IndexArgs a, int max_entries, hipStream_t stream) {
         dim3 grid((max_tiles + 15) / 16, (a.num_rows + 3) / 4);
         hipLaunchKernelGGL((index_mfma_kernel<KD, NHT, DI, 4>), grid, dim3(kThreads), 0, stream, a);
     } else {
-        // about 2048 waves in flight, each streaming a contiguous tile range
+        // one round of waves over the GPU (256 CUs x 4 SIMDs x waves per
+        // SIMD), each streaming a contiguous tile range
+        const int64_t waves = 256 * 4 * waves_per_simd<KD, 1>();
         const int64_t wave_tiles = (int64_t)a.num_rows * max_tiles;
-        int tpw = (int)((wave_tiles + 2047) / 2048);
+        int tpw = (int)((wave_tiles + waves - 1) / waves);
         if (tpw < 1) tpw = 1;
         a.tiles_per_wave = tpw;
         dim3 grid((max_tiles + 4 * tpw - 1) / (4 * tpw), a.num_rows);
