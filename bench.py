@@ -501,6 +501,8 @@ def main():
     ap.add_argument("--no-oracle", action="store_true", help="skip the oracle baseline and parity samples")
     ap.add_argument("--cpu-sample-rows", type=int, default=16)
     ap.add_argument("--no-hot", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run 10 device copies of BYTES bytes (a reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: the decode path is measured on one MI355X "
@@ -512,6 +514,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 10
+        print(json.dumps({"copy_bytes": args.copy_probe, "ms": dt * 1e3, "GB/s": 2 * args.copy_probe / dt / 1e9}))
+        return
     lcca.lib()                                    # raises if liblcca.so is missing
     log("lcca", lcca.version(), "device", torch.cuda.get_device_name(0))
 
@@ -524,11 +537,13 @@ def main():
 
     head = names[0]
     r = results[head]
+    srcs = {"index_logits": "index_logits.hip", "sparse_attn_fwd": "sparse_attn.hip",
+            "topk_select": "topk_select.hip", "compress_append": "compress_append.hip"}
+    for n, e in r["stages"].items():
+        e["traffic"] = measured_traffic(head, n, srcs[n])
     # the dominant kernel of the headline workload: the stage with the most time
     dname, d = max(r["stages"].items(), key=lambda kv: kv[1]["ms"])
-    src = {"index_logits": "index_logits.hip", "sparse_attn_fwd": "sparse_attn.hip",
-           "topk_select": "topk_select.hip", "compress_append": "compress_append.hip"}[dname]
-    traffic = measured_traffic(head, dname, src)
+    traffic = d["traffic"]
     roof = {"kernel": dname, "bound": "hbm", "achieved": d["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": d["hbm_frac"], "traffic": traffic, "algorithmic_bytes": d["bytes"]}
     cfg = synth.CONFIGS[head]
