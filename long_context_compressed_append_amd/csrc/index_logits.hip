@@ -17,9 +17,8 @@
 // reads dI contiguous bytes of its key.
 //
 // Decode (few rows): a workgroup covers one row, its 4 waves stream disjoint
-// tile ranges.  Prefill (many rows): a workgroup covers 4 consecutive rows
-// (one per wave) that share the same tile range, so the keys are fetched
-// from HBM once and re-read from L1/L2 by the other waves.
+// tile ranges.  Prefill (many rows): index_rows_kernel, eight rows per
+// workgroup sharing key tiles staged in LDS.
 #include <type_traits>
 
 #include "device.h"
@@ -69,18 +68,14 @@ struct IntC {
 };
 
 // Register sets of keys per wave (PF - 1 tiles in flight) at two waves per
-// SIMD (the head weights are read from LDS per tile to make room).  Decode
-// streams keys from HBM: FP8 waves (half the registers per tile) keep three
-// tiles in flight; bf16 waves keep one (two measured no faster).  Prefill
-// waves re-read keys their neighbours fetched and keep one.
-template <int KD, int ROWS>
+// SIMD (the head weights are read from LDS per tile to make room): FP8
+// waves (half the registers per tile) keep three tiles in flight, bf16
+// waves one (two measured no faster).
+template <int KD>
 constexpr int key_depth() {
-    return ROWS == 1 && KD == DT_FP8 ? 4 : 2;
+    return KD == DT_FP8 ? 4 : 2;
 }
-template <int KD, int ROWS>
-constexpr int waves_per_simd() {
-    return 2;
-}
+constexpr int kWavesPerSimd = 2;
 
 // Calls f(IntC<J>, tile + J) for J = 0 .. PF-1 while tile + J < t_end.
 template <int J, int PF, class F>
@@ -93,19 +88,18 @@ __device__ __forceinline__ void unroll_steps(F& f, int tile, int t_end) {
     }
 }
 
-template <int KD, int NHT, int DI, int ROWS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KD, ROWS>(),
-                                                                           waves_per_simd<KD, ROWS>()))) void
+template <int KD, int NHT, int DI>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void
 index_mfma_kernel(IndexArgs p) {
     constexpr int KS = DI / 16, HALF = DI / 2;
-    constexpr int PF = key_depth<KD, ROWS>();
+    constexpr int PF = key_depth<KD>();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, j = lane & 31;
-    const int r_raw = ROWS == 1 ? (int)blockIdx.y : (int)blockIdx.y * 4 + wave;
+    const int r_raw = (int)blockIdx.y;
     const bool row_ok = r_raw < p.num_rows;
     const int r = row_ok ? r_raw : p.num_rows - 1;
     const int tpw = p.tiles_per_wave;
-    int t_begin = ROWS == 1 ? ((int)blockIdx.x * 4 + wave) * tpw : (int)blockIdx.x * tpw;
+    const int t_begin = ((int)blockIdx.x * 4 + wave) * tpw;
     const int b = p.row_seq[r];
     const int n = visible_entries(p.row_pos[r], p.m);
     const int ntiles = (n + 31) >> 5;
@@ -133,28 +127,24 @@ index_mfma_kernel(IndexArgs p) {
         pb_next = table(t_begin + PF - 1);
     }
 
-    // The query (HI x DI bf16) and head weights of the workgroup's row(s) are
+    // The query (HI x DI bf16) and head weights of the workgroup's row are
     // staged in LDS once (rows padded by 16 bytes against bank conflicts);
     // every wave then reads its A operands from there instead of from L2.
     constexpr int QROWB = DI * 2 + 16;
-    constexpr int NQ = ROWS == 1 ? 1 : 4;
-    __shared__ __attribute__((aligned(16))) uint8_t q_lds[NQ][NHT * 32 * QROWB];
-    __shared__ __attribute__((aligned(16))) float w_lds[NQ][NHT * 32];
+    __shared__ __attribute__((aligned(16))) uint8_t q_lds[1][NHT * 32 * QROWB];
+    __shared__ __attribute__((aligned(16))) float w_lds[1][NHT * 32];
     {
-        const int slot = ROWS == 1 ? 0 : wave;
-        const int nthr = ROWS == 1 ? kThreads : 64;
-        const int t0 = ROWS == 1 ? (int)threadIdx.x : lane;
         const uint8_t* qg = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)r * p.HI * DI * 2;
         constexpr int UPR = DI * 2 / 16;                         // 16-byte units per head
-        for (int u = t0; u < NHT * 32 * UPR; u += nthr) {
+        for (int u = (int)threadIdx.x; u < NHT * 32 * UPR; u += kThreads) {
             const int h = u / UPR, part = u % UPR;
-            *reinterpret_cast<u32x4*>(&q_lds[slot][h * QROWB + part * 16]) =
+            *reinterpret_cast<u32x4*>(&q_lds[0][h * QROWB + part * 16]) =
                 *reinterpret_cast<const u32x4*>(qg + (int64_t)h * DI * 2 + part * 16);
         }
-        for (int h = t0; h < NHT * 32; h += nthr) w_lds[slot][h] = p.w[(int64_t)r * p.HI + h] * p.s_I;
+        for (int h = (int)threadIdx.x; h < NHT * 32; h += kThreads) w_lds[0][h] = p.w[(int64_t)r * p.HI + h] * p.s_I;
     }
     __syncthreads();
-    const int slot = ROWS == 1 ? 0 : wave;
+    const int slot = 0;
     // query as A operands: head 32t + j, dims [g*HALF + 8s, +8)
     bf16x8 qa[NHT][KS];
 #pragma unroll
@@ -199,6 +189,144 @@ index_mfma_kernel(IndexArgs p) {
     for (int tile = t_begin; tile < t_end; tile += PF) unroll_steps<0, PF>(step, tile, t_end);
 }
 
+// Many rows (prefill): a workgroup of eight waves covers eight rows, one per
+// wave, and a range of tiles.  Rows of one sequence read the same keys, so
+// each 32-entry key tile is staged in LDS once (rows padded by 16 bytes, a
+// ring of three stages, the raw bytes of the next two tiles in flight in
+// registers) and every wave takes its B operands from there; the query
+// stays in VGPRs as A operands.  One barrier per tile: the stage written in
+// step t was last read in step t - 2, before the barrier of step t - 1.
+// Rows of a workgroup that belong to different sequences are handled one
+// sequence after another, the other waves only helping to stage keys.
+constexpr int kRowWaves = 8;
+constexpr int kRowThreads = kRowWaves * 64;
+constexpr int kRowStages = 3;
+
+template <int KD, int NHT, int DI>
+__global__ __launch_bounds__(kRowThreads) void index_rows_kernel(IndexArgs p) {
+    constexpr int KS = DI / 16, HALF = DI / 2;
+    constexpr int KB = KD == DT_BF16 ? DI * 2 : DI;               // bytes of one key
+    constexpr int KBP = KB + 16;                                   // padded LDS row
+    constexpr int UPK = KB / 16;                                   // 16-byte units per key
+    constexpr int UPT = (32 * UPK + kRowThreads - 1) / kRowThreads;   // units per thread per tile
+    __shared__ __attribute__((aligned(16))) uint8_t kst[kRowStages][32 * KBP];
+    __shared__ __attribute__((aligned(16))) float w_lds[kRowWaves][NHT * 32];
+    __shared__ int seq_lds[kRowWaves], n_lds[kRowWaves];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, j = lane & 31;
+    const int r = (int)blockIdx.y * kRowWaves + wave;
+    const bool row_ok = r < p.num_rows;
+    const int rr = row_ok ? r : p.num_rows - 1;
+    const int b = p.row_seq[rr];
+    const int n = row_ok ? visible_entries(p.row_pos[rr], p.m) : 0;
+    const int tpb = p.tiles_per_wave;
+    const int t_begin = (int)blockIdx.x * tpb;
+    if (lane == 0) { seq_lds[wave] = b; n_lds[wave] = n; }
+    for (int h = lane; h < NHT * 32; h += 64) w_lds[wave][h] = p.w[(int64_t)rr * p.HI + h] * p.s_I;
+    // query as A operands: head 32t + j, dims [g*HALF + 8s, +8)
+    bf16x8 qa[NHT][KS];
+    {
+        const uint8_t* qg = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)rr * p.HI * DI * 2;
+#pragma unroll
+        for (int t = 0; t < NHT; ++t)
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2)
+                qa[t][s2] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(qg + ((int64_t)(32 * t + j) * DI + g * HALF + 8 * s2) * 2));
+    }
+    __syncthreads();
+    const int sh = __builtin_ctz(256 / p.m);
+    const uint8_t* keys = reinterpret_cast<const uint8_t*>(p.keys);
+    float* out = p.logits + (int64_t)rr * p.ld;
+    const float* wrow = &w_lds[wave][4 * g];
+
+    for (int i = 0; i < kRowWaves; ++i) {
+        const int sb = seq_lds[i];
+        bool first = true;
+        int nmax = 0;
+        for (int k = 0; k < kRowWaves; ++k) {
+            if (seq_lds[k] == sb) {
+                if (k < i) first = false;
+                nmax = max(nmax, n_lds[k]);
+            }
+        }
+        if (!first) continue;
+        const int t_end = min(t_begin + tpb, (nmax + 31) >> 5);
+        if (t_begin >= t_end) continue;
+        const bool mine = row_ok && b == sb;
+        const int32_t* bt = p.block_table + (int64_t)sb * p.max_blocks;
+        // this thread's units of a tile: key u / UPK, part u % UPK, u = tid + kRowThreads * i
+        auto load = [&](int tile, u32x4 (&v)[UPT]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int q = 0; q < UPT; ++q) {
+                const int u = min(tid + kRowThreads * q, 32 * UPK - 1);
+                const int e = min(min(tile, t_end - 1) * 32 + u / UPK, nmax - 1);
+                const int64_t row = ((int64_t)bt[e >> sh] << sh) + (e & ((1 << sh) - 1));
+                v[q] = *reinterpret_cast<const u32x4*>(keys + row * KB + (u % UPK) * 16);
+            }
+        };
+        auto store = [&](int stage, const u32x4 (&v)[UPT]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int q = 0; q < UPT; ++q) {
+                const int u = tid + kRowThreads * q;
+                if (u < 32 * UPK) *reinterpret_cast<u32x4*>(&kst[stage][(u / UPK) * KBP + (u % UPK) * 16]) = v[q];
+            }
+        };
+        u32x4 ra[UPT], rb[UPT];
+        load(t_begin, ra);
+        load(t_begin + 1, rb);
+        store(0, ra);
+        load(t_begin + 2, ra);
+        __syncthreads();
+        auto step = [&](int tile, int stage, u32x4 (&nxt)[UPT]) __attribute__((always_inline)) {
+            // registers `nxt` hold tile + 1: into the next stage, then refill with tile + 3
+            if (tile + 1 < t_end) store(stage == kRowStages - 1 ? 0 : stage + 1, nxt);
+            load(tile + 3, nxt);
+            if (mine) {
+                f32x16 acc[NHT];
+#pragma unroll
+                for (int t = 0; t < NHT; ++t) acc[t] = f32x16{};
+                const uint8_t* kb = &kst[stage][j * KBP];
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2) {
+                    bf16x8 kop;
+                    if constexpr (KD == DT_BF16) {
+                        kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kb + (g * HALF + 8 * s2) * 2));
+                    } else {
+                        const u32x2 c = *reinterpret_cast<const u32x2*>(kb + g * HALF + 8 * s2);
+                        kop = __builtin_bit_cast(bf16x8, fp8x8_to_bf16(c[0], c[1]));
+                    }
+#pragma unroll
+                    for (int t = 0; t < NHT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t][s2], kop, acc[t], 0, 0, 0);
+                }
+                float l = 0.0f;
+#pragma unroll
+                for (int t = 0; t < NHT; ++t)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 32 * t + 8 * q);
+#pragma unroll
+                        for (int i4 = 0; i4 < 4; ++i4) l = fmaf(w4[i4], fmaxf(acc[t][4 * q + i4], 0.0f), l);
+                    }
+                l += __shfl_xor(l, 32);
+                const int e = tile * 32 + j;
+                if (g == 0 && e < n) out[e] = l;
+            }
+            __syncthreads();
+        };
+        int stage = 0;
+        for (int tile = t_begin; tile < t_end; tile += 2) {
+            step(tile, stage, rb);
+            stage = stage == kRowStages - 1 ? 0 : stage + 1;
+            if (tile + 1 < t_end) {
+                step(tile + 1, stage, ra);
+                stage = stage == kRowStages - 1 ? 0 : stage + 1;
+            }
+        }
+    }
+}
+
 // fp32 path (tiny workloads): one thread per (row, entry), plain FMAs.
 __global__ __launch_bounds__(kThreads) void index_f32_kernel(IndexArgs p) {
     const int r = blockIdx.y;
@@ -223,19 +351,20 @@ template <int KD, int NHT, int DI>
 hipError_t launch_mfma(IndexArgs a, int max_entries, hipStream_t stream) {
     const int max_tiles = (max_entries + 31) / 32;
     if (a.num_rows >= 64) {
-        a.tiles_per_wave = 16;
-        dim3 grid((max_tiles + 15) / 16, (a.num_rows + 3) / 4);
-        hipLaunchKernelGGL((index_mfma_kernel<KD, NHT, DI, 4>), grid, dim3(kThreads), 0, stream, a);
+        constexpr int kTilesPerGroup = 64;
+        a.tiles_per_wave = kTilesPerGroup;
+        dim3 grid((max_tiles + kTilesPerGroup - 1) / kTilesPerGroup, (a.num_rows + kRowWaves - 1) / kRowWaves);
+        hipLaunchKernelGGL((index_rows_kernel<KD, NHT, DI>), grid, dim3(kRowThreads), 0, stream, a);
     } else {
         // one round of waves over the GPU (256 CUs x 4 SIMDs x waves per
         // SIMD), each streaming a contiguous tile range
-        const int64_t waves = 256 * 4 * waves_per_simd<KD, 1>();
+        const int64_t waves = 256 * 4 * kWavesPerSimd;
         const int64_t wave_tiles = (int64_t)a.num_rows * max_tiles;
         int tpw = (int)((wave_tiles + waves - 1) / waves);
         if (tpw < 1) tpw = 1;
         a.tiles_per_wave = tpw;
         dim3 grid((max_tiles + 4 * tpw - 1) / (4 * tpw), a.num_rows);
-        hipLaunchKernelGGL((index_mfma_kernel<KD, NHT, DI, 1>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((index_mfma_kernel<KD, NHT, DI>), grid, dim3(kThreads), 0, stream, a);
     }
     return hipGetLastError();
 }
