@@ -266,6 +266,8 @@ class Workload:
         self.lse = torch.empty((self.nrows, H), dtype=torch.float32, device=dev)
         wsb = lcca.sparse_attn_workspace_size(self.rows, m, H, D, c.dv, c.k, bool(HI), c.window)
         self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+        tkb = lcca.topk_workspace_size(self.rows, m, c.k) if HI else 0
+        self.topk_ws = torch.empty(tkb, dtype=torch.uint8, device=dev) if tkb else None
 
     def snapshot_host(self):
         """Copy the initial state to host numpy arrays (for the oracle)."""
@@ -292,7 +294,7 @@ class Workload:
                            self.ld)
             if ev is not None:
                 ev[2].record()
-            L.topk_select(self.rows, c.m, self.logits, self.ld, c.k, self.topk)
+            L.topk_select(self.rows, c.m, self.logits, self.ld, c.k, self.topk, self.topk_ws)
             idx = self.topk
         elif ev is not None:
             ev[2].record()

@@ -188,10 +188,17 @@ lcca_status lcca_index_logits(void* stream, const lcca_pages* pages, const lcca_
  * selection.
  *   logits    device float [num_rows][ld]
  *   topk_idx  device int32 [num_rows][k]
- *   ws        unused (may be NULL); ws_bytes ignored
+ *   ws        device workspace of at least lcca_topk_workspace_size() bytes
+ *             for the same rows, ratio_m and k, 16-byte aligned; may be NULL
+ *             when that size is 0 (rows of at most 32,768 visible entries).
+ *             Rows longer than that are selected in two launches: the top-k
+ *             of each 16,384-entry slice, then the top-k of those
+ *             candidates (the same set and order).  Too small a workspace
+ *             returns LCCA_ERR_WORKSPACE.
  * Rows of more than 2^18 visible entries ((max_pos + 1) / ratio_m) return
  * LCCA_ERR_UNSUPPORTED (the selection keeps a bitmap of the row in LDS).
  */
+size_t lcca_topk_workspace_size(const lcca_rows* rows, int32_t ratio_m, int32_t k);
 lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_m,
                              const float* logits, int64_t ld, int32_t k, int32_t* topk_idx,
                              void* ws, size_t ws_bytes);

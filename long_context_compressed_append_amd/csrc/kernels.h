@@ -32,12 +32,25 @@ struct IndexArgs {
 
 // top-k rows hold at most this many visible entries (bitmaps of the row in LDS)
 constexpr int kTopkMaxEntries = 1 << 18;
+// rows longer than kTopkSplitAbove entries are selected in two launches:
+// slices of kTopkSlice entries, then their candidates
+constexpr int kTopkSplitAbove = 32768;
+constexpr int kTopkSlice = 16384;
 
 struct TopkArgs {
     const int32_t* row_pos; int32_t num_rows; int32_t m;
     const float* logits; int64_t ld; int32_t k;
     int32_t* idx;
+    // two-launch selection of long rows (workspace)
+    uint32_t* cand_key; int32_t* cand_idx;    // [rows][cand_stride]
+    int64_t cand_stride;
+    int32_t nslices, slice_len;
 };
+
+// slices of a row of max_entries visible entries (1: one launch) and the
+// per-row candidate stride of the workspace (elements, a multiple of 4)
+int topk_slices(int max_entries);
+int64_t topk_cand_stride(int max_entries, int k);
 
 struct AttnArgs {
     const int32_t* block_table; int32_t max_blocks;
@@ -55,7 +68,7 @@ struct AttnArgs {
 
 hipError_t launch_compress_append(const CompressArgs& a, int total_new, hipStream_t stream);
 hipError_t launch_index_logits(const IndexArgs& a, int max_entries, hipStream_t stream);
-hipError_t launch_topk_select(const TopkArgs& a, int max_entries, hipStream_t stream);
+hipError_t launch_topk_select(TopkArgs a, int max_entries, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
 
 // which (dtype, shape) combinations the kernels are built for

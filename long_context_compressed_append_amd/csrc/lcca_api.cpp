@@ -207,9 +207,15 @@ lcca_status lcca_index_logits(void* stream, const lcca_pages* pages, const lcca_
     return hip_status(lcca::launch_index_logits(a, max_entries, (hipStream_t)stream), "index_logits launch");
 }
 
+size_t lcca_topk_workspace_size(const lcca_rows* rows, int32_t ratio_m, int32_t k) {
+    if (!rows || rows->num_rows <= 0 || !valid_m(ratio_m) || k < 1 || rows->max_pos < 0) return 0;
+    const int max_entries = (rows->max_pos + 1) / ratio_m;
+    if (lcca::topk_slices(max_entries) == 1) return 0;
+    return (size_t)rows->num_rows * (size_t)lcca::topk_cand_stride(max_entries, k) * 8;
+}
+
 lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_m, const float* logits, int64_t ld,
                              int32_t k, int32_t* topk_idx, void* ws, size_t ws_bytes) {
-    (void)ws; (void)ws_bytes;
     g_err[0] = 0;
     lcca_status s;
     if (!valid_m(ratio_m)) return fail(LCCA_ERR_INVALID_ARG, "ratio_m=%d", ratio_m);
@@ -221,7 +227,19 @@ lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_
     if (ld < max_entries) return fail(LCCA_ERR_INVALID_ARG, "ld=%lld < max visible entries %d", (long long)ld, max_entries);
     if (max_entries > lcca::kTopkMaxEntries)
         return fail(LCCA_ERR_UNSUPPORTED, "%d visible entries > %d", max_entries, lcca::kTopkMaxEntries);
-    lcca::TopkArgs a{rows->row_pos, rows->num_rows, ratio_m, logits, ld, k, topk_idx};
+    lcca::TopkArgs a{};
+    a.row_pos = rows->row_pos; a.num_rows = rows->num_rows; a.m = ratio_m;
+    a.logits = logits; a.ld = ld; a.k = k; a.idx = topk_idx;
+    if (lcca::topk_slices(max_entries) > 1) {
+        const size_t need = lcca_topk_workspace_size(rows, ratio_m, k);
+        if (!ws || ws_bytes < need)
+            return fail(LCCA_ERR_WORKSPACE, "top-k of %d entries needs %zu workspace bytes (%zu given)", max_entries,
+                        need, ws ? ws_bytes : (size_t)0);
+        if (reinterpret_cast<uintptr_t>(ws) & 15) return fail(LCCA_ERR_INVALID_ARG, "top-k workspace not 16-byte aligned");
+        a.cand_stride = lcca::topk_cand_stride(max_entries, k);
+        a.cand_key = reinterpret_cast<uint32_t*>(ws);
+        a.cand_idx = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + need / 2);
+    }
     return hip_status(lcca::launch_topk_select(a, max_entries, (hipStream_t)stream), "topk_select launch");
 }
 

@@ -108,24 +108,28 @@ __device__ inline void block_exclusive_scan2(uint32_t& a, uint32_t& b, uint32_t 
 // group's load is clamped to the last group that starts below n).  Loads
 // are branch-free: addresses are clamped into the row and entries >= n
 // masked.
-template <int R, bool Half, bool Vec>
+template <int R, bool Half, bool Vec, bool U>
 struct Keys {
     static constexpr int kRounds = R / 4;
     static constexpr bool kFull = R > 0 && !Half;      // full keys without memory reads
     uint32_t u[R == 0 ? 1 : (Half ? R / 2 : R)];
-    const float* L;
+    const float* L;                                    // logits (U false) or order keys (U true)
     int n, rounds;
 
+    __device__ __forceinline__ static uint32_t key_of(uint32_t bits) {
+        return U ? bits : order_key(__uint_as_float(bits));
+    }
     __device__ __forceinline__ void load4(int e, uint32_t* o) const {
+        const uint32_t* B = reinterpret_cast<const uint32_t*>(L);
         if constexpr (Vec) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(L + min(e, (n - 1) & ~3));
+            const u32x4 v = *reinterpret_cast<const u32x4*>(B + min(e, (n - 1) & ~3));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = e + i < n ? order_key(v[i]) : 0u;
+            for (int i = 0; i < 4; ++i) o[i] = e + i < n ? key_of(v[i]) : 0u;
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float x = L[min(e + i, n - 1)];
-                o[i] = e + i < n ? order_key(x) : 0u;
+                const uint32_t x = B[min(e + i, n - 1)];
+                o[i] = e + i < n ? key_of(x) : 0u;
             }
         }
     }
@@ -218,7 +222,7 @@ struct Keys {
     }
     __device__ __forceinline__ uint32_t full_key(int e, uint32_t k) const {
         if constexpr (kFull) return k;
-        else return order_key(L[e]);
+        else return key_of(reinterpret_cast<const uint32_t*>(L)[e]);
     }
 };
 
@@ -274,20 +278,64 @@ __device__ __forceinline__ void refine(Smem& sm, Each each, int top, uint32_t* p
     *prefix_io = prefix; *mask_io = mask; *need_io = need;
 }
 
-template <int R, bool Half, bool Vec>
+// What a selection reads and where its result goes.
+//   kRow:   one row's logits -> topk_idx[r][0..k), ascending entries.
+//   kSlice: slice s of row r (entries [s*L, (s+1)*L)) -> its own top-k as
+//           candidates (order key, entry) in the workspace, ascending
+//           entries, padded with (0, -1).
+//   kCand:  the candidates of all slices of row r, whose positions ascend
+//           with the entries (slice-major), -> topk_idx[r] (the entries
+//           behind the selected positions).  Equal keys: smaller position,
+//           i.e. smaller entry, first.
+enum Mode : int { kRow = 0, kSlice = 1, kCand = 2 };
+
+template <int R, bool Half, bool Vec, int MODE>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
     __shared__ Smem sm;
     const int r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int n = visible_entries(p.row_pos[r], p.m);
+    const int n_row = visible_entries(p.row_pos[r], p.m);
     const int k = p.k;
     int32_t* out = p.idx + (int64_t)r * k;
-    if (n <= k) {
-        for (int i = tid; i < k; i += kThreads) out[i] = i < n ? i : -1;
+    const int s0 = MODE == kSlice ? (int)blockIdx.y * p.slice_len : 0;
+    const int64_t c0 = (int64_t)r * p.cand_stride + (MODE == kSlice ? (int64_t)blockIdx.y * k : 0);
+    int n;
+    const float* base;
+    if constexpr (MODE == kRow) {
+        n = n_row;
+        base = p.logits + (int64_t)r * p.ld;
+    } else if constexpr (MODE == kSlice) {
+        n = max(0, min(n_row - s0, p.slice_len));
+        base = p.logits + (int64_t)r * p.ld + s0;
+    } else {
+        n = p.nslices * k;
+        base = reinterpret_cast<const float*>(p.cand_key + c0);
+    }
+    if (MODE == kSlice ? n <= k : n_row <= k) {
+        if constexpr (MODE == kSlice) {
+            for (int i = tid; i < k; i += kThreads) {
+                p.cand_key[c0 + i] = i < n ? order_key(base[i]) : 0u;
+                p.cand_idx[c0 + i] = i < n ? s0 + i : -1;
+            }
+        } else {
+            for (int i = tid; i < k; i += kThreads) out[i] = i < n_row ? i : -1;
+        }
         return;
     }
-    Keys<R, Half, Vec> K;
-    K.init(p.logits + (int64_t)r * p.ld, n);
+    // the selected position `e` at output slot `pos`
+    auto emit = [&](uint32_t pos, int e) __attribute__((always_inline)) {
+        if (pos >= (uint32_t)k) return;                // never taken; keeps every store in the row
+        if constexpr (MODE == kRow) {
+            out[pos] = e;
+        } else if constexpr (MODE == kSlice) {
+            p.cand_key[c0 + pos] = order_key(base[e]);
+            p.cand_idx[c0 + pos] = s0 + e;
+        } else {
+            out[pos] = p.cand_idx[c0 + e];
+        }
+    };
+    Keys<R, Half, Vec, MODE == kCand> K;
+    K.init(base, n);
 
     {
         u32x4* z = reinterpret_cast<u32x4*>(sm.u.lead);
@@ -355,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
     };
     auto put = [&](uint32_t c, int e, uint32_t key) __attribute__((always_inline)) {
         if (c < (uint32_t)kCandCap) {
-            if constexpr (Keys<R, Half, Vec>::kFull) sm.u.b.cand_key[c] = key;
+            if constexpr (Keys<R, Half, Vec, MODE == kCand>::kFull) sm.u.b.cand_key[c] = key;
             sm.u.b.cand_idx[c] = e;
         }
     };
@@ -390,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
     const uint32_t nc = sm.cand_n;
     uint32_t T = lead << kLeadShift, mask = ~0u << kLeadShift;
     const bool fits = nc <= (uint32_t)kCandCap;
-    if constexpr (!Keys<R, Half, Vec>::kFull) {
+    if constexpr (!Keys<R, Half, Vec, MODE == kCand>::kFull) {
         if (fits) {
             for (int c = tid; c < (int)nc; c += kThreads) sm.u.b.cand_key[c] = K.full_key(sm.u.b.cand_idx[c], 0u);
             __syncthreads();
@@ -432,32 +480,49 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
             const int e = 32 * w + b;
             const bool take = ((g >> b) & 1u) || eq_seen < need;
             eq_seen += (g >> b) & 1u ? 0u : 1u;
-            if (take) {
-                if (pos < (uint32_t)k) out[pos] = e;           // always true; keeps every store in the row
-                ++pos;
-            }
+            if (take) emit(pos++, e);
         }
     }
 }
 
-}  // namespace
-
-template <bool Vec>
-void launch_rows(const TopkArgs& a, int rounds, hipStream_t stream) {
-    const dim3 grid(a.num_rows), block(kThreads);
-    if (rounds <= 2) hipLaunchKernelGGL((topk_kernel<8, false, Vec>), grid, block, 0, stream, a);
-    else if (rounds <= 4) hipLaunchKernelGGL((topk_kernel<16, false, Vec>), grid, block, 0, stream, a);
-    else if (rounds <= 8) hipLaunchKernelGGL((topk_kernel<32, false, Vec>), grid, block, 0, stream, a);
-    else if (rounds <= 32) hipLaunchKernelGGL((topk_kernel<128, true, Vec>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((topk_kernel<0, false, Vec>), grid, block, 0, stream, a);
+template <bool Vec, int MODE>
+void launch_sel(const TopkArgs& a, int entries, dim3 grid, hipStream_t stream) {
+    const int rounds = (entries + kGroup - 1) / kGroup;
+    const dim3 block(kThreads);
+    if (rounds <= 2) hipLaunchKernelGGL((topk_kernel<8, false, Vec, MODE>), grid, block, 0, stream, a);
+    else if (rounds <= 4) hipLaunchKernelGGL((topk_kernel<16, false, Vec, MODE>), grid, block, 0, stream, a);
+    else if (rounds <= 8) hipLaunchKernelGGL((topk_kernel<32, false, Vec, MODE>), grid, block, 0, stream, a);
+    else if (rounds <= 32) hipLaunchKernelGGL((topk_kernel<128, true, Vec, MODE>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((topk_kernel<0, false, Vec, MODE>), grid, block, 0, stream, a);
 }
 
-hipError_t launch_topk_select(const TopkArgs& a, int max_entries, hipStream_t stream) {
+}  // namespace
+
+int topk_slices(int max_entries) {
+    return max_entries > kTopkSplitAbove ? (max_entries + kTopkSlice - 1) / kTopkSlice : 1;
+}
+
+int64_t topk_cand_stride(int max_entries, int k) {
+    return ((int64_t)topk_slices(max_entries) * k + 3) & ~(int64_t)3;
+}
+
+hipError_t launch_topk_select(TopkArgs a, int max_entries, hipStream_t stream) {
     if (a.num_rows <= 0 || a.k <= 0) return hipSuccess;
-    const int rounds = (max_entries + kGroup - 1) / kGroup;
     const bool vec = (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 && a.ld % 4 == 0;
-    if (vec) launch_rows<true>(a, rounds, stream);
-    else launch_rows<false>(a, rounds, stream);
+    const int ns = topk_slices(max_entries);
+    if (ns == 1) {
+        if (vec) launch_sel<true, kRow>(a, max_entries, dim3(a.num_rows), stream);
+        else launch_sel<false, kRow>(a, max_entries, dim3(a.num_rows), stream);
+        return hipGetLastError();
+    }
+    // long rows: each slice's top-k first, then the top-k of their candidates
+    a.nslices = ns;
+    a.slice_len = kTopkSlice;
+    if (vec) launch_sel<true, kSlice>(a, kTopkSlice, dim3(a.num_rows, ns), stream);
+    else launch_sel<false, kSlice>(a, kTopkSlice, dim3(a.num_rows, ns), stream);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    launch_sel<true, kCand>(a, ns * a.k, dim3(a.num_rows), stream);
     return hipGetLastError();
 }
 

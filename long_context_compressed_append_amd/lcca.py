@@ -19,7 +19,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblcca.so")
 
 EXPORTED = ("lcca_compress_append", "lcca_index_logits", "lcca_topk_select", "lcca_sparse_attn_fwd",
-            "lcca_sparse_attn_workspace_size", "lcca_status_string", "lcca_last_error", "lcca_version")
+            "lcca_sparse_attn_workspace_size", "lcca_topk_workspace_size", "lcca_status_string", "lcca_last_error",
+            "lcca_version")
 
 
 class LccaError(RuntimeError):
@@ -72,6 +73,8 @@ def lib():
         L.lcca_sparse_attn_fwd.argtypes = [P, PP, PR, i32, P, i32, i32, f32, PC, P, i32, PW, i32, P, P, P, sz]
         L.lcca_sparse_attn_workspace_size.argtypes = [PR, i32, i32, i32, i32, i32, i32, i32]
         L.lcca_sparse_attn_workspace_size.restype = sz
+        L.lcca_topk_workspace_size.argtypes = [PR, i32, i32]
+        L.lcca_topk_workspace_size.restype = sz
         for n in ("lcca_compress_append", "lcca_index_logits", "lcca_topk_select", "lcca_sparse_attn_fwd"):
             getattr(L, n).restype = i32
         L.lcca_status_string.argtypes = [i32]
@@ -188,9 +191,13 @@ def index_logits(pages: Pages, rows: Rows, q_dtype: int, q_idx, HI: int, w_idx, 
                                    int(ld)))
 
 
-def topk_select(rows: Rows, ratio_m: int, logits, ld: int, k: int, topk_idx, stream=None):
+def topk_workspace_size(rows: Rows, ratio_m: int, k: int) -> int:
+    return lib().lcca_topk_workspace_size(ctypes.byref(rows.c()), ratio_m, k)
+
+
+def topk_select(rows: Rows, ratio_m: int, logits, ld: int, k: int, topk_idx, ws=None, stream=None):
     _check(lib().lcca_topk_select(_stream(stream), ctypes.byref(rows.c()), ratio_m, _ptr(logits), int(ld), k,
-                                  _ptr(topk_idx), None, 0))
+                                  _ptr(topk_idx), _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0))
 
 
 def sparse_attn_workspace_size(rows: Rows, ratio_m: int, H: int, dim: int, d_v: int, k: int, topk_given: bool,

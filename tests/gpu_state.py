@@ -71,7 +71,9 @@ class GpuState:
         nr = len(self.st.row_seq)
         if idx is None:
             idx = torch.empty((nr, c.k), dtype=torch.int32, device=DEV)
-        lcca.topk_select(self.rows, c.m, logits, self.ld, c.k, idx)
+        wsb = lcca.topk_workspace_size(self.rows, c.m, c.k)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
+        lcca.topk_select(self.rows, c.m, logits, self.ld, c.k, idx, ws)
         return idx
 
     def attn(self, idx, out_dtype=lcca.F32, d_v=None):

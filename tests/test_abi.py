@@ -61,6 +61,13 @@ def test_invalid_arguments_rejected_before_launch():
     # top-k: more visible entries than the selection's row bitmaps hold (2^18)
     huge = lcca._Rows(1, 4 * (1 << 18) + 3, 1, 1)
     assert L.lcca_topk_select(None, by(huge), 4, 1, (1 << 18) + 1, 64, 1, None, 0) == lcca.ERR_UNSUPPORTED
+    # rows of more than 32768 entries need the two-launch workspace
+    long_rows = lcca._Rows(3, 4 * 40000 - 1, 1, 1)
+    need = L.lcca_topk_workspace_size(by(long_rows), 4, 2048)
+    assert need == 3 * (3 * 2048) * 8            # 3 slices of 16384, k candidates each, key + entry
+    assert L.lcca_topk_workspace_size(by(rows), 4, 64) == 0
+    assert L.lcca_topk_select(None, by(long_rows), 4, 1, 40000, 2048, 1, None, 0) == lcca.ERR_WORKSPACE
+    assert b"workspace" in L.lcca_last_error()
     ok = lcca._Rows(1, 4 * (1 << 18) - 1, 1, 1)
     assert L.lcca_topk_select(None, by(ok), 4, 1, 1 << 18, 0, 1, None, 0) == lcca.ERR_INVALID_ARG   # k < 1 only
     # attention: workspace too small (16 rows of 64K context need key splits)

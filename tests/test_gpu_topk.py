@@ -26,7 +26,10 @@ def _run(logits, row_pos, m, k):
     rp = torch.from_numpy(row_pos.astype(np.int32)).cuda()
     rs = torch.zeros_like(rp)
     idx = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
-    lcca.topk_select(lcca.Rows(rs, rp, int(row_pos.max())), m, dev, ld, k, idx)
+    rows_ = lcca.Rows(rs, rp, int(row_pos.max()))
+    wsb = lcca.topk_workspace_size(rows_, m, k)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda") if wsb else None
+    lcca.topk_select(rows_, m, dev, ld, k, idx, ws)
     torch.cuda.synchronize()
     want = O.topk(row_pos, m, logits.astype(np.float64), k)
     return idx.cpu().numpy(), want
