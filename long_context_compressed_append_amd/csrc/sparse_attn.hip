@@ -15,19 +15,22 @@
 // tokens.  So every 32-key tile holds either pool entries or window tokens.
 //
 // bf16/MFMA path.  A workgroup = (row, range of tiles, group of 64 heads)
-// with one wave per 16 query heads.  Pipeline per workgroup:
+// with eight waves: two groups of 32 heads, each over four quarters of the
+// shared-KV dimension.  Pipeline per workgroup:
 //   prologue: the block-table range and the top-k indices the split needs are
 //     copied to LDS, so resolving a key to its storage row is two LDS reads;
 //   loads:    each tile's raw bytes (bf16, FP8 or MXFP4 + E8M0 scales) are
 //     loaded into registers P tiles ahead of their use (static register sets,
 //     loop unrolled by P), converted exactly to bf16 and written to one of two
-//     padded LDS stages; one barrier per tile;
-//   compute:  S^T = K Q^T with MFMA 16x16x32 (A = keys from LDS, B = the
-//     wave's queries, resident in VGPRs); online softmax per lane in the exp2
-//     domain; O^T += V^T P^T with V^T read from the same LDS tile by
-//     ds_read_b64_tr_b16 (K = V); P enters as bf16 hi + lo so the value
-//     weights keep 16 significant bits; FP8 window scales multiply the scores
-//     and are folded into P.
+//     padded LDS stages; two barriers per tile;
+//   compute:  partial S^T = K Q^T over a quarter of D with MFMA 16x16x32
+//     (A = keys from LDS, B = the wave's queries, resident in VGPRs), summed
+//     through LDS by the wave that owns eight of the group's heads; online
+//     softmax in the exp2 domain; O^T += V^T P^T over a quarter of the value
+//     dims with V^T read from the same LDS tile by ds_read_b64_tr_b16
+//     (K = V); P enters as bf16 hi + lo so the value weights keep 16
+//     significant bits; FP8 window scales multiply the scores and are folded
+//     into P.
 // Keys are split across workgroups when the rows alone cannot fill the GPU;
 // the partial (max, sum, unnormalised O) states go to the workspace and a
 // merge kernel (one workgroup per row and head) combines them exactly.
@@ -47,6 +50,7 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
 
@@ -177,17 +181,14 @@ struct Tiler {
         R.valid = s.ok;
     }
 
-    // Convert the registers of tile `tile` to bf16 and write them to an LDS stage.
-    // kmeta[0..31]: each key's value scale (FP8 window scale, 1, or -1 for
-    // a masked key); kmeta[32..63]: its score factor scale_log2 * scale.
+    // Convert the registers of tile `tile` to bf16 and write them to an LDS
+    // stage.  kmeta[key]: the key's value scale (FP8 window scale, 1, or -1
+    // for a masked key), which also multiplies its score.
     __device__ __forceinline__ static void store(const RowKeys& rk, int tile, const TileRegs<NU>& R, lds_u8* stage,
-                                                 lds_f32* kmeta, float scale_log2) {
+                                                 lds_f32* kmeta) {
         const int tid = threadIdx.x;
         const int key = tid / kThreadsPerKey, sub = tid % kThreadsPerKey;
-        if (sub == 0) {
-            kmeta[key] = R.valid ? R.kscale : -1.0f;
-            kmeta[kKeys + key] = scale_log2 * R.kscale;
-        }
+        if (sub == 0) kmeta[key] = R.valid ? R.kscale : -1.0f;
         lds_u8* dst = stage + key * Geo<D>::ROWB;
         if (tile >= rk.sel_tiles) store_parts<WD, UPK_W, NU_W>(R, dst, sub);
         else store_parts<KVD, UPK_P, NU_P>(R, dst, sub);
@@ -227,143 +228,174 @@ struct Tiler {
     }
 };
 
-// Per-wave softmax/PV state and the tile computation.  A pair of waves
-// shares HB blocks of 16 heads and splits the shared-KV dimension: each wave
-// computes the partial scores over its half of D (its half of every query
-// stays in VGPRs), the pair swaps partial scores through LDS, and each wave
-// then runs the same softmax and accumulates P V for its half of the value
-// dims.  Every key or value fragment read from LDS feeds HB head blocks.
-template <int D, int DV, int HB>
-struct HalfWave {
-    static constexpr int KS = D / 64;          // k-steps of S^T per half
-    static constexpr int NDT = DV / 32;        // 16-dim tiles of O^T per half
-    static constexpr int NACC = HB == 1 ? 2 : 1;   // accumulators per score sub-tile
-    static constexpr int XS = HB * 8 * 64;     // floats of one wave's score exchange slot
-    bf16x8 qb[HB][KS];
-    f32x4 o[HB][NDT];
-    float m_run[HB], l_run[HB];
+// Per-wave tile computation.  The eight waves of a workgroup form two head
+// groups of 32 heads, each split into four quarters of the shared-KV
+// dimension: a wave holds its head group's queries over its quarter of D in
+// VGPRs and the O^T accumulators of its quarter of the value dims for all 32
+// heads, so every key fragment read from LDS feeds 32 heads.  Per tile:
+//   scores:  partial S^T = K Q^T over the wave's quarter of D (MFMA 16x16x32,
+//            keys on M), written to the wave's slot of the exchange buffer;
+//   softmax: (after a barrier) wave q of a head group owns heads 8q .. 8q+7:
+//            it sums the four partials of its heads, runs the online softmax
+//            (lane: one head, four keys; the tile max over eight lanes),
+//            and writes P as bf16 hi + lo and the heads' rescale factors;
+//   P V:     (after a barrier) every wave rescales its accumulators where a
+//            head's reference max moved and adds V^T P^T over its value
+//            quarter, V^T read from the same LDS tile by ds_read_b64_tr_b16.
+template <int D, int DV>
+struct QuarterWave {
+    static constexpr int KS_ALL = D / 32;                   // k-steps of S^T over D
+    static constexpr int KSQ = (KS_ALL + 3) / 4;            // most k-steps of one quarter
+    static constexpr int DVQ = DV / 4;                       // value dims per quarter
+    static constexpr int NDQ = DVQ / 16;                     // 16-dim tiles of O^T per wave
+    static_assert(D % 32 == 0 && DV % 64 == 0, "shape");
+    static constexpr int XROW = kKeys * 4 + 16;              // exchange row: 32 fp32 scores of a head, padded
+    static constexpr int XSLOT = 32 * XROW;                  // one wave's partial S^T (32 heads)
+    static constexpr int PROW = kKeys * 2 + 16;              // P row: 32 bf16 weights of a head, padded
+    static constexpr int PGRP = 32 * PROW;                   // one head group's P (hi or lo)
+    bf16x8 qb[2][KSQ];
+    f32x4 o[2][NDQ];
+    float m_run, l_run;            // owner state of head 8q + (lane & 7)
+    int ks0, ksn;                  // this quarter's k-steps
 
-    __device__ __forceinline__ void init(const AttnArgs& a, int r, int head0, int g, int half) {
+    __device__ __forceinline__ void init(const AttnArgs& a, int r, int head0, int g, int c16, int q) {
+        constexpr int base = KS_ALL / 4, extra = KS_ALL % 4;
+        ks0 = q * base + min(q, extra);
+        ksn = base + (q < extra ? 1 : 0);
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-            const uint16_t* q =
-                reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + head0 + 16 * hb) * D + half * (D / 2);
+        for (int hb = 0; hb < 2; ++hb) {
+            const uint16_t* qp =
+                reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + head0 + 16 * hb + c16) * D + ks0 * 32 + 8 * g;
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
-                qb[hb][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + 32 * s + 8 * g));
+            for (int s = 0; s < KSQ; ++s)
+                qb[hb][s] = s < ksn ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * s))
+                                    : bf16x8{};
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) o[hb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            m_run[hb] = -INFINITY;
-            l_run[hb] = 0.0f;
+            for (int dt = 0; dt < NDQ; ++dt) o[hb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        m_run = -INFINITY;
+        l_run = 0.0f;
     }
 
-    // xs_mine / xs_pair: this wave's and the partner wave's score exchange
-    // slots, [HB][64 lanes][8] floats each.
-    __device__ __forceinline__ void tile(const lds_u8* lds, const lds_f32* kmeta, lds_f32* xs_mine,
-                                         const lds_f32* xs_pair, int g, int c16, int lane, int half) {
+    // Partial S^T of the tile over this quarter of D, into the wave's exchange
+    // slot as [head][key] rows.
+    __device__ __forceinline__ void scores(const lds_u8* lds, lds_u8* xs_mine, int g, int c16) const {
         constexpr int ROWB = Geo<D>::ROWB;
-        // partial S^T = K Q^T over this half's dims: two 16-key sub-tiles per
-        // head block; each key fragment serves every head block
-        f32x4 sacc[2][HB][NACC];
+        f32x4 sacc[2][2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int hb = 0; hb < HB; ++hb)
+            for (int hb = 0; hb < 2; ++hb) sacc[kt][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const lds_u8* kbase = lds + c16 * ROWB + (ks0 * 32 + 8 * g) * 2;
 #pragma unroll
-                for (int c = 0; c < NACC; ++c) sacc[kt][hb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < KSQ; ++s) {
+            if (s < ksn) {
+                bf16x8 kA[2];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            bf16x8 kA[2];
+                for (int kt = 0; kt < 2; ++kt)
+                    kA[kt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(kbase + kt * 16 * ROWB + 64 * s));
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-                kA[kt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(
-                                                        lds + (kt * 16 + c16) * ROWB + half * D + 16 * g + 64 * s));
+                for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int hb = 0; hb < HB; ++hb)
-                    sacc[kt][hb][s % NACC] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[kt], qb[hb][s], sacc[kt][hb][s % NACC], 0, 0, 0);
+                    for (int hb = 0; hb < 2; ++hb)
+                        sacc[kt][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[kt], qb[hb][s], sacc[kt][hb], 0, 0, 0);
+            }
         }
-        f32x4 sp[2][HB];
+        // lane: keys kt*16 + 4g .. +3 of head hb*16 + c16
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) {
-                sp[kt][hb] = sacc[kt][hb][0];
-                if constexpr (NACC > 1) sp[kt][hb] += sacc[kt][hb][1];
-                *reinterpret_cast<lds_f32x4*>(xs_mine + (hb * 64 + lane) * 8 + 4 * kt) = sp[kt][hb];
-            }
-        __syncthreads();
-        bf16x8 pb[HB], pbl[HB];
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-            float x[2][4], ks[2][4];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const f32x4 pair = *reinterpret_cast<const lds_f32x4*>(xs_pair + (hb * 64 + lane) * 8 + 4 * kt);
-                const f32x4 km = *reinterpret_cast<const lds_f32x4*>(kmeta + kt * 16 + 4 * g);
-                const f32x4 kx = *reinterpret_cast<const lds_f32x4*>(kmeta + kKeys + kt * 16 + 4 * g);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    ks[kt][v] = km[v];
-                    x[kt][v] = km[v] >= 0.0f ? (sp[kt][hb][v] + pair[v]) * kx[v] : -INFINITY;
-                    mx = fmaxf(mx, x[kt][v]);
-                }
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            // Lazy rescaling: the reference max m_run moves only when the tile's
-            // max exceeds it by more than 8 (log2 units), so most tiles leave the
-            // O accumulators untouched; probabilities relative to m_run stay <= 2^8.
-            if (mx > m_run[hb] + 8.0f) {
-                const float alpha = exp2f(m_run[hb] - mx);     // 0 while m_run = -inf
-                l_run[hb] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) o[hb][dt] *= alpha;
-                m_run[hb] = mx;
-            }
-            // reference for the exponent: m_run, or 0 while every key so far is
-            // masked (then every x is -inf and every p is 0)
-            const float mref = m_run[hb] == -INFINITY ? 0.0f : m_run[hb];
-            float psum = 0.0f;
-            uint32_t pk[4], pl[4];
+        for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
+                *reinterpret_cast<lds_f32x4*>(xs_mine + (hb * 16 + c16) * XROW + (kt * 16 + 4 * g) * 4) = sacc[kt][hb];
+    }
+
+    // Owner softmax of heads 8q .. 8q+7 of the head group: lane (h8 = lane & 7,
+    // kg = lane >> 3) takes keys 4kg .. 4kg+3 of head 8q + h8.  xs_grp: the
+    // head group's four exchange slots; kmeta: each key's value scale (FP8
+    // window scale, 1, or -1 for a masked key).  Writes P hi/lo in the order
+    // the P V operands read it and the head's rescale factor alpha.
+    __device__ __forceinline__ void softmax(const lds_u8* xs_grp, const lds_f32* kmeta, lds_u8* p_hi, lds_u8* p_lo,
+                                            lds_f32* alpha, int lane, int q, float scale_log2) {
+        const int h8 = lane & 7, kg = lane >> 3, hq = 8 * q + h8;
+        f32x4 s = *reinterpret_cast<const lds_f32x4*>(xs_grp + hq * XROW + 16 * kg);
 #pragma unroll
-                for (int v = 0; v < 4; v += 2) {
-                    // x - mref <= 8: v_exp_f32 directly (results below 2^-126
-                    // may flush to zero, far below the sum's precision)
-                    const float p0 = __builtin_amdgcn_exp2f(x[kt][v] - mref);
-                    const float p1 = __builtin_amdgcn_exp2f(x[kt][v + 1] - mref);
-                    psum += p0 + p1;
-                    // masked keys have p = 0; FP8 window keys carry their scale
-                    const float w0 = p0 * ks[kt][v], w1 = p1 * ks[kt][v + 1];
-                    const uint32_t h = cvt_pk_bf16(w0, w1);
-                    pk[kt * 2 + v / 2] = h;
-                    pl[kt * 2 + v / 2] = cvt_pk_bf16(w0 - __uint_as_float(h << 16), w1 - __uint_as_float(h & 0xffff0000u));
-                }
-            l_run[hb] += psum;
-            pb[hb] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-            pbl[hb] = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
+        for (int src = 1; src < 4; ++src)
+            s += *reinterpret_cast<const lds_f32x4*>(xs_grp + src * XSLOT + hq * XROW + 16 * kg);
+        const f32x4 km = *reinterpret_cast<const lds_f32x4*>(kmeta + 4 * kg);
+        float x[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            x[v] = km[v] >= 0.0f ? s[v] * (scale_log2 * km[v]) : -INFINITY;
+            mx = fmaxf(mx, x[v]);
         }
-        // O^T += V^T P^T over this half's value dims.  Within each 16-lane block,
-        // ds_read_b64_tr_b16 hands lane i element (i & 3) of the 8-byte chunk
-        // addressed by lane (i >> 2) + 4e, e = 0..3: lane s addresses key
-        // 4g + (s >> 2), dims dt*16 + 4(s & 3) .. +3, so lane i receives keys
-        // 4g + e at dim dt*16 + i.  Each value fragment serves every head
-        // block, hi and lo; the hi and lo products of a dim tile are issued
-        // apart so they do not wait on each other.
-        const lds_u8* vbase = lds + (4 * g + (c16 >> 2)) * ROWB + half * (DV / 2) * 2 + 8 * (c16 & 3);
-        constexpr int G4 = HB == 1 ? 4 : 2;
+        mx = fmaxf(mx, __shfl_xor(mx, 8));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // Lazy rescaling: the reference max m_run moves only when the tile's
+        // max exceeds it by more than 8 (log2 units), so most tiles leave the
+        // accumulators untouched; weights relative to m_run stay <= 2^8.
+        float al = 1.0f;
+        if (mx > m_run + 8.0f) {
+            al = exp2f(m_run - mx);      // 0 while m_run = -inf
+            l_run *= al;
+            m_run = mx;
+        }
+        // reference for the exponent: m_run, or 0 while every key so far is
+        // masked (then every x is -inf and every p is 0)
+        const float mref = m_run == -INFINITY ? 0.0f : m_run;
+        float w[4], psum = 0.0f;
 #pragma unroll
-        for (int d0 = 0; d0 < NDT; d0 += G4) {
+        for (int v = 0; v < 4; ++v) {
+            // x - mref <= 8: v_exp_f32 directly (results below 2^-126 may
+            // flush to zero, far below the sum's precision)
+            const float p = __builtin_amdgcn_exp2f(x[v] - mref);
+            psum += p;
+            w[v] = p * km[v];            // masked keys: p = 0; FP8 window keys carry their scale
+        }
+        l_run += psum;
+        const uint32_t h0 = cvt_pk_bf16(w[0], w[1]), h1 = cvt_pk_bf16(w[2], w[3]);
+        const uint32_t l0 = cvt_pk_bf16(w[0] - __uint_as_float(h0 << 16), w[1] - __uint_as_float(h0 & 0xffff0000u));
+        const uint32_t l1 = cvt_pk_bf16(w[2] - __uint_as_float(h1 << 16), w[3] - __uint_as_float(h1 & 0xffff0000u));
+        // P row order: keys 0-3, 16-19, 4-7, 20-23, ... so that operand lane
+        // group g reads keys 4g .. 4g+3 and 16+4g .. 16+4g+3 as one 16-byte run
+        const int off = hq * PROW + (kg < 4 ? 16 * kg : 16 * (kg - 4) + 8);
+        *reinterpret_cast<lds_u32x2*>(p_hi + off) = u32x2{h0, h1};
+        *reinterpret_cast<lds_u32x2*>(p_lo + off) = u32x2{l0, l1};
+        if (kg == 0) alpha[hq] = al;
+    }
+
+    // O^T += V^T P^T over this wave's value quarter, after rescaling the
+    // columns of heads whose reference max moved.  Within each 16-lane block,
+    // ds_read_b64_tr_b16 hands lane i element (i & 3) of the 8-byte chunk
+    // addressed by lane (i >> 2) + 4e, e = 0..3: lane s addresses key
+    // 4g + (s >> 2), dims dt*16 + 4(s & 3) .. +3, so lane i receives keys
+    // 4g + e at dim dt*16 + i (and 16 + 4g + e from the second read).
+    __device__ __forceinline__ void pv(const lds_u8* lds, const lds_u8* p_hi, const lds_u8* p_lo, const lds_f32* alpha,
+                                       int g, int c16, int q) {
+        constexpr int ROWB = Geo<D>::ROWB;
+        const float a0 = alpha[c16], a1 = alpha[16 + c16];
+        if (__builtin_amdgcn_ballot_w64(a0 != 1.0f || a1 != 1.0f)) {
+#pragma unroll
+            for (int dt = 0; dt < NDQ; ++dt) {
+                o[0][dt] *= a0;
+                o[1][dt] *= a1;
+            }
+        }
+        bf16x8 pb[2], pbl[2];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            pb[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(p_hi + (hb * 16 + c16) * PROW + 16 * g));
+            pbl[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(p_lo + (hb * 16 + c16) * PROW + 16 * g));
+        }
+        const lds_u8* vbase = lds + (4 * g + (c16 >> 2)) * ROWB + q * DVQ * 2 + 8 * (c16 & 3);
+        constexpr int G4 = 3;
+#pragma unroll
+        for (int d0 = 0; d0 < NDQ; d0 += G4) {
             bf16x8 vA[G4];
 #pragma unroll
             for (int j = 0; j < G4; ++j) {
-                if (d0 + j < NDT) {
+                if (d0 + j < NDQ) {
                     const lds_u8* p0 = vbase + (d0 + j) * 32;
                     i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
                     i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 16 * ROWB));
@@ -375,39 +407,40 @@ struct HalfWave {
 #pragma unroll
             for (int j = 0; j < G4; ++j)
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb)
-                    if (d0 + j < NDT)
-                        o[hb][d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA[j], pb[hb], o[hb][d0 + j], 0, 0, 0);
+                for (int hb = 0; hb < 2; ++hb)
+                    if (d0 + j < NDQ) o[hb][d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA[j], pb[hb], o[hb][d0 + j], 0, 0, 0);
 #pragma unroll
             for (int j = 0; j < G4; ++j)
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb)
-                    if (d0 + j < NDT)
-                        o[hb][d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA[j], pbl[hb], o[hb][d0 + j], 0, 0, 0);
+                for (int hb = 0; hb < 2; ++hb)
+                    if (d0 + j < NDQ) o[hb][d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA[j], pbl[hb], o[hb][d0 + j], 0, 0, 0);
         }
     }
 };
 
-constexpr int kHeadBlocks = 1;         // 16-head blocks per wave
+constexpr int kWaves = 8;              // two head groups of 32 x four quarters of D
+constexpr int kThreads = kWaves * 64;
 constexpr int kBtLds = 4096;           // block-table entries cached in LDS
 constexpr int kIdxLds = 2560;          // top-k slots cached in LDS (= max keys per split)
 
-template <int KVD, int WD, int D, int DV, int HB>
-__global__ __launch_bounds__(8 / HB * 64) __attribute__((amdgpu_waves_per_eu(2 / HB, 2 / HB))) void attn_mfma_kernel(
-    AttnArgs a) {
-    constexpr int NW = 8 / HB;                                    // waves: NW/2 head groups x 2 halves of D
+template <int KVD, int WD, int D, int DV>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(AttnArgs a) {
     using G = Geo<D>;
-    constexpr int NT = NW * 64;
+    using QW = QuarterWave<D, DV>;
+    constexpr int NT = kThreads;
     using TL = Tiler<KVD, WD, D, NT>;
     constexpr int NU = TL::NU;
     // tiles held in registers ahead of the LDS stage
     constexpr int kPrefetch = NU <= 12 ? 2 : 1;
     static_assert(kPrefetch == 1 || kPrefetch == 2, "prefetch depth");
     __shared__ __attribute__((aligned(16))) uint8_t stage[2][G::STAGE];
-    __shared__ __attribute__((aligned(16))) float kmeta[2][2 * kKeys];
+    __shared__ __attribute__((aligned(16))) float kmeta[2][kKeys];
     __shared__ int32_t bt_mem[kBtLds];
     __shared__ int32_t idx_mem[kIdxLds];
-    __shared__ __attribute__((aligned(16))) float xs_mem[NW][HalfWave<D, DV, HB>::XS];   // partial-score exchange
+    __shared__ __attribute__((aligned(16))) uint8_t xs_mem[kWaves][QW::XSLOT];     // partial-score exchange
+    __shared__ __attribute__((aligned(16))) uint8_t p_mem[2][2][QW::PGRP];        // [head group][hi, lo]
+    __shared__ __attribute__((aligned(16))) float alpha_mem[2][32];
+    __shared__ float fin_mem[2][2][32];                                           // [head group][m, l][head]
     lds_i32* const bt_lds = (lds_i32*)&bt_mem[0];
     lds_i32* const idx_lds = (lds_i32*)&idx_mem[0];
 
@@ -426,9 +459,8 @@ __global__ __launch_bounds__(8 / HB * 64) __attribute__((amdgpu_waves_per_eu(2 /
         return;
     }
     const int te = min(tb + a.split_tiles, rk.tiles);
-    // waves w and w + NW/2 share 16 HB heads and split the dimensions
-    const int hg = wave % (NW / 2), half = wave / (NW / 2);
-    const int head = (int)blockIdx.z * 64 + hg * 16 * HB + c16;   // this lane's head of head block 0
+    const int hg = wave >> 2, q = wave & 3;
+    const int head0 = (int)blockIdx.z * 64 + hg * 32;       // first head of this wave's group
 
     // prologue: top-k slots and block-table range of this split into LDS
     const int sel_end = min(te, rk.sel_tiles) * kKeys;            // selected slots [tb*32, sel_end)
@@ -451,10 +483,13 @@ __global__ __launch_bounds__(8 / HB * 64) __attribute__((amdgpu_waves_per_eu(2 /
     for (int i = tid; i < min(nblk, kBtLds); i += NT) bt_lds[i] = a.block_table[(int64_t)rk.b * a.max_blocks + blk0 + i];
     __syncthreads();
 
-    HalfWave<D, DV, HB> W;
-    W.init(a, r, head, g, half);
-    lds_f32* const xs_mine = (lds_f32*)&xs_mem[wave][0];
-    const lds_f32* const xs_pair = (lds_f32*)&xs_mem[wave ^ (NW / 2)][0];
+    QW W;
+    W.init(a, r, head0, g, c16, q);
+    lds_u8* const xs_mine = (lds_u8*)&xs_mem[wave][0];
+    const lds_u8* const xs_grp = (const lds_u8*)&xs_mem[hg * 4][0];
+    lds_u8* const p_hi = (lds_u8*)&p_mem[hg][0][0];
+    lds_u8* const p_lo = (lds_u8*)&p_mem[hg][1][0];
+    lds_f32* const alpha = (lds_f32*)&alpha_mem[hg][0];
 
     TileRegs<NU> R[kPrefetch];
     const int ntl = te - tb;
@@ -462,23 +497,30 @@ __global__ __launch_bounds__(8 / HB * 64) __attribute__((amdgpu_waves_per_eu(2 /
     if constexpr (kPrefetch > 1) TL::issue(a, TL::resolve(a, rk, tb + 1, 1 < ntl, idx_lds, idx0, bt_lds, blk0), R[1]);
     lds_u8* const st = (lds_u8*)&stage[0][0];
     lds_f32* const km = (lds_f32*)&kmeta[0][0];
-    TL::store(rk, tb, R[0], st, km, a.scale_log2);
+    TL::store(rk, tb, R[0], st, km);
     TL::issue(a, TL::resolve(a, rk, tb + kPrefetch, kPrefetch < ntl, idx_lds, idx0, bt_lds, blk0), R[0]);
     __syncthreads();
 
     // tile u sits in register set (u - tb) % P until it is stored to stage
     // (u - tb) % 2; the steps of one round are spelled out so that every
-    // register set is addressed statically
+    // register set is addressed statically.  Step t: scores of tile t; a
+    // barrier (every wave is past the P V of tile t - 1, so its stage is
+    // free); tile t + 1 stored there and the loads of tile t + 1 + P issued;
+    // the owner softmax; a barrier; P V of tile t.
     auto step = [&](auto J, int t) __attribute__((always_inline)) {
         constexpr int nxt = (decltype(J)::value + 1) % kPrefetch;
-        // the next loads' storage rows come from LDS before this step's stores
+        const lds_u8* cur = st + (t & 1) * G::STAGE;
+        W.scores(cur, xs_mine, g, c16);
+        // the next loads' storage rows come from LDS before the barrier
         const typename TL::Src nsrc =
             TL::resolve(a, rk, tb + t + 1 + kPrefetch, t + 1 + kPrefetch < ntl, idx_lds, idx0, bt_lds, blk0);
-        if (t + 1 < ntl)
-            TL::store(rk, tb + t + 1, R[nxt], st + ((t + 1) & 1) * G::STAGE, km + ((t + 1) & 1) * 2 * kKeys, a.scale_log2);
-        TL::issue(a, nsrc, R[nxt]);
-        W.tile(st + (t & 1) * G::STAGE, km + (t & 1) * 2 * kKeys, xs_mine, xs_pair, g, c16, lane, half);
         __syncthreads();
+        if (t + 1 < ntl)
+            TL::store(rk, tb + t + 1, R[nxt], st + ((t + 1) & 1) * G::STAGE, km + ((t + 1) & 1) * kKeys);
+        TL::issue(a, nsrc, R[nxt]);
+        W.softmax(xs_grp, km + (t & 1) * kKeys, p_hi, p_lo, alpha, lane, q, a.scale_log2);
+        __syncthreads();
+        W.pv(cur, p_hi, p_lo, alpha, g, c16, q);
     };
     for (int t0 = 0; t0 < ntl; t0 += kPrefetch) {
         step(IntC<0>{}, t0);
@@ -486,37 +528,47 @@ __global__ __launch_bounds__(8 / HB * 64) __attribute__((amdgpu_waves_per_eu(2 /
             if (t0 + 1 < ntl) step(IntC<1>{}, t0 + 1);
     }
 
-    // finish: total row sum of each head over the 4 lane groups
-    constexpr int NDT = HalfWave<D, DV, HB>::NDT;
-    const int dv0 = half * (DV / 2) + 4 * g;
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-        const int hd = head + 16 * hb;
-        float l_tot = W.l_run[hb] + __shfl_xor(W.l_run[hb], 16);
+    // finish: each owner's row sum over its eight lanes, published with the
+    // reference max for the waves that hold the heads' value columns
+    {
+        float l_tot = W.l_run + __shfl_xor(W.l_run, 8);
+        l_tot += __shfl_xor(l_tot, 16);
         l_tot += __shfl_xor(l_tot, 32);
+        if (lane < 8) {
+            fin_mem[hg][0][8 * q + lane] = W.m_run;
+            fin_mem[hg][1][8 * q + lane] = l_tot;
+        }
+    }
+    __syncthreads();
+    constexpr int NDQ = QW::NDQ;
+    const int dv0 = q * QW::DVQ + 4 * g;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        const int hl = 16 * hb + c16, hd = head0 + hl;
+        const float m_tot = fin_mem[hg][0][hl], l_tot = fin_mem[hg][1][hl];
         if (a.nsplit == 1) {
             const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
             const int64_t base = ((int64_t)r * a.H + hd) * DV + dv0;
             if (a.out_dtype == DT_F32) {
                 float* out = reinterpret_cast<float*>(a.out) + base;
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(out + dt * 16) = W.o[hb][dt] * inv;
+                for (int dt = 0; dt < NDQ; ++dt) *reinterpret_cast<f32x4*>(out + dt * 16) = W.o[hb][dt] * inv;
             } else {
                 uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + base;
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
+                for (int dt = 0; dt < NDQ; ++dt) {
                     f32x4 t = W.o[hb][dt] * inv;
                     *reinterpret_cast<u32x2*>(out + dt * 16) = u32x2{cvt_pk_bf16(t[0], t[1]), cvt_pk_bf16(t[2], t[3])};
                 }
             }
-            if (a.lse && g == 0 && half == 0) a.lse[(int64_t)r * a.H + hd] = (W.m_run[hb] + log2f(l_tot)) * kLn2;
+            if (a.lse && g == 0 && q == 0) a.lse[(int64_t)r * a.H + hd] = (m_tot + log2f(l_tot)) * kLn2;
         } else {
             float* po = a.part_o + (((int64_t)r * a.nsplit + split) * a.H + hd) * DV + dv0;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = W.o[hb][dt];
-            if (g == 0 && half == 0) {
+            for (int dt = 0; dt < NDQ; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = W.o[hb][dt];
+            if (g == 0 && q == 0) {
                 float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H;
-                ml[hd] = W.m_run[hb];
+                ml[hd] = m_tot;
                 ml[a.H + hd] = l_tot;
             }
         }
@@ -661,22 +713,22 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     if (a.lse && tid == 0) a.lse[(int64_t)r * a.H + h] = mx + logf(sum);
 }
 
-template <int KVD, int WD, int D, int DV, int HB>
+template <int KVD, int WD, int D, int DV>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
     dim3 grid(a.nsplit, a.num_rows, a.H / 64);
-    hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, HB>), grid, dim3(8 / HB * 64), 0, stream, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV>), grid, dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     hipLaunchKernelGGL(attn_merge_kernel, dim3(a.H, a.num_rows), dim3(kMergeThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-// Workgroups cover 64 heads (eight waves of 16 heads each); more heads add
-// head groups to the grid.
+// Workgroups cover 64 heads (two groups of 32); more heads add head groups
+// to the grid.
 template <int KVD, int WD, int D, int DV>
 hipError_t launch_heads(const AttnArgs& a, hipStream_t stream) {
     if (a.H % 64 != 0) return hipErrorInvalidValue;
-    return launch_mfma<KVD, WD, D, DV, kHeadBlocks>(a, stream);
+    return launch_mfma<KVD, WD, D, DV>(a, stream);
 }
 
 template <int KVD, int WD>
