@@ -102,6 +102,26 @@ index_mfma_kernel(IndexArgs p) {
     const int t_begin = ((int)blockIdx.x * 4 + wave) * tpw;
     const int b = p.row_seq[r];
     const int n = visible_entries(p.row_pos[r], p.m);
+    // The query (HI x DI bf16) and head weights of the workgroup's row are
+    // staged in LDS once (rows padded by 16 bytes against bank conflicts);
+    // every wave then reads its A operands from there instead of from L2.
+    // They depend on the row index alone, so they are requested right after
+    // the row's metadata: memory waits complete in issue order, so requested
+    // after the first key tile they would wait for it.
+    constexpr int QROWB = DI * 2 + 16;
+    constexpr int UPR = DI * 2 / 16;                             // 16-byte units per head
+    constexpr int QUNITS = NHT * 32 * UPR;
+    constexpr int QU = (QUNITS + kThreads - 1) / kThreads;       // units per thread
+    __shared__ __attribute__((aligned(16))) uint8_t q_lds[NHT * 32 * QROWB];
+    __shared__ __attribute__((aligned(16))) float w_lds[NHT * 32];
+    const uint8_t* qg = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)r * p.HI * DI * 2;
+    u32x4 qv[QU];
+#pragma unroll
+    for (int i = 0; i < QU; ++i) {
+        const int u = min((int)threadIdx.x + kThreads * i, QUNITS - 1);      // branch-free, clamped
+        qv[i] = *reinterpret_cast<const u32x4*>(qg + (int64_t)(u / UPR) * DI * 2 + (u % UPR) * 16);
+    }
+    const float wraw = p.w[(int64_t)r * p.HI + min((int)threadIdx.x, NHT * 32 - 1)];
     const int ntiles = (n + 31) >> 5;
     const int t_end = min(t_begin + tpw, ntiles);
     const bool work = row_ok && t_begin < t_end;
@@ -119,32 +139,26 @@ index_mfma_kernel(IndexArgs p) {
     auto row = [&](int tile, int pb) -> int64_t {
         return ((int64_t)pb << sh) + (entry(tile) & ((1 << sh) - 1));
     };
-    int pb_next = 0;
+    // Block-table entries of the first PF tiles, requested unconditionally
+    // (entries clamped into the sequence's table row); then the query and
+    // weights go to LDS, which waits for their loads only; then the first
+    // key tiles are requested.
+    int pbs[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) pbs[i] = bt[max(0, entry(t_begin + i)) >> sh];
+#pragma unroll
+    for (int i = 0; i < QU; ++i) {
+        const int u = (int)threadIdx.x + kThreads * i;
+        if (u < QUNITS) *reinterpret_cast<u32x4*>(&q_lds[(u / UPR) * QROWB + (u % UPR) * 16]) = qv[i];
+    }
+    if ((int)threadIdx.x < NHT * 32) w_lds[threadIdx.x] = wraw * p.s_I;
+    int pb_next = pbs[PF - 1];
     RawKey<KD, KS> kr[PF];
     if (work) {
 #pragma unroll
-        for (int i = 0; i < PF - 1; ++i) load_key<KD, KS>(keys, row(t_begin + i, table(t_begin + i)), g, kr[i]);
-        pb_next = table(t_begin + PF - 1);
-    }
-
-    // The query (HI x DI bf16) and head weights of the workgroup's row are
-    // staged in LDS once (rows padded by 16 bytes against bank conflicts);
-    // every wave then reads its A operands from there instead of from L2.
-    constexpr int QROWB = DI * 2 + 16;
-    __shared__ __attribute__((aligned(16))) uint8_t q_lds[1][NHT * 32 * QROWB];
-    __shared__ __attribute__((aligned(16))) float w_lds[1][NHT * 32];
-    {
-        const uint8_t* qg = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)r * p.HI * DI * 2;
-        constexpr int UPR = DI * 2 / 16;                         // 16-byte units per head
-        for (int u = (int)threadIdx.x; u < NHT * 32 * UPR; u += kThreads) {
-            const int h = u / UPR, part = u % UPR;
-            *reinterpret_cast<u32x4*>(&q_lds[0][h * QROWB + part * 16]) =
-                *reinterpret_cast<const u32x4*>(qg + (int64_t)h * DI * 2 + part * 16);
-        }
-        for (int h = (int)threadIdx.x; h < NHT * 32; h += kThreads) w_lds[0][h] = p.w[(int64_t)r * p.HI + h] * p.s_I;
+        for (int i = 0; i < PF - 1; ++i) load_key<KD, KS>(keys, row(t_begin + i, pbs[i]), g, kr[i]);
     }
     __syncthreads();
-    const int slot = 0;
     // query as A operands: head 32t + j, dims [g*HALF + 8s, +8)
     bf16x8 qa[NHT][KS];
 #pragma unroll
@@ -152,10 +166,10 @@ index_mfma_kernel(IndexArgs p) {
 #pragma unroll
         for (int s = 0; s < KS; ++s)
             qa[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                      &q_lds[slot][(32 * t + j) * QROWB + (g * HALF + 8 * s) * 2]));
+                                                      &q_lds[(32 * t + j) * QROWB + (g * HALF + 8 * s) * 2]));
     // head weights are read from LDS per tile, in C-layout order: head
     // 32t + 8(v/4) + 4g + v%4, four consecutive heads per 16-byte read
-    const float* wrow = &w_lds[slot][4 * g];
+    const float* wrow = &w_lds[4 * g];
 
     float* out = p.logits + (int64_t)r * p.ld;
     auto step = [&](auto J, int tile) __attribute__((always_inline)) {
