@@ -177,9 +177,19 @@ __device__ __forceinline__ void issue_slice(const CompressArgs& p, const SeqChun
 }
 
 // Softmax weights of the group's logits (thread i < m holds logit i) into
-// w_lds (m <= 256).
+// w_lds (m <= 256).  Groups of up to 64 tokens are done by wave 0 alone.
 __device__ void group_weights(int m, float a, float* w_lds, float* red) {
     const int tid = threadIdx.x;
+    if (m <= 64) {
+        if (tid < 64) {
+            const float mx = wave_max(a);
+            const float e = tid < m ? expf(a - mx) : 0.0f;
+            const float s = wave_sum(e);
+            if (tid < m) w_lds[tid] = e / s;
+        }
+        __syncthreads();
+        return;
+    }
     float mx = wave_max(a);
     __syncthreads();
     if ((tid & 63) == 0) red[tid >> 6] = mx;
@@ -228,7 +238,8 @@ __device__ void reduce_slice(const CompressArgs& p, bool ik_stream, int d0, cons
     float v = 0.0f;
     const int dd = tid;                                        // dimension d0 + dd, threads < 64
     if (tid < kSliceDims) {
-        for (int l = 0; l < kLanes; ++l) v += red[l * kSliceDims + dd];
+        const int nl = min(m, kLanes);                         // token lanes holding tokens
+        for (int l = 0; l < nl; ++l) v += red[l * kSliceDims + dd];
     }
     // encode and store (threads < 64 hold one dimension each)
     const int64_t row = L.row;
