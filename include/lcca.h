@@ -149,6 +149,14 @@ typedef struct {
  * elements, elements RNE to E2M1 after division by 2^X, saturating at +-6.
  * Chunks of one sequence must be appended in position order; calls for
  * distinct sequences may be combined freely.
+ * Rebuilding the rings of one layer (pool entries kept, rings lost, as on a
+ * prefix-cache hit): append the sequence's tokens again from the multiple of
+ * ratio_m at or below P - win->window up to P - 1, P being the next position
+ * to append.  Every group of that range is complete within it, so no
+ * remainder slot is read; its entries are rewritten with the same codes,
+ * and the window ring (positions P - window .. P - 1) and the remainder ring
+ * end as after the uninterrupted history.  A replay starting inside a group
+ * would form that group from the remainder ring's stale contents.
  */
 lcca_status lcca_compress_append(void* stream, const lcca_pages* pages,
                                  const int32_t* cu_new, const int32_t* start_pos, int32_t total_new,

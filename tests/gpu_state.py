@@ -49,6 +49,7 @@ class GpuState:
         self.w_idx = dev_typed(st.w_idx) if c.HI else None
         self.ld = c.max_entries
         self.q_dt = LDT[c.q_dtype]
+        self.tok_ldt = LDT[c.tok_dtype]
 
     # ------------------------------------------------------------------
     def compress_append(self, stream=None):
