@@ -505,7 +505,7 @@ int orc_sparse_attn(
         int64_t nk = 0;
         for (int64_t i = 0; i < nsel; ++i) {
             int64_t g = topk_idx ? topk_idx[(int64_t)r * k + i] : i;
-            if (g < 0) continue;
+            if (g < 0 || g >= n) continue;      /* padding, or an entry the row cannot see yet */
             load_row(kv_dtype, kv_data, kv_scale, pool_row(block_table, max_blocks, m, b, g), D, K + nk * D);
             ++nk;
         }

@@ -106,6 +106,13 @@ def test_single_key_zero_scale_and_window_only():
     out, _ = O.sparse_attn(z, np.array([299], np.int32), 4, bt, O.F32, q, H, D, D, 0.0, kv, idx, 3, win, 128)
     K = np.concatenate([_entries(kv, bt, 4, 74, D)[[5, 2, 9]], _window(win, 299, 128, D)])
     assert np.allclose(out[0], np.tile(K.mean(0), (H, 1)), rtol=1e-13, atol=1e-14)
+    # entries the row cannot see yet (g >= n = (p+1)/m) are skipped like -1:
+    # position 199 sees entries 0..49 only
+    idx_bad = np.array([[5, 60, 2, 49, 50, 73, 9]], np.int32)
+    idx_ok = np.array([[5, 2, 49, 9]], np.int32)
+    out_b, lse_b = O.sparse_attn(z, np.array([199], np.int32), 4, bt, O.F32, q, H, D, D, 0.3, kv, idx_bad, 7, win, 128)
+    out_o, lse_o = O.sparse_attn(z, np.array([199], np.int32), 4, bt, O.F32, q, H, D, D, 0.3, kv, idx_ok, 4, win, 128)
+    assert np.array_equal(out_b, out_o) and np.array_equal(lse_b, lse_o)
     # empty selection (-1 only): the window alone
     idx = np.full((1, 4), -1, np.int32)
     out, _ = O.sparse_attn(z, np.array([299], np.int32), 4, bt, O.F32, q, H, D, D, 0.5, kv, idx, 4, win, 128)
