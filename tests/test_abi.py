@@ -104,3 +104,25 @@ def test_binding_raises_on_error():
     with pytest.raises(lcca.LccaError) as e:
         lcca.topk_select(rows, 4, t, 10, 64, t, stream=0)
     assert e.value.status == lcca.ERR_INVALID_ARG
+
+
+def test_empty_calls_return_ok_without_launching():
+    """Zero new tokens / zero rows: validated, then nothing is launched (so
+    these run without a GPU)."""
+    L = lcca.lib()
+    by = ctypes.byref
+    pages = lcca._Pages(1, 4, 1)
+    kv = _pool(lcca.BF16, 576)
+    ik = _pool(lcca.BF16, 128)
+    win = lcca._WindowCache(lcca.BF16, 576, 128, 128, 1, None)
+    rem = lcca._Remainder(lcca.BF16, 1, 1, 1, 1)
+    st = L.lcca_compress_append(None, by(pages), 1, 1, 0, lcca.BF16, None, None, None, None, by(kv), by(ik),
+                                by(win), by(rem))
+    assert st == lcca.OK, L.lcca_last_error()
+    none = lcca._Rows(0, 0, 1, 1)
+    assert L.lcca_index_logits(None, by(pages), by(none), lcca.BF16, 1, 64, 1, 1.0, by(ik), 1, 64) == lcca.OK
+    assert L.lcca_topk_select(None, by(none), 4, 1, 64, 64, 1, None, 0) == lcca.OK
+    assert L.lcca_sparse_attn_workspace_size(by(none), 4, 64, 576, 576, 64, 1, 128) == 0
+    st = L.lcca_sparse_attn_fwd(None, by(pages), by(none), lcca.BF16, 1, 64, 576, 0.04, by(kv), 1, 64, by(win),
+                                lcca.F32, 1, None, None, 0)
+    assert st == lcca.OK, L.lcca_last_error()

@@ -1,0 +1,89 @@
+"""Degenerate rows on the device against the oracle: rows at the start of a
+sequence (no visible entry, or fewer than k), top-k lists holding -1 and
+out-of-range entries and repeats, in both the split (few rows) and the
+one-workgroup-per-row (many rows) attention plans."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import compare as C
+from long_context_compressed_append_amd import lcca, synth
+from state import State, pool_rows
+from gpu_state import GpuState, dev_typed
+
+pytestmark = pytest.mark.gpu
+
+S = synth.CONFIGS
+EDGE = {
+    # one sequence from position 0: rows at positions 0 .. 299 (n = 0 .. 75, k = 64)
+    "start_rows": synth.shrink(S["prefill_8k"], "edge_start", (0,), (300,), k=64, win_cap=512),
+    # decode rows with n = 0, 1, 16, 75 (fewer than k = 64 but the last)
+    "short_rows": synth.shrink(S["csa_64k"], "edge_short", (1, 6, 63, 300), (1, 1, 1, 1), k=64),
+}
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _index_bound(st, rows):
+    """sum_h w_h sum_d |q_hd k_d| for every visible entry of the given rows."""
+    c = st.cfg
+    out = np.zeros((len(rows), c.max_entries))
+    q = st.q_idx.reshape(len(st.row_seq), c.HI, c.dI)
+    qf = O.bf16_decode(q).astype(np.float64)
+    for i, r in enumerate(rows):
+        b, n = st.row_seq[r], (st.row_pos[r] + 1) // c.m
+        K = st.ik.rows(pool_rows(st.bt, c.m, b, np.arange(n)))
+        out[i, :n] = (st.w_idx[r][:, None] * (np.abs(qf[r]) @ np.abs(K).T)).sum(0)
+    return out
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_rows_with_few_or_no_entries(name):
+    cfg = EDGE[name]
+    _say("edge rows", name)
+    st = State(cfg)
+    st.oracle_compress_append()
+    gs = GpuState(st)
+    lg = gs.index()
+    idx = gs.topk(lg)
+    out, lse = gs.attn(idx)
+    torch.cuda.synchronize()
+    nrows = len(st.row_seq)
+    rows = np.arange(nrows)
+    n_r = (st.row_pos + 1) // cfg.m
+    assert (n_r == 0).any() and (n_r < cfg.k).any()
+    lg_h, idx_h = lg.cpu().numpy(), idx.cpu().numpy()
+    # logits of the visible entries, top-k on identical logits, attention on identical lists
+    C.check_logits(lg_h, st.oracle_index(rows), _index_bound(st, rows), n_r)
+    assert np.array_equal(idx_h, O.topk(st.row_pos, cfg.m, lg_h.astype(np.float64), cfg.k))
+    assert (idx_h[n_r == 0] == -1).all()
+    o_want, l_want = st.oracle_attn(idx_h, rows)
+    C.check_attention(out.cpu().numpy(), o_want, "bf16")
+    assert np.abs(lse.cpu().numpy() - l_want).max() <= 1e-3
+
+
+def test_lists_with_invalid_and_repeated_entries():
+    cfg = synth.shrink(S["csa_64k"], "edge_lists", (9999, 4101, 3003), (1, 1, 1), k=512)
+    _say("top-k lists with -1, out-of-range and repeated entries")
+    st = State(cfg)
+    st.oracle_compress_append()
+    gs = GpuState(st)
+    g = np.random.default_rng(5)
+    nrows = len(st.row_seq)
+    n_r = (st.row_pos + 1) // cfg.m
+    idx = np.empty((nrows, cfg.k), np.int32)
+    for r in range(nrows):
+        v = g.integers(0, n_r[r], cfg.k)
+        kind = g.random(cfg.k)
+        v[kind < 0.1] = -1                                  # padding
+        v[(kind >= 0.1) & (kind < 0.15)] = n_r[r] + g.integers(0, 50)   # beyond the visible entries
+        v[(kind >= 0.15) & (kind < 0.2)] = v[0]             # repeats of one entry
+        idx[r] = v
+    out, lse = gs.attn(dev_typed(idx))
+    torch.cuda.synchronize()
+    o_want, l_want = st.oracle_attn(idx, np.arange(nrows))
+    C.check_attention(out.cpu().numpy(), o_want, "bf16")
+    assert np.abs(lse.cpu().numpy() - l_want).max() <= 1e-3
