@@ -224,7 +224,10 @@ lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_
  *     s_j = sm_scale * q[r][h] . k_j,
  *     out[r][h] = sum_j softmax(s)_j v_j,    lse[r][h] = ln sum_j exp(s_j)
  * with all keys in ONE softmax.  Keys are split across workgroups and the
- * partial softmax states are merged exactly (max, rescaled sums).
+ * partial softmax states are merged (max, rescaled sums); for BF16 outputs
+ * a split's O / sum is kept as fp16 (11 significant bits against the
+ * output's 8) with a power-of-two range scale per split, head and quarter of
+ * d_v, for F32 outputs in fp32.
  *   q        device [num_rows][H][kv->dim] of q_dtype (F32 with F32 cache;
  *            BF16 otherwise)
  *   out      device [num_rows][H][d_v] of out_dtype (F32 or BF16)

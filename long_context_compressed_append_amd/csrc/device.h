@@ -39,6 +39,13 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // The same rounding in one instruction (v_cvt_pk_bf16_f32, round to nearest
 // even) for finite values: attention probabilities and outputs.
+// fp16 (IEEE binary16), round to nearest even, two per word (low first).
+__device__ inline uint32_t pack_f16x2(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+__device__ inline float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ inline float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
 __device__ inline uint32_t cvt_pk_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }

@@ -62,8 +62,12 @@ struct AttnArgs {
     int32_t out_dtype; void* out; float* lse;
     // split plan
     int32_t nsplit, split_tiles;       // key splits per row, 32-key tiles per split
-    float* part_o;     // [rows][nsplit][H][d_v]   (nsplit > 1)
+    float* part_o;     // [rows][nsplit][H][d_v]   (nsplit > 1, fp32 partial states)
     float* part_ml;    // [rows][nsplit][2][H]
+    // bf16 outputs: partial O / l as fp16 with a power-of-two range scale
+    // per (split, quarter of d_v, head); part_o is then unused
+    uint16_t* part_h;  // [rows][nsplit][H][d_v]
+    float* part_sc;    // [rows][nsplit][4][H]
 };
 
 hipError_t launch_compress_append(const CompressArgs& a, int total_new, hipStream_t stream);

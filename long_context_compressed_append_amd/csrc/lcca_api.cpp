@@ -300,10 +300,18 @@ lcca_status lcca_sparse_attn_fwd(void* stream, const lcca_pages* pages, const lc
     a.out_dtype = out_dtype; a.out = out; a.lse = lse;
     a.nsplit = plan.nsplit; a.split_tiles = plan.split_tiles;
     if (plan.nsplit > 1) {
-        size_t po = (size_t)rows->num_rows * plan.nsplit * H * d_v * sizeof(float);
-        po = (po + 255) & ~(size_t)255;
-        a.part_o = reinterpret_cast<float*>(ws);
-        a.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + po);
+        const size_t parts = (size_t)rows->num_rows * plan.nsplit * H * d_v;
+        const size_t po = (parts * sizeof(float) + 255) & ~(size_t)255;
+        char* base = reinterpret_cast<char*>(ws);
+        a.part_ml = reinterpret_cast<float*>(base + po);
+        if (out_dtype == LCCA_BF16) {
+            // fp16 partials and their scales fit in the fp32 partials' place
+            const size_t ph = (parts * sizeof(uint16_t) + 255) & ~(size_t)255;
+            a.part_h = reinterpret_cast<uint16_t*>(base);
+            a.part_sc = reinterpret_cast<float*>(base + ph);
+        } else {
+            a.part_o = reinterpret_cast<float*>(base);
+        }
     }
     return hip_status(lcca::launch_sparse_attn(a, (hipStream_t)stream), "sparse_attn launch");
 }

@@ -32,8 +32,13 @@
 //     significant bits; FP8 window scales multiply the scores and are folded
 //     into P.
 // Keys are split across workgroups when the rows alone cannot fill the GPU;
-// the partial (max, sum, unnormalised O) states go to the workspace and a
-// merge kernel (one workgroup per row and head) combines them exactly.
+// the partial (max, sum, O) states go to the workspace and a merge kernel
+// (one workgroup per row and head) combines them.  For fp32 outputs O stays
+// fp32; for bf16 outputs O / sum is stored as fp16 (11 significant bits,
+// eight times finer than the output's rounding) with a power-of-two range
+// scale per split, head and quarter of the value dims.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -562,6 +567,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 }
             }
             if (a.lse && g == 0 && q == 0) a.lse[(int64_t)r * a.H + hd] = (m_tot + log2f(l_tot)) * kLn2;
+        } else if (a.part_h) {
+            // U = O / l, a convex combination of the values, as fp16 scaled
+            // by 2^(15 - e) where max |U| over the head's quarter < 2^e
+            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            float amax = 0.0f;
+#pragma unroll
+            for (int dt = 0; dt < NDQ; ++dt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) amax = fmaxf(amax, fabsf(W.o[hb][dt][v]));
+            amax *= inv;
+            amax = fmaxf(amax, __shfl_xor(amax, 16));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            int ex = 0;
+            (void)frexpf(amax, &ex);
+            const float sc = ldexpf(inv, 15 - ex);
+            uint16_t* ph = a.part_h + (((int64_t)r * a.nsplit + split) * a.H + hd) * DV + dv0;
+#pragma unroll
+            for (int dt = 0; dt < NDQ; ++dt) {
+                const f32x4 t = W.o[hb][dt] * sc;
+                *reinterpret_cast<u32x2*>(ph + dt * 16) = u32x2{pack_f16x2(t[0], t[1]), pack_f16x2(t[2], t[3])};
+            }
+            if (g == 0) a.part_sc[(((int64_t)r * a.nsplit + split) * 4 + q) * a.H + hd] = ldexpf(1.0f, ex - 15);
+            if (g == 0 && q == 0) {
+                float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H;
+                ml[hd] = m_tot;
+                ml[a.H + hd] = l_tot;
+            }
         } else {
             float* po = a.part_o + (((int64_t)r * a.nsplit + split) * a.H + hd) * DV + dv0;
 #pragma unroll
@@ -577,27 +609,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 // Merge the key splits of one (row, head): m* = max m_s, w_s = 2^(m_s - m*),
 // out = sum_s w_s O_s / sum_s w_s l_s, lse = (m* + log2 sum_s w_s l_s) ln 2.
-// Each thread owns 4 value dims.  The partial outputs of the first
-// kMergeBatch splits are requested before anything else, so they are in
-// flight while the block forms the weights (thread s owns split s and
-// s + kMergeThreads).  Empty splits carry m = -inf, weight 0, and their
-// workspace bytes are never used.
+// With fp16 partials (HALF) a split stores U_s = O_s / l_s scaled by a power
+// of two per quarter of the value dims, so its weight in the sum becomes
+// w_s l_s times that scale.  Each thread owns 4 value dims.  The partial
+// outputs of the first kMergeBatch splits are requested before anything
+// else, so they are in flight while the block forms the weights (thread s
+// owns split s and s + kMergeThreads).  Empty splits carry m = -inf,
+// weight 0, and their workspace bytes are never used.
 constexpr int kMergeThreads = 192;     // >= 576 / 4
 constexpr int kMaxSplits = 256;        // <= 2 * kMergeThreads
 constexpr int kMergeBatch = 16;
+
+template <bool HALF>
+struct MergePart {
+    typedef typename std::conditional<HALF, u32x2, f32x4>::type raw;
+    __device__ __forceinline__ static raw load(const AttnArgs& a, int64_t off) {
+        if constexpr (HALF) return *reinterpret_cast<const u32x2*>(a.part_h + off);
+        else return *reinterpret_cast<const f32x4*>(a.part_o + off);
+    }
+    __device__ __forceinline__ static f32x4 value(const raw& x) {
+        if constexpr (HALF) return f32x4{f16_lo(x[0]), f16_hi(x[0]), f16_lo(x[1]), f16_hi(x[1])};
+        else return x;
+    }
+};
+
+template <bool HALF>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     __shared__ float wts[kMaxSplits];
     __shared__ float red[2][kMergeThreads / 64];
+    using MP = MergePart<HALF>;
     const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
     const int H = a.H, DV = a.d_v, ns = a.nsplit;
     const float* ml = a.part_ml + (int64_t)r * ns * 2 * H + h;
     const int d = 4 * tid;
     const bool mine = d < DV;
-    const float* po = a.part_o + ((int64_t)r * ns * H + h) * DV + (mine ? d : 0);
+    const int64_t pbase = ((int64_t)r * ns * H + h) * DV + (mine ? d : 0);
     const int64_t sstride = (int64_t)H * DV;
-    f32x4 os[kMergeBatch];
+    // fp16 partials: this thread's quarter of the value dims picks the scale
+    const float* scp = HALF ? a.part_sc + ((int64_t)r * ns * 4 + (mine ? d / (DV / 4) : 0)) * H + h : nullptr;
+    typename MP::raw os[kMergeBatch];
+    float sc[HALF ? kMergeBatch : 1];
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) os[j] = *reinterpret_cast<const f32x4*>(po + min(j, ns - 1) * sstride);
+    for (int j = 0; j < kMergeBatch; ++j) {
+        os[j] = MP::load(a, pbase + min(j, ns - 1) * sstride);
+        if constexpr (HALF) sc[j] = scp[(int64_t)min(j, ns - 1) * 4 * H];
+    }
     const int s1 = tid + kMergeThreads;
     const float m0 = tid < ns ? ml[(int64_t)tid * 2 * H] : -INFINITY;
     const float l0 = tid < ns ? ml[(int64_t)tid * 2 * H + H] : 0.0f;
@@ -611,8 +667,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[0][i]);
     const float w0 = m0 == -INFINITY ? 0.0f : exp2f(m0 - M);
     const float w1 = m1 == -INFINITY ? 0.0f : exp2f(m1 - M);
-    if (tid < ns) wts[tid] = w0;
-    if (s1 < ns) wts[s1] = w1;
+    // fp16 partials are normalised, so their weight carries l_s
+    if (tid < ns) wts[tid] = HALF ? w0 * l0 : w0;
+    if (s1 < ns) wts[s1] = HALF ? w1 * l1 : w1;
     float L = wave_sum(w0 * l0 + w1 * l1);
     if ((tid & 63) == 0) red[1][tid >> 6] = L;
     __syncthreads();
@@ -621,19 +678,21 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     for (int i = 0; i < kMergeThreads / 64; ++i) L += red[1][i];
     if (a.lse && tid == 0) a.lse[(int64_t)r * H + h] = (M + log2f(L)) * kLn2;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto add = [&](int s, int j) __attribute__((always_inline)) {
+        const float w = s < ns ? wts[s] : 0.0f;
+        const float ws = HALF ? w * sc[HALF ? j : 0] : w;
+        acc = w > 0.0f ? acc + ws * MP::value(os[j]) : acc;
+    };
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-        const float w = j < ns ? wts[j] : 0.0f;
-        acc = w > 0.0f ? acc + w * os[j] : acc;
-    }
+    for (int j = 0; j < kMergeBatch; ++j) add(j, j);
     for (int s0 = kMergeBatch; s0 < ns; s0 += kMergeBatch) {
 #pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) os[j] = *reinterpret_cast<const f32x4*>(po + min(s0 + j, ns - 1) * sstride);
-#pragma unroll
         for (int j = 0; j < kMergeBatch; ++j) {
-            const float w = s0 + j < ns ? wts[s0 + j] : 0.0f;
-            acc = w > 0.0f ? acc + w * os[j] : acc;
+            os[j] = MP::load(a, pbase + min(s0 + j, ns - 1) * sstride);
+            if constexpr (HALF) sc[j] = scp[(int64_t)min(s0 + j, ns - 1) * 4 * H];
         }
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) add(s0 + j, j);
     }
     if (!mine) return;
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -719,7 +778,8 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV>), grid, dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.H, a.num_rows), dim3(kMergeThreads), 0, stream, a);
+    if (a.part_h) hipLaunchKernelGGL(attn_merge_kernel<true>, dim3(a.H, a.num_rows), dim3(kMergeThreads), 0, stream, a);
+    else hipLaunchKernelGGL(attn_merge_kernel<false>, dim3(a.H, a.num_rows), dim3(kMergeThreads), 0, stream, a);
     return hipGetLastError();
 }
 

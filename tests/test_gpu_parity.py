@@ -213,3 +213,37 @@ def test_bf16_output_and_value_dim_512():
                               st.q.reshape(len(st.row_seq), cfg.H, cfg.D), cfg.H, cfg.D, 512, cfg.scale,
                               st.kv.as_dict(), idx.cpu().numpy(), cfg.k, st.win.as_dict(), cfg.window)
     C.check_attention(out.float().cpu().numpy(), o_want, "bf16", out_bf16=True)
+
+
+def test_bf16_output_split_partials_keep_their_range():
+    """Key splits with bf16 outputs keep their partial states as fp16 with a
+    power-of-two range scale.  Scaling the cache by 2^12 while dividing
+    sm_scale by 2^12 leaves every score unchanged, so the outputs must scale
+    by exactly 2^12 (bit for bit) and the lse stay the same; the scaled
+    values (up to ~1e5) are beyond fp16's range without the scale."""
+    cfg = SMALL["csa_small"]
+    _say("split partial range (bf16 output)")
+    st = State(cfg)
+    st.oracle_compress_append()
+    gs = _gpu(st)
+    idx = gs.topk(gs.index())
+    out1, lse1 = gs.attn(idx, out_dtype=lcca.BF16)
+    big = st.copy_caches()
+    big.kv.data[:] = O.bf16_encode(O.bf16_decode(big.kv.data.view(np.uint16)).astype(np.float32) * 4096.0).view(np.uint8)
+    big.win.scale[:] = big.win.scale * np.float32(4096.0)
+    gb = _gpu(big)
+    nr = len(st.row_seq)
+    out2 = torch.empty((nr, cfg.H, cfg.dv), dtype=torch.bfloat16, device="cuda")
+    lse2 = torch.empty((nr, cfg.H), dtype=torch.float32, device="cuda")
+    ws = gb.attn_workspace(idx) if hasattr(gb, "attn_workspace") else None
+    if ws is None:
+        wsb = lcca.sparse_attn_workspace_size(gb.rows, cfg.m, cfg.H, cfg.D, cfg.dv, cfg.k, True, cfg.window)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    lcca.sparse_attn_fwd(gb.pages, gb.rows, gb.q_dt, gb.q, cfg.H, cfg.dv, cfg.scale / 4096.0, gb.kv, idx, cfg.k, gb.win,
+                         lcca.BF16, out2, lse2, ws)
+    torch.cuda.synchronize()
+    a = out1.float().cpu().numpy() * 4096.0
+    b = out2.float().cpu().numpy()
+    assert np.isfinite(b).all()
+    assert np.array_equal(a, b)
+    assert np.array_equal(lse1.cpu().numpy(), lse2.cpu().numpy())
