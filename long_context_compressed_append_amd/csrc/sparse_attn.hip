@@ -158,29 +158,36 @@ struct Tiler {
         return s;
     }
 
-    // Issue the loads of a resolved key into registers.
+    // Issue the loads of a resolved key into registers.  One load sequence
+    // serves both sources (the row's address and part count are selected,
+    // parts past the row re-read part 0): a register written on two branch
+    // paths would make the compiler wait at the join for every older load
+    // still in flight.
     __device__ __forceinline__ static void issue(const AttnArgs& a, const Src& s, TileRegs<NU>& R) {
         const int sub = (int)threadIdx.x % kThreadsPerKey;
-        if (s.win) {
-            const uint8_t* src = reinterpret_cast<const uint8_t*>(a.win_data) + s.row * (WD == DT_BF16 ? 2 * D : D);
+        constexpr int64_t WROWB = WD == DT_BF16 ? 2 * D : D;
+        constexpr int64_t PROWB = KVD == DT_BF16 ? 2 * D : D / 2;
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(s.win ? a.win_data : a.kv_data);
+        const uint8_t* src = base + s.row * (s.win ? WROWB : PROWB);
+        const int upk = s.win ? UPK_W : UPK_P;
 #pragma unroll
-            for (int i = 0; i < NU_W; ++i) {
-                const int part = sub + kThreadsPerKey * i;
-                const int pc = part < UPK_W ? part : 0;
-                R.v[i] = *reinterpret_cast<const u32x4*>(src + pc * 16);
+        for (int i = 0; i < NU; ++i) {
+            const int part = sub + kThreadsPerKey * i;
+            const int pc = part < upk ? part : 0;
+            R.v[i] = *reinterpret_cast<const u32x4*>(src + pc * 16);
+            if constexpr (KVD == DT_MXFP4) {
+                // E8M0 scales of the pool row (row 0's for window tiles, unused)
+                const int ps = part < UPK_P ? part : 0;
+                const uint32_t e = reinterpret_cast<const uint8_t*>(a.kv_scale)[(s.win ? 0 : s.row) * (D / 32) + ps];
+                R.sc[i] = s.win ? 127u : e;
+            } else {
                 R.sc[i] = 127u;
             }
-            R.kscale = WD == DT_FP8 ? a.win_scale[s.row] : 1.0f;
+        }
+        if constexpr (WD == DT_FP8) {
+            const float ws = a.win_scale[s.win ? s.row : 0];
+            R.kscale = s.win ? ws : 1.0f;
         } else {
-            const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv_data) + s.row * (KVD == DT_BF16 ? 2 * D : D / 2);
-            const uint8_t* scs = reinterpret_cast<const uint8_t*>(a.kv_scale) + s.row * (D / 32);
-#pragma unroll
-            for (int i = 0; i < NU_P; ++i) {
-                const int part = sub + kThreadsPerKey * i;
-                const int pc = part < UPK_P ? part : 0;
-                R.v[i] = *reinterpret_cast<const u32x4*>(src + pc * 16);
-                R.sc[i] = KVD == DT_MXFP4 ? (uint32_t)scs[pc] : 127u;
-            }
             R.kscale = 1.0f;
         }
         R.valid = s.ok;
@@ -470,22 +477,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // prologue: top-k slots and block-table range of this split into LDS
     const int sel_end = min(te, rk.sel_tiles) * kKeys;            // selected slots [tb*32, sel_end)
     const int idx0 = tb * kKeys;
-    int blk0 = 0, nblk = 0;
+    int blk0 = 0, nblk = 0, bt_first = 0;
     if (sel_end > idx0) {
         const int E = 256 / a.m;
         if (a.topk) {
             nblk = (rk.n + E - 1) / E;
-            for (int i = tid; i < sel_end - idx0; i += NT)
+            const int nidx = sel_end - idx0;
+            const int first = a.topk[(int64_t)r * a.k + min(idx0 + tid, a.k - 1)];
+            bt_first = a.block_table[(int64_t)rk.b * a.max_blocks + min(tid, a.max_blocks - 1)];
+            if (tid < nidx) idx_lds[tid] = idx0 + tid < rk.nsel ? first : -1;
+            for (int i = tid + NT; i < nidx; i += NT)
                 idx_lds[i] = idx0 + i < rk.nsel ? a.topk[(int64_t)r * a.k + idx0 + i] : -1;
         } else {
             const int g1 = min(sel_end, rk.nsel);
             if (g1 > idx0) {
                 blk0 = idx0 / E;
                 nblk = (g1 - 1) / E - blk0 + 1;
+                bt_first = a.block_table[(int64_t)rk.b * a.max_blocks + min(blk0 + tid, a.max_blocks - 1)];
             }
         }
     }
-    for (int i = tid; i < min(nblk, kBtLds); i += NT) bt_lds[i] = a.block_table[(int64_t)rk.b * a.max_blocks + blk0 + i];
+    // (the first slot and block of each thread are requested together above,
+    // so the common case costs one round trip)
+    const int nbt = min(nblk, kBtLds);
+    if (tid < nbt) bt_lds[tid] = bt_first;
+    for (int i = tid + NT; i < nbt; i += NT) bt_lds[i] = a.block_table[(int64_t)rk.b * a.max_blocks + blk0 + i];
     __syncthreads();
 
     QW W;
