@@ -9,7 +9,7 @@ import torch
 import oracle as O
 import compare as C
 from long_context_compressed_append_amd import lcca, synth
-from state import State, pool_rows
+from state import State, pool_rows, _scatter
 from gpu_state import GpuState, dev_typed
 
 pytestmark = pytest.mark.gpu
@@ -85,5 +85,36 @@ def test_lists_with_invalid_and_repeated_entries():
     out, lse = gs.attn(dev_typed(idx))
     torch.cuda.synchronize()
     o_want, l_want = st.oracle_attn(idx, np.arange(nrows))
+    C.check_attention(out.cpu().numpy(), o_want, "bf16")
+    assert np.abs(lse.cpu().numpy() - l_want).max() <= 1e-3
+
+
+def test_score_far_above_the_first_keys():
+    """One selected entry whose score exceeds every other key's by about 150
+    (log2 units), in the middle of the list: the online softmax must move its
+    reference max and rescale what it has accumulated (a weight taken
+    against the earlier max would overflow).  The output is then the value of
+    that entry (the oracle's softmax is one-hot to fp64 precision)."""
+    cfg = synth.shrink(S["csa_64k"], "edge_peak", (9999, 4101), (1, 1), k=512)
+    _say("selected entry with a score far above the window's")
+    st = State(cfg)
+    st.oracle_compress_append()
+    nrows = len(st.row_seq)
+    n_r = (st.row_pos + 1) // cfg.m
+    g = np.random.default_rng(11)
+    idx = np.stack([np.sort(g.choice(n_r[r], cfg.k, replace=False)).astype(np.int32) for r in range(nrows)])
+    q = st.q.reshape(nrows, cfg.H, cfg.D)
+    big = int(idx[0, 300])
+    q[0, :, 0] = O.bf16_encode(np.float32([60.0]))[0]
+    prow = pool_rows(st.bt, cfg.m, st.row_seq[0], [big])
+    x = st.kv.rows(prow).astype(np.float32)
+    x[0, 0] = 60.0
+    _scatter(st.kv, prow, x)
+    gs = GpuState(st)
+    out, lse = gs.attn(dev_typed(idx))
+    torch.cuda.synchronize()
+    o_want, l_want = st.oracle_attn(idx, np.arange(nrows))
+    # the peak dominates row 0 (every head): its output is the entry's value
+    assert np.abs(o_want[0] - x[0][None, : cfg.dv]).max() < 1e-6
     C.check_attention(out.cpu().numpy(), o_want, "bf16")
     assert np.abs(lse.cpu().numpy() - l_want).max() <= 1e-3
