@@ -628,13 +628,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // With fp16 partials (HALF) a split stores U_s = O_s / l_s scaled by a power
 // of two per quarter of the value dims, so its weight in the sum becomes
 // w_s l_s times that scale.  Each thread owns 4 value dims.  The partial
-// outputs of the first kMergeBatch splits are requested before anything
-// else, so they are in flight while the block forms the weights (thread s
-// owns split s and s + kMergeThreads).  Empty splits carry m = -inf,
-// weight 0, and their workspace bytes are never used.
+// outputs of the first MB splits (MB = 16, or 64 for more than 16 splits)
+// are requested before anything else, so they are in flight while the block
+// forms the weights (thread s owns split s and s + kMergeThreads); loads past
+// the last split are not issued.  Empty splits carry m = -inf, weight 0, and
+// their workspace bytes are never used.
 constexpr int kMergeThreads = 192;     // >= 576 / 4
 constexpr int kMaxSplits = 256;        // <= 2 * kMergeThreads
-constexpr int kMergeBatch = 16;
 
 template <bool HALF>
 struct MergePart {
@@ -649,7 +649,7 @@ struct MergePart {
     }
 };
 
-template <bool HALF>
+template <bool HALF, int MB>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     __shared__ float wts[kMaxSplits];
     __shared__ float red[2][kMergeThreads / 64];
@@ -663,12 +663,14 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     const int64_t sstride = (int64_t)H * DV;
     // fp16 partials: this thread's quarter of the value dims picks the scale
     const float* scp = HALF ? a.part_sc + ((int64_t)r * ns * 4 + (mine ? d / (DV / 4) : 0)) * H + h : nullptr;
-    typename MP::raw os[kMergeBatch];
-    float sc[HALF ? kMergeBatch : 1];
+    typename MP::raw os[MB];
+    float sc[HALF ? MB : 1];
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-        os[j] = MP::load(a, pbase + min(j, ns - 1) * sstride);
-        if constexpr (HALF) sc[j] = scp[(int64_t)min(j, ns - 1) * 4 * H];
+    for (int j = 0; j < MB; ++j) {
+        if (j < ns) {
+            os[j] = MP::load(a, pbase + j * sstride);
+            if constexpr (HALF) sc[j] = scp[(int64_t)j * 4 * H];
+        }
     }
     const int s1 = tid + kMergeThreads;
     const float m0 = tid < ns ? ml[(int64_t)tid * 2 * H] : -INFINITY;
@@ -700,15 +702,19 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
         acc = w > 0.0f ? acc + ws * MP::value(os[j]) : acc;
     };
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) add(j, j);
-    for (int s0 = kMergeBatch; s0 < ns; s0 += kMergeBatch) {
+    for (int j = 0; j < MB; ++j)
+        if (j < ns) add(j, j);
+    for (int s0 = MB; s0 < ns; s0 += MB) {
 #pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) {
-            os[j] = MP::load(a, pbase + min(s0 + j, ns - 1) * sstride);
-            if constexpr (HALF) sc[j] = scp[(int64_t)min(s0 + j, ns - 1) * 4 * H];
+        for (int j = 0; j < MB; ++j) {
+            if (s0 + j < ns) {
+                os[j] = MP::load(a, pbase + (s0 + j) * sstride);
+                if constexpr (HALF) sc[j] = scp[(int64_t)(s0 + j) * 4 * H];
+            }
         }
 #pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) add(s0 + j, j);
+        for (int j = 0; j < MB; ++j)
+            if (s0 + j < ns) add(s0 + j, j);
     }
     if (!mine) return;
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -794,8 +800,14 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV>), grid, dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
-    if (a.part_h) hipLaunchKernelGGL(attn_merge_kernel<true>, dim3(a.H, a.num_rows), dim3(kMergeThreads), 0, stream, a);
-    else hipLaunchKernelGGL(attn_merge_kernel<false>, dim3(a.H, a.num_rows), dim3(kMergeThreads), 0, stream, a);
+    const dim3 mgrid(a.H, a.num_rows);
+    if (a.part_h) {
+        if (a.nsplit <= 16) hipLaunchKernelGGL((attn_merge_kernel<true, 16>), mgrid, dim3(kMergeThreads), 0, stream, a);
+        else hipLaunchKernelGGL((attn_merge_kernel<true, 64>), mgrid, dim3(kMergeThreads), 0, stream, a);
+    } else {
+        if (a.nsplit <= 16) hipLaunchKernelGGL((attn_merge_kernel<false, 16>), mgrid, dim3(kMergeThreads), 0, stream, a);
+        else hipLaunchKernelGGL((attn_merge_kernel<false, 64>), mgrid, dim3(kMergeThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
