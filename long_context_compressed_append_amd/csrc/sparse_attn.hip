@@ -430,6 +430,7 @@ struct QuarterWave {
     }
 };
 
+constexpr int kXcds = 8;               // XCDs of the GPU; workgroup ids are dealt to them round-robin
 constexpr int kWaves = 8;              // two head groups of 32 x four quarters of D
 constexpr int kThreads = kWaves * 64;
 constexpr int kBtLds = 4096;           // block-table entries cached in LDS
@@ -458,13 +459,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    const int split = blockIdx.x, r = blockIdx.y;
+    // workgroup -> (row, split, head block): workgroups are dispatched to the
+    // eight XCDs round-robin by id, so id % 8 picks the XCD, and each XCD
+    // takes an equal contiguous range of the (row, split) units in row order;
+    // a row's queries then reach one or two L2s instead of all eight, and
+    // neighbouring rows (which share most of their window) run side by side
+    const int units = a.num_rows * a.nsplit;
+    const int upx = (units + kXcds - 1) / kXcds;
+    const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
+    const int hblk = slot / upx;
+    const int unit = xcd * upx + slot % upx;
+    if (unit >= units) return;
+    const int r = unit / a.nsplit, split = unit % a.nsplit;
     const RowKeys rk = row_keys(a, r);
     const int tb = split * a.split_tiles;
     if (tb >= rk.tiles) {
         // empty split (a row with fewer tiles than the longest): a zero state
         if (a.nsplit > 1 && tid < 64) {
-            float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H + (int)blockIdx.z * 64 + tid;
+            float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H + hblk * 64 + tid;
             ml[0] = -INFINITY;
             ml[a.H] = 0.0f;
         }
@@ -472,7 +484,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     const int te = min(tb + a.split_tiles, rk.tiles);
     const int hg = wave >> 2, q = wave & 3;
-    const int head0 = (int)blockIdx.z * 64 + hg * 32;       // first head of this wave's group
+    const int head0 = hblk * 64 + hg * 32;                   // first head of this wave's group
 
     // prologue: top-k slots and block-table range of this split into LDS
     const int sel_end = min(te, rk.sel_tiles) * kKeys;            // selected slots [tb*32, sel_end)
@@ -796,7 +808,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
 template <int KVD, int WD, int D, int DV>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
-    dim3 grid(a.nsplit, a.num_rows, a.H / 64);
+    const int64_t upx = ((int64_t)a.num_rows * a.nsplit + kXcds - 1) / kXcds;
+    const dim3 grid((unsigned)(kXcds * upx * (a.H / 64)));
     hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV>), grid, dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
