@@ -24,6 +24,14 @@ SMALL = {
     "hca_small": synth.shrink(S["hca_1m"], "hca_small", (40959, 25600), (1, 1)),
     "prefill_small": synth.shrink(S["prefill_8k"], "prefill_small", (3001,), (1000,), k=256, win_cap=2048),
     "lp_small": synth.shrink(S["lp_512k"], "lp_small", (8191, 5000), (1, 1), k=512),
+    # other built shapes: 128 heads of dim 128 (two 64-head blocks) with a
+    # 32 x 64 indexer; 128 x 64 and 32 x 256 indexers; an MXFP4 pool with a
+    # bf16 window; many rows (no key splits) with 128 heads
+    "h128_d128": synth.shrink(S["csa_64k"], "h128_d128", (5001, 2222), (1, 1), k=256, D=128, H=128, HI=32, dI=64),
+    "idx128x64": synth.shrink(S["csa_64k"], "idx128x64", (4097, 3000), (1, 1), k=256, HI=128, dI=64),
+    "idx32x256": synth.shrink(S["csa_64k"], "idx32x256", (4097, 3000), (1, 1), k=256, HI=32, dI=256),
+    "lp_bf16win": synth.shrink(S["lp_512k"], "lp_bf16win", (6001, 3333), (1, 1), k=256, win_dtype=synth.BF16),
+    "prefill_h128": synth.shrink(S["prefill_8k"], "prefill_h128", (2001,), (300,), k=128, win_cap=1024, H=128),
 }
 
 
