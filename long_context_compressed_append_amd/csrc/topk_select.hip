@@ -46,11 +46,16 @@ constexpr int kLeadCopies = 8;                  // lane & 7 picks the copy
 constexpr int kCandCap = 4096;
 constexpr int kWords = kTopkMaxEntries / 32;
 
-struct alignas(16) Smem {
+// Shared memory of one row's selection.  The full layout (8 histogram copies,
+// bitmaps for 2^18 entries) takes ~148 KB, one workgroup per compute unit;
+// the compact one (2 copies, bitmaps for 32K entries) ~58 KB, so two rows
+// share a compute unit when a launch has more rows than compute units.
+template <int COPIES, int WORDS>
+struct alignas(16) SmemT {
     union alignas(16) {
-        uint32_t lead[kLeadBins * kLeadCopies];       // step 1: [bin][copy]
+        uint32_t lead[kLeadBins * COPIES];            // step 1: [bin][copy]
         struct {
-            uint32_t bits[2][kWords];                 // [0] keys above T, [1] keys equal to T
+            uint32_t bits[2][WORDS];                  // [0] keys above T, [1] keys equal to T
             uint32_t cand_key[kCandCap];
             int32_t cand_idx[kCandCap];
             uint32_t fine[2][256];                    // refinement histograms, double-buffered
@@ -60,6 +65,7 @@ struct alignas(16) Smem {
     uint32_t wsum[2][kWaves];
     uint32_t cand_n, sel_digit, sel_above;
 };
+constexpr int kCompactEntries = 32768;
 
 __device__ inline uint32_t order_key(float x) {
     uint32_t u = __float_as_uint(x);
@@ -247,8 +253,8 @@ __device__ __forceinline__ void pick_digit(const uint32_t* h, uint32_t need, uin
 // `mask`, from bit `top` down; leaves the need-th largest key in *prefix and
 // the number of keys equal to it still needed in *need.  fine[0] must be
 // zero on entry.
-template <class Each>
-__device__ __forceinline__ void refine(Smem& sm, Each each, int top, uint32_t* prefix_io, uint32_t* mask_io, uint32_t* need_io) {
+template <class SM, class Each>
+__device__ __forceinline__ void refine(SM& sm, Each each, int top, uint32_t* prefix_io, uint32_t* mask_io, uint32_t* need_io) {
     const int tid = threadIdx.x;
     uint32_t prefix = *prefix_io, mask = *mask_io, need = *need_io;
     int cur = 0;
@@ -289,9 +295,11 @@ __device__ __forceinline__ void refine(Smem& sm, Each each, int top, uint32_t* p
 //           i.e. smaller entry, first.
 enum Mode : int { kRow = 0, kSlice = 1, kCand = 2 };
 
-template <int R, bool Half, bool Vec, int MODE>
-__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
-    __shared__ Smem sm;
+template <int R, bool Half, bool Vec, int MODE, bool COMPACT>
+__global__ __launch_bounds__(kThreads, COMPACT ? 8 : 4) void topk_kernel(TopkArgs p) {
+    static_assert(!COMPACT || (R > 0 && R <= 32 && !Half), "compact layout: rows of up to 32K entries in registers");
+    constexpr int COPIES = COMPACT ? 2 : kLeadCopies;
+    __shared__ SmemT<COPIES, COMPACT ? kCompactEntries / 32 : kWords> sm;
     const int r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
     const int n_row = visible_entries(p.row_pos[r], p.m);
@@ -339,30 +347,37 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
 
     {
         u32x4* z = reinterpret_cast<u32x4*>(sm.u.lead);
-        for (int i = tid; i < kLeadBins * kLeadCopies / 4; i += kThreads) z[i] = u32x4{0u, 0u, 0u, 0u};
+        for (int i = tid; i < kLeadBins * COPIES / 4; i += kThreads) z[i] = u32x4{0u, 0u, 0u, 0u};
     }
     if (tid == 0) sm.cand_n = 0;
     __syncthreads();
 
     // 1. leading-digit histogram and the boundary bin
     {
-        const int copy = lane & (kLeadCopies - 1);
+        const int copy = lane & (COPIES - 1);
         K.rounds_each([&](int e, const uint32_t* key) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                atomicAdd(&sm.u.lead[(key[i] >> kLeadShift) * kLeadCopies + copy], e + i < n ? 1u : 0u);
+                atomicAdd(&sm.u.lead[(key[i] >> kLeadShift) * COPIES + copy], e + i < n ? 1u : 0u);
         });
     }
     __syncthreads();
-    // sum the copies: lane pairs read one bin's 8 copies as two consecutive
-    // 16-byte chunks and add them across the pair
 #pragma unroll
-    for (int i = 0; i < kLeadBins * kLeadCopies / 4 / kThreads; ++i) {
+    for (int i = 0; i < kLeadBins * COPIES / 4 / kThreads; ++i) {
         const int chunk = tid + kThreads * i;
         const u32x4 x = reinterpret_cast<const u32x4*>(sm.u.lead)[chunk];
-        uint32_t c = x[0] + x[1] + x[2] + x[3];
-        c += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)c, 0xB1, 0xF, 0xF, false);     // quad_perm [1,0,3,2]
-        if ((chunk & 1) == 0) sm.cnt[chunk >> 1] = c;
+        if constexpr (COPIES == 8) {
+            // lane pairs read one bin's 8 copies as two consecutive 16-byte
+            // chunks and add them across the pair
+            uint32_t c = x[0] + x[1] + x[2] + x[3];
+            c += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)c, 0xB1, 0xF, 0xF, false);     // quad_perm [1,0,3,2]
+            if ((chunk & 1) == 0) sm.cnt[chunk >> 1] = c;
+        } else {
+            // a 16-byte chunk holds the 2 copies of two bins
+            static_assert(COPIES == 2, "copies");
+            sm.cnt[2 * chunk] = x[0] + x[1];
+            sm.cnt[2 * chunk + 1] = x[2] + x[3];
+        }
     }
     __syncthreads();
     {
@@ -485,15 +500,26 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
     }
 }
 
+template <int R, bool Vec, int MODE>
+void launch_regs(const TopkArgs& a, bool compact, dim3 grid, hipStream_t stream) {
+    if (compact) hipLaunchKernelGGL((topk_kernel<R, false, Vec, MODE, true>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((topk_kernel<R, false, Vec, MODE, false>), grid, dim3(kThreads), 0, stream, a);
+}
+
+// Rows of up to 32K entries use the compact layout when the launch has more
+// rows than the GPU has compute units (256): then two rows per compute unit
+// hide each other's barriers; with fewer rows the full layout's eight
+// histogram copies keep the one row per compute unit fastest.
 template <bool Vec, int MODE>
 void launch_sel(const TopkArgs& a, int entries, dim3 grid, hipStream_t stream) {
     const int rounds = (entries + kGroup - 1) / kGroup;
     const dim3 block(kThreads);
-    if (rounds <= 2) hipLaunchKernelGGL((topk_kernel<8, false, Vec, MODE>), grid, block, 0, stream, a);
-    else if (rounds <= 4) hipLaunchKernelGGL((topk_kernel<16, false, Vec, MODE>), grid, block, 0, stream, a);
-    else if (rounds <= 8) hipLaunchKernelGGL((topk_kernel<32, false, Vec, MODE>), grid, block, 0, stream, a);
-    else if (rounds <= 32) hipLaunchKernelGGL((topk_kernel<128, true, Vec, MODE>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((topk_kernel<0, false, Vec, MODE>), grid, block, 0, stream, a);
+    const bool compact = (int64_t)grid.x * grid.y > 256;
+    if (rounds <= 2) launch_regs<8, Vec, MODE>(a, compact, grid, stream);
+    else if (rounds <= 4) launch_regs<16, Vec, MODE>(a, compact, grid, stream);
+    else if (rounds <= 8) launch_regs<32, Vec, MODE>(a, compact, grid, stream);
+    else if (rounds <= 32) hipLaunchKernelGGL((topk_kernel<128, true, Vec, MODE, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((topk_kernel<0, false, Vec, MODE, false>), grid, block, 0, stream, a);
 }
 
 }  // namespace

@@ -79,6 +79,35 @@ def test_ties_zeros_and_signs(n):
     _check("ties n=%d" % n, x, np.full(rows, n * m - 1), m, k)
 
 
+@pytest.mark.parametrize("n", [32768, 5000])
+def test_many_rows(n):
+    """More rows than compute units: the compact shared-memory layout (two
+    rows per compute unit, two histogram copies) on the same kinds of rows,
+    each kind repeated down the batch, with ragged lengths."""
+    g = np.random.default_rng(17 + n)
+    rows, m, k = 300, 4, 2048
+    x = np.empty((rows, n), np.float32)
+    for r in range(rows):
+        kind = r % 6
+        if kind == 0:
+            x[r] = 1.25
+        elif kind == 1:
+            x[r] = _relu_like(g, n, 0.99)
+        elif kind == 2:
+            x[r] = np.round(g.standard_normal(n) * 4) / 4
+        elif kind == 3:
+            x[r] = 0.0
+            x[r, ::2] = -0.0
+            x[r, g.integers(0, n, 100)] = 1.0
+        elif kind == 4:
+            x[r] = g.standard_normal(n).astype(np.float32) * 1e-3 + 100.0
+        else:
+            x[r] = g.standard_normal(n).astype(np.float32)
+            x[r, g.integers(0, n, n // 6)] = 3.0
+    lens = np.where(np.arange(rows) % 7 == 0, n, g.integers(1, n + 1, rows))
+    _check("many rows n=%d" % n, x, lens * m - 1, m, k)
+
+
 def test_unaligned_rows_and_small_k():
     g = np.random.default_rng(11)
     rows, m, n = 5, 4, 20001
