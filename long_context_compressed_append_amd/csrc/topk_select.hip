@@ -506,15 +506,19 @@ void launch_regs(const TopkArgs& a, bool compact, dim3 grid, hipStream_t stream)
     else hipLaunchKernelGGL((topk_kernel<R, false, Vec, MODE, false>), grid, dim3(kThreads), 0, stream, a);
 }
 
-// Rows of up to 32K entries use the compact layout when the launch has more
-// rows than the GPU has compute units (256): then two rows per compute unit
-// hide each other's barriers; with fewer rows the full layout's eight
-// histogram copies keep the one row per compute unit fastest.
+// One-launch selections of rows of up to 32K entries use the compact layout
+// when the launch has more rows than the GPU has compute units (256: two rows
+// per compute unit hide each other's barriers) or at most 64 rows (clearing
+// and summing two histogram copies instead of eight is then the gain).  In
+// between, two rows per compute unit could leave compute units idle, and the
+// two-launch path keeps eight copies: its candidate keys are concentrated, so
+// two copies conflict more (lp_512k: 33.9 against 35.6 us).
 template <bool Vec, int MODE>
 void launch_sel(const TopkArgs& a, int entries, dim3 grid, hipStream_t stream) {
     const int rounds = (entries + kGroup - 1) / kGroup;
     const dim3 block(kThreads);
-    const bool compact = (int64_t)grid.x * grid.y > 256;
+    const int64_t wgs = (int64_t)grid.x * grid.y;
+    const bool compact = MODE == kRow && (wgs > 256 || wgs <= 64);
     if (rounds <= 2) launch_regs<8, Vec, MODE>(a, compact, grid, stream);
     else if (rounds <= 4) launch_regs<16, Vec, MODE>(a, compact, grid, stream);
     else if (rounds <= 8) launch_regs<32, Vec, MODE>(a, compact, grid, stream);
