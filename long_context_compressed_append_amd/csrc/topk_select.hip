@@ -25,10 +25,14 @@
 //      second bitmap.  A block scan of the bitmaps' popcounts gives every
 //      thread its output offset, so the result comes out sorted by entry and
 //      the first `need` equal keys (smallest entries) are the ones kept.
-// The leading-digit histogram keeps 8 copies of every bin side by side
+// The leading-digit histogram keeps copies of every bin side by side
 // ([bin][copy], the copy picked by lane), so lanes that hit the same bin land
 // in different banks; the copies are summed into one count per bin before the
-// scan, which then reads 4 consecutive bins per thread.
+// scan, which then reads 4 consecutive bins per thread.  The full layout
+// keeps 8 copies and bitmaps for 2^18 entries (~148 KB of LDS); the compact
+// layout, for rows of up to 32K entries, 2 copies and bitmaps for 32K
+// entries (~60 KB), which lets two rows share a compute unit and clears and
+// sums a quarter of the copies.
 #include "device.h"
 #include "kernels.h"
 
