@@ -79,13 +79,14 @@ def test_ties_zeros_and_signs(n):
     _check("ties n=%d" % n, x, np.full(rows, n * m - 1), m, k)
 
 
-@pytest.mark.parametrize("n", [32768, 5000])
-def test_many_rows(n):
-    """More rows than compute units: the compact shared-memory layout (two
-    rows per compute unit, two histogram copies) on the same kinds of rows,
-    each kind repeated down the batch, with ragged lengths."""
-    g = np.random.default_rng(17 + n)
-    rows, m, k = 300, 4, 2048
+@pytest.mark.parametrize("rows,n", [(300, 32768), (300, 5000), (100, 16384)])
+def test_many_rows(rows, n):
+    """The same kinds of rows, each repeated down a larger batch, with ragged
+    lengths: 300 rows (more than compute units: the compact shared-memory
+    layout, two rows per compute unit) and 100 rows (the full layout in one
+    launch; fewer rows than that take the compact layout again)."""
+    g = np.random.default_rng(17 + n + rows)
+    m, k = 4, 2048
     x = np.empty((rows, n), np.float32)
     for r in range(rows):
         kind = r % 6
@@ -105,7 +106,7 @@ def test_many_rows(n):
             x[r] = g.standard_normal(n).astype(np.float32)
             x[r, g.integers(0, n, n // 6)] = 3.0
     lens = np.where(np.arange(rows) % 7 == 0, n, g.integers(1, n + 1, rows))
-    _check("many rows n=%d" % n, x, lens * m - 1, m, k)
+    _check("%d rows n=%d" % (rows, n), x, lens * m - 1, m, k)
 
 
 def test_unaligned_rows_and_small_k():
