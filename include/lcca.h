@@ -233,7 +233,8 @@ lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_
  *   out      device [num_rows][H][d_v] of out_dtype (F32 or BF16)
  *   lse      device float [num_rows][H] or NULL
  *   ws       device workspace of at least lcca_sparse_attn_workspace_size()
- *            bytes for the same arguments (may be NULL if that size is 0)
+ *            bytes for the same arguments, 16-byte aligned (may be NULL if
+ *            that size is 0)
  * BF16 path: kv dtype BF16 or MXFP4, window BF16 or FP8, H a multiple of 64
  * (64 heads per workgroup), (dim, d_v) in {(576, 576), (576, 512), (128, 128)};
  * with top-k indices, positions below 2^20 (the block-table range a

@@ -289,6 +289,8 @@ lcca_status lcca_sparse_attn_fwd(void* stream, const lcca_pages* pages, const lc
     }
     if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes))
         return fail(LCCA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, plan.ws_bytes);
+    if (plan.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(ws) & 15))
+        return fail(LCCA_ERR_INVALID_ARG, "attention workspace not 16-byte aligned");
     lcca::AttnArgs a{};
     a.block_table = pages->block_table; a.max_blocks = pages->max_blocks_per_seq;
     a.row_seq = rows->row_seq; a.row_pos = rows->row_pos; a.num_rows = rows->num_rows;

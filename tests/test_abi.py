@@ -80,6 +80,10 @@ def test_invalid_arguments_rejected_before_launch():
     st = L.lcca_sparse_attn_fwd(None, by(pg), by(rw), lcca.BF16, 1, 64, 576, 0.04, by(kv), 1, 2048, by(win),
                                 lcca.F32, 1, None, 1, need - 1)
     assert st == lcca.ERR_WORKSPACE
+    # a large enough workspace that is not 16-byte aligned
+    st = L.lcca_sparse_attn_fwd(None, by(pg), by(rw), lcca.BF16, 1, 64, 576, 0.04, by(kv), 1, 2048, by(win),
+                                lcca.F32, 1, None, 8, need)
+    assert st == lcca.ERR_INVALID_ARG and b"aligned" in L.lcca_last_error()
     # FP8 window without its scale array
     win_ns = lcca._WindowCache(lcca.FP8_E4M3, 576, 128, 128, 1, None)
     st = L.lcca_sparse_attn_fwd(None, by(pg), by(rw), lcca.BF16, 1, 64, 576, 0.04, by(kv), 1, 2048, by(win_ns),
