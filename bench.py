@@ -268,6 +268,11 @@ class Workload:
         self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
         tkb = lcca.topk_workspace_size(self.rows, m, c.k) if HI else 0
         self.topk_ws = torch.empty(tkb, dtype=torch.uint8, device=dev) if tkb else None
+        # decode steps with one new token and one row per sequence and rows of
+        # up to 32K entries run compress_append, index_logits and topk_select
+        # as lcca_decode_select (two launches instead of three)
+        self.fused = bool(HI) and c.rows == "last" and all(n == 1 for n in c.n_new) and self.ld <= 32768 \
+            and self.ld % 4 == 0
 
     def snapshot_host(self):
         """Copy the initial state to host numpy arrays (for the oracle)."""
@@ -284,6 +289,17 @@ class Workload:
         kv, ik, win, rem = self.copies[i % self.R]
         if ev is not None:
             ev[0].record()
+        if self.fused:
+            L.decode_select(self.pages, self.rows, self.cu_new, self.start_pos, self.total_new, L.BF16, self.new_kv,
+                            self.new_kv_logit, self.new_ik, self.new_ik_logit, kv, ik, win, rem, L.BF16, self.q_idx,
+                            c.HI, self.w_idx, 1.0, self.logits, self.ld, c.k, self.topk)
+            if ev is not None:
+                ev[1].record()
+            L.sparse_attn_fwd(self.pages, self.rows, L.BF16, self.q, c.H, c.dv, c.scale, kv, self.topk, c.k, win,
+                              L.BF16, self.out, self.lse, self.ws)
+            if ev is not None:
+                ev[4].record()
+            return
         L.compress_append(self.pages, self.cu_new, self.start_pos, self.total_new, L.BF16, self.new_kv,
                           self.new_kv_logit, self.new_ik, self.new_ik_logit, kv, ik, win, rem)
         if ev is not None:
@@ -322,8 +338,11 @@ def time_steps(torch, wl, steps, warmup):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - wall0) * 1e3 / steps
     total = t0.elapsed_time(t1) / steps
-    names = ("compress_append", "index_logits", "topk_select", "sparse_attn_fwd")
-    pairs = ((0, 1), (1, 2), (2, 3), (3, 4))
+    if wl.fused:
+        names, pairs = ("decode_select", "sparse_attn_fwd"), ((0, 1), (1, 4))
+    else:
+        names = ("compress_append", "index_logits", "topk_select", "sparse_attn_fwd")
+        pairs = ((0, 1), (1, 2), (2, 3), (3, 4))
     stage = {}
     for n, (a, b) in zip(names, pairs):
         stage[n] = sum(e[a].elapsed_time(e[b]) for e in evs) / steps
@@ -429,18 +448,30 @@ def parity_summary(wl, rows, out_ref, idx_ref):
 # HBM traffic measured by rocprofv3 counters (profiles/), if still current
 # --------------------------------------------------------------------------
 
-def kernel_source_hash(fname):
-    p = os.path.join(ROOT, "long_context_compressed_append_amd", "csrc", fname)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+# the source files of each stage's kernels
+STAGE_SOURCES = {"compress_append": ("compress_append.hip", "compress_dev.h"),
+                 "index_logits": ("index_logits.hip",),
+                 "topk_select": ("topk_select.hip", "compress_dev.h"),
+                 "sparse_attn_fwd": ("sparse_attn.hip",),
+                 "decode_select": ("index_logits.hip", "topk_select.hip", "compress_dev.h")}
 
 
-def measured_traffic(workload, kernel, source):
-    """Per-launch HBM bytes from profiles/hbm_traffic.txt when the line for
-    (workload, kernel) carries the current hash of the kernel's source."""
+def kernel_source_hash(fnames):
+    h = hashlib.sha256()
+    for f in fnames:
+        h.update(open(os.path.join(ROOT, "long_context_compressed_append_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, stage):
+    """Per-step HBM bytes of a stage from profiles/hbm_traffic.txt when the
+    line for (workload, stage) carries the current hash of the stage's kernel
+    sources."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     if not os.path.exists(path):
         return None
-    want = kernel_source_hash(source)
+    want = kernel_source_hash(STAGE_SOURCES[stage])
+    kernel = stage
     for line in open(path):
         f = line.split()
         if len(f) >= 4 and f[0] == workload and f[1] == kernel and f[2] == want:
@@ -467,6 +498,9 @@ def run_workload(torch, lcca, synth, name, args, with_oracle, cpu_seconds=0.0):
         hot_total = plain_steps(torch, wl, steps)
         wl.R = saved
     work = stage_work(wl.cfg)
+    if wl.fused:
+        parts = [work.pop(n) for n in ("compress_append", "index_logits", "topk_select")]
+        work = {"decode_select": (sum(b for b, _ in parts), sum(f for _, f in parts)), **work}
     step_bytes = sum(b for b, _ in work.values())
     step_flops = sum(f for _, f in work.values())
     per = {}
@@ -549,10 +583,8 @@ def main():
 
     head = names[0]
     r = results[head]
-    srcs = {"index_logits": "index_logits.hip", "sparse_attn_fwd": "sparse_attn.hip",
-            "topk_select": "topk_select.hip", "compress_append": "compress_append.hip"}
     for n, e in r["stages"].items():
-        e["traffic"] = measured_traffic(head, n, srcs[n])
+        e["traffic"] = measured_traffic(head, n)
     # the dominant kernel of the headline workload: the stage with the most time
     dname, d = max(r["stages"].items(), key=lambda kv: kv[1]["ms"])
     traffic = d["traffic"]

@@ -212,6 +212,38 @@ lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_
                              void* ws, size_t ws_bytes);
 
 /*
+ * lcca_decode_select -- compress_append, index_logits and topk_select of a
+ * decode step in two launches instead of three.
+ *
+ * [P1 "Kako funkcionira optimizacija KV cachea?" and P3 "Vykon neprinesl
+ * jeden kernel": the same three stages as above.]  Every sequence appends
+ * exactly one token and queries at it: total_new == pages->batch ==
+ * rows->num_rows, and for every b, cu_new[b] == b, row_seq[b] == b and
+ * row_pos[b] == start_pos[b].  Launch 1 computes the logits of every row;
+ * the entry a row's own token completes (not yet in the pool) is formed by
+ * the kernel from the remainder ring and the token with compress_append's
+ * arithmetic, so it is scored from exactly the codes the pool receives.
+ * Launch 2 runs the top-k selection of every row and, beside it, the whole
+ * of compress_append for the new tokens.  Pools, rings, logits and top-k
+ * lists equal those of lcca_compress_append, lcca_index_logits and
+ * lcca_topk_select called in that order.  A row whose sequence does not
+ * satisfy the device-side part of the contract (cu_new, start_pos) gets a
+ * NaN logit for the entry its token completes.
+ * Arguments: those of the three calls (topk_select without workspace).
+ * Supported: BF16 queries and tokens, an indexer pool, fewer than 64 rows,
+ * ratio_m <= 4, at most 32,768 visible entries per row, ld % 4 == 0 and
+ * 16-byte aligned logits; otherwise LCCA_ERR_UNSUPPORTED and nothing runs.
+ */
+lcca_status lcca_decode_select(void* stream, const lcca_pages* pages, const lcca_rows* rows,
+                               const int32_t* cu_new, const int32_t* start_pos, int32_t total_new,
+                               int32_t tok_dtype, const void* kv_tok, const float* kv_logit,
+                               const void* ik_tok, const float* ik_logit,
+                               const lcca_paged_cache* kv, const lcca_paged_cache* ik,
+                               const lcca_window_cache* win, const lcca_remainder* rem,
+                               int32_t q_dtype, const void* q_idx, int32_t HI, const float* w_idx, float s_I,
+                               float* logits, int64_t ld, int32_t k, int32_t* topk_idx);
+
+/*
  * lcca_sparse_attn_fwd -- attention over selected entries plus the window.
  *
  * [P1 "Kako funkcionira optimizacija KV cachea?": shared KV vectors, top-k

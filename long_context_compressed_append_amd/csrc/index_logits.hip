@@ -88,6 +88,109 @@ __device__ __forceinline__ void unroll_steps(F& f, int tile, int t_end) {
     }
 }
 
+// Inputs of the entry a row's own token completes (decode launches ahead of
+// the step's compress_append, groups of m <= 4 tokens): lane i < m holds
+// token i's logit; every lane holds its DI / 64 dimensions of the group's
+// tokens as raw bits (bf16 or fp32); the earlier m - 1 tokens come from the
+// remainder ring (slot i), the last is token r of the batch; and the
+// sequence's cu_new and start_pos entries, which check that it is.
+template <int DI>
+struct FreshIn {
+    static constexpr int DPL = DI / 64;                          // dimensions per lane
+    float logit;
+    uint32_t raw[4][DPL];
+    int cu0, cu1, sp;                                            // cu_new[b], cu_new[b + 1], start_pos[b]
+
+    __device__ __forceinline__ void load(const IndexArgs& p, int r, int b) {
+        const int m = p.m, lane = threadIdx.x & 63;
+        cu0 = p.cu_new[b];
+        cu1 = p.cu_new[b + 1];
+        sp = p.start_pos[b];
+        logit = -INFINITY;
+        if (lane < m) logit = lane == m - 1 ? p.ik_logit[r] : p.rem_ik_logit[(int64_t)b * m + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool last = i == m - 1;
+            const void* base = last ? p.ik_tok : p.rem_ik;
+            const int64_t row = last ? (int64_t)r : (int64_t)b * m + i;
+#pragma unroll
+            for (int j = 0; j < DPL; ++j) {
+                const int64_t el = row * DI + lane * DPL + j;
+                raw[i][j] = 0u;
+                if (i < m)
+                    raw[i][j] = p.tok_dtype == DT_F32 ? reinterpret_cast<const uint32_t*>(base)[el]
+                                                      : (uint32_t)reinterpret_cast<const uint16_t*>(base)[el];
+            }
+        }
+    }
+};
+
+// Logit of that entry, formed by one wave with compress_append's arithmetic,
+// so its bits are those the pool will hold: the softmax weights of the
+// group's logits by one wave, each dimension's products w_i x_i summed in
+// token order, then the pool dtype's rounding; then scored from its stored
+// value like the entries read from the pool (lane = head).  A row that is
+// not the one new token of its sequence gets a NaN logit.
+template <int KD, int NHT, int DI>
+__device__ __forceinline__ void score_fresh(const IndexArgs& p, const FreshIn<DI>& in, int r, int b, int pos, int e,
+                                            const uint8_t* q_lds, const float* w_lds, float* k_lds, float* out) {
+    constexpr int DPL = DI / 64;
+    constexpr int QROWB = DI * 2 + 16;
+    const int m = p.m, lane = threadIdx.x & 63;
+    const bool ok = in.cu0 == r && in.cu1 == r + 1 && in.sp == pos;
+    const float mx = wave_max(in.logit);
+    const float ex = lane < m ? expf(in.logit - mx) : 0.0f;
+    const float wsum = wave_sum(ex);
+    const float w_mine = ex / wsum;
+    float v[DPL];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) v[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (i < m) {
+            const float w = __shfl(w_mine, i);
+#pragma unroll
+            for (int j = 0; j < DPL; ++j) {
+                const float x = p.tok_dtype == DT_F32 ? __uint_as_float(in.raw[i][j]) : bf16_to_f32(in.raw[i][j]);
+                v[j] += fmaf(w, x, 0.0f);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) {
+        float kd;
+        if constexpr (KD == DT_FP8) kd = bf16_to_f32(fp8x8_to_bf16(f32_to_fp8(v[j]), 0u)[0] & 0xffffu);
+        else kd = bf16_to_f32(f32_to_bf16(v[j]));
+        k_lds[lane * DPL + j] = kd;
+    }
+    float l = 0.0f;
+#pragma unroll
+    for (int h0 = 0; h0 < NHT * 32; h0 += 64) {
+        const int h = h0 + lane;
+        if (h < NHT * 32) {
+            const uint8_t* qh = q_lds + h * QROWB;
+            float dot = 0.0f;
+#pragma unroll 4
+            for (int d = 0; d < DI; d += 8) {
+                const u32x4 qq = *reinterpret_cast<const u32x4*>(qh + 2 * d);
+                const f32x4 k0 = *reinterpret_cast<const f32x4*>(k_lds + d);
+                const f32x4 k1 = *reinterpret_cast<const f32x4*>(k_lds + d + 4);
+                dot = fmaf(bf16_to_f32(qq[0] & 0xffffu), k0[0], dot);
+                dot = fmaf(bf16_to_f32(qq[0] >> 16), k0[1], dot);
+                dot = fmaf(bf16_to_f32(qq[1] & 0xffffu), k0[2], dot);
+                dot = fmaf(bf16_to_f32(qq[1] >> 16), k0[3], dot);
+                dot = fmaf(bf16_to_f32(qq[2] & 0xffffu), k1[0], dot);
+                dot = fmaf(bf16_to_f32(qq[2] >> 16), k1[1], dot);
+                dot = fmaf(bf16_to_f32(qq[3] & 0xffffu), k1[2], dot);
+                dot = fmaf(bf16_to_f32(qq[3] >> 16), k1[3], dot);
+            }
+            l = fmaf(w_lds[h], fmaxf(dot, 0.0f), l);
+        }
+    }
+    l = wave_sum(l);
+    if (lane == 0) out[e] = ok ? l : __builtin_nanf("");
+}
+
 template <int KD, int NHT, int DI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void
 index_mfma_kernel(IndexArgs p) {
@@ -101,7 +204,16 @@ index_mfma_kernel(IndexArgs p) {
     const int tpw = p.tiles_per_wave;
     const int t_begin = ((int)blockIdx.x * 4 + wave) * tpw;
     const int b = p.row_seq[r];
-    const int n = visible_entries(p.row_pos[r], p.m);
+    const int pos = p.row_pos[r];
+    const int n_all = visible_entries(pos, p.m);
+    // the entry this row's token completes is scored by score_fresh
+    const bool fresh = p.fresh && row_ok && (pos + 1) % p.m == 0;
+    const int n = fresh ? n_all - 1 : n_all;
+    // the wave whose tile range holds the fresh entry scores it after its
+    // tiles; its inputs are requested now
+    const bool fresh_owner = fresh && ((n_all - 1) >> 5) / p.tiles_per_wave == (int)blockIdx.x * 4 + wave;
+    FreshIn<DI> fin;
+    if (fresh_owner) fin.load(p, r, b);
     // The query (HI x DI bf16) and head weights of the workgroup's row are
     // staged in LDS once (rows padded by 16 bytes against bank conflicts);
     // every wave then reads its A operands from there instead of from L2.
@@ -199,8 +311,12 @@ index_mfma_kernel(IndexArgs p) {
         const int e = tile * 32 + j;
         if (g == 0 && e < n) out[e] = l;
     };
-    if (!work) return;
-    for (int tile = t_begin; tile < t_end; tile += PF) unroll_steps<0, PF>(step, tile, t_end);
+    if (work)
+        for (int tile = t_begin; tile < t_end; tile += PF) unroll_steps<0, PF>(step, tile, t_end);
+    if (fresh_owner) {
+        __shared__ __attribute__((aligned(16))) float fresh_k[DI];
+        score_fresh<KD, NHT, DI>(p, fin, r, b, pos, n_all - 1, q_lds, w_lds, fresh_k, out);
+    }
 }
 
 // Many rows (prefill): a workgroup of eight waves covers eight rows, one per

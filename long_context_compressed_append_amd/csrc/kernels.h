@@ -28,6 +28,13 @@ struct IndexArgs {
     float* logits; int64_t ld;
     // launch plan
     int32_t tiles_per_wave;      // 32-entry tiles per wave (decode) / per workgroup (prefill)
+    // Decode launches ahead of the step's compress_append (fresh != 0, m <= 4):
+    // row r is the one new token of its sequence (token r of the batch), and
+    // an entry that token completes is not in the pool yet, so the kernel
+    // forms it from the remainder ring and the token and scores it itself.
+    int32_t fresh;
+    const int32_t* cu_new; const int32_t* start_pos; int32_t tok_dtype;
+    const void* ik_tok; const float* ik_logit; const void* rem_ik; const float* rem_ik_logit;
 };
 
 // top-k rows hold at most this many visible entries (bitmaps of the row in LDS)
@@ -73,6 +80,10 @@ struct AttnArgs {
 hipError_t launch_compress_append(const CompressArgs& a, int total_new, hipStream_t stream);
 hipError_t launch_index_logits(const IndexArgs& a, int max_entries, hipStream_t stream);
 hipError_t launch_topk_select(TopkArgs a, int max_entries, hipStream_t stream);
+// top-k selection of every row (one launch, rows of up to 32K entries, 16-byte
+// aligned rows) with compress_append of the new bf16 tokens in the same launch
+bool topk_compress_supported(const TopkArgs& a, int max_entries, int tok_dtype);
+hipError_t launch_topk_compress(TopkArgs a, int max_entries, const CompressArgs& c, int total_new, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
 
 // which (dtype, shape) combinations the kernels are built for

@@ -140,12 +140,16 @@ const char* lcca_status_string(lcca_status s) {
     return "unknown status";
 }
 
-lcca_status lcca_compress_append(void* stream, const lcca_pages* pages, const int32_t* cu_new,
-                                 const int32_t* start_pos, int32_t total_new, int32_t tok_dtype, const void* kv_tok,
-                                 const float* kv_logit, const void* ik_tok, const float* ik_logit,
-                                 const lcca_paged_cache* kv, const lcca_paged_cache* ik,
-                                 const lcca_window_cache* win, const lcca_remainder* rem) {
-    g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+// Validation and kernel arguments of each stage, shared by its own entry
+// point and by lcca_decode_select.
+lcca_status prep_compress(const lcca_pages* pages, const int32_t* cu_new, const int32_t* start_pos, int32_t total_new,
+                          int32_t tok_dtype, const void* kv_tok, const float* kv_logit, const void* ik_tok,
+                          const float* ik_logit, const lcca_paged_cache* kv, const lcca_paged_cache* ik,
+                          const lcca_window_cache* win, const lcca_remainder* rem, lcca::CompressArgs& a) {
     lcca_status s;
     if ((s = check_pages(pages))) return s;
     if ((s = check_pool(kv, "kv"))) return s;
@@ -167,7 +171,7 @@ lcca_status lcca_compress_append(void* stream, const lcca_pages* pages, const in
     if (kv->dim > 2048) return fail(LCCA_ERR_UNSUPPORTED, "kv dim %d > 2048", kv->dim);
     if (!rem || rem->tok_dtype != tok_dtype || !rem->kv || !rem->kv_logit || (ik && (!rem->ik || !rem->ik_logit)))
         return fail(LCCA_ERR_INVALID_ARG, "remainder ring missing or of another token dtype");
-    lcca::CompressArgs a{};
+    a = lcca::CompressArgs{};
     a.block_table = pages->block_table; a.max_blocks = pages->max_blocks_per_seq;
     a.cu_new = cu_new; a.start_pos = start_pos; a.batch = pages->batch;
     a.tok_dtype = tok_dtype;
@@ -178,18 +182,19 @@ lcca_status lcca_compress_append(void* stream, const lcca_pages* pages, const in
     a.win_dtype = win ? win->dtype : lcca::DT_NONE; a.win_cap = win ? win->capacity : 1;
     a.win_data = win ? win->data : nullptr; a.win_scale = win ? win->scale : nullptr;
     a.rem_kv = rem->kv; a.rem_ik = rem->ik; a.rem_kv_logit = rem->kv_logit; a.rem_ik_logit = rem->ik_logit;
-    return hip_status(lcca::launch_compress_append(a, total_new, (hipStream_t)stream), "compress_append launch");
+    return LCCA_OK;
 }
 
-lcca_status lcca_index_logits(void* stream, const lcca_pages* pages, const lcca_rows* rows, int32_t q_dtype,
-                              const void* q_idx, int32_t HI, const float* w_idx, float s_I,
-                              const lcca_paged_cache* ik, float* logits, int64_t ld) {
-    g_err[0] = 0;
+// `empty`: nothing to launch (no rows)
+lcca_status prep_index(const lcca_pages* pages, const lcca_rows* rows, int32_t q_dtype, const void* q_idx,
+                       int32_t HI, const float* w_idx, float s_I, const lcca_paged_cache* ik, float* logits,
+                       int64_t ld, lcca::IndexArgs& a, int& max_entries, bool& empty) {
     lcca_status s;
+    empty = false;
     if ((s = check_pages(pages))) return s;
     if ((s = check_pool(ik, "ik"))) return s;
     if ((s = check_rows(rows, ik->ratio_m, pages->max_blocks_per_seq))) return s;
-    if (rows->num_rows == 0) return LCCA_OK;
+    if (rows->num_rows == 0) { empty = true; return LCCA_OK; }
     if (!q_idx || !w_idx || !logits) return fail(LCCA_ERR_INVALID_ARG, "q_idx/w_idx/logits NULL");
     if (HI < 1) return fail(LCCA_ERR_INVALID_ARG, "HI=%d", HI);
     if (ik->dtype == LCCA_FP8_E4M3 && ik->scale)
@@ -197,13 +202,42 @@ lcca_status lcca_index_logits(void* stream, const lcca_pages* pages, const lcca_
     if (!lcca::index_supported(q_dtype, ik->dtype, HI, ik->dim))
         return fail(LCCA_ERR_UNSUPPORTED, "index_logits: q dtype %d, key dtype %d, HI=%d, dim=%d not built", q_dtype,
                     ik->dtype, HI, ik->dim);
-    const int max_entries = (rows->max_pos + 1) / ik->ratio_m;
+    max_entries = (rows->max_pos + 1) / ik->ratio_m;
     if (ld < max_entries) return fail(LCCA_ERR_INVALID_ARG, "ld=%lld < max visible entries %d", (long long)ld, max_entries);
-    lcca::IndexArgs a{};
+    a = lcca::IndexArgs{};
     a.block_table = pages->block_table; a.max_blocks = pages->max_blocks_per_seq;
     a.row_seq = rows->row_seq; a.row_pos = rows->row_pos; a.num_rows = rows->num_rows;
     a.q = q_idx; a.w = w_idx; a.s_I = s_I; a.HI = HI; a.dI = ik->dim; a.m = ik->ratio_m;
     a.key_dtype = ik->dtype; a.keys = ik->data; a.logits = logits; a.ld = ld;
+    return LCCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lcca_status lcca_compress_append(void* stream, const lcca_pages* pages, const int32_t* cu_new,
+                                 const int32_t* start_pos, int32_t total_new, int32_t tok_dtype, const void* kv_tok,
+                                 const float* kv_logit, const void* ik_tok, const float* ik_logit,
+                                 const lcca_paged_cache* kv, const lcca_paged_cache* ik,
+                                 const lcca_window_cache* win, const lcca_remainder* rem) {
+    g_err[0] = 0;
+    lcca::CompressArgs a;
+    const lcca_status s = prep_compress(pages, cu_new, start_pos, total_new, tok_dtype, kv_tok, kv_logit, ik_tok,
+                                        ik_logit, kv, ik, win, rem, a);
+    if (s) return s;
+    return hip_status(lcca::launch_compress_append(a, total_new, (hipStream_t)stream), "compress_append launch");
+}
+
+lcca_status lcca_index_logits(void* stream, const lcca_pages* pages, const lcca_rows* rows, int32_t q_dtype,
+                              const void* q_idx, int32_t HI, const float* w_idx, float s_I,
+                              const lcca_paged_cache* ik, float* logits, int64_t ld) {
+    g_err[0] = 0;
+    lcca::IndexArgs a;
+    int max_entries = 0;
+    bool empty = false;
+    const lcca_status s = prep_index(pages, rows, q_dtype, q_idx, HI, w_idx, s_I, ik, logits, ld, a, max_entries, empty);
+    if (s || empty) return s;
     return hip_status(lcca::launch_index_logits(a, max_entries, (hipStream_t)stream), "index_logits launch");
 }
 
@@ -214,20 +248,24 @@ size_t lcca_topk_workspace_size(const lcca_rows* rows, int32_t ratio_m, int32_t 
     return (size_t)rows->num_rows * (size_t)lcca::topk_cand_stride(max_entries, k) * 8;
 }
 
-lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_m, const float* logits, int64_t ld,
-                             int32_t k, int32_t* topk_idx, void* ws, size_t ws_bytes) {
-    g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+lcca_status prep_topk(const lcca_rows* rows, int32_t ratio_m, const float* logits, int64_t ld, int32_t k,
+                      int32_t* topk_idx, void* ws, size_t ws_bytes, lcca::TopkArgs& a, int& max_entries, bool& empty) {
     lcca_status s;
+    empty = false;
     if (!valid_m(ratio_m)) return fail(LCCA_ERR_INVALID_ARG, "ratio_m=%d", ratio_m);
     if ((s = check_rows(rows, ratio_m, 0))) return s;
     if (k < 1) return fail(LCCA_ERR_INVALID_ARG, "k=%d", k);
-    if (rows->num_rows == 0) return LCCA_OK;
+    if (rows->num_rows == 0) { empty = true; return LCCA_OK; }
     if (!logits || !topk_idx) return fail(LCCA_ERR_INVALID_ARG, "logits/topk_idx NULL");
-    const int max_entries = (rows->max_pos + 1) / ratio_m;
+    max_entries = (rows->max_pos + 1) / ratio_m;
     if (ld < max_entries) return fail(LCCA_ERR_INVALID_ARG, "ld=%lld < max visible entries %d", (long long)ld, max_entries);
     if (max_entries > lcca::kTopkMaxEntries)
         return fail(LCCA_ERR_UNSUPPORTED, "%d visible entries > %d", max_entries, lcca::kTopkMaxEntries);
-    lcca::TopkArgs a{};
+    a = lcca::TopkArgs{};
     a.row_pos = rows->row_pos; a.num_rows = rows->num_rows; a.m = ratio_m;
     a.logits = logits; a.ld = ld; a.k = k; a.idx = topk_idx;
     if (lcca::topk_slices(max_entries) > 1) {
@@ -240,7 +278,62 @@ lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_
         a.cand_key = reinterpret_cast<uint32_t*>(ws);
         a.cand_idx = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + need / 2);
     }
+    return LCCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_m, const float* logits, int64_t ld,
+                             int32_t k, int32_t* topk_idx, void* ws, size_t ws_bytes) {
+    g_err[0] = 0;
+    lcca::TopkArgs a;
+    int max_entries = 0;
+    bool empty = false;
+    const lcca_status s = prep_topk(rows, ratio_m, logits, ld, k, topk_idx, ws, ws_bytes, a, max_entries, empty);
+    if (s || empty) return s;
     return hip_status(lcca::launch_topk_select(a, max_entries, (hipStream_t)stream), "topk_select launch");
+}
+
+lcca_status lcca_decode_select(void* stream, const lcca_pages* pages, const lcca_rows* rows, const int32_t* cu_new,
+                               const int32_t* start_pos, int32_t total_new, int32_t tok_dtype, const void* kv_tok,
+                               const float* kv_logit, const void* ik_tok, const float* ik_logit,
+                               const lcca_paged_cache* kv, const lcca_paged_cache* ik, const lcca_window_cache* win,
+                               const lcca_remainder* rem, int32_t q_dtype, const void* q_idx, int32_t HI,
+                               const float* w_idx, float s_I, float* logits, int64_t ld, int32_t k,
+                               int32_t* topk_idx) {
+    g_err[0] = 0;
+    lcca_status s;
+    if (!ik) return fail(LCCA_ERR_INVALID_ARG, "decode_select needs the indexer pool");
+    lcca::CompressArgs c;
+    if ((s = prep_compress(pages, cu_new, start_pos, total_new, tok_dtype, kv_tok, kv_logit, ik_tok, ik_logit, kv, ik,
+                           win, rem, c)))
+        return s;
+    lcca::IndexArgs ia;
+    int idx_entries = 0;
+    bool empty = false;
+    if ((s = prep_index(pages, rows, q_dtype, q_idx, HI, w_idx, s_I, ik, logits, ld, ia, idx_entries, empty))) return s;
+    if (rows->num_rows != total_new || total_new != pages->batch)
+        return fail(LCCA_ERR_INVALID_ARG, "decode_select: rows=%d, new tokens=%d, batch=%d (one new token and one row "
+                    "per sequence)", rows->num_rows, total_new, pages->batch);
+    if (empty) return LCCA_OK;
+    if ((rows->max_pos + 1) / ik->ratio_m > 32768)
+        return fail(LCCA_ERR_UNSUPPORTED, "decode_select: rows of more than 32,768 visible entries");
+    lcca::TopkArgs ta;
+    int sel_entries = 0;
+    if ((s = prep_topk(rows, ik->ratio_m, logits, ld, k, topk_idx, nullptr, 0, ta, sel_entries, empty))) return s;
+    if (q_dtype != LCCA_BF16 || rows->num_rows >= 64 || ik->ratio_m > 4 ||
+        !lcca::topk_compress_supported(ta, sel_entries, tok_dtype))
+        return fail(LCCA_ERR_UNSUPPORTED, "decode_select: needs bf16 queries and tokens, fewer than 64 rows, ratio_m "
+                    "<= 4, rows of at most 32,768 entries and 16-byte aligned logit rows");
+    ia.fresh = 1;
+    ia.cu_new = cu_new; ia.start_pos = start_pos; ia.tok_dtype = tok_dtype;
+    ia.ik_tok = ik_tok; ia.ik_logit = ik_logit; ia.rem_ik = rem->ik; ia.rem_ik_logit = rem->ik_logit;
+    if ((s = hip_status(lcca::launch_index_logits(ia, idx_entries, (hipStream_t)stream), "index_logits launch")))
+        return s;
+    return hip_status(lcca::launch_topk_compress(ta, sel_entries, c, total_new, (hipStream_t)stream),
+                      "topk_select + compress_append launch");
 }
 
 size_t lcca_sparse_attn_workspace_size(const lcca_rows* rows, int32_t ratio_m, int32_t H, int32_t dim, int32_t d_v,

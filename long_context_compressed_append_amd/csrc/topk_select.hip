@@ -33,6 +33,7 @@
 // layout, for rows of up to 32K entries, 2 copies and bitmaps for 32K
 // entries (~60 KB), which lets two rows share a compute unit and clears and
 // sums a quarter of the copies.
+#include "compress_dev.h"
 #include "device.h"
 #include "kernels.h"
 
@@ -299,18 +300,18 @@ __device__ __forceinline__ void refine(SM& sm, Each each, int top, uint32_t* pre
 //           i.e. smaller entry, first.
 enum Mode : int { kRow = 0, kSlice = 1, kCand = 2 };
 
+// The selection of row r (slice `by` of it in kSlice mode) by one workgroup.
 template <int R, bool Half, bool Vec, int MODE, bool COMPACT>
-__global__ __launch_bounds__(kThreads, COMPACT ? 8 : 4) void topk_kernel(TopkArgs p) {
+__device__ __forceinline__ void topk_body(const TopkArgs& p, int r, int by) {
     static_assert(!COMPACT || (R > 0 && R <= 32 && !Half), "compact layout: rows of up to 32K entries in registers");
     constexpr int COPIES = COMPACT ? 2 : kLeadCopies;
     __shared__ SmemT<COPIES, COMPACT ? kCompactEntries / 32 : kWords> sm;
-    const int r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
     const int n_row = visible_entries(p.row_pos[r], p.m);
     const int k = p.k;
     int32_t* out = p.idx + (int64_t)r * k;
-    const int s0 = MODE == kSlice ? (int)blockIdx.y * p.slice_len : 0;
-    const int64_t c0 = (int64_t)r * p.cand_stride + (MODE == kSlice ? (int64_t)blockIdx.y * k : 0);
+    const int s0 = MODE == kSlice ? by * p.slice_len : 0;
+    const int64_t c0 = (int64_t)r * p.cand_stride + (MODE == kSlice ? (int64_t)by * k : 0);
     int n;
     const float* base;
     if constexpr (MODE == kRow) {
@@ -504,6 +505,29 @@ __global__ __launch_bounds__(kThreads, COMPACT ? 8 : 4) void topk_kernel(TopkArg
     }
 }
 
+template <int R, bool Half, bool Vec, int MODE, bool COMPACT>
+__global__ __launch_bounds__(kThreads, COMPACT ? 8 : 4) void topk_kernel(TopkArgs p) {
+    topk_body<R, Half, Vec, MODE, COMPACT>(p, blockIdx.x, blockIdx.y);
+}
+
+// One decode launch holding the top-k selections of the rows (workgroups
+// 0 .. rows-1, compact layout) and, on the compute units they leave idle,
+// compress_append of the step's new tokens: workgroup rows + i runs item i
+// of compress_append's (token, slice) grid on its first four waves (the
+// other waves exit at once, so its barriers count the four).  Nothing the
+// selections read is written by compress_append.
+template <int R, int TOK>
+__global__ __launch_bounds__(kThreads) void topk_compress_kernel(TopkArgs p, CompressArgs c, int items) {
+    const int w = (int)blockIdx.x;
+    if (w < p.num_rows) {
+        topk_body<R, false, true, kRow, true>(p, w, 0);
+        return;
+    }
+    if ((int)threadIdx.x >= cmp::kThreads) return;
+    const int it = w - p.num_rows;
+    cmp::compress_append_body<TOK>(c, it / items, it % items);
+}
+
 template <int R, bool Vec, int MODE>
 void launch_regs(const TopkArgs& a, bool compact, dim3 grid, hipStream_t stream) {
     if (compact) hipLaunchKernelGGL((topk_kernel<R, false, Vec, MODE, true>), grid, dim3(kThreads), 0, stream, a);
@@ -538,6 +562,26 @@ int topk_slices(int max_entries) {
 
 int64_t topk_cand_stride(int max_entries, int k) {
     return ((int64_t)topk_slices(max_entries) * k + 3) & ~(int64_t)3;
+}
+
+bool topk_compress_supported(const TopkArgs& a, int max_entries, int tok_dtype) {
+    const bool vec = (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 && a.ld % 4 == 0;
+    return vec && max_entries <= 8 * kGroup && tok_dtype == DT_BF16;
+}
+
+hipError_t launch_topk_compress(TopkArgs a, int max_entries, const CompressArgs& c, int total_new, hipStream_t stream) {
+    if (!topk_compress_supported(a, max_entries, c.tok_dtype)) return hipErrorInvalidValue;
+    const int SK = (c.D + cmp::kSliceDims - 1) / cmp::kSliceDims;
+    const int SI = c.ik_data != nullptr ? (c.dI + cmp::kSliceDims - 1) / cmp::kSliceDims : 0;
+    const int items = SK + SI + 1;
+    const dim3 grid((unsigned)(a.num_rows + (int64_t)total_new * items)), block(kThreads);
+    const int rounds = (max_entries + kGroup - 1) / kGroup;
+#define LCCA_TC(R) hipLaunchKernelGGL((topk_compress_kernel<R, DT_BF16>), grid, block, 0, stream, a, c, items);
+    if (rounds <= 2) { LCCA_TC(8) }
+    else if (rounds <= 4) { LCCA_TC(16) }
+    else { LCCA_TC(32) }
+#undef LCCA_TC
+    return hipGetLastError();
 }
 
 hipError_t launch_topk_select(TopkArgs a, int max_entries, hipStream_t stream) {

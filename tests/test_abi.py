@@ -130,3 +130,34 @@ def test_empty_calls_return_ok_without_launching():
     st = L.lcca_sparse_attn_fwd(None, by(pages), by(none), lcca.BF16, 1, 64, 576, 0.04, by(kv), 1, 64, by(win),
                                 lcca.F32, 1, None, None, 0)
     assert st == lcca.OK, L.lcca_last_error()
+
+
+def test_decode_select_rejects_what_it_does_not_cover():
+    """The fused decode call checks its contract and supported shapes on the
+    host and launches nothing when they fail."""
+    L = lcca.lib()
+    by = ctypes.byref
+    pages = lcca._Pages(16, 256, 1)
+    kv = _pool(lcca.BF16, 576, blocks=4096)
+    ik = _pool(lcca.BF16, 128, blocks=4096)
+    win = lcca._WindowCache(lcca.FP8_E4M3, 576, 128, 128, 1, 1)
+    rem = lcca._Remainder(lcca.BF16, 1, 1, 1, 1)
+    rows = lcca._Rows(16, 65535, 1, 1)
+
+    def call(rows=rows, total_new=16, tok=lcca.BF16, ik=ik, rem=rem, ld=16384, pages=pages):
+        return L.lcca_decode_select(None, by(pages), by(rows), 1, 1, total_new, tok, 1, 1, 1, 1, by(kv),
+                                    by(ik) if ik is not None else None, by(win), by(rem), lcca.BF16, 1, 64, 1, 1.0,
+                                    16, ld, 2048, 1)
+
+    # one row and one new token per sequence
+    assert call(total_new=15) == lcca.ERR_INVALID_ARG
+    assert call(rows=lcca._Rows(8, 65535, 1, 1)) == lcca.ERR_INVALID_ARG
+    assert b"one new token" in L.lcca_last_error()
+    # the indexer pool is required
+    assert call(ik=None) == lcca.ERR_INVALID_ARG
+    # fp32 tokens, rows longer than 32,768 entries, logit rows not 16-byte aligned
+    rem32 = lcca._Remainder(lcca.F32, 1, 1, 1, 1)
+    assert call(tok=lcca.F32, rem=rem32) == lcca.ERR_UNSUPPORTED
+    big = lcca._Pages(16, 1024, 1)
+    assert call(rows=lcca._Rows(16, 4 * 40000 - 1, 1, 1), ld=40000, pages=big) == lcca.ERR_UNSUPPORTED
+    assert call(ld=16386) == lcca.ERR_UNSUPPORTED
