@@ -268,11 +268,13 @@ class Workload:
         self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
         tkb = lcca.topk_workspace_size(self.rows, m, c.k) if HI else 0
         self.topk_ws = torch.empty(tkb, dtype=torch.uint8, device=dev) if tkb else None
-        # decode steps with one new token and one row per sequence and rows of
-        # up to 32K entries run compress_append, index_logits and topk_select
-        # as lcca_decode_select (two launches instead of three)
-        self.fused = bool(HI) and c.rows == "last" and all(n == 1 for n in c.n_new) and self.ld <= 32768 \
-            and self.ld % 4 == 0
+        # decode steps with one new token and one row per sequence run
+        # compress_append, index_logits and topk_select as lcca_decode_select
+        # (one launch fewer) when its selection covers the rows: up to 32K
+        # entries, or 16K-entry slices whose top-k candidates total <= 32K
+        slices = 1 if self.ld <= 32768 else -(-self.ld // 16384)
+        self.fused = bool(HI) and c.rows == "last" and all(n == 1 for n in c.n_new) and self.ld % 4 == 0 \
+            and (slices == 1 or slices * c.k <= 32768)
 
     def snapshot_host(self):
         """Copy the initial state to host numpy arrays (for the oracle)."""
@@ -292,7 +294,7 @@ class Workload:
         if self.fused:
             L.decode_select(self.pages, self.rows, self.cu_new, self.start_pos, self.total_new, L.BF16, self.new_kv,
                             self.new_kv_logit, self.new_ik, self.new_ik_logit, kv, ik, win, rem, L.BF16, self.q_idx,
-                            c.HI, self.w_idx, 1.0, self.logits, self.ld, c.k, self.topk)
+                            c.HI, self.w_idx, 1.0, self.logits, self.ld, c.k, self.topk, self.topk_ws)
             if ev is not None:
                 ev[1].record()
             L.sparse_attn_fwd(self.pages, self.rows, L.BF16, self.q, c.H, c.dv, c.scale, kv, self.topk, c.k, win,

@@ -213,7 +213,7 @@ lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_
 
 /*
  * lcca_decode_select -- compress_append, index_logits and topk_select of a
- * decode step in two launches instead of three.
+ * decode step with one launch fewer.
  *
  * [P1 "Kako funkcionira optimizacija KV cachea?" and P3 "Vykon neprinesl
  * jeden kernel": the same three stages as above.]  Every sequence appends
@@ -229,10 +229,15 @@ lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_
  * lcca_topk_select called in that order.  A row whose sequence does not
  * satisfy the device-side part of the contract (cu_new, start_pos) gets a
  * NaN logit for the entry its token completes.
- * Arguments: those of the three calls (topk_select without workspace).
+ * Rows of more than 32,768 visible entries take three launches: the top-k
+ * of each slice (as in lcca_topk_select, with the same workspace), then the
+ * selection among the candidates beside compress_append.
+ * Arguments: those of the three calls; ws / ws_bytes as for
+ * lcca_topk_select (lcca_topk_workspace_size).
  * Supported: BF16 queries and tokens, an indexer pool, fewer than 64 rows,
- * ratio_m <= 4, at most 32,768 visible entries per row, ld % 4 == 0 and
- * 16-byte aligned logits; otherwise LCCA_ERR_UNSUPPORTED and nothing runs.
+ * ratio_m <= 4, ld % 4 == 0 and 16-byte aligned logits, and rows of at most
+ * 32,768 visible entries or with at most 32,768 slice candidates (16,384-entry
+ * slices times k); otherwise LCCA_ERR_UNSUPPORTED and nothing runs.
  */
 lcca_status lcca_decode_select(void* stream, const lcca_pages* pages, const lcca_rows* rows,
                                const int32_t* cu_new, const int32_t* start_pos, int32_t total_new,
@@ -241,7 +246,8 @@ lcca_status lcca_decode_select(void* stream, const lcca_pages* pages, const lcca
                                const lcca_paged_cache* kv, const lcca_paged_cache* ik,
                                const lcca_window_cache* win, const lcca_remainder* rem,
                                int32_t q_dtype, const void* q_idx, int32_t HI, const float* w_idx, float s_I,
-                               float* logits, int64_t ld, int32_t k, int32_t* topk_idx);
+                               float* logits, int64_t ld, int32_t k, int32_t* topk_idx,
+                               void* ws, size_t ws_bytes);
 
 /*
  * lcca_sparse_attn_fwd -- attention over selected entries plus the window.

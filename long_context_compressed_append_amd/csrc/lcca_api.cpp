@@ -302,7 +302,7 @@ lcca_status lcca_decode_select(void* stream, const lcca_pages* pages, const lcca
                                const lcca_paged_cache* kv, const lcca_paged_cache* ik, const lcca_window_cache* win,
                                const lcca_remainder* rem, int32_t q_dtype, const void* q_idx, int32_t HI,
                                const float* w_idx, float s_I, float* logits, int64_t ld, int32_t k,
-                               int32_t* topk_idx) {
+                               int32_t* topk_idx, void* ws, size_t ws_bytes) {
     g_err[0] = 0;
     lcca_status s;
     if (!ik) return fail(LCCA_ERR_INVALID_ARG, "decode_select needs the indexer pool");
@@ -318,15 +318,14 @@ lcca_status lcca_decode_select(void* stream, const lcca_pages* pages, const lcca
         return fail(LCCA_ERR_INVALID_ARG, "decode_select: rows=%d, new tokens=%d, batch=%d (one new token and one row "
                     "per sequence)", rows->num_rows, total_new, pages->batch);
     if (empty) return LCCA_OK;
-    if ((rows->max_pos + 1) / ik->ratio_m > 32768)
-        return fail(LCCA_ERR_UNSUPPORTED, "decode_select: rows of more than 32,768 visible entries");
     lcca::TopkArgs ta;
     int sel_entries = 0;
-    if ((s = prep_topk(rows, ik->ratio_m, logits, ld, k, topk_idx, nullptr, 0, ta, sel_entries, empty))) return s;
+    if ((s = prep_topk(rows, ik->ratio_m, logits, ld, k, topk_idx, ws, ws_bytes, ta, sel_entries, empty))) return s;
     if (q_dtype != LCCA_BF16 || rows->num_rows >= 64 || ik->ratio_m > 4 ||
         !lcca::topk_compress_supported(ta, sel_entries, tok_dtype))
         return fail(LCCA_ERR_UNSUPPORTED, "decode_select: needs bf16 queries and tokens, fewer than 64 rows, ratio_m "
-                    "<= 4, rows of at most 32,768 entries and 16-byte aligned logit rows");
+                    "<= 4, 16-byte aligned logit rows, and rows of at most 32,768 entries or slices whose k "
+                    "candidates total at most 32,768");
     ia.fresh = 1;
     ia.cu_new = cu_new; ia.start_pos = start_pos; ia.tok_dtype = tok_dtype;
     ia.ik_tok = ik_tok; ia.ik_logit = ik_logit; ia.rem_ik = rem->ik; ia.rem_ik_logit = rem->ik_logit;

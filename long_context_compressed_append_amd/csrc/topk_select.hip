@@ -510,17 +510,18 @@ __global__ __launch_bounds__(kThreads, COMPACT ? 8 : 4) void topk_kernel(TopkArg
     topk_body<R, Half, Vec, MODE, COMPACT>(p, blockIdx.x, blockIdx.y);
 }
 
-// One decode launch holding the top-k selections of the rows (workgroups
-// 0 .. rows-1, compact layout) and, on the compute units they leave idle,
-// compress_append of the step's new tokens: workgroup rows + i runs item i
-// of compress_append's (token, slice) grid on its first four waves (the
-// other waves exit at once, so its barriers count the four).  Nothing the
-// selections read is written by compress_append.
-template <int R, int TOK>
+// One decode launch holding the rows' one-launch top-k selections (kRow) or
+// the selections among their slices' candidates (kCand) in workgroups
+// 0 .. rows-1 with the compact layout, and, on the compute units they leave
+// idle, compress_append of the step's new tokens: workgroup rows + i runs
+// item i of compress_append's (token, slice) grid on its first four waves
+// (the other waves exit at once, so its barriers count the four).  Nothing
+// the selections read is written by compress_append.
+template <int R, int MODE, int TOK>
 __global__ __launch_bounds__(kThreads) void topk_compress_kernel(TopkArgs p, CompressArgs c, int items) {
     const int w = (int)blockIdx.x;
     if (w < p.num_rows) {
-        topk_body<R, false, true, kRow, true>(p, w, 0);
+        topk_body<R, false, true, MODE, true>(p, w, 0);
         return;
     }
     if ((int)threadIdx.x >= cmp::kThreads) return;
@@ -564,9 +565,16 @@ int64_t topk_cand_stride(int max_entries, int k) {
     return ((int64_t)topk_slices(max_entries) * k + 3) & ~(int64_t)3;
 }
 
+// Entries the compact-layout selection of the fused launch takes: the row
+// itself (one launch) or its slices' candidates (two launches).
+static int64_t fused_sel_entries(int max_entries, int k) {
+    const int ns = topk_slices(max_entries);
+    return ns == 1 ? (int64_t)max_entries : (int64_t)ns * k;
+}
+
 bool topk_compress_supported(const TopkArgs& a, int max_entries, int tok_dtype) {
     const bool vec = (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 && a.ld % 4 == 0;
-    return vec && max_entries <= 8 * kGroup && tok_dtype == DT_BF16;
+    return vec && fused_sel_entries(max_entries, a.k) <= 8 * kGroup && tok_dtype == DT_BF16;
 }
 
 hipError_t launch_topk_compress(TopkArgs a, int max_entries, const CompressArgs& c, int total_new, hipStream_t stream) {
@@ -575,8 +583,20 @@ hipError_t launch_topk_compress(TopkArgs a, int max_entries, const CompressArgs&
     const int SI = c.ik_data != nullptr ? (c.dI + cmp::kSliceDims - 1) / cmp::kSliceDims : 0;
     const int items = SK + SI + 1;
     const dim3 grid((unsigned)(a.num_rows + (int64_t)total_new * items)), block(kThreads);
-    const int rounds = (max_entries + kGroup - 1) / kGroup;
-#define LCCA_TC(R) hipLaunchKernelGGL((topk_compress_kernel<R, DT_BF16>), grid, block, 0, stream, a, c, items);
+    const int ns = topk_slices(max_entries);
+    if (ns > 1) {
+        // each slice's top-k first (as in launch_topk_select), then the
+        // selection among the candidates beside compress_append
+        a.nslices = ns;
+        a.slice_len = kTopkSlice;
+        launch_sel<true, kSlice>(a, kTopkSlice, dim3(a.num_rows, ns), stream);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int rounds = (int)((fused_sel_entries(max_entries, a.k) + kGroup - 1) / kGroup);
+#define LCCA_TC(R)                                                                                         \
+    if (ns == 1) hipLaunchKernelGGL((topk_compress_kernel<R, kRow, DT_BF16>), grid, block, 0, stream, a, c, items); \
+    else hipLaunchKernelGGL((topk_compress_kernel<R, kCand, DT_BF16>), grid, block, 0, stream, a, c, items);
     if (rounds <= 2) { LCCA_TC(8) }
     else if (rounds <= 4) { LCCA_TC(16) }
     else { LCCA_TC(32) }

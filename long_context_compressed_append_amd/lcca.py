@@ -72,7 +72,7 @@ def lib():
         L.lcca_topk_select.argtypes = [P, PR, i32, P, i64, i32, P, P, sz]
         L.lcca_sparse_attn_fwd.argtypes = [P, PP, PR, i32, P, i32, i32, f32, PC, P, i32, PW, i32, P, P, P, sz]
         L.lcca_decode_select.argtypes = [P, PP, PR, P, P, i32, i32, P, P, P, P, PC, PC, PW, PM,
-                                         i32, P, i32, P, f32, P, i64, i32, P]
+                                         i32, P, i32, P, f32, P, i64, i32, P, P, sz]
         L.lcca_sparse_attn_workspace_size.argtypes = [PR, i32, i32, i32, i32, i32, i32, i32]
         L.lcca_sparse_attn_workspace_size.restype = sz
         L.lcca_topk_workspace_size.argtypes = [PR, i32, i32]
@@ -205,14 +205,16 @@ def topk_select(rows: Rows, ratio_m: int, logits, ld: int, k: int, topk_idx, ws=
 
 def decode_select(pages: Pages, rows: Rows, cu_new, start_pos, total_new: int, tok_dtype: int, kv_tok, kv_logit,
                   ik_tok, ik_logit, kv: PagedCache, ik: PagedCache, win: Optional[WindowCache], rem: Remainder,
-                  q_dtype: int, q_idx, HI: int, w_idx, s_I: float, logits, ld: int, k: int, topk_idx, stream=None):
+                  q_dtype: int, q_idx, HI: int, w_idx, s_I: float, logits, ld: int, k: int, topk_idx, ws=None,
+                  stream=None):
     """compress_append + index_logits + topk_select of a decode step (one new
-    token and one row per sequence) in two launches."""
+    token and one row per sequence) with one launch fewer."""
     _check(lib().lcca_decode_select(
         _stream(stream), ctypes.byref(pages.c()), ctypes.byref(rows.c()), _ptr(cu_new), _ptr(start_pos),
         int(total_new), tok_dtype, _ptr(kv_tok), _ptr(kv_logit), _ptr(ik_tok), _ptr(ik_logit), ctypes.byref(kv.c()),
         ctypes.byref(ik.c()), _ref(win.c() if win else None), ctypes.byref(rem.c()), q_dtype, _ptr(q_idx), HI,
-        _ptr(w_idx), float(s_I), _ptr(logits), int(ld), k, _ptr(topk_idx)))
+        _ptr(w_idx), float(s_I), _ptr(logits), int(ld), k, _ptr(topk_idx), _ptr(ws),
+        ws.numel() * ws.element_size() if ws is not None else 0))
 
 
 def sparse_attn_workspace_size(rows: Rows, ratio_m: int, H: int, dim: int, d_v: int, k: int, topk_given: bool,

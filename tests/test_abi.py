@@ -147,7 +147,7 @@ def test_decode_select_rejects_what_it_does_not_cover():
     def call(rows=rows, total_new=16, tok=lcca.BF16, ik=ik, rem=rem, ld=16384, pages=pages):
         return L.lcca_decode_select(None, by(pages), by(rows), 1, 1, total_new, tok, 1, 1, 1, 1, by(kv),
                                     by(ik) if ik is not None else None, by(win), by(rem), lcca.BF16, 1, 64, 1, 1.0,
-                                    16, ld, 2048, 1)
+                                    16, ld, 2048, 1, None, 0)
 
     # one row and one new token per sequence
     assert call(total_new=15) == lcca.ERR_INVALID_ARG
@@ -155,9 +155,17 @@ def test_decode_select_rejects_what_it_does_not_cover():
     assert b"one new token" in L.lcca_last_error()
     # the indexer pool is required
     assert call(ik=None) == lcca.ERR_INVALID_ARG
-    # fp32 tokens, rows longer than 32,768 entries, logit rows not 16-byte aligned
+    # fp32 tokens, logit rows not 16-byte aligned
     rem32 = lcca._Remainder(lcca.F32, 1, 1, 1, 1)
     assert call(tok=lcca.F32, rem=rem32) == lcca.ERR_UNSUPPORTED
-    big = lcca._Pages(16, 1024, 1)
-    assert call(rows=lcca._Rows(16, 4 * 40000 - 1, 1, 1), ld=40000, pages=big) == lcca.ERR_UNSUPPORTED
     assert call(ld=16386) == lcca.ERR_UNSUPPORTED
+    # rows of more than 32K entries: the slices' workspace is required, and
+    # their candidates (slices x k) must fit the compact selection
+    big = lcca._Pages(16, 1024, 1)
+    assert call(rows=lcca._Rows(16, 4 * 40000 - 1, 1, 1), ld=40000, pages=big) == lcca.ERR_WORKSPACE
+    huge = lcca._Pages(16, 4096, 1)
+    rows_long = lcca._Rows(16, 4 * 262143 - 1, 1, 1)
+    need = L.lcca_topk_workspace_size(by(rows_long), 4, 4096)
+    st = L.lcca_decode_select(None, by(huge), by(rows_long), 1, 1, 16, lcca.BF16, 1, 1, 1, 1, by(kv), by(ik), by(win),
+                              by(rem), lcca.BF16, 1, 64, 1, 1.0, 16, 262144, 4096, 1, 16, need)
+    assert st == lcca.ERR_UNSUPPORTED       # 16 slices x 4096 candidates > 32,768

@@ -1,5 +1,5 @@
 """lcca_decode_select (compress_append + index_logits + topk_select of a
-decode step in two launches) against the three separate calls on identical
+decode step with one launch fewer) against the three separate calls on identical
 device copies of the same state: pools, window and remainder rings and the
 logits of every entry already in the pool bit for bit; the logit of the entry
 a row's own token completes (formed and scored inside the indexer launch)
@@ -25,6 +25,8 @@ CASES = {
     "csa_all_fresh": synth.shrink(S["csa_64k"], "ds_fresh", (8191, 4095, 1023, 3), (1, 1, 1, 1), k=256),
     # FP8 indexer keys, MXFP4 pool
     "lp_fp8_keys": synth.shrink(S["lp_512k"], "ds_lp", (8191, 5002, 6003), (1, 1, 1), k=512),
+    # rows over 32K entries: slices' top-k first, then the candidates beside compress_append
+    "lp_two_launch": synth.shrink(S["lp_512k"], "ds_lp_long", (140003, 131071, 70000), (1, 1, 1), k=2048),
 }
 
 
@@ -49,9 +51,11 @@ def _fused(gs, ld):
     nr = len(gs.st.row_seq)
     lg = torch.zeros((nr, ld), dtype=torch.float32, device=DEV)
     idx = torch.empty((nr, c.k), dtype=torch.int32, device=DEV)
+    wsb = lcca.topk_workspace_size(gs.rows, c.m, c.k)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV) if wsb else None
     lcca.decode_select(gs.pages, gs.rows, gs.cu_new, gs.start_pos, int(gs.st.cu_new[-1]), gs.tok_ldt, gs.new_kv,
                        gs.new_kv_logit, gs.new_ik, gs.new_ik_logit, gs.kv, gs.ik, gs.win, gs.rem, gs.q_dt, gs.q_idx,
-                       c.HI, gs.w_idx, 1.0, lg, ld, c.k, idx)
+                       c.HI, gs.w_idx, 1.0, lg, ld, c.k, idx, ws)
     return lg, idx
 
 
