@@ -108,3 +108,25 @@ def test_decode_select_equals_the_three_calls(name):
     assert torch.equal(idx_a, idx_b)
     want = O.topk(st.row_pos, m, la.astype(np.float64), c.k)
     assert np.array_equal(idx_a.cpu().numpy(), want)
+
+
+def test_rows_that_are_not_the_new_tokens_get_nan():
+    """The device-side half of the contract: when a sequence does not append
+    exactly one token at its row's position (here sequence 0 appends none and
+    sequence 1 two, which the host cannot see), the entry a row's token
+    would complete gets a NaN logit instead of a logit of stale pool bytes."""
+    cfg = synth.shrink(S["csa_64k"], "ds_contract", (9999, 3003), (1, 1), k=256)
+    _say("decode_select contract check")
+    st = State(cfg)
+    ld = _ld(cfg)
+    gs = GpuState(st)
+    gs.cu_new = torch.tensor([0, 0, 2], dtype=torch.int32, device=DEV)
+    lg, _ = _fused(gs, ld)
+    torch.cuda.synchronize()
+    pos = st.row_pos.astype(np.int64)
+    n_r = (pos + 1) // cfg.m
+    assert ((pos + 1) % cfg.m == 0).all()
+    lh = lg.cpu().numpy()
+    for r in range(len(pos)):
+        assert np.isnan(lh[r, n_r[r] - 1])
+        assert np.isfinite(lh[r, : n_r[r] - 1]).all()
