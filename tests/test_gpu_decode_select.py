@@ -25,6 +25,9 @@ CASES = {
     "csa_all_fresh": synth.shrink(S["csa_64k"], "ds_fresh", (8191, 4095, 1023, 3), (1, 1, 1, 1), k=256),
     # FP8 indexer keys, MXFP4 pool
     "lp_fp8_keys": synth.shrink(S["lp_512k"], "ds_lp", (8191, 5002, 6003), (1, 1, 1), k=512),
+    # indexers of 128 heads x 64 dims (one dimension per lane) and 32 x 256 (four)
+    "idx128x64": synth.shrink(S["csa_64k"], "ds_i128", (4095, 3001, 2047), (1, 1, 1), k=256, HI=128, dI=64),
+    "idx32x256": synth.shrink(S["csa_64k"], "ds_i32", (4095, 3001, 2047), (1, 1, 1), k=256, HI=32, dI=256),
     # rows over 32K entries: slices' top-k first, then the candidates beside compress_append
     "lp_two_launch": synth.shrink(S["lp_512k"], "ds_lp_long", (140003, 131071, 70000), (1, 1, 1), k=2048),
 }
