@@ -275,6 +275,9 @@ class Workload:
         slices = 1 if self.ld <= 32768 else -(-self.ld // 16384)
         self.fused = bool(HI) and c.rows == "last" and all(n == 1 for n in c.n_new) and self.ld % 4 == 0 \
             and (slices == 1 or slices * c.k <= 32768)
+        # its workspace: allocated zeroed once, left zeroed by every call
+        self.ds_ws = torch.zeros(max(lcca.decode_select_workspace_size(self.rows, m, c.k), 16), dtype=torch.uint8,
+                                 device=dev) if self.fused else None
 
     def snapshot_host(self):
         """Copy the initial state to host numpy arrays (for the oracle)."""
@@ -294,7 +297,7 @@ class Workload:
         if self.fused:
             L.decode_select(self.pages, self.rows, self.cu_new, self.start_pos, self.total_new, L.BF16, self.new_kv,
                             self.new_kv_logit, self.new_ik, self.new_ik_logit, kv, ik, win, rem, L.BF16, self.q_idx,
-                            c.HI, self.w_idx, 1.0, self.logits, self.ld, c.k, self.topk, self.topk_ws)
+                            c.HI, self.w_idx, 1.0, self.logits, self.ld, c.k, self.topk, self.ds_ws)
             if ev is not None:
                 ev[1].record()
             L.sparse_attn_fwd(self.pages, self.rows, L.BF16, self.q, c.H, c.dv, c.scale, kv, self.topk, c.k, win,

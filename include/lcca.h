@@ -232,8 +232,16 @@ lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_
  * Rows of more than 32,768 visible entries take three launches: the top-k
  * of each slice (as in lcca_topk_select, with the same workspace), then the
  * selection among the candidates beside compress_append.
- * Arguments: those of the three calls; ws / ws_bytes as for
- * lcca_topk_select (lcca_topk_workspace_size).
+ * With rows of up to 32,768 visible entries the indexer launch also counts,
+ * per row, the logits whose order keys share each leading 12-bit digit, and
+ * the selection starts from those counts instead of counting itself.
+ * Arguments: those of the three calls, and
+ *   ws   device workspace of at least lcca_decode_select_workspace_size()
+ *        bytes for the same rows, ratio_m and k, 16-byte aligned.  Rows of
+ *        up to 32,768 entries: the counts, uint32 [num_rows][4096], which
+ *        must be all zero before the first call on this workspace; every
+ *        call leaves them zero (the selection clears what it reads).  Longer
+ *        rows: the slices' candidates, as for lcca_topk_select.
  * Supported: BF16 queries and tokens, an indexer pool, fewer than 64 rows,
  * ratio_m <= 4, ld % 4 == 0 and 16-byte aligned logits, and rows of at most
  * 32,768 visible entries or with at most 32,768 slice candidates (16,384-entry
@@ -248,6 +256,7 @@ lcca_status lcca_decode_select(void* stream, const lcca_pages* pages, const lcca
                                int32_t q_dtype, const void* q_idx, int32_t HI, const float* w_idx, float s_I,
                                float* logits, int64_t ld, int32_t k, int32_t* topk_idx,
                                void* ws, size_t ws_bytes);
+size_t lcca_decode_select_workspace_size(const lcca_rows* rows, int32_t ratio_m, int32_t k);
 
 /*
  * lcca_sparse_attn_fwd -- attention over selected entries plus the window.

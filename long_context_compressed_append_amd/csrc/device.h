@@ -142,4 +142,14 @@ __device__ inline float wave_sum(float v) {
 
 __device__ inline int visible_entries(int pos, int m) { return (pos + 1) / m; }
 
+// Order-preserving u32 key of a logit (-0.0 folded onto +0.0): larger
+// logits have larger keys.  The top-k selection ranks by it, and the
+// decode indexer counts the leading kTopkLeadBits bits of its logits' keys
+// with it.
+__device__ inline uint32_t order_key(float x) {
+    uint32_t u = __float_as_uint(x);
+    if (u == 0x80000000u) u = 0u;                               // -0.0 ties +0.0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 }  // namespace lcca

@@ -133,7 +133,8 @@ struct FreshIn {
 // not the one new token of its sequence gets a NaN logit.
 template <int KD, int NHT, int DI>
 __device__ __forceinline__ void score_fresh(const IndexArgs& p, const FreshIn<DI>& in, int r, int b, int pos, int e,
-                                            const uint8_t* q_lds, const float* w_lds, float* k_lds, float* out) {
+                                            const uint8_t* q_lds, const float* w_lds, float* k_lds, float* out,
+                                            uint32_t* lead) {
     constexpr int DPL = DI / 64;
     constexpr int QROWB = DI * 2 + 16;
     const int m = p.m, lane = threadIdx.x & 63;
@@ -188,7 +189,11 @@ __device__ __forceinline__ void score_fresh(const IndexArgs& p, const FreshIn<DI
         }
     }
     l = wave_sum(l);
-    if (lane == 0) out[e] = ok ? l : __builtin_nanf("");
+    if (lane == 0) {
+        const float v_out = ok ? l : __builtin_nanf("");
+        out[e] = v_out;
+        if (lead) atomicAdd(&lead[order_key(v_out) >> (32 - kTopkLeadBits)], 1u);
+    }
 }
 
 template <int KD, int NHT, int DI>
@@ -264,6 +269,14 @@ index_mfma_kernel(IndexArgs p) {
         if (u < QUNITS) *reinterpret_cast<u32x4*>(&q_lds[(u / UPR) * QROWB + (u % UPR) * 16]) = qv[i];
     }
     if ((int)threadIdx.x < NHT * 32) w_lds[threadIdx.x] = wraw * p.s_I;
+    // leading-digit counts of this workgroup's logits (fused decode launch),
+    // added to the row's counts in memory at the end
+    constexpr int kLeadBins = 1 << kTopkLeadBits;
+    __shared__ __attribute__((aligned(16))) uint32_t lead_lds[kLeadBins];
+    uint32_t* const lead = p.lead_hist ? lead_lds : nullptr;
+    if (lead)
+        for (int i = (int)threadIdx.x; i < kLeadBins / 4; i += kThreads)
+            reinterpret_cast<u32x4*>(lead_lds)[i] = u32x4{0u, 0u, 0u, 0u};
     int pb_next = pbs[PF - 1];
     RawKey<KD, KS> kr[PF];
     if (work) {
@@ -309,13 +322,26 @@ index_mfma_kernel(IndexArgs p) {
             }
         l += __shfl_xor(l, 32);
         const int e = tile * 32 + j;
-        if (g == 0 && e < n) out[e] = l;
+        if (g == 0 && e < n) {
+            out[e] = l;
+            if (lead) atomicAdd(&lead_lds[order_key(l) >> (32 - kTopkLeadBits)], 1u);
+        }
     };
     if (work)
         for (int tile = t_begin; tile < t_end; tile += PF) unroll_steps<0, PF>(step, tile, t_end);
     if (fresh_owner) {
         __shared__ __attribute__((aligned(16))) float fresh_k[DI];
-        score_fresh<KD, NHT, DI>(p, fin, r, b, pos, n_all - 1, q_lds, w_lds, fresh_k, out);
+        score_fresh<KD, NHT, DI>(p, fin, r, b, pos, n_all - 1, q_lds, w_lds, fresh_k, out, lead);
+    }
+    if (lead) {
+        __syncthreads();
+        uint32_t* const row_lead = p.lead_hist + (int64_t)r * kLeadBins;
+        for (int i = (int)threadIdx.x; i < kLeadBins / 4; i += kThreads) {
+            const u32x4 c = reinterpret_cast<const u32x4*>(lead_lds)[i];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (c[q]) atomicAdd(&row_lead[4 * i + q], c[q]);
+        }
     }
 }
 

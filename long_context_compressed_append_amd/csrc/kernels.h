@@ -35,8 +35,14 @@ struct IndexArgs {
     int32_t fresh;
     const int32_t* cu_new; const int32_t* start_pos; int32_t tok_dtype;
     const void* ik_tok; const float* ik_logit; const void* rem_ik; const float* rem_ik_logit;
+    // non-null: the decode kernel also adds, per row, how many of its logits
+    // have each leading kTopkLeadBits-bit key digit ([rows][2^kTopkLeadBits],
+    // zero before the launch; the top-k selection reads and clears it)
+    uint32_t* lead_hist;
 };
 
+// leading key bits of the top-k's first (histogram) pass
+constexpr int kTopkLeadBits = 12;
 // top-k rows hold at most this many visible entries (bitmaps of the row in LDS)
 constexpr int kTopkMaxEntries = 1 << 18;
 // rows longer than kTopkSplitAbove entries are selected in two launches:
@@ -52,6 +58,10 @@ struct TopkArgs {
     uint32_t* cand_key; int32_t* cand_idx;    // [rows][cand_stride]
     int64_t cand_stride;
     int32_t nslices, slice_len;
+    // one-launch selections (kRow) of the fused decode launch: the rows'
+    // leading-digit counts from the indexer, read instead of counted, then
+    // cleared for the next call
+    uint32_t* lead_hist;
 };
 
 // slices of a row of max_entries visible entries (1: one launch) and the

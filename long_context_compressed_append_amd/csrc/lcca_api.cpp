@@ -296,6 +296,13 @@ lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_
     return hip_status(lcca::launch_topk_select(a, max_entries, (hipStream_t)stream), "topk_select launch");
 }
 
+size_t lcca_decode_select_workspace_size(const lcca_rows* rows, int32_t ratio_m, int32_t k) {
+    if (!rows || rows->num_rows <= 0 || !valid_m(ratio_m) || k < 1 || rows->max_pos < 0) return 0;
+    const int max_entries = (rows->max_pos + 1) / ratio_m;
+    if (lcca::topk_slices(max_entries) > 1) return lcca_topk_workspace_size(rows, ratio_m, k);
+    return (size_t)rows->num_rows * ((size_t)1 << lcca::kTopkLeadBits) * sizeof(uint32_t);
+}
+
 lcca_status lcca_decode_select(void* stream, const lcca_pages* pages, const lcca_rows* rows, const int32_t* cu_new,
                                const int32_t* start_pos, int32_t total_new, int32_t tok_dtype, const void* kv_tok,
                                const float* kv_logit, const void* ik_tok, const float* ik_logit,
@@ -326,6 +333,17 @@ lcca_status lcca_decode_select(void* stream, const lcca_pages* pages, const lcca
         return fail(LCCA_ERR_UNSUPPORTED, "decode_select: needs bf16 queries and tokens, fewer than 64 rows, ratio_m "
                     "<= 4, 16-byte aligned logit rows, and rows of at most 32,768 entries or slices whose k "
                     "candidates total at most 32,768");
+    if (lcca::topk_slices(sel_entries) == 1) {
+        // one-launch selections: the indexer counts the logits' leading key
+        // digits into the workspace, the selection reads and clears them
+        const size_t need = lcca_decode_select_workspace_size(rows, ik->ratio_m, k);
+        if (!ws || ws_bytes < need)
+            return fail(LCCA_ERR_WORKSPACE, "decode_select needs %zu workspace bytes (%zu given)", need,
+                        ws ? ws_bytes : (size_t)0);
+        if (reinterpret_cast<uintptr_t>(ws) & 15)
+            return fail(LCCA_ERR_INVALID_ARG, "decode_select workspace not 16-byte aligned");
+        ia.lead_hist = ta.lead_hist = reinterpret_cast<uint32_t*>(ws);
+    }
     ia.fresh = 1;
     ia.cu_new = cu_new; ia.start_pos = start_pos; ia.tok_dtype = tok_dtype;
     ia.ik_tok = ik_tok; ia.ik_logit = ik_logit; ia.rem_ik = rem->ik; ia.rem_ik_logit = rem->ik_logit;

@@ -44,7 +44,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kGroup = 4 * kThreads;            // entries per load round
-constexpr int kLeadBits = 12;
+constexpr int kLeadBits = kTopkLeadBits;
 constexpr int kLeadShift = 32 - kLeadBits;
 constexpr int kLeadBins = 1 << kLeadBits;
 constexpr int kLeadCopies = 8;                  // lane & 7 picks the copy
@@ -71,12 +71,6 @@ struct alignas(16) SmemT {
     uint32_t cand_n, sel_digit, sel_above;
 };
 constexpr int kCompactEntries = 32768;
-
-__device__ inline uint32_t order_key(float x) {
-    uint32_t u = __float_as_uint(x);
-    if (u == 0x80000000u) u = 0u;                               // -0.0 ties +0.0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 // OR of x over each aligned group of 8 lanes (DPP: swap within pairs, within
 // quads, then mirror the two quads of the group).
@@ -324,7 +318,18 @@ __device__ __forceinline__ void topk_body(const TopkArgs& p, int r, int by) {
         n = p.nslices * k;
         base = reinterpret_cast<const float*>(p.cand_key + c0);
     }
+    // leading-digit counts of this row from the indexer (fused decode launch)
+    // (cleared once read: the clearing store is issued only after the counts
+    // have arrived)
+    u32x4* const hist = MODE == kRow && p.lead_hist ? reinterpret_cast<u32x4*>(p.lead_hist + (int64_t)r * kLeadBins)
+                                                    : nullptr;
+    u32x4 hist_v = u32x4{0u, 0u, 0u, 0u};
+    if (hist) hist_v = hist[tid];
     if (MODE == kSlice ? n <= k : n_row <= k) {
+        if (hist) {
+            asm volatile("" ::"v"(hist_v[0]) : "memory");        // the counts have arrived
+            hist[tid] = u32x4{0u, 0u, 0u, 0u};
+        }
         if constexpr (MODE == kSlice) {
             for (int i = tid; i < k; i += kThreads) {
                 p.cand_key[c0 + i] = i < n ? order_key(base[i]) : 0u;
@@ -350,6 +355,15 @@ __device__ __forceinline__ void topk_body(const TopkArgs& p, int r, int by) {
     Keys<R, Half, Vec, MODE == kCand> K;
     K.init(base, n);
 
+    if (hist) {
+        // 1. the counts the indexer took (4096 bins = 1024 threads x 4)
+        static_assert(kLeadBins == 4 * kThreads, "one 16-byte chunk of counts per thread");
+        reinterpret_cast<u32x4*>(sm.cnt)[tid] = hist_v;
+        asm volatile("" ::"v"(hist_v[0]) : "memory");            // the counts have arrived
+        hist[tid] = u32x4{0u, 0u, 0u, 0u};
+        if (tid == 0) sm.cand_n = 0;
+        __syncthreads();
+    } else {
     {
         u32x4* z = reinterpret_cast<u32x4*>(sm.u.lead);
         for (int i = tid; i < kLeadBins * COPIES / 4; i += kThreads) z[i] = u32x4{0u, 0u, 0u, 0u};
@@ -385,6 +399,7 @@ __device__ __forceinline__ void topk_body(const TopkArgs& p, int r, int by) {
         }
     }
     __syncthreads();
+    }
     {
         // thread t owns bins 4095-4t .. 4092-4t, so thread order is descending bins
         const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.cnt[kLeadBins - 4 - 4 * tid]);

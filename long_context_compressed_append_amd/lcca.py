@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "liblcca.so")
 
 EXPORTED = ("lcca_compress_append", "lcca_index_logits", "lcca_topk_select", "lcca_sparse_attn_fwd",
             "lcca_sparse_attn_workspace_size", "lcca_topk_workspace_size", "lcca_status_string", "lcca_last_error",
-            "lcca_version", "lcca_decode_select")
+            "lcca_version", "lcca_decode_select", "lcca_decode_select_workspace_size")
 
 
 class LccaError(RuntimeError):
@@ -77,6 +77,8 @@ def lib():
         L.lcca_sparse_attn_workspace_size.restype = sz
         L.lcca_topk_workspace_size.argtypes = [PR, i32, i32]
         L.lcca_topk_workspace_size.restype = sz
+        L.lcca_decode_select_workspace_size.argtypes = [PR, i32, i32]
+        L.lcca_decode_select_workspace_size.restype = sz
         for n in ("lcca_compress_append", "lcca_index_logits", "lcca_topk_select", "lcca_sparse_attn_fwd",
                   "lcca_decode_select"):
             getattr(L, n).restype = i32
@@ -201,6 +203,12 @@ def topk_workspace_size(rows: Rows, ratio_m: int, k: int) -> int:
 def topk_select(rows: Rows, ratio_m: int, logits, ld: int, k: int, topk_idx, ws=None, stream=None):
     _check(lib().lcca_topk_select(_stream(stream), ctypes.byref(rows.c()), ratio_m, _ptr(logits), int(ld), k,
                                   _ptr(topk_idx), _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0))
+
+
+def decode_select_workspace_size(rows: Rows, ratio_m: int, k: int) -> int:
+    """Bytes of decode_select's workspace; allocate it zeroed (torch.zeros)
+    once and reuse it: every call leaves its counts zero."""
+    return lib().lcca_decode_select_workspace_size(ctypes.byref(rows.c()), ratio_m, k)
 
 
 def decode_select(pages: Pages, rows: Rows, cu_new, start_pos, total_new: int, tok_dtype: int, kv_tok, kv_logit,

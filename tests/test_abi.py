@@ -155,6 +155,13 @@ def test_decode_select_rejects_what_it_does_not_cover():
     assert b"one new token" in L.lcca_last_error()
     # the indexer pool is required
     assert call(ik=None) == lcca.ERR_INVALID_ARG
+    # the workspace of the leading-digit counts: missing, or not 16-byte aligned
+    assert call() == lcca.ERR_WORKSPACE
+    need = L.lcca_decode_select_workspace_size(by(rows), 4, 2048)
+    assert need == 16 * 4096 * 4
+    st = L.lcca_decode_select(None, by(pages), by(rows), 1, 1, 16, lcca.BF16, 1, 1, 1, 1, by(kv), by(ik), by(win),
+                              by(rem), lcca.BF16, 1, 64, 1, 1.0, 16, 16384, 2048, 1, 8, need)
+    assert st == lcca.ERR_INVALID_ARG and b"aligned" in L.lcca_last_error()
     # fp32 tokens, logit rows not 16-byte aligned
     rem32 = lcca._Remainder(lcca.F32, 1, 1, 1, 1)
     assert call(tok=lcca.F32, rem=rem32) == lcca.ERR_UNSUPPORTED

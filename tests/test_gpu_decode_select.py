@@ -54,11 +54,16 @@ def _fused(gs, ld):
     nr = len(gs.st.row_seq)
     lg = torch.zeros((nr, ld), dtype=torch.float32, device=DEV)
     idx = torch.empty((nr, c.k), dtype=torch.int32, device=DEV)
-    wsb = lcca.topk_workspace_size(gs.rows, c.m, c.k)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV) if wsb else None
-    lcca.decode_select(gs.pages, gs.rows, gs.cu_new, gs.start_pos, int(gs.st.cu_new[-1]), gs.tok_ldt, gs.new_kv,
-                       gs.new_kv_logit, gs.new_ik, gs.new_ik_logit, gs.kv, gs.ik, gs.win, gs.rem, gs.q_dt, gs.q_idx,
-                       c.HI, gs.w_idx, 1.0, lg, ld, c.k, idx, ws)
+    ws = torch.zeros(lcca.decode_select_workspace_size(gs.rows, c.m, c.k), dtype=torch.uint8, device=DEV)
+    for _ in range(2):
+        # twice on the same workspace: the counts it holds must be back to
+        # zero after each call (the step is idempotent at fixed positions)
+        lcca.decode_select(gs.pages, gs.rows, gs.cu_new, gs.start_pos, int(gs.st.cu_new[-1]), gs.tok_ldt,
+                           gs.new_kv, gs.new_kv_logit, gs.new_ik, gs.new_ik_logit, gs.kv, gs.ik, gs.win, gs.rem,
+                           gs.q_dt, gs.q_idx, c.HI, gs.w_idx, 1.0, lg, ld, c.k, idx, ws)
+        if c.max_entries <= 32768:
+            torch.cuda.synchronize()
+            assert not ws.any(), "leading-digit counts left in the workspace"
     return lg, idx
 
 
