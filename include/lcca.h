@@ -224,9 +224,12 @@ lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_
  * the kernel from the remainder ring and the token with compress_append's
  * arithmetic, so it is scored from exactly the codes the pool receives.
  * Launch 2 runs the top-k selection of every row and, beside it, the whole
- * of compress_append for the new tokens.  Pools, rings, logits and top-k
- * lists equal those of lcca_compress_append, lcca_index_logits and
- * lcca_topk_select called in that order.  A row whose sequence does not
+ * of compress_append for the new tokens.  Pools, rings and the logits of
+ * the entries already in the pool equal those of lcca_compress_append,
+ * lcca_index_logits and lcca_topk_select called in that order; the logit of
+ * the entry a row's token completes is summed in another order (within the
+ * indexer's fp32 bound of theirs); the top-k lists are lcca_topk_select's on
+ * these logits.  A row whose sequence does not
  * satisfy the device-side part of the contract (cu_new, start_pos) gets a
  * NaN logit for the entry its token completes.
  * Rows of more than 32,768 visible entries take three launches: the top-k
