@@ -12,7 +12,9 @@
 // again for each pass over them.
 //   1. Histogram of the leading 12 key bits (sign, exponent, 3 mantissa
 //      bits) in LDS; a block scan from the top bin finds the bin holding the
-//      k-th largest key and how many keys lie above it.
+//      k-th largest key and how many keys lie above it.  In the fused decode
+//      launch the indexer has already counted the row's keys per leading
+//      digit; the selection loads those counts (and clears them) instead.
 //   2. One pass marks every key of a higher bin in a bitmap of the row
 //      (each 8-lane group assembles its 32-bit word with DPP moves and
 //      stores it, no atomics) and collects the keys of the boundary bin,
