@@ -43,8 +43,14 @@
  *   g % E.
  *
  *   Window ring (lcca_window_cache): data [batch][capacity][dim]; token at
- *   position t of sequence b lives in slot t % capacity.  FP8 windows carry
- *   a float scale per slot [batch][capacity]: code = RNE(x / s) with
+ *   position t of sequence b lives in slot t % capacity.  A query row at
+ *   position p reads slots of positions p - window + 1 .. p, so every row
+ *   attended after a chunk of n new tokens was appended needs those
+ *   positions still in the ring: capacity >= window + n - 1 when rows
+ *   inside the chunk are attended (chunked prefill), capacity >= window when
+ *   only the chunk's last position is (decode).  A smaller ring gives early
+ *   rows of the chunk the later tokens that overwrote their slots, silently.
+ *   FP8 windows carry a float scale per slot [batch][capacity]: code = RNE(x / s) with
  *   s = max|x| / 448 (1 if the token is zero).  A window of full vectors of
  *   the most recent positions sits beside the compressed entries [P1 "Kako
  *   funkcionira optimizacija KV cachea?"; FP8, 128 positions: P3 "Proc je
@@ -91,7 +97,7 @@ typedef struct {
 typedef struct {
     int32_t dtype;        /* LCCA_F32, LCCA_BF16 or LCCA_FP8_E4M3                */
     int32_t dim;          /* elements per token (= the pool's dim)               */
-    int32_t capacity;     /* slots per sequence (>= window)                      */
+    int32_t capacity;     /* slots per sequence (>= window; see the ring rule above) */
     int32_t window;       /* positions attended: max(0, p-window+1) .. p          */
     void*   data;         /* device [batch][capacity][row bytes]                 */
     float*  scale;        /* device [batch][capacity]; FP8 only                  */
@@ -109,6 +115,14 @@ typedef struct {
     const int32_t* row_seq;     /* device [num_rows] sequence of each row        */
     const int32_t* row_pos;     /* device [num_rows] position of each row        */
 } lcca_rows;
+
+/* The remainder ring's four arrays may be carved from one allocation of
+ * lcca_remainder_bytes() bytes: kv at offset 0, then ik, kv_logit and ik_logit,
+ * each starting at the previous array's end rounded up to 256 bytes (ik and
+ * ik_logit are absent, 0 bytes, when ik_dim is 0).  Returns 0 for an invalid
+ * argument (batch < 1, ratio_m not dividing 256, kv_dim < 1, ik_dim < 0, a
+ * token dtype other than F32 or BF16). */
+size_t lcca_remainder_bytes(int32_t batch, int32_t ratio_m, int32_t kv_dim, int32_t ik_dim, int32_t tok_dtype);
 
 typedef struct {
     int32_t tok_dtype;          /* LCCA_F32 or LCCA_BF16 (the token dtype)       */
@@ -133,7 +147,8 @@ typedef struct {
  * encoded to the pool dtype and stored as entry g.  Group tokens older than
  * the chunk are read from the remainder ring; new tokens of a still
  * incomplete group are stored into it.  The last min(n_b, capacity) new
- * tokens are encoded into the window ring.
+ * tokens are encoded into the window ring (rows later attended inside the
+ * chunk need capacity >= window + n_b - 1, see the window ring above).
  *   cu_new     device int32 [batch+1], cu_new[0] = 0, nondecreasing
  *   start_pos  device int32 [batch]
  *   total_new  host: cu_new[batch] (the grid has one block per new token)
@@ -204,7 +219,9 @@ lcca_status lcca_index_logits(void* stream, const lcca_pages* pages, const lcca_
  *             candidates (the same set and order).  Too small a workspace
  *             returns LCCA_ERR_WORKSPACE.
  * Rows of more than 2^18 visible entries ((max_pos + 1) / ratio_m) return
- * LCCA_ERR_UNSUPPORTED (the selection keeps a bitmap of the row in LDS).
+ * LCCA_ERR_UNSUPPORTED (the selection keeps a bitmap of the row in LDS), and
+ * so do rows over 32,768 entries whose slices' candidates (slices times k)
+ * exceed 2^18: the candidates' selection keeps the same bitmap.
  */
 size_t lcca_topk_workspace_size(const lcca_rows* rows, int32_t ratio_m, int32_t k);
 lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_m,
@@ -269,7 +286,9 @@ size_t lcca_decode_select_workspace_size(const lcca_rows* rows, int32_t ratio_m,
  * vectors.]  For row r (sequence b, position p) the keys are the dequantised
  * entries listed in topk_idx[r][0..k) (entries < 0 or >= n_r are skipped;
  * topk_idx NULL means every visible entry g < n_r), followed by the window
- * tokens max(0, p - win->window + 1) .. p.  One vector is key and value
+ * tokens max(0, p - win->window + 1) .. p (read from ring slots t % capacity,
+ * so they must not have been overwritten since: see the window ring above).
+ * One vector is key and value
  * (value = its first d_v elements).  For each head h:
  *     s_j = sm_scale * q[r][h] . k_j,
  *     out[r][h] = sum_j softmax(s)_j v_j,    lse[r][h] = ln sum_j exp(s_j)

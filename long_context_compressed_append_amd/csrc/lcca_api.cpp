@@ -127,6 +127,19 @@ extern "C" {
 
 const char* lcca_last_error(void) { return g_err; }
 
+size_t lcca_remainder_bytes(int32_t batch, int32_t ratio_m, int32_t kv_dim, int32_t ik_dim, int32_t tok_dtype) {
+    if (batch < 1 || !valid_m(ratio_m) || kv_dim < 1 || ik_dim < 0 || (tok_dtype != LCCA_F32 && tok_dtype != LCCA_BF16))
+        return 0;
+    const size_t esz = tok_dtype == LCCA_F32 ? 4 : 2;
+    const size_t slots = (size_t)batch * ratio_m;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    size_t n = up(slots * kv_dim * esz);                  // kv
+    n += up(slots * ik_dim * esz);                        // ik
+    n += ik_dim ? up(slots * sizeof(float)) : slots * sizeof(float);   // kv_logit
+    if (ik_dim) n += slots * sizeof(float);               // ik_logit
+    return n;
+}
+
 const char* lcca_version(void) { return "lcca 0.1.0 (gfx950)"; }
 
 const char* lcca_status_string(lcca_status s) {
@@ -265,6 +278,12 @@ lcca_status prep_topk(const lcca_rows* rows, int32_t ratio_m, const float* logit
     if (ld < max_entries) return fail(LCCA_ERR_INVALID_ARG, "ld=%lld < max visible entries %d", (long long)ld, max_entries);
     if (max_entries > lcca::kTopkMaxEntries)
         return fail(LCCA_ERR_UNSUPPORTED, "%d visible entries > %d", max_entries, lcca::kTopkMaxEntries);
+    // the candidates' selection of long rows keeps a bitmap of its slices x k
+    // candidates in the same LDS space as a row's
+    if (lcca::topk_slices(max_entries) > 1 &&
+        (int64_t)lcca::topk_slices(max_entries) * k > (int64_t)lcca::kTopkMaxEntries)
+        return fail(LCCA_ERR_UNSUPPORTED, "%d slices x k=%d candidates > %d", lcca::topk_slices(max_entries), k,
+                    lcca::kTopkMaxEntries);
     a = lcca::TopkArgs{};
     a.row_pos = rows->row_pos; a.num_rows = rows->num_rows; a.m = ratio_m;
     a.logits = logits; a.ld = ld; a.k = k; a.idx = topk_idx;

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "liblcca.so")
 
 EXPORTED = ("lcca_compress_append", "lcca_index_logits", "lcca_topk_select", "lcca_sparse_attn_fwd",
             "lcca_sparse_attn_workspace_size", "lcca_topk_workspace_size", "lcca_status_string", "lcca_last_error",
-            "lcca_version", "lcca_decode_select", "lcca_decode_select_workspace_size")
+            "lcca_version", "lcca_decode_select", "lcca_decode_select_workspace_size", "lcca_remainder_bytes")
 
 
 class LccaError(RuntimeError):
@@ -79,6 +79,8 @@ def lib():
         L.lcca_topk_workspace_size.restype = sz
         L.lcca_decode_select_workspace_size.argtypes = [PR, i32, i32]
         L.lcca_decode_select_workspace_size.restype = sz
+        L.lcca_remainder_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.lcca_remainder_bytes.restype = sz
         for n in ("lcca_compress_append", "lcca_index_logits", "lcca_topk_select", "lcca_sparse_attn_fwd",
                   "lcca_decode_select"):
             getattr(L, n).restype = i32
@@ -170,6 +172,29 @@ class Remainder:
 
     def c(self):
         return _Remainder(self.tok_dtype, _ptr(self.kv), _ptr(self.ik), _ptr(self.kv_logit), _ptr(self.ik_logit))
+
+
+def remainder_bytes(batch: int, ratio_m: int, kv_dim: int, ik_dim: int, tok_dtype: int) -> int:
+    return lib().lcca_remainder_bytes(batch, ratio_m, kv_dim, ik_dim, tok_dtype)
+
+
+def remainder_in(buf: torch.Tensor, batch: int, ratio_m: int, kv_dim: int, ik_dim: int, tok_dtype: int) -> Remainder:
+    """A Remainder whose four arrays are views of one uint8 buffer of
+    remainder_bytes() bytes, at the offsets include/lcca.h states."""
+    need = remainder_bytes(batch, ratio_m, kv_dim, ik_dim, tok_dtype)
+    if need == 0 or buf.numel() * buf.element_size() < need:
+        raise LccaError(ERR_INVALID_ARG, "remainder buffer of %d bytes (need %d)" % (buf.numel(), need))
+    esz = 4 if tok_dtype == F32 else 2
+    slots = batch * ratio_m
+    up = lambda x: (x + 255) // 256 * 256
+    o_ik = up(slots * kv_dim * esz)
+    o_kl = o_ik + up(slots * ik_dim * esz)
+    o_il = o_kl + up(slots * 4)
+    kv = buf[:slots * kv_dim * esz]
+    ik = buf[o_ik:o_ik + slots * ik_dim * esz] if ik_dim else None
+    kl = buf[o_kl:o_kl + slots * 4].view(torch.float32)
+    il = buf[o_il:o_il + slots * 4].view(torch.float32) if ik_dim else None
+    return Remainder(tok_dtype, kv, kl, ik, il)
 
 
 def _ref(x):

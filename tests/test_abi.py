@@ -70,6 +70,16 @@ def test_invalid_arguments_rejected_before_launch():
     assert b"workspace" in L.lcca_last_error()
     ok = lcca._Rows(1, 4 * (1 << 18) - 1, 1, 1)
     assert L.lcca_topk_select(None, by(ok), 4, 1, 1 << 18, 0, 1, None, 0) == lcca.ERR_INVALID_ARG   # k < 1 only
+    # long rows whose slices' candidates (16 slices x k) exceed the 2^18 bits of
+    # the candidates' selection bitmaps, with an ample workspace
+    need = L.lcca_topk_workspace_size(by(ok), 4, 16385)
+    assert L.lcca_topk_select(None, by(ok), 4, 1, 1 << 18, 16385, 1, 16, need) == lcca.ERR_UNSUPPORTED
+    assert b"candidates" in L.lcca_last_error()
+    # at the limit (16 x 16384 = 2^18) the call gets past validation; the
+    # misaligned workspace pointer then stops it before any launch
+    need = L.lcca_topk_workspace_size(by(ok), 4, 16384)
+    assert L.lcca_topk_select(None, by(ok), 4, 1, 1 << 18, 16384, 1, 8, need) == lcca.ERR_INVALID_ARG
+    assert b"aligned" in L.lcca_last_error()
     # attention: workspace too small (16 rows of 64K context need key splits)
     kv = _pool(lcca.BF16, 576, blocks=4096)
     win = lcca._WindowCache(lcca.FP8_E4M3, 576, 128, 128, 1, 1)
@@ -176,3 +186,32 @@ def test_decode_select_rejects_what_it_does_not_cover():
     st = L.lcca_decode_select(None, by(huge), by(rows_long), 1, 1, 16, lcca.BF16, 1, 1, 1, 1, by(kv), by(ik), by(win),
                               by(rem), lcca.BF16, 1, 64, 1, 1.0, 16, 262144, 4096, 1, 16, need)
     assert st == lcca.ERR_UNSUPPORTED       # 16 slices x 4096 candidates > 32,768
+
+
+def test_remainder_bytes_layout():
+    """lcca_remainder_bytes: kv, ik, kv_logit, ik_logit carved from one
+    buffer, each starting on a 256-byte boundary."""
+    L = lcca.lib()
+    up = lambda x: (x + 255) // 256 * 256
+    # 16 sequences, m = 4, bf16 tokens of 576 + 128 dims
+    want = up(16 * 4 * 576 * 2) + up(16 * 4 * 128 * 2) + up(16 * 4 * 4) + 16 * 4 * 4
+    assert L.lcca_remainder_bytes(16, 4, 576, 128, lcca.BF16) == want
+    # no indexer stream: kv and kv_logit only
+    assert L.lcca_remainder_bytes(4, 128, 576, 0, lcca.BF16) == up(4 * 128 * 576 * 2) + 4 * 128 * 4
+    # fp32 tokens
+    assert L.lcca_remainder_bytes(1, 4, 128, 32, lcca.F32) == up(4 * 128 * 4) + up(4 * 32 * 4) + up(16) + 16
+    # invalid arguments: 0
+    for args in ((0, 4, 576, 128, lcca.BF16), (1, 3, 576, 128, lcca.BF16), (1, 4, 0, 128, lcca.BF16),
+                 (1, 4, 576, -1, lcca.BF16), (1, 4, 576, 128, lcca.FP8_E4M3)):
+        assert L.lcca_remainder_bytes(*args) == 0, args
+    import torch
+    buf = torch.zeros(want, dtype=torch.uint8)
+    rem = lcca.remainder_in(buf, 16, 4, 576, 128, lcca.BF16)
+    base = buf.data_ptr()
+    assert rem.kv.data_ptr() == base
+    assert rem.ik.data_ptr() - base == up(16 * 4 * 576 * 2)
+    assert rem.kv_logit.data_ptr() - base == up(16 * 4 * 576 * 2) + up(16 * 4 * 128 * 2)
+    assert rem.ik_logit.data_ptr() - rem.kv_logit.data_ptr() == up(16 * 4 * 4)
+    assert rem.ik_logit.data_ptr() + rem.ik_logit.numel() * 4 - base == want
+    with pytest.raises(lcca.LccaError):
+        lcca.remainder_in(buf[:want - 1], 16, 4, 576, 128, lcca.BF16)
