@@ -144,7 +144,7 @@ def stage_work(c):
 class Workload:
     """Device tensors of one step of a workload and R rotated cache copies."""
 
-    def __init__(self, name, torch, lcca, synth, cold=True):
+    def __init__(self, name, torch, lcca, synth, cold=True, out_dtype="f32"):
         self.name = name
         self.cfg = c = synth.CONFIGS[name]
         self.torch, self.lcca = torch, lcca
@@ -262,7 +262,7 @@ class Workload:
             self.copies.append((kv, ik, win, rem))
         self.logits = torch.empty((self.nrows, max(self.ld, 1)), dtype=torch.float32, device=dev) if HI else None
         self.topk = torch.empty((self.nrows, max(c.k, 1)), dtype=torch.int32, device=dev) if HI else None
-        self.out = torch.empty((self.nrows, H, c.dv), dtype=torch.bfloat16, device=dev)
+        self.set_out_dtype(out_dtype)
         self.lse = torch.empty((self.nrows, H), dtype=torch.float32, device=dev)
         wsb = lcca.sparse_attn_workspace_size(self.rows, m, H, D, c.dv, c.k, bool(HI), c.window)
         self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
@@ -278,6 +278,14 @@ class Workload:
         # its workspace: allocated zeroed once, left zeroed by every call
         self.ds_ws = torch.zeros(max(lcca.decode_select_workspace_size(self.rows, m, c.k), 16), dtype=torch.uint8,
                                  device=dev) if self.fused else None
+
+    def set_out_dtype(self, out_dtype):
+        """Attention output in fp32 ("f32") or bf16 ("bf16")."""
+        torch, c = self.torch, self.cfg
+        self.out_dtype = out_dtype
+        self.out_ldt = self.lcca.F32 if out_dtype == "f32" else self.lcca.BF16
+        self.out = torch.empty((self.nrows, c.H, c.dv), dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16,
+                               device="cuda")
 
     def snapshot_host(self):
         """Copy the initial state to host numpy arrays (for the oracle)."""
@@ -301,7 +309,7 @@ class Workload:
             if ev is not None:
                 ev[1].record()
             L.sparse_attn_fwd(self.pages, self.rows, L.BF16, self.q, c.H, c.dv, c.scale, kv, self.topk, c.k, win,
-                              L.BF16, self.out, self.lse, self.ws)
+                              self.out_ldt, self.out, self.lse, self.ws)
             if ev is not None:
                 ev[4].record()
             return
@@ -322,7 +330,7 @@ class Workload:
         if ev is not None:
             ev[3].record()
         L.sparse_attn_fwd(self.pages, self.rows, L.BF16, self.q, c.H, c.dv, c.scale, kv, idx,
-                          c.k if idx is not None else 0, win, L.BF16, self.out, self.lse, self.ws)
+                          c.k if idx is not None else 0, win, self.out_ldt, self.out, self.lse, self.ws)
         if ev is not None:
             ev[4].record()
 
@@ -430,18 +438,26 @@ def cpu_baseline(wl, rows, dt, passes):
                       "%.1f s in all" % (len(rows), wl.nrows, wl.name, passes, dt, dt * passes)}
 
 
+# BASELINE bounds for bf16/FP8 paths (MXFP4 pools: max-abs 5e-2)
+PARITY_BOUNDS = {"max_abs": 2e-2, "mean_abs": 2e-3, "rel_l2": 1e-2}
+
+
 def parity_summary(wl, rows, out_ref, idx_ref):
-    """Device output (bf16) against the oracle's fp64 output on the sampled
-    rows; `max_abs_excess` discounts the output's own bf16 rounding (half an
-    ulp of the oracle's value), which the tests also allow."""
+    """Device output against the oracle's fp64 output on the sampled rows, on
+    the raw values.  A bf16 output also reports `max_abs_excess`, the error
+    beyond its own rounding (half an ulp of the oracle's value)."""
     import numpy as np
     got = wl.out[rows].float().cpu().numpy().astype(np.float64)
     d = np.abs(got - out_ref)
-    a = np.abs(out_ref)
-    half_ulp = 0.5 * 2.0 ** (np.floor(np.log2(np.where(a > 0, a, 1.0))).clip(-126) - 7)
-    res = {"rows": len(rows), "max_abs": float(d.max()), "mean_abs": float(d.mean()),
-           "max_abs_excess": float(np.maximum(d - half_ulp, 0).max()),
+    res = {"rows": len(rows), "out_dtype": wl.out_dtype, "max_abs": float(d.max()), "mean_abs": float(d.mean()),
            "rel_l2": float(np.linalg.norm(got - out_ref) / max(np.linalg.norm(out_ref), 1e-30))}
+    if wl.out_dtype == "bf16":
+        a = np.abs(out_ref)
+        half_ulp = 0.5 * 2.0 ** (np.floor(np.log2(np.where(a > 0, a, 1.0))).clip(-126) - 7)
+        res["max_abs_excess"] = float(np.maximum(d - half_ulp, 0).max())
+    bounds = dict(PARITY_BOUNDS, max_abs=5e-2 if wl.cfg.kv_dtype == "mxfp4" else PARITY_BOUNDS["max_abs"])
+    res["bounds"] = bounds
+    res["within_bounds"] = bool(all(res[k] <= v for k, v in bounds.items()))
     if idx_ref is not None:
         gi = wl.topk[rows].cpu().numpy()
         res["topk_set_diff"] = int(sum(len(set(gi[i].tolist()) ^ set(idx_ref[i].tolist())) // 2
@@ -484,9 +500,9 @@ def measured_traffic(workload, stage):
     return None
 
 
-def run_workload(torch, lcca, synth, name, args, with_oracle, cpu_seconds=0.0):
+def run_workload(torch, lcca, synth, name, args, with_oracle, cpu_seconds=0.0, bf16_variant=False):
     log("workload", name, "building")
-    wl = Workload(name, torch, lcca, synth, cold=True)
+    wl = Workload(name, torch, lcca, synth, cold=True, out_dtype="f32")
     torch.cuda.synchronize()
     if with_oracle:
         wl.snapshot_host()
@@ -533,6 +549,17 @@ def run_workload(torch, lcca, synth, name, args, with_oracle, cpu_seconds=0.0):
         res["parity"] = parity_summary(wl, rows, out_ref, idx_ref)
         baseline = cpu_baseline(wl, rows, dt, passes)
         log(name, "oracle %.2f s x %d; parity %s" % (dt, passes, json.dumps(res["parity"])))
+    if bf16_variant:
+        # the same step with bf16 attention outputs (fp16 split partials)
+        wl.set_out_dtype("bf16")
+        for i in range(args.warmup):
+            wl.step(i)
+        t = plain_steps(torch, wl, steps)
+        v = {"rows_per_s": round(wl.nrows / (t / 1e3), 1), "ms_per_step": round(t, 5)}
+        if with_oracle:
+            v["parity"] = parity_summary(wl, rows, out_ref, idx_ref)
+        res["bf16_out"] = v
+        log(name, "bf16 outputs", json.dumps(v))
     log(name, json.dumps({k: v for k, v in res.items() if k != "stages"}))
     del wl
     torch.cuda.empty_cache()
@@ -551,6 +578,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the headline workload's oracle pass for at least this long (CPU baseline)")
     ap.add_argument("--no-hot", action="store_true")
+    ap.add_argument("--no-bf16-variant", action="store_true",
+                    help="skip the headline step with bf16 attention outputs (reported beside the fp32 one)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run 10 device copies of BYTES bytes (a reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -584,7 +613,8 @@ def main():
     with torch.cuda.stream(stream):
         for name in names:
             results[name], baselines[name] = run_workload(torch, lcca, synth, name, args, not args.no_oracle,
-                                                          args.cpu_seconds if name == names[0] else 0.0)
+                                                          args.cpu_seconds if name == names[0] else 0.0,
+                                                          bf16_variant=name == names[0] and not args.no_bf16_variant)
 
     head = names[0]
     r = results[head]
@@ -602,13 +632,14 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": head, "batch": cfg.batch, "context": cfg.total_len(0), "ratio_m": cfg.m,
                    "top_k": cfg.k, "window": cfg.window, "kv": cfg.kv_dtype, "window_cache": cfg.win_dtype,
-                   "heads": cfg.H, "dim": cfg.D, "cold_cache_copies": r["R"]},
+                   "heads": cfg.H, "dim": cfg.D, "out": "f32", "cold_cache_copies": r["R"]},
         "step_hbm_GB/s": round(r["step_GB/s"], 1), "step_hbm_frac": round(r["step_hbm_frac"], 4),
         "roofline": roof,
         "cpu_baseline": baselines.get(head),
         "stages": r["stages"],
         "hot_rows_per_s": round(r["hot_rows_per_s"], 1) if r["hot_rows_per_s"] else None,
         "parity": r.get("parity"),
+        "bf16_out": r.get("bf16_out"),
         "also": {n: {"rows_per_s": round(v["rows_per_s"], 1), "ms_per_step": round(v["ms_per_step"], 5),
                      "rows": v["rows"], "step_hbm_GB/s": round(v["step_GB/s"], 1),
                      "step_hbm_frac": round(v["step_hbm_frac"], 4), "step_TFLOP/s": round(v["step_TFLOP/s"], 2),

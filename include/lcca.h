@@ -295,8 +295,8 @@ size_t lcca_decode_select_workspace_size(const lcca_rows* rows, int32_t ratio_m,
  * with all keys in ONE softmax.  Keys are split across workgroups and the
  * partial softmax states are merged (max, rescaled sums); for BF16 outputs
  * a split's O / sum is kept as fp16 (11 significant bits against the
- * output's 8) with a power-of-two range scale per split, head and quarter of
- * d_v, for F32 outputs in fp32.
+ * output's 8) with a power-of-two range scale per split, head and 32 value
+ * dims, for F32 outputs in fp32.
  *   q        device [num_rows][H][kv->dim] of q_dtype (F32 with F32 cache;
  *            BF16 otherwise)
  *   out      device [num_rows][H][d_v] of out_dtype (F32 or BF16)
@@ -306,9 +306,8 @@ size_t lcca_decode_select_workspace_size(const lcca_rows* rows, int32_t ratio_m,
  *            that size is 0)
  * BF16 path: kv dtype BF16 or MXFP4, window BF16 or FP8, H a multiple of 64
  * (64 heads per workgroup), (dim, d_v) in {(576, 576), (576, 512), (128, 128)};
- * with top-k indices, positions below 2^20 (the block-table range a
- * workgroup caches); an FP8 window's scale array must be given.  Other
- * combinations return LCCA_ERR_UNSUPPORTED.
+ * an FP8 window's scale array must be given.  Other combinations return
+ * LCCA_ERR_UNSUPPORTED.
  */
 lcca_status lcca_sparse_attn_fwd(void* stream, const lcca_pages* pages, const lcca_rows* rows,
                                  int32_t q_dtype, const void* q, int32_t H, int32_t d_v, float sm_scale,

@@ -140,6 +140,18 @@ __device__ inline float wave_sum(float v) {
     return v;
 }
 
+// max of v over lanes l, l ^ 16, l ^ 32 and l ^ 48, on the VALU (gfx950's
+// v_permlane32_swap exchanges the upper 32 lanes of one operand with the
+// lower 32 of the other, v_permlane16_swap the odd 16-lane rows of one with
+// the even rows of the other; with both operands holding v, the two results
+// hold the two partners' values, in some order).
+__device__ inline float max_across_rows(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ inline int visible_entries(int pos, int m) { return (pos + 1) / m; }
 
 // Order-preserving u32 key of a logit (-0.0 folded onto +0.0): larger

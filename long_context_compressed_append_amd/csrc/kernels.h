@@ -82,9 +82,9 @@ struct AttnArgs {
     float* part_o;     // [rows][nsplit][H][d_v]   (nsplit > 1, fp32 partial states)
     float* part_ml;    // [rows][nsplit][2][H]
     // bf16 outputs: partial O / l as fp16 with a power-of-two range scale
-    // per (split, quarter of d_v, head); part_o is then unused
+    // per (split, 32 value dims, head); part_o is then unused
     uint16_t* part_h;  // [rows][nsplit][H][d_v]
-    float* part_sc;    // [rows][nsplit][4][H]
+    float* part_sc;    // [rows][nsplit][d_v / 32][H]
 };
 
 hipError_t launch_compress_append(const CompressArgs& a, int total_new, hipStream_t stream);

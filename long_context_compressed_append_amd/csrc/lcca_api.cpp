@@ -17,7 +17,6 @@ int attn_f32_max_keys();
 int attn_max_split_tiles();
 int attn_max_splits();
 int attn_tile_keys();
-int attn_max_table_blocks();
 }
 
 namespace {
@@ -402,9 +401,6 @@ lcca_status lcca_sparse_attn_fwd(void* stream, const lcca_pages* pages, const lc
     const int m = kv->ratio_m;
     const bool f32 = q_dtype == LCCA_F32;
     AttnPlan plan = attn_plan(rows->num_rows, rows->max_pos, m, H, d_v, k, topk_idx != nullptr, win->window);
-    if (!f32 && topk_idx && ((int64_t)rows->max_pos + 1) / 256 + 1 > lcca::attn_max_table_blocks())
-        return fail(LCCA_ERR_UNSUPPORTED, "sparse_attn: positions up to %d need more than %d block-table entries",
-                    rows->max_pos, lcca::attn_max_table_blocks());
     if (!f32 && plan.split_tiles > lcca::attn_max_split_tiles())
         return fail(LCCA_ERR_UNSUPPORTED, "sparse_attn: %d key tiles per split needed (> %d)", plan.split_tiles,
                     lcca::attn_max_split_tiles());

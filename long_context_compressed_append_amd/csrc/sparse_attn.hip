@@ -15,28 +15,28 @@
 // tokens.  So every 32-key tile holds either pool entries or window tokens.
 //
 // bf16/MFMA path.  A workgroup = (row, range of tiles, group of 64 heads)
-// with eight waves: two groups of 32 heads, each over four quarters of the
-// shared-KV dimension.  Pipeline per workgroup:
-//   prologue: the block-table range and the top-k indices the split needs are
-//     copied to LDS, so resolving a key to its storage row is two LDS reads;
+// with four waves, one per SIMD: two groups of 32 heads, each over two halves
+// of the shared-KV dimension.  Pipeline per workgroup:
+//   prologue: the storage row of every selected slot of the split is resolved
+//     through the top-k list and the block table once, into LDS;
 //   loads:    each tile's raw bytes (bf16, FP8 or MXFP4 + E8M0 scales) are
-//     loaded into registers P tiles ahead of their use (static register sets,
-//     loop unrolled by P), converted exactly to bf16 and written to one of two
-//     padded LDS stages; two barriers per tile;
-//   compute:  partial S^T = K Q^T over a quarter of D with MFMA 16x16x32
-//     (A = keys from LDS, B = the wave's queries, resident in VGPRs), summed
-//     through LDS by the wave that owns eight of the group's heads; online
-//     softmax in the exp2 domain; O^T += V^T P^T over a quarter of the value
-//     dims with V^T read from the same LDS tile by ds_read_b64_tr_b16
-//     (K = V); P enters as bf16 hi + lo so the value weights keep 16
-//     significant bits; FP8 window scales multiply the scores and are folded
-//     into P.
+//     loaded into registers two tiles ahead of their LDS stage (two static
+//     register sets, loop unrolled by two), converted exactly to bf16 and
+//     written to one of three padded LDS stages; one barrier per tile;
+//   compute:  partial S^T = K Q^T over a half of D with MFMA 32x32x16 (A =
+//     keys from LDS, B = the wave's queries, resident in VGPRs); the two
+//     halves of a head group exchange partials through LDS and both form the
+//     same full scores; online softmax in the exp2 domain in registers; O^T +=
+//     V^T P^T over a half of the value dims with V^T read from the same LDS
+//     tile by ds_read_b64_tr_b16 (K = V) and P taken straight from the score
+//     registers as a bf16 hi + lo pair (16 significant bits); FP8 window
+//     scales multiply the scores and are folded into P.
 // Keys are split across workgroups when the rows alone cannot fill the GPU;
 // the partial (max, sum, O) states go to the workspace and a merge kernel
 // (one workgroup per row and head) combines them.  For fp32 outputs O stays
 // fp32; for bf16 outputs O / sum is stored as fp16 (11 significant bits,
 // eight times finer than the output's rounding) with a power-of-two range
-// scale per split, head and quarter of the value dims.
+// scale per split, head and 32 value dims.
 #include <type_traits>
 
 #include "device.h"
@@ -48,6 +48,7 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kKeys = 32;              // keys per tile
+constexpr float kLazy = 16.0f;         // reference-max slack of the online softmax (log2 units)
 
 // LDS-typed pointers: stage addresses are formed in address space 3 so no
 // generic-to-LDS conversion is ever needed on a run-time selected pointer.
@@ -94,19 +95,6 @@ __device__ inline RowKeys row_keys(const AttnArgs& a, int r) {
     return k;
 }
 
-// Storage row of slot j of the selected part (-1: masked).  The block-table
-// range of the split is in LDS.
-__device__ __forceinline__ int64_t pool_row(const AttnArgs& a, const RowKeys& rk, int j, const lds_i32* idx_lds, int idx0,
-                                            const lds_i32* bt_lds, int blk0) {
-    const int g = a.topk ? idx_lds[j - idx0] : j;
-    const bool ok = j < rk.nsel && g >= 0 && g < rk.n;
-    const int sh = __builtin_ctz(256 / a.m);                  // E = 256/m entries per block, a power of two
-    const int gc = ok ? g : blk0 << sh;
-    const int lb = gc >> sh;
-    const int pb = bt_lds[lb - blk0];
-    return ok ? ((int64_t)pb << sh) + (gc & ((1 << sh) - 1)) : -1;
-}
-
 // Tile staging.  NT / 32 threads share a key: thread t stages key t / (NT/32)
 // of the 32 keys of a tile, 16-byte parts (t % (NT/32)) + (NT/32) i, so each
 // thread resolves one storage row per tile and its loads and LDS writes
@@ -137,13 +125,14 @@ struct Tiler {
     // stored.  `live` false (a tile past the split): row 0 is read and
     // nothing is used; issuing those loads anyway keeps the number of loads
     // per step fixed, so the compiler's wait counts stay exact.  Masked keys
-    // also read row 0 and are zeroed when stored.
+    // also read row 0 and are zeroed when stored.  rows_lds holds the storage
+    // row of every selected slot of the split from idx0 on (-1: masked).
     struct Src {
         int64_t row;
         bool ok, win;
     };
     __device__ __forceinline__ static Src resolve(const AttnArgs& a, const RowKeys& rk, int tile, bool live,
-                                                  const lds_i32* idx_lds, int idx0, const lds_i32* bt_lds, int blk0) {
+                                                  const lds_i32* rows_lds, int idx0) {
         const int key = (int)threadIdx.x / kThreadsPerKey;
         Src s;
         s.win = live && tile >= rk.sel_tiles;                       // uniform over the workgroup
@@ -152,7 +141,7 @@ struct Tiler {
             s.ok = w < rk.nwin;
             s.row = (int64_t)rk.b * a.win_cap + (rk.t0 + (s.ok ? w : 0)) % a.win_cap;
         } else {
-            const int64_t prow = pool_row(a, rk, (live ? tile * kKeys : idx0) + key, idx_lds, idx0, bt_lds, blk0);
+            const int prow = rows_lds[(live ? tile * kKeys - idx0 : 0) + key];
             s.ok = live && prow >= 0;
             s.row = s.ok ? prow : 0;
         }
@@ -241,225 +230,173 @@ struct Tiler {
     }
 };
 
-// Per-wave tile computation.  The eight waves of a workgroup form two head
-// groups of 32 heads, each split into four quarters of the shared-KV
-// dimension: a wave holds its head group's queries over its quarter of D in
-// VGPRs and the O^T accumulators of its quarter of the value dims for all 32
-// heads, so every key fragment read from LDS feeds 32 heads.  Per tile:
-//   scores:  partial S^T = K Q^T over the wave's quarter of D (MFMA 16x16x32,
-//            keys on M), written to the wave's slot of the exchange buffer;
-//   softmax: (after a barrier) wave q of a head group owns heads 8q .. 8q+7:
-//            it sums the four partials of its heads, runs the online softmax
-//            (lane: one head, four keys; the tile max over eight lanes),
-//            and writes P as bf16 hi + lo and the heads' rescale factors;
-//   P V:     (after a barrier) every wave rescales its accumulators where a
-//            head's reference max moved and adds V^T P^T over its value
-//            quarter, V^T read from the same LDS tile by ds_read_b64_tr_b16.
-template <int D, int DV>
-struct QuarterWave {
-    static constexpr int KS_ALL = D / 32;                   // k-steps of S^T over D
-    static constexpr int KSQ = (KS_ALL + 3) / 4;            // most k-steps of one quarter
-    static constexpr int DVQ = DV / 4;                       // value dims per quarter
-    static constexpr int NDQ = DVQ / 16;                     // 16-dim tiles of O^T per wave
-    static_assert(D % 32 == 0 && DV % 64 == 0, "shape");
-    static constexpr int XROW = kKeys * 4 + 16;              // exchange row: 32 fp32 scores of a head, padded
-    static constexpr int XSLOT = 32 * XROW;                  // one wave's partial S^T (32 heads)
-    static constexpr int PROW = kKeys * 2 + 16;              // P row: 32 bf16 weights of a head, padded
-    static constexpr int PGRP = 32 * PROW;                   // one head group's P (hi or lo)
-    bf16x8 qb[2][KSQ];
-    f32x4 o[2][NDQ];
-    float m_run, l_run;            // owner state of head 8q + (lane & 7)
-    int ks0, ksn;                  // this quarter's k-steps
+// Two kinds of waves share a workgroup (eight waves, two per SIMD):
+//   score waves 0..3 each hold the queries of 16 heads over the whole of D in
+//     VGPRs (B operands) and run, per 32-key tile, S^T = K Q^T with MFMA
+//     16x16x32 (keys on M in two 16-key blocks, heads on N; A = keys from LDS),
+//     the online softmax in registers (a lane holds 8 keys of one head: the C
+//     layout, keys 4g..4g+3 and 16+4g..16+4g+3, g = lane >> 4), and write P as
+//     a bf16 hi + lo pair (16 significant bits) in B-operand order, with each
+//     head's rescale factor, to LDS; they also load the key tiles;
+//   value waves 4..7 each hold the O^T accumulators of all 64 heads over a
+//     quarter of the value dims and run O^T += V^T P^T with MFMA 16x16x32,
+//     V^T read from the same LDS tile (K = V) by ds_read_b64_tr_b16 in the key
+//     order of the C layout, each V^T fragment feeding the four head blocks.
+// Each SIMD hosts one wave of each kind, so the score wave's softmax, loads
+// and tile stores overlap the value wave's MFMAs.  One barrier per tile: in
+// step k the score waves work on tile k while the value waves finish tile
+// k - 1.
+template <int D>
+struct ScoreWave {
+    static constexpr int KS = D / 32;                        // 32-dim k-steps over D
+    bf16x8 qb[KS];
+    float m_run, l_run;                                      // head (lane & 15): reference max, this lane's keys' sum
 
-    __device__ __forceinline__ void init(const AttnArgs& a, int r, int head0, int g, int c16, int q) {
-        constexpr int base = KS_ALL / 4, extra = KS_ALL % 4;
-        ks0 = q * base + min(q, extra);
-        ksn = base + (q < extra ? 1 : 0);
+    __device__ __forceinline__ void init(const AttnArgs& a, int r, int head0, int lane) {
+        const int c16 = lane & 15, g = lane >> 4;
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + head0 + c16) * D + 8 * g;
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            const uint16_t* qp =
-                reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + head0 + 16 * hb + c16) * D + ks0 * 32 + 8 * g;
-#pragma unroll
-            for (int s = 0; s < KSQ; ++s)
-                qb[hb][s] = s < ksn ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * s))
-                                    : bf16x8{};
-#pragma unroll
-            for (int dt = 0; dt < NDQ; ++dt) o[hb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int s = 0; s < KS; ++s) qb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * s));
         m_run = -INFINITY;
         l_run = 0.0f;
     }
 
-    // Partial S^T of the tile over this quarter of D, into the wave's exchange
-    // slot as [head][key] rows.
-    __device__ __forceinline__ void scores(const lds_u8* lds, lds_u8* xs_mine, int g, int c16) const {
+    // S^T of the tile: lane (head = lane & 15, g = lane >> 4) gets keys
+    // 16 b + 4g + j in sacc[b][j].
+    __device__ __forceinline__ void scores(const lds_u8* st, int lane, f32x4 (&sacc)[2]) const {
         constexpr int ROWB = Geo<D>::ROWB;
-        f32x4 sacc[2][2];
+        const lds_u8* kb = st + (lane & 15) * ROWB + 16 * (lane >> 4);
+        sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int s = 0; s < KS; ++s) {
 #pragma unroll
-            for (int hb = 0; hb < 2; ++hb) sacc[kt][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const lds_u8* kbase = lds + c16 * ROWB + (ks0 * 32 + 8 * g) * 2;
-#pragma unroll
-        for (int s = 0; s < KSQ; ++s) {
-            if (s < ksn) {
-                bf16x8 kA[2];
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-                    kA[kt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(kbase + kt * 16 * ROWB + 64 * s));
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int hb = 0; hb < 2; ++hb)
-                        sacc[kt][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[kt], qb[hb][s], sacc[kt][hb], 0, 0, 0);
+            for (int b = 0; b < 2; ++b) {
+                const bf16x8 k = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(kb + 16 * b * ROWB + 64 * s));
+                sacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qb[s], sacc[b], 0, 0, 0);
             }
         }
-        // lane: keys kt*16 + 4g .. +3 of head hb*16 + c16
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-                *reinterpret_cast<lds_f32x4*>(xs_mine + (hb * 16 + c16) * XROW + (kt * 16 + 4 * g) * 4) = sacc[kt][hb];
     }
 
-    // Owner softmax of heads 8q .. 8q+7 of the head group: lane (h8 = lane & 7,
-    // kg = lane >> 3) takes keys 4kg .. 4kg+3 of head 8q + h8.  xs_grp: the
-    // head group's four exchange slots; kmeta: each key's value scale (FP8
-    // window scale, 1, or -1 for a masked key).  Writes P hi/lo in the order
-    // the P V operands read it and the head's rescale factor alpha.
-    __device__ __forceinline__ void softmax(const lds_u8* xs_grp, const lds_f32* kmeta, lds_u8* p_hi, lds_u8* p_lo,
-                                            lds_f32* alpha, int lane, int q, float scale_log2) {
-        const int h8 = lane & 7, kg = lane >> 3, hq = 8 * q + h8;
-        f32x4 s = *reinterpret_cast<const lds_f32x4*>(xs_grp + hq * XROW + 16 * kg);
-#pragma unroll
-        for (int src = 1; src < 4; ++src)
-            s += *reinterpret_cast<const lds_f32x4*>(xs_grp + src * XSLOT + hq * XROW + 16 * kg);
-        const f32x4 km = *reinterpret_cast<const lds_f32x4*>(kmeta + 4 * kg);
-        float x[4];
+    // Online softmax of the tile (this lane: 8 keys of one head).  kmeta[key]:
+    // the key's value scale (FP8 window scale, 1, or -1 for a masked key),
+    // which also multiplies its score.  Returns the rescale factor of the
+    // head's accumulators and P hi / lo in B-operand order.
+    __device__ __forceinline__ float softmax(f32x4 (&s)[2], const lds_f32* kmeta, int lane, float scale_log2,
+                                             u32x4& h, u32x4& l) {
+        const int g = lane >> 4;
+        f32x4 km[2];
         float mx = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            x[v] = km[v] >= 0.0f ? s[v] * (scale_log2 * km[v]) : -INFINITY;
-            mx = fmaxf(mx, x[v]);
+        for (int b = 0; b < 2; ++b) {
+            km[b] = *reinterpret_cast<const lds_f32x4*>(kmeta + 16 * b + 4 * g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                s[b][j] = km[b][j] >= 0.0f ? s[b][j] * (scale_log2 * km[b][j]) : -INFINITY;
+                mx = fmaxf(mx, s[b][j]);
+            }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 8));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // Lazy rescaling: the reference max m_run moves only when the tile's
-        // max exceeds it by more than 8 (log2 units), so most tiles leave the
-        // accumulators untouched; weights relative to m_run stay <= 2^8.
+        mx = max_across_rows(mx);
+        // Lazy rescaling: the reference max moves only when the tile's max
+        // exceeds it by more than kLazy (log2 units); weights relative to it
+        // stay below 2^kLazy, far inside fp32 and bf16 range.
         float al = 1.0f;
-        if (mx > m_run + 8.0f) {
-            al = exp2f(m_run - mx);      // 0 while m_run = -inf
+        if (mx > m_run + kLazy) {
+            al = exp2f(m_run - mx);          // 0 while m_run = -inf
             l_run *= al;
             m_run = mx;
         }
-        // reference for the exponent: m_run, or 0 while every key so far is
-        // masked (then every x is -inf and every p is 0)
         const float mref = m_run == -INFINITY ? 0.0f : m_run;
-        float w[4], psum = 0.0f;
+        float psum = 0.0f;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            // x - mref <= 8: v_exp_f32 directly (results below 2^-126 may
-            // flush to zero, far below the sum's precision)
-            const float p = __builtin_amdgcn_exp2f(x[v] - mref);
-            psum += p;
-            w[v] = p * km[v];            // masked keys: p = 0; FP8 window keys carry their scale
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                // x - mref <= kLazy: v_exp_f32 directly (results below 2^-126
+                // may flush to zero, far below the sum's precision)
+                const float p0 = __builtin_amdgcn_exp2f(s[b][2 * t] - mref);
+                const float p1 = __builtin_amdgcn_exp2f(s[b][2 * t + 1] - mref);
+                psum += p0 + p1;
+                // masked keys: p = 0; FP8 window keys carry their scale
+                const float a0 = p0 * km[b][2 * t], a1 = p1 * km[b][2 * t + 1];
+                const uint32_t hh = cvt_pk_bf16(a0, a1);
+                h[2 * b + t] = hh;
+                l[2 * b + t] = cvt_pk_bf16(a0 - __uint_as_float(hh << 16), a1 - __uint_as_float(hh & 0xffff0000u));
+            }
         }
         l_run += psum;
-        const uint32_t h0 = cvt_pk_bf16(w[0], w[1]), h1 = cvt_pk_bf16(w[2], w[3]);
-        const uint32_t l0 = cvt_pk_bf16(w[0] - __uint_as_float(h0 << 16), w[1] - __uint_as_float(h0 & 0xffff0000u));
-        const uint32_t l1 = cvt_pk_bf16(w[2] - __uint_as_float(h1 << 16), w[3] - __uint_as_float(h1 & 0xffff0000u));
-        // P row order: keys 0-3, 16-19, 4-7, 20-23, ... so that operand lane
-        // group g reads keys 4g .. 4g+3 and 16+4g .. 16+4g+3 as one 16-byte run
-        const int off = hq * PROW + (kg < 4 ? 16 * kg : 16 * (kg - 4) + 8);
-        *reinterpret_cast<lds_u32x2*>(p_hi + off) = u32x2{h0, h1};
-        *reinterpret_cast<lds_u32x2*>(p_lo + off) = u32x2{l0, l1};
-        if (kg == 0) alpha[hq] = al;
+        return al;
+    }
+};
+
+template <int D, int DV>
+struct ValueWave {
+    static constexpr int DVQ = DV / 4;                       // value dims per wave
+    static constexpr int NDT = DVQ / 16;                     // 16-dim tiles of O^T per head block
+    static_assert(DV % 64 == 0, "shape");
+    f32x4 o[4][NDT];                                         // [head block][dim tile]
+    int vbase;
+
+    __device__ __forceinline__ void init(int q) {
+        vbase = q * DVQ;
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) o[hb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // O^T += V^T P^T over this wave's value quarter, after rescaling the
-    // columns of heads whose reference max moved.  Within each 16-lane block,
-    // ds_read_b64_tr_b16 hands lane i element (i & 3) of the 8-byte chunk
-    // addressed by lane (i >> 2) + 4e, e = 0..3: lane s addresses key
-    // 4g + (s >> 2), dims dt*16 + 4(s & 3) .. +3, so lane i receives keys
-    // 4g + e at dim dt*16 + i (and 16 + 4g + e from the second read).
-    __device__ __forceinline__ void pv(const lds_u8* lds, const lds_u8* p_hi, const lds_u8* p_lo, const lds_f32* alpha,
-                                       int g, int c16, int q) {
+    // O^T += V^T P^T over this wave's value quarter for the four head blocks.
+    // Within each 16-lane block, ds_read_b64_tr_b16 hands lane i element
+    // (i & 3) of the 8-byte chunk addressed by lane (i >> 2) + 4e, e = 0..3;
+    // lane s of block g addresses key 4g + (s >> 2) (+ 16 for the second
+    // read), dims 16 dt + 4 (s & 3) .. +3 of the quarter, so lane i receives
+    // dim 16 dt + i for keys 4g + e and 16 + 4g + e: the A operand of a
+    // 16x16x32 MFMA in the key order of the score waves' C layout.
+    __device__ __forceinline__ void pv(const lds_u8* st, const bf16x8 (&phi)[4], const bf16x8 (&plo)[4], int lane) {
         constexpr int ROWB = Geo<D>::ROWB;
-        const float a0 = alpha[c16], a1 = alpha[16 + c16];
-        if (__builtin_amdgcn_ballot_w64(a0 != 1.0f || a1 != 1.0f)) {
+        const int g = lane >> 4, i16 = lane & 15;
+        const lds_u8* vb = st + (4 * g + (i16 >> 2)) * ROWB + (vbase + 4 * (i16 & 3)) * 2;
 #pragma unroll
-            for (int dt = 0; dt < NDQ; ++dt) {
-                o[0][dt] *= a0;
-                o[1][dt] *= a1;
+        for (int dt = 0; dt < NDT; ++dt) {
+            const lds_u8* p0 = vb + 32 * dt;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 16 * ROWB));
+            const bf16x8 va = __builtin_bit_cast(
+                bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                              __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) {
+                o[hb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[hb], o[hb][dt], 0, 0, 0);
+                o[hb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[hb], o[hb][dt], 0, 0, 0);
             }
-        }
-        bf16x8 pb[2], pbl[2];
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            pb[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(p_hi + (hb * 16 + c16) * PROW + 16 * g));
-            pbl[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(p_lo + (hb * 16 + c16) * PROW + 16 * g));
-        }
-        const lds_u8* vbase = lds + (4 * g + (c16 >> 2)) * ROWB + q * DVQ * 2 + 8 * (c16 & 3);
-        constexpr int G4 = 3;
-#pragma unroll
-        for (int d0 = 0; d0 < NDQ; d0 += G4) {
-            bf16x8 vA[G4];
-#pragma unroll
-            for (int j = 0; j < G4; ++j) {
-                if (d0 + j < NDQ) {
-                    const lds_u8* p0 = vbase + (d0 + j) * 32;
-                    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-                    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 16 * ROWB));
-                    vA[j] = __builtin_bit_cast(
-                        bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                                      __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < G4; ++j)
-#pragma unroll
-                for (int hb = 0; hb < 2; ++hb)
-                    if (d0 + j < NDQ) o[hb][d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA[j], pb[hb], o[hb][d0 + j], 0, 0, 0);
-#pragma unroll
-            for (int j = 0; j < G4; ++j)
-#pragma unroll
-                for (int hb = 0; hb < 2; ++hb)
-                    if (d0 + j < NDQ) o[hb][d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA[j], pbl[hb], o[hb][d0 + j], 0, 0, 0);
         }
     }
 };
 
 constexpr int kXcds = 8;               // XCDs of the GPU; workgroup ids are dealt to them round-robin
-constexpr int kWaves = 8;              // two head groups of 32 x four quarters of D
+constexpr int kWaves = 8;              // four score waves, four value waves
 constexpr int kThreads = kWaves * 64;
-constexpr int kBtLds = 4096;           // block-table entries cached in LDS
-constexpr int kIdxLds = 2560;          // top-k slots cached in LDS (= max keys per split)
+constexpr int kLoadThreads = 256;      // the score waves load the key tiles
+constexpr int kStages = 3;             // LDS stages of the key tiles
+constexpr int kRowsLds = 2560;         // storage rows of a split's selected slots cached in LDS (= max keys per split)
 
 template <int KVD, int WD, int D, int DV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(AttnArgs a) {
     using G = Geo<D>;
-    using QW = QuarterWave<D, DV>;
-    constexpr int NT = kThreads;
-    using TL = Tiler<KVD, WD, D, NT>;
+    using SW = ScoreWave<D>;
+    using VW = ValueWave<D, DV>;
+    using TL = Tiler<KVD, WD, D, kLoadThreads>;
     constexpr int NU = TL::NU;
-    // tiles held in registers ahead of the LDS stage
-    constexpr int kPrefetch = NU <= 12 ? 2 : 1;
-    static_assert(kPrefetch == 1 || kPrefetch == 2, "prefetch depth");
-    __shared__ __attribute__((aligned(16))) uint8_t stage[2][G::STAGE];
-    __shared__ __attribute__((aligned(16))) float kmeta[2][kKeys];
-    __shared__ int32_t bt_mem[kBtLds];
-    __shared__ int32_t idx_mem[kIdxLds];
-    __shared__ __attribute__((aligned(16))) uint8_t xs_mem[kWaves][QW::XSLOT];     // partial-score exchange
-    __shared__ __attribute__((aligned(16))) uint8_t p_mem[2][2][QW::PGRP];        // [head group][hi, lo]
-    __shared__ __attribute__((aligned(16))) float alpha_mem[2][32];
-    __shared__ float fin_mem[2][2][32];                                           // [head group][m, l][head]
-    lds_i32* const bt_lds = (lds_i32*)&bt_mem[0];
-    lds_i32* const idx_lds = (lds_i32*)&idx_mem[0];
+    constexpr int NT = kThreads;
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kStages][G::STAGE];
+    __shared__ __attribute__((aligned(16))) float kmeta[kStages][kKeys];
+    __shared__ __attribute__((aligned(16))) uint8_t p_mem[2][2][4][64 * 16];   // [step parity][hi, lo][head block][lane]
+    __shared__ __attribute__((aligned(16))) float al_mem[2][64];                 // [step parity][head]
+    __shared__ float fin_mem[2][64];                                              // [m, l][head]
+    __shared__ int32_t rows_mem[kRowsLds];
+    lds_i32* const rows_lds = (lds_i32*)&rows_mem[0];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, c16 = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // workgroup -> (row, split, head block): workgroups are dispatched to the
     // eight XCDs round-robin by id, so id % 8 picks the XCD, and each XCD
     // takes an equal contiguous range of the (row, split) units in row order;
@@ -484,154 +421,196 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         return;
     }
     const int te = min(tb + a.split_tiles, rk.tiles);
-    const int hg = wave >> 2, q = wave & 3;
-    const int head0 = hblk * 64 + hg * 32;                   // first head of this wave's group
+    const int ntl = te - tb;
+    const int head0 = hblk * 64;
 
-    // prologue: top-k slots and block-table range of this split into LDS
-    const int sel_end = min(te, rk.sel_tiles) * kKeys;            // selected slots [tb*32, sel_end)
+    // prologue: the storage row of every selected slot of this split (-1:
+    // masked), resolved through the top-k list and the block table once,
+    // into LDS; each thread requests all of its slots' loads before waiting
     const int idx0 = tb * kKeys;
-    int blk0 = 0, nblk = 0, bt_first = 0;
-    if (sel_end > idx0) {
-        const int E = 256 / a.m;
-        if (a.topk) {
-            nblk = (rk.n + E - 1) / E;
-            const int nidx = sel_end - idx0;
-            const int first = a.topk[(int64_t)r * a.k + min(idx0 + tid, a.k - 1)];
-            bt_first = a.block_table[(int64_t)rk.b * a.max_blocks + min(tid, a.max_blocks - 1)];
-            if (tid < nidx) idx_lds[tid] = idx0 + tid < rk.nsel ? first : -1;
-            for (int i = tid + NT; i < nidx; i += NT)
-                idx_lds[i] = idx0 + i < rk.nsel ? a.topk[(int64_t)r * a.k + idx0 + i] : -1;
-        } else {
-            const int g1 = min(sel_end, rk.nsel);
-            if (g1 > idx0) {
-                blk0 = idx0 / E;
-                nblk = (g1 - 1) / E - blk0 + 1;
-                bt_first = a.block_table[(int64_t)rk.b * a.max_blocks + min(blk0 + tid, a.max_blocks - 1)];
+    const int nslots = max(0, min(te, rk.sel_tiles) * kKeys - idx0);
+    {
+        constexpr int kPer = kRowsLds / NT;
+        const int sh = __builtin_ctz(256 / a.m);             // E = 256/m entries per block, a power of two
+        int gs[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int j = idx0 + tid + NT * i;
+            gs[i] = -1;
+            if (tid + NT * i < nslots && j < rk.nsel) gs[i] = a.topk ? a.topk[(int64_t)r * a.k + j] : j;
+        }
+        int pbs[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const bool ok = gs[i] >= 0 && gs[i] < rk.n;
+            pbs[i] = ok ? a.block_table[(int64_t)rk.b * a.max_blocks + (gs[i] >> sh)] : -1;
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            if (tid + NT * i < nslots) {
+                const bool ok = gs[i] >= 0 && gs[i] < rk.n;
+                rows_lds[tid + NT * i] = ok ? (pbs[i] << sh) | (gs[i] & ((1 << sh) - 1)) : -1;
             }
         }
     }
-    // (the first slot and block of each thread are requested together above,
-    // so the common case costs one round trip)
-    const int nbt = min(nblk, kBtLds);
-    if (tid < nbt) bt_lds[tid] = bt_first;
-    for (int i = tid + NT; i < nbt; i += NT) bt_lds[i] = a.block_table[(int64_t)rk.b * a.max_blocks + blk0 + i];
     __syncthreads();
-
-    QW W;
-    W.init(a, r, head0, g, c16, q);
-    lds_u8* const xs_mine = (lds_u8*)&xs_mem[wave][0];
-    const lds_u8* const xs_grp = (const lds_u8*)&xs_mem[hg * 4][0];
-    lds_u8* const p_hi = (lds_u8*)&p_mem[hg][0][0];
-    lds_u8* const p_lo = (lds_u8*)&p_mem[hg][1][0];
-    lds_f32* const alpha = (lds_f32*)&alpha_mem[hg][0];
-
-    TileRegs<NU> R[kPrefetch];
-    const int ntl = te - tb;
-    TL::issue(a, TL::resolve(a, rk, tb, true, idx_lds, idx0, bt_lds, blk0), R[0]);
-    if constexpr (kPrefetch > 1) TL::issue(a, TL::resolve(a, rk, tb + 1, 1 < ntl, idx_lds, idx0, bt_lds, blk0), R[1]);
     lds_u8* const st = (lds_u8*)&stage[0][0];
     lds_f32* const km = (lds_f32*)&kmeta[0][0];
-    TL::store(rk, tb, R[0], st, km);
-    TL::issue(a, TL::resolve(a, rk, tb + kPrefetch, kPrefetch < ntl, idx_lds, idx0, bt_lds, blk0), R[0]);
-    __syncthreads();
+    lds_u8* const pm = (lds_u8*)&p_mem[0][0][0][0];
+    lds_f32* const alm = (lds_f32*)&al_mem[0][0];
+    constexpr int PPAR = 2 * 4 * 64 * 16;                    // bytes between the two P parities
+    const int c16 = lane & 15, g = lane >> 4;
 
-    // tile u sits in register set (u - tb) % P until it is stored to stage
-    // (u - tb) % 2; the steps of one round are spelled out so that every
-    // register set is addressed statically.  Step t: scores of tile t; a
-    // barrier (every wave is past the P V of tile t - 1, so its stage is
-    // free); tile t + 1 stored there and the loads of tile t + 1 + P issued;
-    // the owner softmax; a barrier; P V of tile t.
-    auto step = [&](auto J, int t) __attribute__((always_inline)) {
-        constexpr int nxt = (decltype(J)::value + 1) % kPrefetch;
-        const lds_u8* cur = st + (t & 1) * G::STAGE;
-        W.scores(cur, xs_mine, g, c16);
-        // the next loads' storage rows come from LDS before the barrier
-        const typename TL::Src nsrc =
-            TL::resolve(a, rk, tb + t + 1 + kPrefetch, t + 1 + kPrefetch < ntl, idx_lds, idx0, bt_lds, blk0);
+    if (wave < 4) {
+        // ---- score waves: head block `wave`, and the key tile loads ----
+        const int hb = wave;
+        SW W;
+        W.init(a, r, head0 + 16 * hb, lane);
+        // tile 0 into stage 0; tiles 1 and 2 in flight in the two register sets
+        TileRegs<NU> R[2];
+        TL::issue(a, TL::resolve(a, rk, tb, true, rows_lds, idx0), R[0]);
+        TL::issue(a, TL::resolve(a, rk, tb + 1, 1 < ntl, rows_lds, idx0), R[1]);
+        TL::store(rk, tb, R[0], st, km);
+        TL::issue(a, TL::resolve(a, rk, tb + 2, 2 < ntl, rows_lds, idx0), R[0]);
         __syncthreads();
-        if (t + 1 < ntl)
-            TL::store(rk, tb + t + 1, R[nxt], st + ((t + 1) & 1) * G::STAGE, km + ((t + 1) & 1) * kKeys);
-        TL::issue(a, nsrc, R[nxt]);
-        W.softmax(xs_grp, km + (t & 1) * kKeys, p_hi, p_lo, alpha, lane, q, a.scale_log2);
-        __syncthreads();
-        W.pv(cur, p_hi, p_lo, alpha, g, c16, q);
-    };
-    for (int t0 = 0; t0 < ntl; t0 += kPrefetch) {
-        step(IntC<0>{}, t0);
-        if constexpr (kPrefetch > 1)
-            if (t0 + 1 < ntl) step(IntC<1>{}, t0 + 1);
-    }
-
-    // finish: each owner's row sum over its eight lanes, published with the
-    // reference max for the waves that hold the heads' value columns
-    {
-        float l_tot = W.l_run + __shfl_xor(W.l_run, 8);
-        l_tot += __shfl_xor(l_tot, 16);
-        l_tot += __shfl_xor(l_tot, 32);
-        if (lane < 8) {
-            fin_mem[hg][0][8 * q + lane] = W.m_run;
-            fin_mem[hg][1][8 * q + lane] = l_tot;
+        // step k: scores, softmax and P of tile k (stage k % 3); register set
+        // (k + 1) & 1 (tile k + 1) into stage (k + 1) % 3, which the value
+        // waves left in step k - 1, and the loads of tile k + 3 into it; then
+        // the barrier.  Register sets are addressed statically (unrolled by two).
+        auto step = [&](auto J, int k) __attribute__((always_inline)) {
+            constexpr int rs = (decltype(J)::value + 1) & 1;
+            const int sc = k % kStages, sn = (k + 1) % kStages;
+            f32x4 sv[2];
+            W.scores(st + sc * G::STAGE, lane, sv);
+            const typename TL::Src nsrc = TL::resolve(a, rk, tb + k + 3, k + 3 < ntl, rows_lds, idx0);
+            u32x4 h, l;
+            const float al = W.softmax(sv, km + sc * kKeys, lane, a.scale_log2, h, l);
+            lds_u8* pw = pm + (k & 1) * PPAR + hb * 1024 + lane * 16;
+            *reinterpret_cast<lds_u32x4*>(pw) = h;
+            *reinterpret_cast<lds_u32x4*>(pw + 4096) = l;
+            if (g == 0) alm[(k & 1) * 64 + 16 * hb + c16] = al;
+            if (k + 1 < ntl) TL::store(rk, tb + k + 1, R[rs], st + sn * G::STAGE, km + sn * kKeys);
+            TL::issue(a, nsrc, R[rs]);
+            __syncthreads();
+        };
+        for (int k0 = 0; k0 < ntl; k0 += 2) {
+            step(IntC<0>{}, k0);
+            if (k0 + 1 < ntl) step(IntC<1>{}, k0 + 1);
         }
+        __syncthreads();                                     // the value waves finish the last tile
+        // the row sum of each head over all lanes' keys, with its reference max
+        float l_tot = W.l_run + __shfl_xor(W.l_run, 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        const int hd = head0 + 16 * hb + c16;
+        if (g == 0) {
+            fin_mem[0][16 * hb + c16] = W.m_run;
+            fin_mem[1][16 * hb + c16] = l_tot;
+            if (a.nsplit == 1) {
+                if (a.lse) a.lse[(int64_t)r * a.H + hd] = (W.m_run + log2f(l_tot)) * kLn2;
+            } else {
+                float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H;
+                ml[hd] = W.m_run;
+                ml[a.H + hd] = l_tot;
+            }
+        }
+        __syncthreads();
+        return;
     }
-    __syncthreads();
-    constexpr int NDQ = QW::NDQ;
-    const int dv0 = q * QW::DVQ + 4 * g;
+
+    // ---- value waves: quarter `wave - 4` of the value dims, all 64 heads ----
+    VW V;
+    V.init(wave - 4);
+    __syncthreads();                                         // tile 0 in stage 0
+    // step k: the score waves' tile k; here P V of tile k - 1 (stage
+    // (k - 1) % 3, P of parity (k - 1) & 1); then the barrier
+    for (int k = 0; k < ntl; ++k) {
+        if (k > 0) {
+            const int kp = k - 1;
+            bf16x8 phi[4], plo[4];
+            const lds_u8* pr = pm + (kp & 1) * PPAR + lane * 16;
+            float al[4];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+            for (int hb = 0; hb < 4; ++hb) {
+                phi[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(pr + hb * 1024));
+                plo[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(pr + 4096 + hb * 1024));
+                al[hb] = alm[(kp & 1) * 64 + 16 * hb + c16];
+            }
+            if (__builtin_amdgcn_ballot_w64(al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f)) {
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+                    for (int dt = 0; dt < VW::NDT; ++dt) V.o[hb][dt] *= al[hb];
+            }
+            V.pv(st + (kp % kStages) * G::STAGE, phi, plo, lane);
+        }
+        __syncthreads();
+    }
+    {
+        // the last tile
+        const int kp = ntl - 1;
+        bf16x8 phi[4], plo[4];
+        const lds_u8* pr = pm + (kp & 1) * PPAR + lane * 16;
+        float al[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+            phi[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(pr + hb * 1024));
+            plo[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(pr + 4096 + hb * 1024));
+            al[hb] = alm[(kp & 1) * 64 + 16 * hb + c16];
+        }
+        if (__builtin_amdgcn_ballot_w64(al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f)) {
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+                for (int dt = 0; dt < VW::NDT; ++dt) V.o[hb][dt] *= al[hb];
+        }
+        V.pv(st + (kp % kStages) * G::STAGE, phi, plo, lane);
+    }
+    __syncthreads();                                         // matches the score waves' closing barrier
+    __syncthreads();                                         // their m and l are in LDS
+    // outputs of this quarter: lane (head c16 of block hb, g) holds dims
+    // 16 dt + 4g .. +3
+    constexpr int NDT = VW::NDT;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
         const int hl = 16 * hb + c16, hd = head0 + hl;
-        const float m_tot = fin_mem[hg][0][hl], l_tot = fin_mem[hg][1][hl];
+        const float l_tot = fin_mem[1][hl];
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         if (a.nsplit == 1) {
-            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-            const int64_t base = ((int64_t)r * a.H + hd) * DV + dv0;
+            const int64_t base = ((int64_t)r * a.H + hd) * DV + V.vbase + 4 * g;
             if (a.out_dtype == DT_F32) {
                 float* out = reinterpret_cast<float*>(a.out) + base;
 #pragma unroll
-                for (int dt = 0; dt < NDQ; ++dt) *reinterpret_cast<f32x4*>(out + dt * 16) = W.o[hb][dt] * inv;
+                for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(out + 16 * dt) = V.o[hb][dt] * inv;
             } else {
                 uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + base;
 #pragma unroll
-                for (int dt = 0; dt < NDQ; ++dt) {
-                    f32x4 t = W.o[hb][dt] * inv;
-                    *reinterpret_cast<u32x2*>(out + dt * 16) = u32x2{cvt_pk_bf16(t[0], t[1]), cvt_pk_bf16(t[2], t[3])};
+                for (int dt = 0; dt < NDT; ++dt) {
+                    const f32x4 v = V.o[hb][dt] * inv;
+                    *reinterpret_cast<u32x2*>(out + 16 * dt) = u32x2{cvt_pk_bf16(v[0], v[1]), cvt_pk_bf16(v[2], v[3])};
                 }
             }
-            if (a.lse && g == 0 && q == 0) a.lse[(int64_t)r * a.H + hd] = (m_tot + log2f(l_tot)) * kLn2;
         } else if (a.part_h) {
-            // U = O / l, a convex combination of the values, as fp16 scaled
-            // by 2^(15 - e) where max |U| over the head's quarter < 2^e
-            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-            float amax = 0.0f;
+            // U = O / l, a convex combination of the values, as fp16 scaled by
+            // 2^(15 - e) where max |U| over the head's 16-dim tile < 2^e
+            const int64_t su = (int64_t)r * a.nsplit + split;
+            uint16_t* ph = a.part_h + (su * a.H + hd) * DV + V.vbase + 4 * g;
 #pragma unroll
-            for (int dt = 0; dt < NDQ; ++dt)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) amax = fmaxf(amax, fabsf(W.o[hb][dt][v]));
-            amax *= inv;
-            amax = fmaxf(amax, __shfl_xor(amax, 16));
-            amax = fmaxf(amax, __shfl_xor(amax, 32));
-            int ex = 0;
-            (void)frexpf(amax, &ex);
-            const float sc = ldexpf(inv, 15 - ex);
-            uint16_t* ph = a.part_h + (((int64_t)r * a.nsplit + split) * a.H + hd) * DV + dv0;
-#pragma unroll
-            for (int dt = 0; dt < NDQ; ++dt) {
-                const f32x4 t = W.o[hb][dt] * sc;
-                *reinterpret_cast<u32x2*>(ph + dt * 16) = u32x2{pack_f16x2(t[0], t[1]), pack_f16x2(t[2], t[3])};
-            }
-            if (g == 0) a.part_sc[(((int64_t)r * a.nsplit + split) * 4 + q) * a.H + hd] = ldexpf(1.0f, ex - 15);
-            if (g == 0 && q == 0) {
-                float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H;
-                ml[hd] = m_tot;
-                ml[a.H + hd] = l_tot;
+            for (int dt = 0; dt < NDT; ++dt) {
+                float amax = fmaxf(fmaxf(fabsf(V.o[hb][dt][0]), fabsf(V.o[hb][dt][1])),
+                                   fmaxf(fabsf(V.o[hb][dt][2]), fabsf(V.o[hb][dt][3])));
+                amax = fmaxf(amax, __shfl_xor(amax, 16));
+                amax = fmaxf(amax, __shfl_xor(amax, 32)) * inv;
+                int ex = 0;
+                (void)frexpf(amax, &ex);
+                const f32x4 v = V.o[hb][dt] * ldexpf(inv, 15 - ex);
+                *reinterpret_cast<u32x2*>(ph + 16 * dt) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+                if (g == 0) a.part_sc[(su * (DV / 16) + V.vbase / 16 + dt) * a.H + hd] = ldexpf(1.0f, ex - 15);
             }
         } else {
-            float* po = a.part_o + (((int64_t)r * a.nsplit + split) * a.H + hd) * DV + dv0;
+            const int64_t su = (int64_t)r * a.nsplit + split;
+            float* po = a.part_o + (su * a.H + hd) * DV + V.vbase + 4 * g;
 #pragma unroll
-            for (int dt = 0; dt < NDQ; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = W.o[hb][dt];
-            if (g == 0 && q == 0) {
-                float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H;
-                ml[hd] = m_tot;
-                ml[a.H + hd] = l_tot;
-            }
+            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt) = V.o[hb][dt];
         }
     }
 }
@@ -639,7 +618,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // Merge the key splits of one (row, head): m* = max m_s, w_s = 2^(m_s - m*),
 // out = sum_s w_s O_s / sum_s w_s l_s, lse = (m* + log2 sum_s w_s l_s) ln 2.
 // With fp16 partials (HALF) a split stores U_s = O_s / l_s scaled by a power
-// of two per quarter of the value dims, so its weight in the sum becomes
+// of two per 16 value dims, so its weight in the sum becomes
 // w_s l_s times that scale.  Each thread owns 4 value dims.  The partial
 // outputs of the first MB splits (MB = 16, or 64 for more than 16 splits)
 // are requested before anything else, so they are in flight while the block
@@ -674,15 +653,16 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     const bool mine = d < DV;
     const int64_t pbase = ((int64_t)r * ns * H + h) * DV + (mine ? d : 0);
     const int64_t sstride = (int64_t)H * DV;
-    // fp16 partials: this thread's quarter of the value dims picks the scale
-    const float* scp = HALF ? a.part_sc + ((int64_t)r * ns * 4 + (mine ? d / (DV / 4) : 0)) * H + h : nullptr;
+    // fp16 partials: this thread's 16-dim tile of the value dims picks the scale
+    const int64_t sc_stride = (int64_t)(DV / 16) * H;       // between splits
+    const float* scp = HALF ? a.part_sc + ((int64_t)r * ns * (DV / 16) + (mine ? d / 16 : 0)) * H + h : nullptr;
     typename MP::raw os[MB];
     float sc[HALF ? MB : 1];
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
         if (j < ns) {
             os[j] = MP::load(a, pbase + j * sstride);
-            if constexpr (HALF) sc[j] = scp[(int64_t)j * 4 * H];
+            if constexpr (HALF) sc[j] = scp[(int64_t)j * sc_stride];
         }
     }
     const int s1 = tid + kMergeThreads;
@@ -722,7 +702,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
         for (int j = 0; j < MB; ++j) {
             if (s0 + j < ns) {
                 os[j] = MP::load(a, pbase + (s0 + j) * sstride);
-                if constexpr (HALF) sc[j] = scp[(int64_t)(s0 + j) * 4 * H];
+                if constexpr (HALF) sc[j] = scp[(int64_t)(s0 + j) * sc_stride];
             }
         }
 #pragma unroll
@@ -844,10 +824,9 @@ hipError_t launch_dims(const AttnArgs& a, hipStream_t stream) {
 }  // namespace
 
 int attn_f32_max_keys() { return kF32MaxKeys; }
-int attn_max_split_tiles() { return kIdxLds / kKeys; }
+int attn_max_split_tiles() { return kRowsLds / kKeys; }
 int attn_max_splits() { return kMaxSplits; }
 int attn_tile_keys() { return kKeys; }
-int attn_max_table_blocks() { return kBtLds; }
 
 bool attn_supported(int q_dtype, int kv_dtype, int win_dtype, int H, int D, int d_v) {
     if (q_dtype == DT_F32)

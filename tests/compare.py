@@ -13,8 +13,12 @@
 * End-to-end top-k: with L_k the oracle's k-th largest logit and
   tau = 1e-3 |L_k|, the device set holds every entry above L_k + tau and
   none below L_k - tau, and has min(k, n) entries.
-* Attention outputs: max-abs 2e-2 and mean-abs 2e-3 for bf16/FP8 paths,
-  max-abs 5e-2 for MXFP4 caches; fp32 workloads max-abs 1e-5.
+* Attention outputs: max-abs 2e-2, mean-abs 2e-3 and relative L2 1e-2 for
+  bf16/FP8 paths, max-abs 5e-2 for MXFP4 caches, on the raw fp32 outputs;
+  fp32 workloads max-abs 1e-5.  Tests of the bf16-output variant (and only
+  those) pass out_bf16=True, which discounts the output's own rounding, half
+  a bf16 ulp of the value: at the csa outlier channels' magnitudes (16-32)
+  that is up to 0.0625, beyond the 2e-2 bound by itself.
 """
 import numpy as np
 
@@ -108,9 +112,13 @@ def check_topk_band(got_idx, ora_logits, n, k):
     return len(s ^ ora) // 2
 
 
-def check_attention(got, want, kind, out_bf16=False):
+def check_attention(got, want, kind, out_bf16=False, rel_l2=True):
     """out_bf16: the device output is stored in bf16, whose own rounding
-    (half an ulp of the value) is added to the tolerance."""
+    (half an ulp of the value) is added to the tolerance.  rel_l2=False for
+    comparisons across two different (both valid) top-k selections: one
+    entry swapped inside the tie band moves a flat-softmax output by about
+    1/k of a value vector, some 2 % of the output's norm, while max-abs and
+    mean-abs stay within their bounds."""
     got = got.astype(np.float64)
     d = np.abs(got - want)
     if out_bf16:
@@ -122,4 +130,4 @@ def check_attention(got, want, kind, out_bf16=False):
     assert d.max() <= max_abs, "max-abs %.3g > %.3g" % (d.max(), max_abs)
     assert d.mean() <= 2e-3, "mean-abs %.3g" % d.mean()
     rel = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30)
-    assert rel <= 1e-2, "relative L2 %.3g" % rel
+    assert rel <= 1e-2 or not rel_l2, "relative L2 %.3g" % rel
