@@ -320,6 +320,32 @@ lcca_status lcca_sparse_attn_fwd(void* stream, const lcca_pages* pages, const lc
 size_t lcca_sparse_attn_workspace_size(const lcca_rows* rows, int32_t ratio_m, int32_t H, int32_t dim,
                                        int32_t d_v, int32_t k, int32_t topk_given, int32_t window);
 
+/*
+ * lcca_sparse_attn_fwd_noalloc -- lcca_sparse_attn_fwd without a workspace.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops that must not call hipMalloc, harnesses that forbid
+ * it.  Same arguments, results and kernels as lcca_sparse_attn_fwd; the split
+ * partial states go to the library's own device scratch array of
+ * LCCA_ATTN_SCRATCH_BYTES (64 MiB), one per GPU, held from the library's load
+ * on that GPU until the process ends.  The call allocates nothing and frees
+ * nothing.
+ *   - A call whose partial states (lcca_sparse_attn_workspace_size for the
+ *     same arguments) exceed LCCA_ATTN_SCRATCH_BYTES returns
+ *     LCCA_ERR_UNSUPPORTED and launches nothing.
+ *   - Every call on one GPU uses the same array: calls that overlap on one
+ *     GPU (on different streams, or from different threads without ordering)
+ *     race and give undefined results.  Calls ordered on one stream are safe.
+ *     Nothing in the array needs clearing between calls.
+ *   - The array's device address is looked up on the first call on each GPU
+ *     (with that GPU current); a failure returns LCCA_ERR_HIP.
+ */
+#define LCCA_ATTN_SCRATCH_BYTES ((size_t)64 << 20)
+lcca_status lcca_sparse_attn_fwd_noalloc(void* stream, const lcca_pages* pages, const lcca_rows* rows,
+                                         int32_t q_dtype, const void* q, int32_t H, int32_t d_v, float sm_scale,
+                                         const lcca_paged_cache* kv, const int32_t* topk_idx, int32_t k,
+                                         const lcca_window_cache* win, int32_t out_dtype, void* out, float* lse);
+
 const char* lcca_status_string(lcca_status s);
 const char* lcca_last_error(void);
 const char* lcca_version(void);

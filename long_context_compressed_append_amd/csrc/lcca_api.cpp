@@ -17,6 +17,9 @@ int attn_f32_max_keys();
 int attn_max_split_tiles();
 int attn_max_splits();
 int attn_tile_keys();
+// the scratch array of lcca_sparse_attn_fwd_noalloc (attn_scratch.hip)
+size_t attn_scratch_bytes();
+hipError_t attn_scratch(void** ptr);
 }
 
 namespace {
@@ -378,10 +381,18 @@ size_t lcca_sparse_attn_workspace_size(const lcca_rows* rows, int32_t ratio_m, i
     return attn_plan(rows->num_rows, rows->max_pos, ratio_m, H, d_v, k, topk_given != 0, window).ws_bytes;
 }
 
-lcca_status lcca_sparse_attn_fwd(void* stream, const lcca_pages* pages, const lcca_rows* rows, int32_t q_dtype,
-                                 const void* q, int32_t H, int32_t d_v, float sm_scale, const lcca_paged_cache* kv,
-                                 const int32_t* topk_idx, int32_t k, const lcca_window_cache* win, int32_t out_dtype,
-                                 void* out, float* lse, void* ws, size_t ws_bytes) {
+}  // extern "C"
+
+namespace {
+
+// The attention call with its partial states in `ws` (the caller's
+// workspace), or, with `scratch` set, in the library's per-device scratch
+// array, whose maximum size is checked against the plan before it is looked
+// up.
+lcca_status attn_call(void* stream, const lcca_pages* pages, const lcca_rows* rows, int32_t q_dtype, const void* q,
+                      int32_t H, int32_t d_v, float sm_scale, const lcca_paged_cache* kv, const int32_t* topk_idx,
+                      int32_t k, const lcca_window_cache* win, int32_t out_dtype, void* out, float* lse, void* ws,
+                      size_t ws_bytes, bool scratch) {
     g_err[0] = 0;
     lcca_status s;
     if ((s = check_pages(pages))) return s;
@@ -412,6 +423,13 @@ lcca_status lcca_sparse_attn_fwd(void* stream, const lcca_pages* pages, const lc
                         lcca::attn_f32_max_keys());
         plan = AttnPlan{1, 1, 0};
     }
+    if (scratch && plan.ws_bytes > 0) {
+        if (plan.ws_bytes > lcca::attn_scratch_bytes())
+            return fail(LCCA_ERR_UNSUPPORTED, "sparse_attn_fwd_noalloc: partial states of %zu bytes exceed the %zu-byte "
+                        "scratch array", plan.ws_bytes, lcca::attn_scratch_bytes());
+        if ((s = hip_status(lcca::attn_scratch(&ws), "scratch array lookup"))) return s;
+        ws_bytes = lcca::attn_scratch_bytes();
+    }
     if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes))
         return fail(LCCA_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, plan.ws_bytes);
     if (plan.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(ws) & 15))
@@ -441,6 +459,26 @@ lcca_status lcca_sparse_attn_fwd(void* stream, const lcca_pages* pages, const lc
         }
     }
     return hip_status(lcca::launch_sparse_attn(a, (hipStream_t)stream), "sparse_attn launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+lcca_status lcca_sparse_attn_fwd(void* stream, const lcca_pages* pages, const lcca_rows* rows, int32_t q_dtype,
+                                 const void* q, int32_t H, int32_t d_v, float sm_scale, const lcca_paged_cache* kv,
+                                 const int32_t* topk_idx, int32_t k, const lcca_window_cache* win, int32_t out_dtype,
+                                 void* out, float* lse, void* ws, size_t ws_bytes) {
+    return attn_call(stream, pages, rows, q_dtype, q, H, d_v, sm_scale, kv, topk_idx, k, win, out_dtype, out, lse, ws,
+                     ws_bytes, false);
+}
+
+lcca_status lcca_sparse_attn_fwd_noalloc(void* stream, const lcca_pages* pages, const lcca_rows* rows,
+                                         int32_t q_dtype, const void* q, int32_t H, int32_t d_v, float sm_scale,
+                                         const lcca_paged_cache* kv, const int32_t* topk_idx, int32_t k,
+                                         const lcca_window_cache* win, int32_t out_dtype, void* out, float* lse) {
+    return attn_call(stream, pages, rows, q_dtype, q, H, d_v, sm_scale, kv, topk_idx, k, win, out_dtype, out, lse,
+                     nullptr, 0, true);
 }
 
 }  // extern "C"

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_PKG, "liblcca.so")
 
 EXPORTED = ("lcca_compress_append", "lcca_index_logits", "lcca_topk_select", "lcca_sparse_attn_fwd",
             "lcca_sparse_attn_workspace_size", "lcca_topk_workspace_size", "lcca_status_string", "lcca_last_error",
-            "lcca_version", "lcca_decode_select", "lcca_decode_select_workspace_size", "lcca_remainder_bytes")
+            "lcca_version", "lcca_decode_select", "lcca_decode_select_workspace_size", "lcca_remainder_bytes",
+            "lcca_sparse_attn_fwd_noalloc")
 
 
 class LccaError(RuntimeError):
@@ -71,6 +72,7 @@ def lib():
         L.lcca_index_logits.argtypes = [P, PP, PR, i32, P, i32, P, f32, PC, P, i64]
         L.lcca_topk_select.argtypes = [P, PR, i32, P, i64, i32, P, P, sz]
         L.lcca_sparse_attn_fwd.argtypes = [P, PP, PR, i32, P, i32, i32, f32, PC, P, i32, PW, i32, P, P, P, sz]
+        L.lcca_sparse_attn_fwd_noalloc.argtypes = [P, PP, PR, i32, P, i32, i32, f32, PC, P, i32, PW, i32, P, P]
         L.lcca_decode_select.argtypes = [P, PP, PR, P, P, i32, i32, P, P, P, P, PC, PC, PW, PM,
                                          i32, P, i32, P, f32, P, i64, i32, P, P, sz]
         L.lcca_sparse_attn_workspace_size.argtypes = [PR, i32, i32, i32, i32, i32, i32, i32]
@@ -82,7 +84,7 @@ def lib():
         L.lcca_remainder_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.lcca_remainder_bytes.restype = sz
         for n in ("lcca_compress_append", "lcca_index_logits", "lcca_topk_select", "lcca_sparse_attn_fwd",
-                  "lcca_decode_select"):
+                  "lcca_decode_select", "lcca_sparse_attn_fwd_noalloc"):
             getattr(L, n).restype = i32
         L.lcca_status_string.argtypes = [i32]
         for n in ("lcca_status_string", "lcca_last_error", "lcca_version"):
@@ -262,3 +264,14 @@ def sparse_attn_fwd(pages: Pages, rows: Rows, q_dtype: int, q, H: int, d_v: int,
     _check(lib().lcca_sparse_attn_fwd(_stream(stream), ctypes.byref(pages.c()), ctypes.byref(rows.c()), q_dtype,
                                       _ptr(q), H, d_v, float(sm_scale), ctypes.byref(kv.c()), _ptr(topk_idx), k,
                                       ctypes.byref(win.c()), out_dtype, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes))
+
+
+def sparse_attn_fwd_noalloc(pages: Pages, rows: Rows, q_dtype: int, q, H: int, d_v: int, sm_scale: float,
+                            kv: PagedCache, topk_idx, k: int, win: WindowCache, out_dtype: int, out, lse=None,
+                            stream=None):
+    """sparse_attn_fwd with the split partial states in the library's own
+    device scratch array (no workspace, no allocation)."""
+    _check(lib().lcca_sparse_attn_fwd_noalloc(_stream(stream), ctypes.byref(pages.c()), ctypes.byref(rows.c()),
+                                              q_dtype, _ptr(q), H, d_v, float(sm_scale), ctypes.byref(kv.c()),
+                                              _ptr(topk_idx), k, ctypes.byref(win.c()), out_dtype, _ptr(out),
+                                              _ptr(lse)))

@@ -215,3 +215,23 @@ def test_remainder_bytes_layout():
     assert rem.ik_logit.data_ptr() + rem.ik_logit.numel() * 4 - base == want
     with pytest.raises(lcca.LccaError):
         lcca.remainder_in(buf[:want - 1], 16, 4, 576, 128, lcca.BF16)
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch():
+    """lcca_sparse_attn_fwd_noalloc refuses, before any launch, arguments whose
+    split partial states exceed its scratch array (64 MiB)."""
+    L = lcca.lib()
+    by = ctypes.byref
+    pages = lcca._Pages(100, 4096, 1)
+    rows = lcca._Rows(100, (1 << 20) - 1, 1, 1)
+    kv = _pool(lcca.BF16, 576, m=128, blocks=4096 * 100)
+    win = lcca._WindowCache(lcca.FP8_E4M3, 576, 128, 128, 1, 1)
+    need = L.lcca_sparse_attn_workspace_size(by(rows), 128, 640, 576, 576, 0, 0, 128)
+    assert need > (64 << 20)
+    st = L.lcca_sparse_attn_fwd_noalloc(None, by(pages), by(rows), lcca.BF16, 1, 640, 576, 0.04, by(kv), None, 0,
+                                        by(win), lcca.F32, 1, None)
+    assert st == lcca.ERR_UNSUPPORTED and b"scratch" in L.lcca_last_error()
+    # the same validation as the workspace entry point
+    st = L.lcca_sparse_attn_fwd_noalloc(None, by(pages), by(rows), lcca.BF16, None, 640, 576, 0.04, by(kv), None,
+                                        0, by(win), lcca.F32, 1, None)
+    assert st == lcca.ERR_INVALID_ARG
