@@ -1,7 +1,19 @@
-// compress_append kernel: grid (new token, slice); the device code is in
-// compress_dev.h.
+// compress_append kernels; the per-slice device code is in compress_dev.h.
 // [Page "vLLM uveo DeepSeek V4 s 8,7x manjim KV cacheom", section "Kako
-//  funkcionira optimizacija KV cachea?": weighted summation of tokens.]
+//  funkcionira optimizacija KV cachea?": weighted summation of tokens;
+//  section "Sto je vLLM morao rijesiti u integraciji?": 256-position blocks,
+//  remainder of the compressor kept as sliding-window state.]
+//
+// Two launch shapes:
+//   * few new tokens (decode) or groups of more than 32 tokens: grid (new
+//     token, slice) of compress_dev.h;
+//   * chunks (chunked prefill): one workgroup per 16 consecutive new tokens
+//     (counted over the whole call), which writes their window slots, forms
+//     every group one of them completes (both streams, all dimensions) and,
+//     for the sequence it is assigned to, the remainder ring.  The entries'
+//     arithmetic is the slice kernel's, step for step (weights by one wave's
+//     max, exponentials and butterfly sum; products w_i x_i rounded one by one
+//     and summed in token order), so both shapes store the same codes.
 #include "compress_dev.h"
 
 namespace lcca {
@@ -13,10 +25,287 @@ __global__ __launch_bounds__(cmp::kThreads) void compress_append_kernel(Compress
     cmp::compress_append_body<TOK>(p, blockIdx.x, blockIdx.y);
 }
 
+constexpr int kChunkTokens = 16;            // new tokens per workgroup
+constexpr int kChunkMaxM = 8;               // largest group the chunk kernel forms
+constexpr int kChunkMinTokens = 64;         // calls with fewer new tokens use the slice grid
+constexpr int kRoundSlots = 4;              // 8-dimension items per thread per round of loads
+
+// The encode of one 8-dimension chunk of an entry (v: its aggregate values)
+// into the pool; MXFP4 blocks of 32 dimensions are held by four adjacent
+// lanes (amax over them by two lane exchanges, the scale byte by the first).
+__device__ __forceinline__ void store_entry_chunk(const CompressArgs& p, bool ik, int64_t row, int d0, const float (&v)[8],
+                                                  bool active) {
+    const int dim = ik ? p.dI : p.D;
+    const int dt = ik ? p.ik_dtype : p.kv_dtype;
+    uint8_t* data = reinterpret_cast<uint8_t*>(ik ? p.ik_data : p.kv_data);
+    if (dt == DT_MXFP4) {
+        // (every lane takes part in the exchanges; inactive lanes hold zeros)
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
+        a = fmaxf(a, __shfl_xor(a, 1));
+        a = fmaxf(a, __shfl_xor(a, 2));
+        const int X = mx_scale_exp(a);
+        uint32_t wd = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wd |= fp4_code(ldexpf(v[e], -X)) << (4 * e);
+        if (active) {
+            *reinterpret_cast<uint32_t*>(data + row * (int64_t)(dim / 2) + d0 / 2) = wd;
+            if ((d0 & 31) == 0) reinterpret_cast<uint8_t*>(p.kv_scale)[row * (int64_t)(dim / 32) + d0 / 32] = (uint8_t)(X + 127);
+        }
+        return;
+    }
+    if (!active) return;
+    if (dt == DT_BF16) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(data) + row * dim + d0;
+        *reinterpret_cast<u32x4*>(o) = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                                             pack_bf16x2(v[6], v[7])};
+    } else if (dt == DT_FP8) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            lo |= f32_to_fp8(v[e]) << (8 * e);
+            hi |= f32_to_fp8(v[4 + e]) << (8 * e);
+        }
+        *reinterpret_cast<u32x2*>(data + row * (int64_t)dim + d0) = u32x2{lo, hi};
+    } else {
+        float* o = reinterpret_cast<float*>(data) + row * dim + d0;
+        *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    }
+}
+
+// One 8-value chunk of a token into its window slot (F32, BF16, or FP8 with
+// the token's scale `sc`).
+__device__ __forceinline__ void store_window_chunk(const CompressArgs& p, int64_t slot, int d0, const float (&x)[8],
+                                                   float sc) {
+    const int D = p.D;
+    uint8_t* wd = reinterpret_cast<uint8_t*>(p.win_data);
+    if (p.win_dtype == DT_FP8) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            lo |= f32_to_fp8(x[e] / sc) << (8 * e);
+            hi |= f32_to_fp8(x[4 + e] / sc) << (8 * e);
+        }
+        *reinterpret_cast<u32x2*>(wd + slot * D + d0) = u32x2{lo, hi};
+    } else if (p.win_dtype == DT_BF16) {
+        *reinterpret_cast<u32x4*>(wd + (slot * D + d0) * 2) =
+            u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+    } else {
+        float* o = reinterpret_cast<float*>(wd) + slot * D + d0;
+        *reinterpret_cast<f32x4*>(o) = f32x4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<f32x4*>(o + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    }
+}
+
+template <int TOK>
+__global__ __launch_bounds__(cmp::kThreads) void compress_chunk_kernel(CompressArgs p, int total_new) {
+    constexpr int NT = cmp::kThreads;
+    __shared__ int cu_lds[cmp::kSeqLds + 1], sp_lds[cmp::kSeqLds];
+    __shared__ int tk_b[kChunkTokens], tk_pos[kChunkTokens], tk_start[kChunkTokens], tk_end[kChunkTokens];
+    __shared__ long long tk_c0[kChunkTokens];
+    __shared__ int grp_tok[kChunkTokens], n_grp, tail_tok;
+    __shared__ long long grp_row[kChunkTokens];
+    __shared__ float w_lds[2][kChunkTokens][kChunkMaxM];
+    __shared__ unsigned int amax_lds[kChunkTokens];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = (int)blockIdx.x * kChunkTokens;
+    const int ntok = min(kChunkTokens, total_new - t0);
+    const int m = p.m;
+    const bool in_lds = p.batch <= cmp::kSeqLds;
+    if (in_lds) {
+        for (int i = tid; i <= p.batch; i += NT) {
+            cu_lds[i] = p.cu_new[i];
+            if (i < p.batch) sp_lds[i] = p.start_pos[i];
+        }
+    }
+    if (tid == 0) { n_grp = 0; tail_tok = -1; }
+    if (tid < kChunkTokens) amax_lds[tid] = 0u;
+    __syncthreads();
+    // each token: its sequence, position, and whether it completes a group
+    // or carries the sequence's remainder-ring duty
+    if (tid < ntok) {
+        const int t = t0 + tid;
+        auto cu = [&](int i) { return in_lds ? cu_lds[i] : p.cu_new[i]; };
+        int lo = 0, hi = p.batch - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cu(mid) <= t) lo = mid; else hi = mid - 1;
+        }
+        const int c0 = cu(lo), n = cu(lo + 1) - c0;
+        const int start = in_lds ? sp_lds[lo] : p.start_pos[lo];
+        const int end = start + n, pos = start + (t - c0);
+        tk_b[tid] = lo; tk_pos[tid] = pos; tk_start[tid] = start; tk_end[tid] = end; tk_c0[tid] = c0;
+        const int g0 = start / m;
+        // the chunk reads ring slots (its first group starts before it) and
+        // rewrites ring slots (it ends inside a group): the tail waits for the
+        // first group's reads, in the workgroup that forms it
+        const bool race = (start % m) != 0 && (end % m) != 0 && end >= (g0 + 1) * m;
+        const bool tail_here = (end % m) != 0 && (race ? pos == (g0 + 1) * m - 1 : pos == end - 1);
+        if (tail_here) tail_tok = tid;
+        if ((pos + 1) % m == 0) {
+            const int k = atomicAdd(&n_grp, 1);
+            grp_tok[k] = tid;
+            const int g = pos / m, E = 256 / m;
+            grp_row[k] = (long long)p.block_table[(int64_t)lo * p.max_blocks + g / E] * E + g % E;
+        }
+    }
+    __syncthreads();
+    const int ng = n_grp;
+    // softmax weights of each group's logits, one wave per (group, stream),
+    // with the slice kernel's reductions
+    const int nstream = p.ik_data != nullptr ? 2 : 1;
+    for (int it = wave; it < ng * nstream; it += NT / 64) {
+        const int k = it / nstream, s = it % nstream;
+        const int tk = grp_tok[k];
+        const int b = tk_b[tk], start = tk_start[tk], g = tk_pos[tk] / m;
+        const float* lg = s ? p.ik_logit : p.kv_logit;
+        const float* rlg = s ? p.rem_ik_logit : p.rem_kv_logit;
+        float a = -INFINITY;
+        if (lane < m) {
+            const int t = g * m + lane;
+            a = t >= start ? lg[tk_c0[tk] + (t - start)] : rlg[(int64_t)b * m + t % m];
+        }
+        const float mx = wave_max(a);
+        const float e = lane < m ? expf(a - mx) : 0.0f;
+        const float sum = wave_sum(e);
+        if (lane < m) w_lds[s][k][lane] = e / sum;
+    }
+    __syncthreads();
+    // entries: items (group, stream, 8-dimension chunk), SLOTS per thread per
+    // round; a round requests all of its tokens' chunks before forming any.
+    // A group's items are padded to a multiple of four, and MXFP4 pools (kv
+    // only) have dimensions in multiples of 32, so the four chunks of an MXFP4
+    // block sit on four adjacent lanes.
+    {
+        constexpr int SLOTS = TOK == DT_F32 ? kRoundSlots / 2 : kRoundSlots;
+        const int nkv = p.D / 8, nik = p.ik_data != nullptr ? p.dI / 8 : 0;
+        const int per = nkv + ((nik + 3) & ~3);
+        const int items = ng * per;
+        for (int base = 0; base < items; base += NT * SLOTS) {
+            cmp::RawChunk<TOK> raw[SLOTS][kChunkMaxM];
+#pragma unroll
+            for (int j = 0; j < SLOTS; ++j) {
+                const int it = base + tid + NT * j;
+                if (it < items && it % per < nkv + nik) {
+                    const int k = it / per, u = it % per, tk = grp_tok[k];
+                    const bool ik = u >= nkv;
+                    const int d0 = ik ? (u - nkv) * 8 : u * 8, dim = ik ? p.dI : p.D;
+                    const int b = tk_b[tk], start = tk_start[tk], g = tk_pos[tk] / m;
+                    const void* tok = ik ? p.ik_tok : p.kv_tok;
+                    const void* rtok = ik ? p.rem_ik : p.rem_kv;
+#pragma unroll
+                    for (int i = 0; i < kChunkMaxM; ++i) {
+                        if (i < m) {
+                            const int t = g * m + i;
+                            const int64_t trow = t >= start ? tk_c0[tk] + (t - start) : (int64_t)b * m + t % m;
+                            cmp::load_chunk<TOK>(t >= start ? tok : rtok, trow * dim + d0, raw[j][i]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < SLOTS; ++j) {
+                const int it = base + tid + NT * j;
+                const bool active = it < items && it % per < nkv + nik;
+                const int k = active ? it / per : 0, u = active ? it % per : 0;
+                const bool ik = u >= nkv;
+                const int d0 = ik ? (u - nkv) * 8 : u * 8;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+                if (active) {
+                    // the products rounded one by one, then summed in token
+                    // order, as in the slice kernel
+#pragma clang fp contract(off)
+                    const float* w = &w_lds[ik ? 1 : 0][k][0];
+#pragma unroll
+                    for (int i = 0; i < kChunkMaxM; ++i) {
+                        if (i < m) {
+                            float x[8];
+                            cmp::unpack_chunk<TOK>(raw[j][i], x);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) v[e] = v[e] + fmaf(w[i], x[e], 0.0f);
+                        }
+                    }
+                }
+                // MXFP4 lane exchanges: every lane of the wave takes part
+                store_entry_chunk(p, ik, active ? grp_row[k] : 0, d0, v, active);
+            }
+        }
+    }
+    // window slots of the tokens among the last `capacity` of their chunk:
+    // items (token, 8-value chunk).  FP8 windows take each token's max first
+    // (a pass of loads and an LDS max), then encode in a second pass.
+    if (p.win_data != nullptr) {
+        const int nch = p.D / 8;
+        const int items = ntok * nch;
+        const bool fp8 = p.win_dtype == DT_FP8;
+        for (int pass = fp8 ? 0 : 1; pass < 2; ++pass) {
+            if (pass == 1 && fp8) __syncthreads();
+            for (int base = 0; base < items; base += NT * kRoundSlots) {
+                cmp::RawChunk<TOK> raw[kRoundSlots];
+#pragma unroll
+                for (int j = 0; j < kRoundSlots; ++j) {
+                    const int it = base + tid + NT * j;
+                    if (it < items) {
+                        const int tk = it / nch, c = it % nch;
+                        if (tk_pos[tk] >= tk_end[tk] - p.win_cap)
+                            cmp::load_chunk<TOK>(p.kv_tok, (int64_t)(t0 + tk) * p.D + 8 * c, raw[j]);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < kRoundSlots; ++j) {
+                    const int it = base + tid + NT * j;
+                    if (it >= items) continue;
+                    const int tk = it / nch, c = it % nch;
+                    const int pos = tk_pos[tk];
+                    if (pos < tk_end[tk] - p.win_cap) continue;
+                    float x[8];
+                    cmp::unpack_chunk<TOK>(raw[j], x);
+                    if (pass == 0) {
+                        float a = 0.0f;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[e]));
+                        atomicMax(&amax_lds[tk], __float_as_uint(a));      // non-negative: ordered as integers
+                    } else {
+                        float sc = 1.0f;
+                        const int64_t slot = (int64_t)tk_b[tk] * p.win_cap + pos % p.win_cap;
+                        if (fp8) {
+                            const float amax = __uint_as_float(amax_lds[tk]);
+                            sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+                            if (c == 0) p.win_scale[slot] = sc;
+                        }
+                        store_window_chunk(p, slot, 8 * c, x, sc);
+                    }
+                }
+            }
+        }
+    }
+    // remainder ring of the sequence this workgroup carries the duty for:
+    // after every read of the ring above
+    __syncthreads();
+    if (tail_tok >= 0) {
+        const int tk = tail_tok;
+        const cmp::SeqChunk q{tk_b[tk], tk_start[tk], tk_end[tk], tk_end[tk] - tk_start[tk], tk_c0[tk]};
+        const int tail0 = max((q.end / m) * m, q.start);
+        for (int tt = tail0; tt < q.end; ++tt) cmp::write_ring<TOK>(p, q, tt);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_compress_append(const CompressArgs& a, int total_new, hipStream_t stream) {
     if (total_new <= 0) return hipSuccess;
+    if (total_new >= kChunkMinTokens && a.m <= kChunkMaxM) {
+        const dim3 grid((total_new + kChunkTokens - 1) / kChunkTokens);
+        if (a.tok_dtype == DT_F32)
+            hipLaunchKernelGGL(compress_chunk_kernel<DT_F32>, grid, dim3(cmp::kThreads), 0, stream, a, total_new);
+        else
+            hipLaunchKernelGGL(compress_chunk_kernel<DT_BF16>, grid, dim3(cmp::kThreads), 0, stream, a, total_new);
+        return hipGetLastError();
+    }
     const int SK = (a.D + cmp::kSliceDims - 1) / cmp::kSliceDims;
     const int SI = a.ik_data != nullptr ? (a.dI + cmp::kSliceDims - 1) / cmp::kSliceDims : 0;
     dim3 grid(total_new, SK + SI + 1);
