@@ -23,8 +23,15 @@
  *     bytes.
  *   - Arguments are validated on the host before any launch; a failing call
  *     launches nothing and returns a negative lcca_status, with details in
- *     lcca_last_error() (thread-local).  Device-side indices (block table,
- *     top-k indices, positions) are trusted: the host cannot see them.
+ *     lcca_last_error() (thread-local).  Indices that live in device memory
+ *     (block-table entries, row_seq, row_pos, cu_new, start_pos) cannot be
+ *     seen by the host: the release library uses them as given, and values
+ *     outside their contract make kernels read or write outside the
+ *     buffers.  The debug library (liblcca_debug.so, built with LCCA_DEBUG)
+ *     checks each of them on the device before it forms an address, uses a
+ *     value inside the range instead of a bad one, and records the violation
+ *     for lcca_debug_check() (see there).  Top-k indices need no such check:
+ *     entries < 0 or >= the row's visible count are skipped by contract.
  *
  * Data layout
  *   dtype codes: LCCA_F32 (4 B), LCCA_BF16 (2 B), LCCA_FP8_E4M3 (1 B, OCP
@@ -82,6 +89,15 @@ typedef int32_t lcca_status;
 #define LCCA_ERR_UNSUPPORTED (-2)   /* dtype or shape combination not built          */
 #define LCCA_ERR_WORKSPACE   (-3)   /* workspace missing or smaller than required    */
 #define LCCA_ERR_HIP         (-4)   /* a HIP runtime call or kernel launch failed    */
+#define LCCA_ERR_DEVICE_INDEX (-5)  /* debug build: a device-side index was out of range */
+
+/* Bits of the debug library's device error word (lcca_debug_check). */
+#define LCCA_DBG_BLOCK 1u   /* a block-table entry read outside [0, pool num_blocks)     */
+#define LCCA_DBG_ROW   2u   /* row_seq outside [0, batch) or row_pos outside [0, max_pos] */
+#define LCCA_DBG_CHUNK 4u   /* cu_new / start_pos of compress_append outside their contract:
+                               cu_new[b] <= t < cu_new[b+1] <= total_new fails for a new
+                               token t, start_pos[b] < 0, or the chunk ends beyond the
+                               block table (max_blocks_per_seq * 256 positions)          */
 
 typedef enum { LCCA_F32 = 0, LCCA_BF16 = 1, LCCA_FP8_E4M3 = 2, LCCA_MXFP4 = 3 } lcca_dtype;
 
@@ -295,7 +311,7 @@ size_t lcca_decode_select_workspace_size(const lcca_rows* rows, int32_t ratio_m,
  * with all keys in ONE softmax.  Keys are split across workgroups and the
  * partial softmax states are merged (max, rescaled sums); for BF16 outputs
  * a split's O / sum is kept as fp16 (11 significant bits against the
- * output's 8) with a power-of-two range scale per split, head and 32 value
+ * output's 8) with a power-of-two range scale per split, head and 16 value
  * dims, for F32 outputs in fp32.
  *   q        device [num_rows][H][kv->dim] of q_dtype (F32 with F32 cache;
  *            BF16 otherwise)
@@ -345,6 +361,29 @@ lcca_status lcca_sparse_attn_fwd_noalloc(void* stream, const lcca_pages* pages, 
                                          int32_t q_dtype, const void* q, int32_t H, int32_t d_v, float sm_scale,
                                          const lcca_paged_cache* kv, const int32_t* topk_idx, int32_t k,
                                          const lcca_window_cache* win, int32_t out_dtype, void* out, float* lse);
+
+/*
+ * lcca_debug_check -- index violations the debug library's kernels found.
+ *
+ * For development and for callers that cannot vouch for their device-side
+ * indices.  In the debug library (liblcca_debug.so: every kernel built with
+ * LCCA_DEBUG, the same entry points and results for valid inputs) each
+ * block-table entry, row_seq, row_pos, cu_new and start_pos value a kernel
+ * reads is checked before it forms an address.  A value outside its range
+ * (LCCA_DBG_* above) is replaced by the range's first value (block 0,
+ * sequence 0, position 0; a compress_append token of a bad chunk is treated
+ * as a chunk of its own at position 0), so every access stays inside the
+ * caller's buffers and every kernel finishes; the outputs of such a call are
+ * unspecified, and the violation's bit is set in the current device's error
+ * word.  lcca_debug_check waits for `stream`, reads the word into *bits (may
+ * be NULL) and clears it.  Returns LCCA_OK if no bit was set,
+ * LCCA_ERR_DEVICE_INDEX (with the bits named in lcca_last_error()) if one
+ * was, LCCA_ERR_HIP if a runtime call failed.  The word is shared by every
+ * stream of the device: calls on other streams that run meanwhile add their
+ * bits.  The release library keeps no word: there it sets *bits = 0 and
+ * returns LCCA_ERR_UNSUPPORTED.
+ */
+lcca_status lcca_debug_check(void* stream, uint32_t* bits);
 
 const char* lcca_status_string(lcca_status s);
 const char* lcca_last_error(void);

@@ -1,9 +1,12 @@
-"""Build liblcca.so (gfx950) in-tree with hipcc.
+"""Build liblcca.so and liblcca_debug.so (gfx950) in-tree with hipcc.
 
-    python -m long_context_compressed_append_amd.build
+    python -m long_context_compressed_append_amd.build [--release-only]
 
-Each source compiles to an object under _build/ at the repository root, then
-everything links into long_context_compressed_append_amd/liblcca.so.
+Each source compiles to an object under _build/ (the debug library's under
+_build/debug/) at the repository root, then everything links into
+long_context_compressed_append_amd/liblcca.so.  The debug library is the same
+sources built with LCCA_DEBUG: its kernels check every index they read from
+device memory before forming an address (lcca_debug_check in lcca.h).
 Device code is built with packed-fp32 instructions disabled.
 """
 import os
@@ -16,6 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblcca.so")
+DEBUG_LIB = os.path.join(PKG, "liblcca_debug.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 ARCH = "gfx950"
@@ -40,10 +44,11 @@ def sources():
     return out
 
 
-def _compile(item, verbose):
+def _compile(item, verbose, debug):
     src, device = item
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + (DEVICE if device else []) + EXTRA.get(os.path.basename(src), []) + COMMON + ["-c", src, "-o", obj]
+    obj = os.path.join(BUILD, "debug" if debug else "", os.path.basename(src) + ".o")
+    cmd = [HIPCC] + (DEVICE if device else []) + EXTRA.get(os.path.basename(src), []) + COMMON + \
+        (["-DLCCA_DEBUG"] if debug else []) + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,22 +58,33 @@ def _compile(item, verbose):
     return obj, warn
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build_one(debug: bool, verbose: bool = False, jobs: int = 8) -> str:
+    """Compile and link one of the two libraries; returns its path."""
+    lib = DEBUG_LIB if debug else LIB
+    os.makedirs(os.path.join(BUILD, "debug") if debug else BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(lambda it: _compile(it, verbose), sources()))
+        results = list(ex.map(lambda it: _compile(it, verbose, debug), sources()))
     for _, warn in results:
         if warn and verbose:
             print(warn, file=sys.stderr)
     objs = [o for o, _ in results]
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False, jobs: int = 8, debug: bool = True) -> str:
+    """Build liblcca.so and (unless debug is False) liblcca_debug.so; returns
+    the release library's path."""
+    path = build_one(False, verbose, jobs)
+    if debug:
+        build_one(True, verbose, jobs)
+    return path
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, debug="--release-only" not in sys.argv))

@@ -105,7 +105,8 @@ __global__ __launch_bounds__(cmp::kThreads) void compress_chunk_kernel(CompressA
     __shared__ int cu_lds[cmp::kSeqLds + 1], sp_lds[cmp::kSeqLds];
     __shared__ int tk_b[kChunkTokens], tk_pos[kChunkTokens], tk_start[kChunkTokens], tk_end[kChunkTokens];
     __shared__ long long tk_c0[kChunkTokens];
-    __shared__ int grp_tok[kChunkTokens], n_grp, tail_tok;
+    __shared__ int grp_tok[kChunkTokens], n_grp;
+    __shared__ unsigned int tail_mask;         // tokens that carry their sequence's remainder-ring duty
     __shared__ long long grp_row[kChunkTokens];
     __shared__ float w_lds[2][kChunkTokens][kChunkMaxM];
     __shared__ unsigned int amax_lds[kChunkTokens];
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(cmp::kThreads) void compress_chunk_kernel(CompressA
             if (i < p.batch) sp_lds[i] = p.start_pos[i];
         }
     }
-    if (tid == 0) { n_grp = 0; tail_tok = -1; }
+    if (tid == 0) { n_grp = 0; tail_mask = 0u; }
     if (tid < kChunkTokens) amax_lds[tid] = 0u;
     __syncthreads();
     // each token: its sequence, position, and whether it completes a group
@@ -133,8 +134,11 @@ __global__ __launch_bounds__(cmp::kThreads) void compress_chunk_kernel(CompressA
             const int mid = (lo + hi + 1) >> 1;
             if (cu(mid) <= t) lo = mid; else hi = mid - 1;
         }
-        const int c0 = cu(lo), n = cu(lo + 1) - c0;
-        const int start = in_lds ? sp_lds[lo] : p.start_pos[lo];
+        int c0 = cu(lo), n = cu(lo + 1) - c0;
+        int start = in_lds ? sp_lds[lo] : p.start_pos[lo];
+        if (chunk_invalid(t, c0, c0 + n, start, p.total_new, p.max_blocks, p.dbg, kDbgChunk)) {
+            c0 = t; n = 1; start = 0;             // (debug builds) a chunk of this token alone at position 0
+        }
         const int end = start + n, pos = start + (t - c0);
         tk_b[tid] = lo; tk_pos[tid] = pos; tk_start[tid] = start; tk_end[tid] = end; tk_c0[tid] = c0;
         const int g0 = start / m;
@@ -143,12 +147,15 @@ __global__ __launch_bounds__(cmp::kThreads) void compress_chunk_kernel(CompressA
         // first group's reads, in the workgroup that forms it
         const bool race = (start % m) != 0 && (end % m) != 0 && end >= (g0 + 1) * m;
         const bool tail_here = (end % m) != 0 && (race ? pos == (g0 + 1) * m - 1 : pos == end - 1);
-        if (tail_here) tail_tok = tid;
+        if (tail_here) atomicOr(&tail_mask, 1u << tid);
         if ((pos + 1) % m == 0) {
             const int k = atomicAdd(&n_grp, 1);
             grp_tok[k] = tid;
             const int g = pos / m, E = 256 / m;
-            grp_row[k] = (long long)p.block_table[(int64_t)lo * p.max_blocks + g / E] * E + g % E;
+            grp_row[k] =
+                (long long)checked(p.block_table[(int64_t)lo * p.max_blocks + g / E], 0, p.n_blocks - 1, p.dbg, kDbgBlock) *
+                    E +
+                g % E;
         }
     }
     __syncthreads();
@@ -283,11 +290,12 @@ __global__ __launch_bounds__(cmp::kThreads) void compress_chunk_kernel(CompressA
             }
         }
     }
-    // remainder ring of the sequence this workgroup carries the duty for:
-    // after every read of the ring above
+    // remainder rings of the sequences this workgroup carries the duty for
+    // (several short chunks may end in one workgroup): after every read of
+    // the rings above
     __syncthreads();
-    if (tail_tok >= 0) {
-        const int tk = tail_tok;
+    for (unsigned int mask = tail_mask; mask != 0u; mask &= mask - 1u) {
+        const int tk = __builtin_ctz(mask);
         const cmp::SeqChunk q{tk_b[tk], tk_start[tk], tk_end[tk], tk_end[tk] - tk_start[tk], tk_c0[tk]};
         const int tail0 = max((q.end / m) * m, q.start);
         for (int tt = tail0; tt < q.end; ++tt) cmp::write_ring<TOK>(p, q, tt);

@@ -102,6 +102,9 @@ __device__ inline SeqChunk seq_of(const CompressArgs& p, int t, int* cu_lds, int
     q.c0 = cu(lo);
     q.n = cu(lo + 1) - (int)q.c0;
     q.start = in_lds ? sp_lds[lo] : p.start_pos[lo];
+    if (chunk_invalid(t, (int)q.c0, (int)q.c0 + q.n, q.start, p.total_new, p.max_blocks, p.dbg, kDbgChunk)) {
+        q.c0 = t; q.n = 1; q.start = 0;           // (debug builds) a chunk of this token alone at position 0
+    }
     q.end = q.start + q.n;
     return q;
 }
@@ -176,7 +179,8 @@ __device__ __forceinline__ void issue_slice(const CompressArgs& p, const SeqChun
         L.logit = t >= q.start ? lg[q.c0 + (t - q.start)] : rlg[(int64_t)q.b * m + t % m];
     }
     const int E = 256 / m;
-    L.row = (int64_t)p.block_table[(int64_t)q.b * p.max_blocks + g / E] * E + g % E;
+    L.row = (int64_t)checked(p.block_table[(int64_t)q.b * p.max_blocks + g / E], 0, p.n_blocks - 1, p.dbg, kDbgBlock) * E +
+            g % E;
 }
 
 // Softmax weights of the group's logits (thread i < m holds logit i) into

@@ -154,6 +154,40 @@ __device__ inline float max_across_rows(float v) {
 
 __device__ inline int visible_entries(int pos, int m) { return (pos + 1) / m; }
 
+// ---------------------------------------------------------------------------
+// Index checks of the debug build
+// ---------------------------------------------------------------------------
+// With LCCA_DEBUG defined, an index read from device memory is tested against
+// its range [lo, hi] before it forms an address; outside it, `lo` is used
+// instead and `bit` is set in the device error word `word`, so every load
+// stays inside its buffer and the kernel finishes normally.  Without
+// LCCA_DEBUG the value is used as read (the caller vouches for it).
+__device__ __forceinline__ int checked(int v, int lo, int hi, uint32_t* word, uint32_t bit) {
+#ifdef LCCA_DEBUG
+    if (v < lo || v > hi) {
+        atomicOr(word, bit);
+        return lo;
+    }
+#endif
+    (void)lo; (void)hi; (void)word; (void)bit;
+    return v;
+}
+
+// Whether a debug build has found a chunk description invalid (cu_new and
+// start_pos of new token t, as read): always false in release builds.
+__device__ __forceinline__ bool chunk_invalid(int t, int c0, int c1, int start, int total_new, int max_blocks,
+                                              uint32_t* word, uint32_t bit) {
+#ifdef LCCA_DEBUG
+    const bool bad = c0 < 0 || c0 > t || c1 <= t || c1 > total_new || start < 0 ||
+                     (int64_t)start + (c1 - c0) > (int64_t)max_blocks * 256;
+    if (bad) atomicOr(word, bit);
+    return bad;
+#else
+    (void)t; (void)c0; (void)c1; (void)start; (void)total_new; (void)max_blocks; (void)word; (void)bit;
+    return false;
+#endif
+}
+
 // Order-preserving u32 key of a logit (-0.0 folded onto +0.0): larger
 // logits have larger keys.  The top-k selection ranks by it, and the
 // decode indexer counts the leading kTopkLeadBits bits of its logits' keys

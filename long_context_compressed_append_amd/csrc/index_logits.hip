@@ -208,8 +208,8 @@ index_mfma_kernel(IndexArgs p) {
     const int r = row_ok ? r_raw : p.num_rows - 1;
     const int tpw = p.tiles_per_wave;
     const int t_begin = ((int)blockIdx.x * 4 + wave) * tpw;
-    const int b = p.row_seq[r];
-    const int pos = p.row_pos[r];
+    const int b = checked(p.row_seq[r], 0, p.batch - 1, p.dbg, kDbgRow);
+    const int pos = checked(p.row_pos[r], 0, p.max_pos, p.dbg, kDbgRow);
     const int n_all = visible_entries(pos, p.m);
     // the entry this row's token completes is scored by score_fresh
     const bool fresh = p.fresh && row_ok && (pos + 1) % p.m == 0;
@@ -252,7 +252,7 @@ index_mfma_kernel(IndexArgs p) {
     // ahead of their MFMAs, in a ring of PF register sets addressed
     // statically (the tile loop is unrolled by PF).
     auto entry = [&](int tile) { return min(min(tile, t_end - 1) * 32 + j, n - 1); };
-    auto table = [&](int tile) { return bt[entry(tile) >> sh]; };
+    auto table = [&](int tile) { return checked(bt[entry(tile) >> sh], 0, p.n_blocks - 1, p.dbg, kDbgBlock); };
     auto row = [&](int tile, int pb) -> int64_t {
         return ((int64_t)pb << sh) + (entry(tile) & ((1 << sh) - 1));
     };
@@ -262,7 +262,8 @@ index_mfma_kernel(IndexArgs p) {
     // key tiles are requested.
     int pbs[PF];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) pbs[i] = bt[max(0, entry(t_begin + i)) >> sh];
+    for (int i = 0; i < PF; ++i)
+        pbs[i] = checked(bt[max(0, entry(t_begin + i)) >> sh], 0, p.n_blocks - 1, p.dbg, kDbgBlock);
 #pragma unroll
     for (int i = 0; i < QU; ++i) {
         const int u = (int)threadIdx.x + kThreads * i;
@@ -374,8 +375,8 @@ __global__ __launch_bounds__(kRowThreads) void index_rows_kernel(IndexArgs p) {
     const int r = (int)blockIdx.y * kRowWaves + wave;
     const bool row_ok = r < p.num_rows;
     const int rr = row_ok ? r : p.num_rows - 1;
-    const int b = p.row_seq[rr];
-    const int n = row_ok ? visible_entries(p.row_pos[rr], p.m) : 0;
+    const int b = checked(p.row_seq[rr], 0, p.batch - 1, p.dbg, kDbgRow);
+    const int n = row_ok ? visible_entries(checked(p.row_pos[rr], 0, p.max_pos, p.dbg, kDbgRow), p.m) : 0;
     const int tpb = p.tiles_per_wave;
     const int t_begin = (int)blockIdx.x * tpb;
     if (lane == 0) { seq_lds[wave] = b; n_lds[wave] = n; }
@@ -418,7 +419,8 @@ __global__ __launch_bounds__(kRowThreads) void index_rows_kernel(IndexArgs p) {
             for (int q = 0; q < UPT; ++q) {
                 const int u = min(tid + kRowThreads * q, 32 * UPK - 1);
                 const int e = min(min(tile, t_end - 1) * 32 + u / UPK, nmax - 1);
-                const int64_t row = ((int64_t)bt[e >> sh] << sh) + (e & ((1 << sh) - 1));
+                const int64_t row =
+                    ((int64_t)checked(bt[e >> sh], 0, p.n_blocks - 1, p.dbg, kDbgBlock) << sh) + (e & ((1 << sh) - 1));
                 v[q] = *reinterpret_cast<const u32x4*>(keys + row * KB + (u % UPK) * 16);
             }
         };
@@ -487,11 +489,13 @@ __global__ __launch_bounds__(kRowThreads) void index_rows_kernel(IndexArgs p) {
 __global__ __launch_bounds__(kThreads) void index_f32_kernel(IndexArgs p) {
     const int r = blockIdx.y;
     const int e = blockIdx.x * kThreads + threadIdx.x;
-    const int n = visible_entries(p.row_pos[r], p.m);
+    const int n = visible_entries(checked(p.row_pos[r], 0, p.max_pos, p.dbg, kDbgRow), p.m);
     if (e >= n) return;
     const int E = 256 / p.m;
-    const int b = p.row_seq[r];
-    const int64_t row = (int64_t)p.block_table[(int64_t)b * p.max_blocks + e / E] * E + e % E;
+    const int b = checked(p.row_seq[r], 0, p.batch - 1, p.dbg, kDbgRow);
+    const int64_t row =
+        (int64_t)checked(p.block_table[(int64_t)b * p.max_blocks + e / E], 0, p.n_blocks - 1, p.dbg, kDbgBlock) * E +
+        e % E;
     const float* k = reinterpret_cast<const float*>(p.keys) + row * p.dI;
     const float* q = reinterpret_cast<const float*>(p.q) + (int64_t)r * p.HI * p.dI;
     float l = 0.0f;

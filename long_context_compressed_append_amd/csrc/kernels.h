@@ -1,15 +1,27 @@
 // Internal interface between the host entry points (lcca_api.cpp) and the
 // gfx950 kernels.  Plain structs of device pointers and sizes, validated by
 // the host before a launch.
+//
+// Every struct carries the bounds of the indices its kernels read from
+// device memory (batch, max_pos, n_blocks, total_new) and `dbg`, the device
+// error word of debug builds (LCCA_DEBUG): there each such index is checked
+// against its bounds before it forms an address (see checked() in device.h).
+// Release builds pass dbg = nullptr and never read it.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace lcca {
 
+// bits of the device error word (the public LCCA_DBG_* values)
+constexpr uint32_t kDbgBlock = 1u;     // block-table entry outside the pool
+constexpr uint32_t kDbgRow = 2u;       // row_seq outside the batch or row_pos outside [0, max_pos]
+constexpr uint32_t kDbgChunk = 4u;     // cu_new / start_pos outside their contract
+
 struct CompressArgs {
     const int32_t* block_table; int32_t max_blocks;
     const int32_t* cu_new; const int32_t* start_pos; int32_t batch;
+    int32_t total_new; int32_t n_blocks; uint32_t* dbg;  // n_blocks: the smaller pool's
     int32_t tok_dtype;
     const void* kv_tok; const float* kv_logit; const void* ik_tok; const float* ik_logit;
     int32_t m, D, dI;
@@ -22,6 +34,7 @@ struct CompressArgs {
 struct IndexArgs {
     const int32_t* block_table; int32_t max_blocks;
     const int32_t* row_seq; const int32_t* row_pos; int32_t num_rows;
+    int32_t batch, max_pos, n_blocks; uint32_t* dbg;
     const void* q; const float* w; float s_I;
     int32_t HI, dI, m;
     int32_t key_dtype; const void* keys;
@@ -52,6 +65,7 @@ constexpr int kTopkSlice = 16384;
 
 struct TopkArgs {
     const int32_t* row_pos; int32_t num_rows; int32_t m;
+    int32_t max_pos; uint32_t* dbg;
     const float* logits; int64_t ld; int32_t k;
     int32_t* idx;
     // two-launch selection of long rows (workspace)
@@ -72,6 +86,7 @@ int64_t topk_cand_stride(int max_entries, int k);
 struct AttnArgs {
     const int32_t* block_table; int32_t max_blocks;
     const int32_t* row_seq; const int32_t* row_pos; int32_t num_rows;
+    int32_t batch, max_pos, n_blocks; uint32_t* dbg;
     const void* q; int32_t H, D, d_v; float scale_log2;     // sm_scale * log2(e)
     int32_t m; int32_t kv_dtype; const void* kv_data; const void* kv_scale;
     const int32_t* topk; int32_t k;                         // topk == nullptr: dense over visible entries
@@ -82,9 +97,9 @@ struct AttnArgs {
     float* part_o;     // [rows][nsplit][H][d_v]   (nsplit > 1, fp32 partial states)
     float* part_ml;    // [rows][nsplit][2][H]
     // bf16 outputs: partial O / l as fp16 with a power-of-two range scale
-    // per (split, 32 value dims, head); part_o is then unused
+    // per (split, 16 value dims, head); part_o is then unused
     uint16_t* part_h;  // [rows][nsplit][H][d_v]
-    float* part_sc;    // [rows][nsplit][d_v / 32][H]
+    float* part_sc;    // [rows][nsplit][d_v / 16][H]
 };
 
 hipError_t launch_compress_append(const CompressArgs& a, int total_new, hipStream_t stream);
@@ -95,6 +110,10 @@ hipError_t launch_topk_select(TopkArgs a, int max_entries, hipStream_t stream);
 bool topk_compress_supported(const TopkArgs& a, int max_entries, int tok_dtype);
 hipError_t launch_topk_compress(TopkArgs a, int max_entries, const CompressArgs& c, int total_new, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
+
+// The device error word of debug builds on the current device (its address,
+// found once per device); nullptr in release builds.
+hipError_t debug_word(uint32_t** word);
 
 // which (dtype, shape) combinations the kernels are built for
 bool index_supported(int q_dtype, int key_dtype, int HI, int dI);

@@ -3,6 +3,7 @@
 // returns an error code and launches nothing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -22,6 +23,9 @@ size_t attn_scratch_bytes();
 hipError_t attn_scratch(void** ptr);
 }
 
+static_assert(lcca::kDbgBlock == LCCA_DBG_BLOCK && lcca::kDbgRow == LCCA_DBG_ROW && lcca::kDbgChunk == LCCA_DBG_CHUNK,
+              "device error word bits");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -40,6 +44,10 @@ lcca_status hip_status(hipError_t e, const char* what) {
 }
 
 bool valid_m(int m) { return m >= 1 && m <= 256 && 256 % m == 0; }
+
+// The device error word the kernels of a debug build record index
+// violations in (nullptr in release builds).
+lcca_status debug_word(uint32_t** w) { return hip_status(lcca::debug_word(w), "debug error word lookup"); }
 
 bool valid_dtype(int d) { return d >= LCCA_F32 && d <= LCCA_MXFP4; }
 
@@ -142,7 +150,36 @@ size_t lcca_remainder_bytes(int32_t batch, int32_t ratio_m, int32_t kv_dim, int3
     return n;
 }
 
-const char* lcca_version(void) { return "lcca 0.1.0 (gfx950)"; }
+#ifdef LCCA_DEBUG
+const char* lcca_version(void) { return "lcca 0.2.0 (gfx950, LCCA_DEBUG)"; }
+#else
+const char* lcca_version(void) { return "lcca 0.2.0 (gfx950)"; }
+#endif
+
+lcca_status lcca_debug_check(void* stream, uint32_t* bits) {
+    g_err[0] = 0;
+    if (bits) *bits = 0;
+#ifdef LCCA_DEBUG
+    uint32_t* w = nullptr;
+    lcca_status s;
+    if ((s = debug_word(&w))) return s;
+    uint32_t v = 0;
+    const hipStream_t st = (hipStream_t)stream;
+    if ((s = hip_status(hipMemcpyAsync(&v, w, sizeof v, hipMemcpyDeviceToHost, st), "debug word read"))) return s;
+    if ((s = hip_status(hipMemsetAsync(w, 0, sizeof v, st), "debug word clear"))) return s;
+    if ((s = hip_status(hipStreamSynchronize(st), "debug word wait"))) return s;
+    if (bits) *bits = v;
+    if (v)
+        return fail(LCCA_ERR_DEVICE_INDEX, "device indices out of range (bits 0x%x:%s%s%s)", v,
+                    (v & LCCA_DBG_BLOCK) ? " block-table entry outside the pool;" : "",
+                    (v & LCCA_DBG_ROW) ? " row_seq / row_pos outside batch / max_pos;" : "",
+                    (v & LCCA_DBG_CHUNK) ? " cu_new / start_pos outside their contract;" : "");
+    return LCCA_OK;
+#else
+    (void)stream;
+    return fail(LCCA_ERR_UNSUPPORTED, "lcca_debug_check: this library was built without LCCA_DEBUG");
+#endif
+}
 
 const char* lcca_status_string(lcca_status s) {
     switch (s) {
@@ -151,6 +188,7 @@ const char* lcca_status_string(lcca_status s) {
     case LCCA_ERR_UNSUPPORTED: return "unsupported dtype/shape combination";
     case LCCA_ERR_WORKSPACE: return "workspace missing or too small";
     case LCCA_ERR_HIP: return "HIP runtime error";
+    case LCCA_ERR_DEVICE_INDEX: return "device-side index out of range (debug build)";
     }
     return "unknown status";
 }
@@ -187,8 +225,11 @@ lcca_status prep_compress(const lcca_pages* pages, const int32_t* cu_new, const 
     if (!rem || rem->tok_dtype != tok_dtype || !rem->kv || !rem->kv_logit || (ik && (!rem->ik || !rem->ik_logit)))
         return fail(LCCA_ERR_INVALID_ARG, "remainder ring missing or of another token dtype");
     a = lcca::CompressArgs{};
+    if ((s = debug_word(&a.dbg))) return s;
     a.block_table = pages->block_table; a.max_blocks = pages->max_blocks_per_seq;
     a.cu_new = cu_new; a.start_pos = start_pos; a.batch = pages->batch;
+    a.total_new = total_new;
+    a.n_blocks = ik ? std::min(kv->num_blocks, ik->num_blocks) : kv->num_blocks;
     a.tok_dtype = tok_dtype;
     a.kv_tok = kv_tok; a.kv_logit = kv_logit; a.ik_tok = ik ? ik_tok : nullptr; a.ik_logit = ik ? ik_logit : nullptr;
     a.m = kv->ratio_m; a.D = kv->dim; a.dI = ik ? ik->dim : 0;
@@ -220,8 +261,10 @@ lcca_status prep_index(const lcca_pages* pages, const lcca_rows* rows, int32_t q
     max_entries = (rows->max_pos + 1) / ik->ratio_m;
     if (ld < max_entries) return fail(LCCA_ERR_INVALID_ARG, "ld=%lld < max visible entries %d", (long long)ld, max_entries);
     a = lcca::IndexArgs{};
+    if ((s = debug_word(&a.dbg))) return s;
     a.block_table = pages->block_table; a.max_blocks = pages->max_blocks_per_seq;
     a.row_seq = rows->row_seq; a.row_pos = rows->row_pos; a.num_rows = rows->num_rows;
+    a.batch = pages->batch; a.max_pos = rows->max_pos; a.n_blocks = ik->num_blocks;
     a.q = q_idx; a.w = w_idx; a.s_I = s_I; a.HI = HI; a.dI = ik->dim; a.m = ik->ratio_m;
     a.key_dtype = ik->dtype; a.keys = ik->data; a.logits = logits; a.ld = ld;
     return LCCA_OK;
@@ -287,7 +330,8 @@ lcca_status prep_topk(const lcca_rows* rows, int32_t ratio_m, const float* logit
         return fail(LCCA_ERR_UNSUPPORTED, "%d slices x k=%d candidates > %d", lcca::topk_slices(max_entries), k,
                     lcca::kTopkMaxEntries);
     a = lcca::TopkArgs{};
-    a.row_pos = rows->row_pos; a.num_rows = rows->num_rows; a.m = ratio_m;
+    if ((s = debug_word(&a.dbg))) return s;
+    a.row_pos = rows->row_pos; a.num_rows = rows->num_rows; a.m = ratio_m; a.max_pos = rows->max_pos;
     a.logits = logits; a.ld = ld; a.k = k; a.idx = topk_idx;
     if (lcca::topk_slices(max_entries) > 1) {
         const size_t need = lcca_topk_workspace_size(rows, ratio_m, k);
@@ -435,8 +479,10 @@ lcca_status attn_call(void* stream, const lcca_pages* pages, const lcca_rows* ro
     if (plan.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(ws) & 15))
         return fail(LCCA_ERR_INVALID_ARG, "attention workspace not 16-byte aligned");
     lcca::AttnArgs a{};
+    if ((s = debug_word(&a.dbg))) return s;
     a.block_table = pages->block_table; a.max_blocks = pages->max_blocks_per_seq;
     a.row_seq = rows->row_seq; a.row_pos = rows->row_pos; a.num_rows = rows->num_rows;
+    a.batch = pages->batch; a.max_pos = rows->max_pos; a.n_blocks = kv->num_blocks;
     a.q = q; a.H = H; a.D = kv->dim; a.d_v = d_v; a.scale_log2 = sm_scale * 1.4426950408889634f;
     a.m = m; a.kv_dtype = kv->dtype; a.kv_data = kv->data; a.kv_scale = kv->scale;
     a.topk = topk_idx; a.k = topk_idx ? k : 0;

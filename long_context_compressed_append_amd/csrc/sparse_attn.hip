@@ -84,8 +84,8 @@ struct RowKeys {
 
 __device__ inline RowKeys row_keys(const AttnArgs& a, int r) {
     RowKeys k;
-    k.b = a.row_seq[r];
-    k.p = a.row_pos[r];
+    k.b = checked(a.row_seq[r], 0, a.batch - 1, a.dbg, kDbgRow);
+    k.p = checked(a.row_pos[r], 0, a.max_pos, a.dbg, kDbgRow);
     k.n = visible_entries(k.p, a.m);
     k.nsel = a.topk ? a.k : k.n;
     k.sel_tiles = (k.nsel + kKeys - 1) / kKeys;
@@ -443,7 +443,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const bool ok = gs[i] >= 0 && gs[i] < rk.n;
-            pbs[i] = ok ? a.block_table[(int64_t)rk.b * a.max_blocks + (gs[i] >> sh)] : -1;
+            pbs[i] = ok ? checked(a.block_table[(int64_t)rk.b * a.max_blocks + (gs[i] >> sh)], 0, a.n_blocks - 1,
+                                  a.dbg, kDbgBlock)
+                        : -1;
         }
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -727,7 +729,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     __shared__ float sc[kF32MaxKeys];
     __shared__ float red[4];
     const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
-    const int b = a.row_seq[r], p = a.row_pos[r];
+    const int b = checked(a.row_seq[r], 0, a.batch - 1, a.dbg, kDbgRow);
+    const int p = checked(a.row_pos[r], 0, a.max_pos, a.dbg, kDbgRow);
     const int n = visible_entries(p, a.m);
     const int nsel = a.topk ? a.k : n;
     const int t0 = max(0, p - a.window + 1);
@@ -742,7 +745,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
         if (j < nsel) {
             const int g = a.topk ? a.topk[(int64_t)r * a.k + j] : j;
             if (g < 0 || g >= n) return nullptr;
-            return kvd + ((int64_t)a.block_table[(int64_t)b * a.max_blocks + g / E] * E + g % E) * D;
+            const int pb = checked(a.block_table[(int64_t)b * a.max_blocks + g / E], 0, a.n_blocks - 1, a.dbg, kDbgBlock);
+            return kvd + ((int64_t)pb * E + g % E) * D;
         }
         return wd + ((int64_t)b * a.win_cap + (t0 + j - nsel) % a.win_cap) * D;
     };

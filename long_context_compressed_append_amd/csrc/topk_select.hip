@@ -303,7 +303,7 @@ __device__ __forceinline__ void topk_body(const TopkArgs& p, int r, int by) {
     constexpr int COPIES = COMPACT ? 2 : kLeadCopies;
     __shared__ SmemT<COPIES, COMPACT ? kCompactEntries / 32 : kWords> sm;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int n_row = visible_entries(p.row_pos[r], p.m);
+    const int n_row = visible_entries(checked(p.row_pos[r], 0, p.max_pos, p.dbg, kDbgRow), p.m);
     const int k = p.k;
     int32_t* out = p.idx + (int64_t)r * k;
     const int s0 = MODE == kSlice ? by * p.slice_len : 0;

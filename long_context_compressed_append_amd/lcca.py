@@ -4,6 +4,10 @@ Argument marshalling only: torch tensors supply device pointers, the current
 torch stream supplies the hipStream_t, and every computation runs in the
 library's gfx950 kernels.  There is no fallback: if the library cannot be
 loaded, every call raises.
+
+use_debug_library(True) (or LCCA_DEBUG_LIBRARY=1 in the environment) routes
+every following call to liblcca_debug.so, whose kernels check the indices
+they read from device memory; debug_check() then reports what they found.
 """
 import ctypes
 import os
@@ -13,15 +17,17 @@ from typing import Optional
 import torch
 
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_DEVICE_INDEX = 0, -1, -2, -3, -4, -5
+DBG_BLOCK, DBG_ROW, DBG_CHUNK = 1, 2, 4
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblcca.so")
+DEBUG_LIB_PATH = os.path.join(_PKG, "liblcca_debug.so")
 
 EXPORTED = ("lcca_compress_append", "lcca_index_logits", "lcca_topk_select", "lcca_sparse_attn_fwd",
             "lcca_sparse_attn_workspace_size", "lcca_topk_workspace_size", "lcca_status_string", "lcca_last_error",
             "lcca_version", "lcca_decode_select", "lcca_decode_select_workspace_size", "lcca_remainder_bytes",
-            "lcca_sparse_attn_fwd_noalloc")
+            "lcca_sparse_attn_fwd_noalloc", "lcca_debug_check")
 
 
 class LccaError(RuntimeError):
@@ -54,17 +60,25 @@ class _Remainder(ctypes.Structure):
                 ("kv_logit", ctypes.c_void_p), ("ik_logit", ctypes.c_void_p)]
 
 
-_LIB = None
+_LIBS = {}
+_USE_DEBUG = os.environ.get("LCCA_DEBUG_LIBRARY") == "1"
+
+
+def use_debug_library(on: bool = True):
+    """Route the calls that follow to liblcca_debug.so (on) or liblcca.so."""
+    global _USE_DEBUG
+    _USE_DEBUG = bool(on)
 
 
 def lib():
-    """Load liblcca.so (built in-tree; compiled first only if absent)."""
-    global _LIB
-    if _LIB is None:
-        if not os.path.exists(LIB_PATH):
+    """The library in use (built in-tree; compiled first only if absent)."""
+    path = DEBUG_LIB_PATH if _USE_DEBUG else LIB_PATH
+    L = _LIBS.get(path)
+    if L is None:
+        if not os.path.exists(path):
             from . import build as _b
-            _b.build()
-        L = ctypes.CDLL(LIB_PATH)
+            _b.build_one(_USE_DEBUG)
+        L = ctypes.CDLL(path)
         P, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
         PP, PR, PC, PW, PM = (ctypes.POINTER(_Pages), ctypes.POINTER(_Rows), ctypes.POINTER(_PagedCache),
                               ctypes.POINTER(_WindowCache), ctypes.POINTER(_Remainder))
@@ -86,11 +100,24 @@ def lib():
         for n in ("lcca_compress_append", "lcca_index_logits", "lcca_topk_select", "lcca_sparse_attn_fwd",
                   "lcca_decode_select", "lcca_sparse_attn_fwd_noalloc"):
             getattr(L, n).restype = i32
+        L.lcca_debug_check.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
+        L.lcca_debug_check.restype = i32
         L.lcca_status_string.argtypes = [i32]
         for n in ("lcca_status_string", "lcca_last_error", "lcca_version"):
             getattr(L, n).restype = ctypes.c_char_p
-        _LIB = L
-    return _LIB
+        _LIBS[path] = L
+    return L
+
+
+def debug_check(stream=None) -> int:
+    """Wait for the stream, then read and clear the debug library's device
+    error word: 0 if its kernels found no index out of range, else the
+    DBG_* bits of what they found.  Raises on the release library."""
+    bits = ctypes.c_uint32(0)
+    status = lib().lcca_debug_check(_stream(stream), ctypes.byref(bits))
+    if status not in (OK, ERR_DEVICE_INDEX):
+        _check(status)
+    return int(bits.value)
 
 
 def version():

@@ -29,8 +29,27 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings():
     L = lcca.lib()
-    for s in (0, -1, -2, -3, -4):
-        assert L.lcca_status_string(s)
+    for s in (0, -1, -2, -3, -4, -5):
+        assert L.lcca_status_string(s) != b"unknown status"
+
+
+def test_debug_library_exports_the_same_symbols():
+    import ctypes as C
+    D = C.CDLL(lcca.DEBUG_LIB_PATH)
+    for n in _declared():
+        assert hasattr(D, n), n
+    D.lcca_version.restype = C.c_char_p
+    assert b"LCCA_DEBUG" in D.lcca_version()
+    assert b"LCCA_DEBUG" not in lcca.lib().lcca_version()
+
+
+def test_release_library_has_no_debug_word():
+    bits = ctypes.c_uint32(7)
+    assert lcca.lib().lcca_debug_check(None, ctypes.byref(bits)) == lcca.ERR_UNSUPPORTED
+    assert bits.value == 0
+    assert b"LCCA_DEBUG" in lcca.lib().lcca_last_error()
+    with pytest.raises(lcca.LccaError):
+        lcca.debug_check(0)                  # the null stream: nothing runs on it
 
 
 def _pool(dtype=lcca.BF16, dim=576, m=4, blocks=4, data=1):

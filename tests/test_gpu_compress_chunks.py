@@ -4,7 +4,8 @@ workgroup) against the same tokens appended sequence by sequence in halves of
 fewer than 64 tokens (the slice kernel).  Pools, window ring and the live
 slots of the remainder ring must agree bit for bit, including the chunk that starts inside a group,
 completes it and ends inside a later group (its first group reads ring slots
-its tail rewrites)."""
+its tail rewrites), and short chunks of several sequences that end inside one
+workgroup."""
 import numpy as np
 import pytest
 import torch
@@ -21,6 +22,10 @@ CASES = [
     synth.shrink(S["lp_512k"], "chunks_lp", (2047, 777), (100, 63), k=64),
     synth.shrink(S["prefill_8k"], "chunks_prefill", (3001,), (126,), k=64, win_cap=2048),
     synth.shrink(S["tiny"], "chunks_tiny", (0, 5), (100, 90), win_cap=2048),
+    # ten short chunks (66 new tokens): several sequences end inside one
+    # 16-token workgroup, each with its own remainder-ring tail
+    synth.shrink(S["csa_64k"], "chunks_short", (1001, 1022, 3, 517, 0, 64, 7, 130, 250, 33),
+                 (7, 5, 9, 6, 8, 3, 11, 4, 6, 7), k=64),
 ]
 
 
