@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 
 #include "../../include/lcca.h"
@@ -44,6 +45,21 @@ lcca_status hip_status(hipError_t e, const char* what) {
 }
 
 bool valid_m(int m) { return m >= 1 && m <= 256 && 256 % m == 0; }
+
+// Visible entries of a row at position max_pos, without int overflow.
+int64_t max_visible(int32_t max_pos, int m) { return ((int64_t)max_pos + 1) / m; }
+
+// Byte counts that saturate at SIZE_MAX (a workspace no caller can provide)
+// instead of wrapping.
+size_t mul_sat(size_t a, size_t b) {
+    size_t r;
+    return __builtin_mul_overflow(a, b, &r) ? SIZE_MAX : r;
+}
+size_t add_sat(size_t a, size_t b) {
+    size_t r;
+    return __builtin_add_overflow(a, b, &r) ? SIZE_MAX : r;
+}
+size_t up256(size_t x) { return x > SIZE_MAX - 255 ? SIZE_MAX : (x + 255) & ~(size_t)255; }
 
 // The device error word the kernels of a debug build record index
 // violations in (nullptr in release builds).
@@ -107,7 +123,7 @@ struct AttnPlan {
 AttnPlan attn_plan(int rows, int max_pos, int m, int H, int d_v, int k, bool topk_given, int window) {
     AttnPlan p{1, 1, 0};
     if (rows <= 0) return p;
-    const int64_t nvis = (int64_t)(max_pos + 1) / m;
+    const int64_t nvis = max_visible(max_pos, m);
     const int64_t nsel = topk_given ? (int64_t)k : nvis;
     const int64_t nwin = std::min<int64_t>(window, (int64_t)max_pos + 1);
     const int64_t key_tiles = lcca::attn_tile_keys();
@@ -124,9 +140,9 @@ AttnPlan attn_plan(int rows, int max_pos, int m, int H, int d_v, int k, bool top
     p.nsplit = (int)nsplit;
     p.split_tiles = (int)tps;
     if (p.nsplit > 1) {
-        size_t po = (size_t)rows * p.nsplit * H * d_v * sizeof(float);
-        po = (po + 255) & ~(size_t)255;
-        p.ws_bytes = po + (size_t)rows * p.nsplit * 2 * H * sizeof(float);
+        const size_t parts = mul_sat(mul_sat(mul_sat((size_t)rows, (size_t)p.nsplit), (size_t)H), (size_t)d_v);
+        const size_t po = up256(mul_sat(parts, sizeof(float)));
+        p.ws_bytes = add_sat(po, mul_sat(mul_sat((size_t)rows * p.nsplit, 2 * (size_t)H), sizeof(float)));
     }
     return p;
 }
@@ -142,11 +158,11 @@ size_t lcca_remainder_bytes(int32_t batch, int32_t ratio_m, int32_t kv_dim, int3
         return 0;
     const size_t esz = tok_dtype == LCCA_F32 ? 4 : 2;
     const size_t slots = (size_t)batch * ratio_m;
-    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    size_t n = up(slots * kv_dim * esz);                  // kv
-    n += up(slots * ik_dim * esz);                        // ik
-    n += ik_dim ? up(slots * sizeof(float)) : slots * sizeof(float);   // kv_logit
-    if (ik_dim) n += slots * sizeof(float);               // ik_logit
+    const size_t logits = slots * sizeof(float);
+    size_t n = up256(mul_sat(mul_sat(slots, (size_t)kv_dim), esz));                    // kv
+    n = add_sat(n, up256(mul_sat(mul_sat(slots, (size_t)ik_dim), esz)));               // ik
+    n = add_sat(n, ik_dim ? up256(logits) : logits);                                  // kv_logit
+    if (ik_dim) n = add_sat(n, logits);                                               // ik_logit
     return n;
 }
 
@@ -258,7 +274,9 @@ lcca_status prep_index(const lcca_pages* pages, const lcca_rows* rows, int32_t q
     if (!lcca::index_supported(q_dtype, ik->dtype, HI, ik->dim))
         return fail(LCCA_ERR_UNSUPPORTED, "index_logits: q dtype %d, key dtype %d, HI=%d, dim=%d not built", q_dtype,
                     ik->dtype, HI, ik->dim);
-    max_entries = (rows->max_pos + 1) / ik->ratio_m;
+    if (max_visible(rows->max_pos, ik->ratio_m) > INT32_MAX)
+        return fail(LCCA_ERR_UNSUPPORTED, "index_logits: %lld visible entries", (long long)max_visible(rows->max_pos, 1));
+    max_entries = (int)max_visible(rows->max_pos, ik->ratio_m);
     if (ld < max_entries) return fail(LCCA_ERR_INVALID_ARG, "ld=%lld < max visible entries %d", (long long)ld, max_entries);
     a = lcca::IndexArgs{};
     if ((s = debug_word(&a.dbg))) return s;
@@ -301,9 +319,11 @@ lcca_status lcca_index_logits(void* stream, const lcca_pages* pages, const lcca_
 
 size_t lcca_topk_workspace_size(const lcca_rows* rows, int32_t ratio_m, int32_t k) {
     if (!rows || rows->num_rows <= 0 || !valid_m(ratio_m) || k < 1 || rows->max_pos < 0) return 0;
-    const int max_entries = (rows->max_pos + 1) / ratio_m;
+    const int64_t nvis = max_visible(rows->max_pos, ratio_m);
+    if (nvis > lcca::kTopkMaxEntries) return 0;                 // the selection itself is unsupported
+    const int max_entries = (int)nvis;
     if (lcca::topk_slices(max_entries) == 1) return 0;
-    return (size_t)rows->num_rows * (size_t)lcca::topk_cand_stride(max_entries, k) * 8;
+    return mul_sat(mul_sat((size_t)rows->num_rows, (size_t)lcca::topk_cand_stride(max_entries, k)), 8);
 }
 
 }  // extern "C"
@@ -319,10 +339,11 @@ lcca_status prep_topk(const lcca_rows* rows, int32_t ratio_m, const float* logit
     if (k < 1) return fail(LCCA_ERR_INVALID_ARG, "k=%d", k);
     if (rows->num_rows == 0) { empty = true; return LCCA_OK; }
     if (!logits || !topk_idx) return fail(LCCA_ERR_INVALID_ARG, "logits/topk_idx NULL");
-    max_entries = (rows->max_pos + 1) / ratio_m;
+    if (max_visible(rows->max_pos, ratio_m) > lcca::kTopkMaxEntries)
+        return fail(LCCA_ERR_UNSUPPORTED, "%lld visible entries > %d", (long long)max_visible(rows->max_pos, ratio_m),
+                    lcca::kTopkMaxEntries);
+    max_entries = (int)max_visible(rows->max_pos, ratio_m);
     if (ld < max_entries) return fail(LCCA_ERR_INVALID_ARG, "ld=%lld < max visible entries %d", (long long)ld, max_entries);
-    if (max_entries > lcca::kTopkMaxEntries)
-        return fail(LCCA_ERR_UNSUPPORTED, "%d visible entries > %d", max_entries, lcca::kTopkMaxEntries);
     // the candidates' selection of long rows keeps a bitmap of its slices x k
     // candidates in the same LDS space as a row's
     if (lcca::topk_slices(max_entries) > 1 &&
@@ -363,8 +384,9 @@ lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_
 
 size_t lcca_decode_select_workspace_size(const lcca_rows* rows, int32_t ratio_m, int32_t k) {
     if (!rows || rows->num_rows <= 0 || !valid_m(ratio_m) || k < 1 || rows->max_pos < 0) return 0;
-    const int max_entries = (rows->max_pos + 1) / ratio_m;
-    if (lcca::topk_slices(max_entries) > 1) return lcca_topk_workspace_size(rows, ratio_m, k);
+    const int64_t nvis = max_visible(rows->max_pos, ratio_m);
+    if (nvis > lcca::kTopkMaxEntries) return 0;                 // the selection itself is unsupported
+    if (lcca::topk_slices((int)nvis) > 1) return lcca_topk_workspace_size(rows, ratio_m, k);
     return (size_t)rows->num_rows * ((size_t)1 << lcca::kTopkLeadBits) * sizeof(uint32_t);
 }
 
@@ -460,7 +482,7 @@ lcca_status attn_call(void* stream, const lcca_pages* pages, const lcca_rows* ro
         return fail(LCCA_ERR_UNSUPPORTED, "sparse_attn: %d key tiles per split needed (> %d)", plan.split_tiles,
                     lcca::attn_max_split_tiles());
     if (f32) {
-        const int64_t L = (topk_idx ? (int64_t)k : (int64_t)(rows->max_pos + 1) / m) +
+        const int64_t L = (topk_idx ? (int64_t)k : max_visible(rows->max_pos, m)) +
                           std::min<int64_t>(win->window, (int64_t)rows->max_pos + 1);
         if (L > lcca::attn_f32_max_keys())
             return fail(LCCA_ERR_UNSUPPORTED, "fp32 attention: %lld keys per row > %d", (long long)L,

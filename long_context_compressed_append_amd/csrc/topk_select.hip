@@ -575,7 +575,7 @@ void launch_sel(const TopkArgs& a, int entries, dim3 grid, hipStream_t stream) {
 }  // namespace
 
 int topk_slices(int max_entries) {
-    return max_entries > kTopkSplitAbove ? (max_entries + kTopkSlice - 1) / kTopkSlice : 1;
+    return max_entries > kTopkSplitAbove ? (max_entries - 1) / kTopkSlice + 1 : 1;
 }
 
 int64_t topk_cand_stride(int max_entries, int k) {
