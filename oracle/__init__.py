@@ -41,13 +41,16 @@ def lib():
         i32, i64, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_double
         L.orc_compress_append.argtypes = [i32, i32, P, P, P, i32, P, P, P, P, i32, i32, i32,
                                           i32, P, P, i32, P, P, i32, i32, P, P, P, P, P, P]
+        L.orc_compress_append_gated.argtypes = L.orc_compress_append.argtypes
         L.orc_index_logits.argtypes = [i32, P, P, i32, i32, P, i32, P, i32, i32, P, dbl, i32, P, P, P, i64]
         L.orc_topk.argtypes = [i32, P, i32, P, i64, i32, P]
         L.orc_sparse_attn.argtypes = [i32, P, P, i32, i32, P, i32, P, i32, i32, i32, dbl,
                                       i32, P, P, P, i32, i32, i32, i32, P, P, P, P]
-        for name in ("orc_compress_append", "orc_index_logits", "orc_topk", "orc_sparse_attn"):
+        for name in ("orc_compress_append", "orc_compress_append_gated", "orc_index_logits", "orc_topk",
+                     "orc_sparse_attn"):
             getattr(L, name).restype = ctypes.c_int
         L.orc_group_compress.argtypes = [i32, i32, P, P, P]
+        L.orc_group_compress_gated.argtypes = [i32, i32, P, P, P]
         L.orc_store_rows.argtypes = [i32, P, P, i64, i64, i32, P]
         L.orc_load_rows.argtypes = [i32, P, P, i64, i64, i32, P]
         L.orc_mx_scale_exp.argtypes = [ctypes.c_float]
@@ -167,6 +170,17 @@ def group_compress(x, a):
     return C
 
 
+def group_compress_gated(x, a):
+    """Per-channel-gated aggregation of one group: x [m][dim], a [m][dim] -> C [dim] (fp64)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    m, dim = x.shape
+    assert a.shape == (m, dim)
+    C = np.empty(dim, np.float64)
+    lib().orc_group_compress_gated(m, dim, _p(x), _p(a), _p(C))
+    return C
+
+
 # --------------------------------------------------------------------------
 # the four stages (arrays are numpy; caches are mutated in place)
 # --------------------------------------------------------------------------
@@ -176,16 +190,18 @@ def _i32(a):
 
 
 def compress_append(block_table, cu_new, start_pos, tok_dtype, kv_tok, kv_logit, ik_tok, ik_logit,
-                    m, D, dI, kv, ik, win, rem):
+                    m, D, dI, kv, ik, win, rem, gated=False):
     """kv/ik: dict(dtype, data, scale); win: dict(dtype, cap, data, scale) or None;
     rem: dict(kv, ik, kv_logit, ik_logit).  Token arrays hold raw bytes of the
-    token dtype (float32 or bf16 bit patterns as uint16)."""
+    token dtype (float32 or bf16 bit patterns as uint16).  gated: the
+    per-channel-gated variant (logits [n][dim], ring logits [batch][m][dim])."""
     bt = _i32(block_table)
     batch, max_blocks = bt.shape
     cu = _i32(cu_new)
     sp = _i32(start_pos)
     has_ik = ik is not None and ik_tok is not None
-    rc = lib().orc_compress_append(
+    fn = lib().orc_compress_append_gated if gated else lib().orc_compress_append
+    rc = fn(
         batch, max_blocks, _p(bt), _p(cu), _p(sp),
         tok_dtype, _p(kv_tok), _p(np.ascontiguousarray(kv_logit, np.float32)),
         _p(ik_tok) if has_ik else None,

@@ -278,6 +278,29 @@ void orc_group_compress(int m, int dim, const double* x /*[m][dim]*/, const doub
     free(w);
 }
 
+/* The per-channel-gated variant: every channel d of every token carries its
+ * own logit a[i][d], and the softmax runs over the group's m tokens for each
+ * channel separately: w_id = exp(a_id - mu_d) / sum_j exp(a_jd - mu_d) with
+ * mu_d the channel's group maximum, C_d = sum_i w_id x_id, accumulated in i
+ * order, in fp64.  [P1 "Kako funkcionira optimizacija KV cachea?": tokens
+ * are folded by weighted summation; weights per channel instead of per token
+ * are the variant read R-1 names, the pages give no formula for either.]
+ * With the same logit in every channel it is orc_group_compress. */
+void orc_group_compress_gated(int m, int dim, const double* x /*[m][dim]*/, const double* a /*[m][dim]*/, double* C)
+{
+    double* w = (double*)malloc(sizeof(double) * (size_t)m);
+    for (int d = 0; d < dim; ++d) {
+        double mu = a[d];
+        for (int i = 1; i < m; ++i) if (a[(int64_t)i * dim + d] > mu) mu = a[(int64_t)i * dim + d];
+        double S = 0.0;
+        for (int i = 0; i < m; ++i) { w[i] = exp(a[(int64_t)i * dim + d] - mu); S += w[i]; }
+        double acc = 0.0;
+        for (int i = 0; i < m; ++i) acc += (w[i] / S) * x[(int64_t)i * dim + d];
+        C[d] = acc;
+    }
+    free(w);
+}
+
 /* Append a chunk of new tokens per sequence.
  *
  * Sequence b receives n_b = cu_new[b+1] - cu_new[b] tokens at positions
@@ -293,7 +316,8 @@ void orc_group_compress(int m, int dim, const double* x /*[m][dim]*/, const doub
  * they are written).  A window of full vectors for recent positions sits
  * beside the compressed entries [P1 "Kako funkcionira ..."; FP8 window of 128
  * positions: P3 "Proc je obnova sliding-window cache draha"]. */
-int orc_compress_append(
+static int compress_append_impl(
+    int gated,
     int batch, int max_blocks, const int32_t* block_table,
     const int32_t* cu_new, const int32_t* start_pos,
     int tok_dtype, const void* kv_tok, const float* kv_logit,
@@ -322,8 +346,10 @@ int orc_compress_append(
             int pdt = st ? ik_dtype : kv_dtype;
             void* pdata = st ? ik_data : kv_data;
             void* pscale = st ? ik_scale : kv_scale;
+            /* logits per token, or per token and channel (gated) */
+            const int la = gated ? dim : 1;
             double* x = (double*)malloc(sizeof(double) * (size_t)m * dim);
-            double* a = (double*)malloc(sizeof(double) * (size_t)m);
+            double* a = (double*)malloc(sizeof(double) * (size_t)m * la);
             double* C = (double*)malloc(sizeof(double) * (size_t)dim);
             float* Cf = (float*)malloc(sizeof(float) * (size_t)dim);
             for (int64_t g = g_first; g < g_end; ++g) {
@@ -332,14 +358,15 @@ int orc_compress_append(
                     if (t >= start) {
                         int64_t row = c0 + (t - start);
                         for (int d = 0; d < dim; ++d) x[(int64_t)i * dim + d] = tok_elem(tok_dtype, tok, row * dim + d);
-                        a[i] = lg[row];
+                        for (int d = 0; d < la; ++d) a[(int64_t)i * la + d] = lg[row * la + d];
                     } else {
                         int64_t row = (int64_t)b * m + t % m;
                         for (int d = 0; d < dim; ++d) x[(int64_t)i * dim + d] = tok_elem(tok_dtype, rtok, row * dim + d);
-                        a[i] = rlg[row];
+                        for (int d = 0; d < la; ++d) a[(int64_t)i * la + d] = rlg[row * la + d];
                     }
                 }
-                orc_group_compress(m, dim, x, a, C);
+                if (gated) orc_group_compress_gated(m, dim, x, a, C);
+                else orc_group_compress(m, dim, x, a, C);
                 /* The encoding decision is taken on the fp32 value. */
                 for (int d = 0; d < dim; ++d) Cf[d] = (float)C[d];
                 store_row(pdt, pdata, pscale, pool_row(block_table, max_blocks, m, b, g), dim, Cf);
@@ -363,15 +390,51 @@ int orc_compress_append(
         for (int64_t t = tail0; t < end; ++t) {
             int64_t row = c0 + (t - start);
             int64_t slot = (int64_t)b * m + t % m;
+            const int lk = gated ? D : 1, li = gated ? dI : 1;
             tok_copy(tok_dtype, kv_tok, row, rem_kv, slot, D);
-            rem_kv_logit[slot] = kv_logit[row];
+            for (int d = 0; d < lk; ++d) rem_kv_logit[slot * lk + d] = kv_logit[row * lk + d];
             if (streams == 2) {
                 tok_copy(tok_dtype, ik_tok, row, rem_ik, slot, dI);
-                rem_ik_logit[slot] = ik_logit[row];
+                for (int d = 0; d < li; ++d) rem_ik_logit[slot * li + d] = ik_logit[row * li + d];
             }
         }
     }
     return 0;
+}
+
+int orc_compress_append(
+    int batch, int max_blocks, const int32_t* block_table,
+    const int32_t* cu_new, const int32_t* start_pos,
+    int tok_dtype, const void* kv_tok, const float* kv_logit,
+    const void* ik_tok, const float* ik_logit,
+    int m, int D, int dI,
+    int kv_dtype, void* kv_data, void* kv_scale,
+    int ik_dtype, void* ik_data, void* ik_scale,
+    int win_dtype, int win_cap, void* win_data, float* win_scale,
+    void* rem_kv, void* rem_ik, float* rem_kv_logit, float* rem_ik_logit)
+{
+    return compress_append_impl(0, batch, max_blocks, block_table, cu_new, start_pos, tok_dtype, kv_tok, kv_logit,
+                                ik_tok, ik_logit, m, D, dI, kv_dtype, kv_data, kv_scale, ik_dtype, ik_data, ik_scale,
+                                win_dtype, win_cap, win_data, win_scale, rem_kv, rem_ik, rem_kv_logit, rem_ik_logit);
+}
+
+/* orc_compress_append with per-channel-gated groups (orc_group_compress_gated):
+ * the logits are [n_new][D] and [n_new][dI], the remainder ring's logits
+ * [batch][m][D] and [batch][m][dI]; everything else is unchanged. */
+int orc_compress_append_gated(
+    int batch, int max_blocks, const int32_t* block_table,
+    const int32_t* cu_new, const int32_t* start_pos,
+    int tok_dtype, const void* kv_tok, const float* kv_logit,
+    const void* ik_tok, const float* ik_logit,
+    int m, int D, int dI,
+    int kv_dtype, void* kv_data, void* kv_scale,
+    int ik_dtype, void* ik_data, void* ik_scale,
+    int win_dtype, int win_cap, void* win_data, float* win_scale,
+    void* rem_kv, void* rem_ik, float* rem_kv_logit, float* rem_ik_logit)
+{
+    return compress_append_impl(1, batch, max_blocks, block_table, cu_new, start_pos, tok_dtype, kv_tok, kv_logit,
+                                ik_tok, ik_logit, m, D, dI, kv_dtype, kv_data, kv_scale, ik_dtype, ik_data, ik_scale,
+                                win_dtype, win_cap, win_data, win_scale, rem_kv, rem_ik, rem_kv_logit, rem_ik_logit);
 }
 
 /* ------------------------------------------------------------------------ */
