@@ -197,6 +197,33 @@ lcca_status lcca_compress_append(void* stream, const lcca_pages* pages,
                                  const lcca_window_cache* win, const lcca_remainder* rem);
 
 /*
+ * lcca_compress_append_gated -- lcca_compress_append with per-channel gates.
+ *
+ * [P1 "Kako funkcionira optimizacija KV cachea?": tokens are folded by
+ * weighted summation; here every channel of a token carries its own
+ * aggregation logit, the per-channel variant of the same weighted sum.]  For
+ * each completed group g, stream and channel c:
+ *     w_ic = softmax_i(a_{g m + i, c})  over the group's m tokens,
+ *     C_gc = sum_i w_ic x_{g m + i, c}  (fp32),
+ * with the same encode, pages, window ring and remainder ring as
+ * lcca_compress_append.  With equal logits in every channel the entries
+ * equal the per-token call's.  Arguments as lcca_compress_append, except:
+ *   kv_logit   device float [total_new][kv->dim]
+ *   ik_logit   device float [total_new][ik->dim] (NULL iff ik NULL)
+ *   rem        its kv_logit is float [batch][ratio_m][kv->dim] and its
+ *              ik_logit float [batch][ratio_m][ik->dim]: a ring slot holds
+ *              the token's whole logit row
+ * Token and logit arrays are read in 16-byte units: 16-byte aligned.
+ * One workgroup per new token.
+ */
+lcca_status lcca_compress_append_gated(void* stream, const lcca_pages* pages,
+                                       const int32_t* cu_new, const int32_t* start_pos, int32_t total_new,
+                                       int32_t tok_dtype, const void* kv_tok, const float* kv_logit,
+                                       const void* ik_tok, const float* ik_logit,
+                                       const lcca_paged_cache* kv, const lcca_paged_cache* ik,
+                                       const lcca_window_cache* win, const lcca_remainder* rem);
+
+/*
  * lcca_index_logits -- sparse MQA logits of the indexer.
  *
  * [P3 "Vykon neprinesl jeden kernel": the indexer scores only candidate

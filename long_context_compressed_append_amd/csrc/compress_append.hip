@@ -302,6 +302,170 @@ __global__ __launch_bounds__(cmp::kThreads) void compress_chunk_kernel(CompressA
     }
 }
 
+// ---------------------------------------------------------------------------
+// Per-channel-gated groups
+// ---------------------------------------------------------------------------
+// Every channel of every token carries its own logit and the group's softmax
+// is taken per channel: w_ic = exp(a_ic - max_j a_jc) / sum_j exp(a_jc - ...),
+// C_c = sum_i w_ic x_ic.  One workgroup of kGatedThreads per new token; its
+// threads cover the token's 8-channel chunks (both streams, an MXFP4 block's
+// four chunks on four adjacent lanes) and, if the token completes a group,
+// form that group's chunks: the channel maxima, the exponentials and their
+// sum, then the weighted sum, in token order; then the pool dtype's encode.
+// The window slot and the remainder ring (tokens and their logit rows) are
+// written as in the per-token kernels, including the ordering of a chunk
+// whose first group reads ring slots its tail rewrites.
+constexpr int kGatedThreads = 128;
+
+// One 8-channel chunk of group g of a stream: x from the token arrays (or the
+// ring for tokens before the chunk), logits from the [n][dim] rows (or the
+// ring's [batch*m][dim] rows).
+template <int TOK>
+__device__ __forceinline__ void gated_chunk(const CompressArgs& p, const cmp::SeqChunk& q, int g, bool ik, int d0,
+                                            float (&v)[8]) {
+    const int m = p.m, dim = ik ? p.dI : p.D;
+    const void* tok = ik ? p.ik_tok : p.kv_tok;
+    const void* rtok = ik ? p.rem_ik : p.rem_kv;
+    const float* lg = ik ? p.ik_logit : p.kv_logit;
+    const float* rlg = ik ? p.rem_ik_logit : p.rem_kv_logit;
+    auto row_of = [&](int i, bool& fresh) -> int64_t {
+        const int t = g * m + i;
+        fresh = t >= q.start;
+        return fresh ? q.c0 + (t - q.start) : (int64_t)q.b * m + t % m;
+    };
+    auto logits = [&](int i, float (&a)[8]) {
+        bool fresh;
+        const int64_t r = row_of(i, fresh);
+        const f32x4* src = reinterpret_cast<const f32x4*>((fresh ? lg : rlg) + r * dim + d0);
+        const f32x4 lo = src[0], hi = src[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[4 + e] = hi[e]; }
+    };
+    float mx[8], sum[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { mx[e] = -INFINITY; sum[e] = 0.0f; v[e] = 0.0f; }
+    for (int i = 0; i < m; ++i) {
+        float a[8];
+        logits(i, a);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], a[e]);
+    }
+    for (int i = 0; i < m; ++i) {
+        float a[8];
+        logits(i, a);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum[e] += expf(a[e] - mx[e]);
+    }
+    for (int i = 0; i < m; ++i) {
+        float a[8], x[8];
+        logits(i, a);
+        bool fresh;
+        const int64_t r = row_of(i, fresh);
+        cmp::RawChunk<TOK> raw;
+        cmp::load_chunk<TOK>(fresh ? tok : rtok, r * dim + d0, raw);
+        cmp::unpack_chunk<TOK>(raw, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = fmaf(expf(a[e] - mx[e]) / sum[e], x[e], v[e]);
+    }
+}
+
+// Token tt of the chunk into its remainder-ring slot: the token's vectors and
+// logit rows of both streams (16-byte units, all threads of the workgroup).
+template <int TOK>
+__device__ void write_ring_gated(const CompressArgs& p, const cmp::SeqChunk& q, int tt) {
+    constexpr int esz = TOK == DT_F32 ? 4 : 2;
+    const int64_t src = q.c0 + (tt - q.start);
+    const int64_t slot = (int64_t)q.b * p.m + tt % p.m;
+    auto copy = [&](const void* s, void* d, int64_t bytes_per_row) {
+        const u32x4* s4 = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(s) + src * bytes_per_row);
+        u32x4* d4 = reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(d) + slot * bytes_per_row);
+        for (int i = threadIdx.x; i < bytes_per_row / 16; i += kGatedThreads) d4[i] = s4[i];
+    };
+    copy(p.kv_tok, p.rem_kv, (int64_t)p.D * esz);
+    copy(p.kv_logit, p.rem_kv_logit, (int64_t)p.D * 4);
+    if (p.ik_data != nullptr) {
+        copy(p.ik_tok, p.rem_ik, (int64_t)p.dI * esz);
+        copy(p.ik_logit, p.rem_ik_logit, (int64_t)p.dI * 4);
+    }
+}
+
+template <int TOK>
+__global__ __launch_bounds__(kGatedThreads) void compress_gated_kernel(CompressArgs p) {
+    constexpr int NT = kGatedThreads;
+    constexpr int kWinChunks = 2048 / 8 / NT;            // kv dims <= 2048
+    __shared__ int cu_lds[cmp::kSeqLds + 1], sp_lds[cmp::kSeqLds];
+    __shared__ unsigned int amax_lds;
+    const int t = (int)blockIdx.x, tid = threadIdx.x;
+    if (tid == 0) amax_lds = 0u;
+    __syncthreads();
+    const cmp::SeqChunk q = cmp::seq_of<NT>(p, t, cu_lds, sp_lds);
+    const int m = p.m;
+    const int pos = q.start + (t - (int)q.c0);
+    const int g0 = q.start / m;
+    const bool race = (q.start % m) != 0 && (q.end % m) != 0 && q.end >= (g0 + 1) * m;
+    const int tail0 = max((q.end / m) * m, q.start);
+    const int nkv = p.D / 8, nik = p.ik_data != nullptr ? p.dI / 8 : 0;
+    const int per = nkv + ((nik + 3) & ~3);
+
+    // (1) the group this token completes
+    if ((pos + 1) % m == 0) {
+        const int g = pos / m, E = 256 / m;
+        const int64_t row =
+            (int64_t)checked(p.block_table[(int64_t)q.b * p.max_blocks + g / E], 0, p.n_blocks - 1, p.dbg, kDbgBlock) * E +
+            g % E;
+        for (int base = 0; base < per; base += NT) {
+            const int u = base + tid;
+            const bool active = u < per && u - nkv < nik;
+            const bool ik = u >= nkv;
+            const int d0 = ik ? (u - nkv) * 8 : u * 8;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+            if (active) gated_chunk<TOK>(p, q, g, ik, d0, v);
+            store_entry_chunk(p, ik, row, d0, v, active);
+        }
+        if (race && g == g0) {
+            // this workgroup read the ring slots the chunk's tail rewrites
+            __syncthreads();
+            for (int tt = tail0; tt < q.end; ++tt) write_ring_gated<TOK>(p, q, tt);
+        }
+    }
+    // (2) window slot
+    if (p.win_data != nullptr && pos >= q.end - p.win_cap) {
+        const int64_t slot = (int64_t)q.b * p.win_cap + pos % p.win_cap;
+        float x[kWinChunks][8];
+        float a = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kWinChunks; ++j) {
+            const int c = tid + NT * j;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[j][e] = 0.0f;
+            if (c < nkv) {
+                cmp::RawChunk<TOK> raw;
+                cmp::load_chunk<TOK>(p.kv_tok, (int64_t)t * p.D + 8 * c, raw);
+                cmp::unpack_chunk<TOK>(raw, x[j]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[j][e]));
+            }
+        }
+        float sc = 1.0f;
+        if (p.win_dtype == DT_FP8) {
+            atomicMax(&amax_lds, __float_as_uint(a));        // non-negative: ordered as integers
+            __syncthreads();
+            const float amax = __uint_as_float(amax_lds);
+            sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+            if (tid == 0) p.win_scale[slot] = sc;
+        }
+#pragma unroll
+        for (int j = 0; j < kWinChunks; ++j) {
+            const int c = tid + NT * j;
+            if (c < nkv) store_window_chunk(p, slot, 8 * c, x[j], sc);
+        }
+    }
+    // (3) remainder ring: the token itself if it is in the incomplete tail
+    if (!race && pos >= tail0) write_ring_gated<TOK>(p, q, pos);
+}
+
 }  // namespace
 
 hipError_t launch_compress_append(const CompressArgs& a, int total_new, hipStream_t stream) {
@@ -321,6 +485,15 @@ hipError_t launch_compress_append(const CompressArgs& a, int total_new, hipStrea
         hipLaunchKernelGGL(compress_append_kernel<DT_F32>, grid, dim3(cmp::kThreads), 0, stream, a);
     else
         hipLaunchKernelGGL(compress_append_kernel<DT_BF16>, grid, dim3(cmp::kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_compress_gated(const CompressArgs& a, int total_new, hipStream_t stream) {
+    if (total_new <= 0) return hipSuccess;
+    if (a.tok_dtype == DT_F32)
+        hipLaunchKernelGGL(compress_gated_kernel<DT_F32>, dim3(total_new), dim3(kGatedThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(compress_gated_kernel<DT_BF16>, dim3(total_new), dim3(kGatedThreads), 0, stream, a);
     return hipGetLastError();
 }
 

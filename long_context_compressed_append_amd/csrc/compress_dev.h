@@ -81,11 +81,13 @@ constexpr int kSeqLds = 1024;                 // batches up to this size search 
 
 // Sequence of token t: the largest b with cu_new[b] <= t.  For batches of up
 // to kSeqLds sequences, cu_new and start_pos are first copied to LDS in one
-// round of loads, so the search costs no dependent global loads.
+// round of loads (by the NT threads of the workgroup), so the search costs no
+// dependent global loads.
+template <int NT = kThreads>
 __device__ inline SeqChunk seq_of(const CompressArgs& p, int t, int* cu_lds, int* sp_lds) {
     const bool in_lds = p.batch <= kSeqLds;
     if (in_lds) {
-        for (int i = threadIdx.x; i <= p.batch; i += kThreads) {
+        for (int i = threadIdx.x; i <= p.batch; i += NT) {
             cu_lds[i] = p.cu_new[i];
             if (i < p.batch) sp_lds[i] = p.start_pos[i];
         }

@@ -29,6 +29,9 @@ struct CompressArgs {
     int32_t ik_dtype; void* ik_data; void* ik_scale;     // ik_data == nullptr: no indexer stream
     int32_t win_dtype; int32_t win_cap; void* win_data; float* win_scale;   // win_data == nullptr: no window
     void* rem_kv; void* rem_ik; float* rem_kv_logit; float* rem_ik_logit;
+    // per-channel-gated groups: logits [n][dim] per stream, ring logits
+    // [batch][m][dim] (launch_compress_gated only)
+    int32_t gated;
 };
 
 struct IndexArgs {
@@ -103,6 +106,7 @@ struct AttnArgs {
 };
 
 hipError_t launch_compress_append(const CompressArgs& a, int total_new, hipStream_t stream);
+hipError_t launch_compress_gated(const CompressArgs& a, int total_new, hipStream_t stream);
 hipError_t launch_index_logits(const IndexArgs& a, int max_entries, hipStream_t stream);
 hipError_t launch_topk_select(TopkArgs a, int max_entries, hipStream_t stream);
 // top-k selection of every row (one launch, rows of up to 32K entries, 16-byte

@@ -305,6 +305,20 @@ lcca_status lcca_compress_append(void* stream, const lcca_pages* pages, const in
     return hip_status(lcca::launch_compress_append(a, total_new, (hipStream_t)stream), "compress_append launch");
 }
 
+lcca_status lcca_compress_append_gated(void* stream, const lcca_pages* pages, const int32_t* cu_new,
+                                       const int32_t* start_pos, int32_t total_new, int32_t tok_dtype,
+                                       const void* kv_tok, const float* kv_logit, const void* ik_tok,
+                                       const float* ik_logit, const lcca_paged_cache* kv, const lcca_paged_cache* ik,
+                                       const lcca_window_cache* win, const lcca_remainder* rem) {
+    g_err[0] = 0;
+    lcca::CompressArgs a;
+    const lcca_status s = prep_compress(pages, cu_new, start_pos, total_new, tok_dtype, kv_tok, kv_logit, ik_tok,
+                                        ik_logit, kv, ik, win, rem, a);
+    if (s) return s;
+    a.gated = 1;
+    return hip_status(lcca::launch_compress_gated(a, total_new, (hipStream_t)stream), "compress_append_gated launch");
+}
+
 lcca_status lcca_index_logits(void* stream, const lcca_pages* pages, const lcca_rows* rows, int32_t q_dtype,
                               const void* q_idx, int32_t HI, const float* w_idx, float s_I,
                               const lcca_paged_cache* ik, float* logits, int64_t ld) {

@@ -27,7 +27,7 @@ DEBUG_LIB_PATH = os.path.join(_PKG, "liblcca_debug.so")
 EXPORTED = ("lcca_compress_append", "lcca_index_logits", "lcca_topk_select", "lcca_sparse_attn_fwd",
             "lcca_sparse_attn_workspace_size", "lcca_topk_workspace_size", "lcca_status_string", "lcca_last_error",
             "lcca_version", "lcca_decode_select", "lcca_decode_select_workspace_size", "lcca_remainder_bytes",
-            "lcca_sparse_attn_fwd_noalloc", "lcca_debug_check")
+            "lcca_sparse_attn_fwd_noalloc", "lcca_debug_check", "lcca_compress_append_gated")
 
 
 class LccaError(RuntimeError):
@@ -83,6 +83,7 @@ def lib():
         PP, PR, PC, PW, PM = (ctypes.POINTER(_Pages), ctypes.POINTER(_Rows), ctypes.POINTER(_PagedCache),
                               ctypes.POINTER(_WindowCache), ctypes.POINTER(_Remainder))
         L.lcca_compress_append.argtypes = [P, PP, P, P, i32, i32, P, P, P, P, PC, PC, PW, PM]
+        L.lcca_compress_append_gated.argtypes = L.lcca_compress_append.argtypes
         L.lcca_index_logits.argtypes = [P, PP, PR, i32, P, i32, P, f32, PC, P, i64]
         L.lcca_topk_select.argtypes = [P, PR, i32, P, i64, i32, P, P, sz]
         L.lcca_sparse_attn_fwd.argtypes = [P, PP, PR, i32, P, i32, i32, f32, PC, P, i32, PW, i32, P, P, P, sz]
@@ -98,7 +99,7 @@ def lib():
         L.lcca_remainder_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.lcca_remainder_bytes.restype = sz
         for n in ("lcca_compress_append", "lcca_index_logits", "lcca_topk_select", "lcca_sparse_attn_fwd",
-                  "lcca_decode_select", "lcca_sparse_attn_fwd_noalloc"):
+                  "lcca_decode_select", "lcca_sparse_attn_fwd_noalloc", "lcca_compress_append_gated"):
             getattr(L, n).restype = i32
         L.lcca_debug_check.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
         L.lcca_debug_check.restype = i32
@@ -238,6 +239,17 @@ def compress_append(pages: Pages, cu_new, start_pos, total_new: int, tok_dtype: 
                     ik_tok, ik_logit, kv: PagedCache, ik: Optional[PagedCache], win: Optional[WindowCache],
                     rem: Remainder, stream=None):
     _check(lib().lcca_compress_append(
+        _stream(stream), ctypes.byref(pages.c()), _ptr(cu_new), _ptr(start_pos), int(total_new), tok_dtype,
+        _ptr(kv_tok), _ptr(kv_logit), _ptr(ik_tok), _ptr(ik_logit), ctypes.byref(kv.c()),
+        _ref(ik.c() if ik else None), _ref(win.c() if win else None), ctypes.byref(rem.c())))
+
+
+def compress_append_gated(pages: Pages, cu_new, start_pos, total_new: int, tok_dtype: int, kv_tok, kv_logit,
+                          ik_tok, ik_logit, kv: PagedCache, ik: Optional[PagedCache], win: Optional[WindowCache],
+                          rem: Remainder, stream=None):
+    """compress_append with per-channel logits ([n][dim] per stream; the
+    remainder ring's logits are [batch][ratio_m][dim])."""
+    _check(lib().lcca_compress_append_gated(
         _stream(stream), ctypes.byref(pages.c()), _ptr(cu_new), _ptr(start_pos), int(total_new), tok_dtype,
         _ptr(kv_tok), _ptr(kv_logit), _ptr(ik_tok), _ptr(ik_logit), ctypes.byref(kv.c()),
         _ref(ik.c() if ik else None), _ref(win.c() if win else None), ctypes.byref(rem.c())))

@@ -35,6 +35,7 @@ SEED_ROOT = 0x1CCA
 T_KV_ENTRIES, T_IK_ENTRIES, T_WIN, T_REM_KV, T_REM_IK, T_REM_KV_LOGIT, T_REM_IK_LOGIT = 1, 2, 3, 4, 5, 6, 7
 T_NEW_KV, T_NEW_IK, T_NEW_KV_LOGIT, T_NEW_IK_LOGIT = 8, 9, 10, 11
 T_Q, T_Q_IDX, T_W_IDX, T_BLOCK_PERM, T_OUTLIER = 12, 13, 14, 15, 16
+T_REM_KV_GATE, T_REM_IK_GATE, T_NEW_KV_GATE, T_NEW_IK_GATE = 17, 18, 19, 20
 
 F32, BF16, FP8, MXFP4 = "f32", "bf16", "fp8", "mxfp4"
 
@@ -229,6 +230,19 @@ def new_tokens(cfg: Config, b: int):
     a = normal(cfg, T_NEW_KV_LOGIT, b, (n,))
     ai = normal(cfg, T_NEW_IK_LOGIT, b, (n,)) if cfg.HI else None
     return kv, ik, a, ai
+
+
+def gate_logits(cfg: Config, b: int):
+    """Per-channel aggregation logits of sequence b, N(0,1) like the
+    per-token ones: (remainder-ring tokens kv [r][D], ik [r][dI]; new tokens
+    kv [n][D], ik [n][dI]); the ik arrays are None without an indexer."""
+    r = cfg.prior_len[b] - (cfg.prior_len[b] // cfg.m) * cfg.m
+    n = cfg.n_new[b]
+    rk = normal(cfg, T_REM_KV_GATE, b, (r, cfg.D))
+    ri = normal(cfg, T_REM_IK_GATE, b, (r, cfg.dI)) if cfg.HI else None
+    nk = normal(cfg, T_NEW_KV_GATE, b, (n, cfg.D))
+    ni = normal(cfg, T_NEW_IK_GATE, b, (n, cfg.dI)) if cfg.HI else None
+    return rk, ri, nk, ni
 
 
 def queries(cfg: Config, b: int, nrows: int):
