@@ -100,16 +100,20 @@ def enc_mxfp4(torch, x):
 # workload construction (device-side, seeded)
 # --------------------------------------------------------------------------
 
-def stage_work(c):
+def stage_work(c, gated=False):
     """Algorithmic (bytes, flops) per stage: the unique bytes each stage
     must read and write (every cache row counted once per step, however
-    many rows or heads use it) and the multiply-adds it must do."""
+    many rows or heads use it) and the multiply-adds it must do.  gated:
+    compress_append with a logit per token and channel."""
     import numpy as np
     m, D, H, HI, dI, k, w = c.m, c.D, c.H, c.HI, c.dI, c.k, c.window
     kv_row = {"bf16": 2 * D, "mxfp4": D // 2 + D // 32}[c.kv_dtype]
     ik_row = {"bf16": 2 * dI, "fp8": dI}[c.ik_dtype] if HI else 0
     win_row = {"fp8": D + 4, "bf16": 2 * D}[c.win_dtype]
-    tok_row = 2 * D + 4 + ((2 * dI + 4) if HI else 0)      # bf16 token + its logit, both streams
+    if gated:                                               # bf16 token + its logit row, both streams
+        tok_row = 6 * D + (6 * dI if HI else 0)
+    else:                                                   # bf16 token + its logit, both streams
+        tok_row = 2 * D + 4 + ((2 * dI + 4) if HI else 0)
     seq, pos = c.rows_of()
     pos = pos.astype(np.int64)
     n_r = (pos + 1) // m
@@ -500,6 +504,38 @@ def measured_traffic(workload, stage):
     return None
 
 
+def gated_leg(torch, lcca, wl, steps, warmup):
+    """Mean time (ms) of lcca_compress_append_gated on the workload's new
+    tokens, with N(0,1) logits per token and channel, over the rotated cache
+    copies (the same positions each call, so every call stores the same
+    bytes)."""
+    c = wl.cfg
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed_base + 17)
+    nk = torch.randn((wl.total_new, c.D), generator=g, device="cuda")
+    ni = torch.randn((wl.total_new, c.dI), generator=g, device="cuda") if c.HI else None
+    rk = torch.randn((wl.B * c.m, c.D), generator=g, device="cuda")
+    ri = torch.randn((wl.B * c.m, c.dI), generator=g, device="cuda") if c.HI else None
+    rems = [lcca.Remainder(lcca.BF16, rem.kv, rk, rem.ik, ri) for (_, _, _, rem) in wl.copies]
+
+    def call(i):
+        kv, ik, win, _ = wl.copies[i % wl.R]
+        lcca.compress_append_gated(wl.pages, wl.cu_new, wl.start_pos, wl.total_new, lcca.BF16, wl.new_kv, nk,
+                                   wl.new_ik, ni, kv, ik, win, rems[i % wl.R])
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        call(i)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
 def run_workload(torch, lcca, synth, name, args, with_oracle, cpu_seconds=0.0, bf16_variant=False):
     log("workload", name, "building")
     wl = Workload(name, torch, lcca, synth, cold=True, out_dtype="f32")
@@ -560,6 +596,12 @@ def run_workload(torch, lcca, synth, name, args, with_oracle, cpu_seconds=0.0, b
             v["parity"] = parity_summary(wl, rows, out_ref, idx_ref)
         res["bf16_out"] = v
         log(name, "bf16 outputs", json.dumps(v))
+    if not args.no_gated:
+        t = gated_leg(torch, lcca, wl, steps, args.warmup)
+        b = stage_work(wl.cfg, gated=True)["compress_append"][0]
+        res["gated_compress"] = {"ms": round(t, 5), "GB/s": round(b / t / 1e6, 1),
+                                 "hbm_frac": round(b / t / 1e6 / HBM_PEAK_GBS, 4), "bytes": b}
+        log(name, "compress_append_gated", json.dumps(res["gated_compress"]))
     log(name, json.dumps({k: v for k, v in res.items() if k != "stages"}))
     del wl
     torch.cuda.empty_cache()
@@ -578,6 +620,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the headline workload's oracle pass for at least this long (CPU baseline)")
     ap.add_argument("--no-hot", action="store_true")
+    ap.add_argument("--no-gated", action="store_true",
+                    help="skip the per-channel-gated compress_append leg of each workload")
     ap.add_argument("--no-bf16-variant", action="store_true",
                     help="skip the headline step with bf16 attention outputs (reported beside the fp32 one)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -640,12 +684,13 @@ def main():
         "hot_rows_per_s": round(r["hot_rows_per_s"], 1) if r["hot_rows_per_s"] else None,
         "parity": r.get("parity"),
         "bf16_out": r.get("bf16_out"),
+        "gated_compress": r.get("gated_compress"),
         "also": {n: {"rows_per_s": round(v["rows_per_s"], 1), "ms_per_step": round(v["ms_per_step"], 5),
                      "rows": v["rows"], "step_hbm_GB/s": round(v["step_GB/s"], 1),
                      "step_hbm_frac": round(v["step_hbm_frac"], 4), "step_TFLOP/s": round(v["step_TFLOP/s"], 2),
                      "hot_rows_per_s": round(v["hot_rows_per_s"], 1) if v["hot_rows_per_s"] else None,
                      "stages": v["stages"], "cold_cache_copies": v["R"], "steps": v["steps"],
-                     "parity": v.get("parity")}
+                     "parity": v.get("parity"), "gated_compress": v.get("gated_compress")}
                  for n, v in results.items() if n != head},
     }
     print(json.dumps(line), flush=True)

@@ -370,8 +370,8 @@ __device__ __forceinline__ void gated_chunk(const CompressArgs& p, const cmp::Se
 }
 
 // Token tt of the chunk into its remainder-ring slot: the token's vectors and
-// logit rows of both streams (16-byte units, all threads of the workgroup).
-template <int TOK>
+// logit rows of both streams (16-byte units, all NT threads of the workgroup).
+template <int TOK, int NT = kGatedThreads>
 __device__ void write_ring_gated(const CompressArgs& p, const cmp::SeqChunk& q, int tt) {
     constexpr int esz = TOK == DT_F32 ? 4 : 2;
     const int64_t src = q.c0 + (tt - q.start);
@@ -379,7 +379,7 @@ __device__ void write_ring_gated(const CompressArgs& p, const cmp::SeqChunk& q, 
     auto copy = [&](const void* s, void* d, int64_t bytes_per_row) {
         const u32x4* s4 = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(s) + src * bytes_per_row);
         u32x4* d4 = reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(d) + slot * bytes_per_row);
-        for (int i = threadIdx.x; i < bytes_per_row / 16; i += kGatedThreads) d4[i] = s4[i];
+        for (int i = threadIdx.x; i < bytes_per_row / 16; i += NT) d4[i] = s4[i];
     };
     copy(p.kv_tok, p.rem_kv, (int64_t)p.D * esz);
     copy(p.kv_logit, p.rem_kv_logit, (int64_t)p.D * 4);
@@ -466,6 +466,133 @@ __global__ __launch_bounds__(kGatedThreads) void compress_gated_kernel(CompressA
     if (!race && pos >= tail0) write_ring_gated<TOK>(p, q, pos);
 }
 
+// Groups of more than kChunkMaxM tokens (decode with m = 128): the grid of
+// the per-token slice kernel, (new token, 64-dimension slice), 256 threads =
+// 32 token lanes x 8 chunks of 8 dimensions.  Each lane holds the logit and
+// token chunks of tokens lane, lane + 32, ...; the channel maxima, the sums
+// of exponentials and the weighted sums are each reduced over the lanes in
+// LDS; wave 0 then encodes the slice's 64 dimensions (one per thread).
+template <int TOK>
+__device__ void gated_slice(const CompressArgs& p, const cmp::SeqChunk& q, int g, bool ik, int d0, float* red,
+                            float* stat) {
+    constexpr int LANES = cmp::kLanes, SD = cmp::kSliceDims, TPL = cmp::kMaxTokPerLane;
+    const int m = p.m, dim = ik ? p.dI : p.D;
+    const int tid = threadIdx.x, lane = tid / (SD / 8), ch = tid % (SD / 8);
+    const int d = d0 + ch * 8;
+    const bool active = d < dim;
+    const void* tok = ik ? p.ik_tok : p.kv_tok;
+    const void* rtok = ik ? p.rem_ik : p.rem_kv;
+    const float* lg = ik ? p.ik_logit : p.kv_logit;
+    const float* rlg = ik ? p.rem_ik_logit : p.rem_kv_logit;
+    cmp::RawChunk<TOK> raw[TPL];
+    float a[TPL][8];
+#pragma unroll
+    for (int j = 0; j < TPL; ++j) {
+        const int i = lane + LANES * j;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[j][e] = -INFINITY;
+        if (active && i < m) {
+            const int t = g * m + i;
+            const bool fresh = t >= q.start;
+            const int64_t r = fresh ? q.c0 + (t - q.start) : (int64_t)q.b * m + t % m;
+            cmp::load_chunk<TOK>(fresh ? tok : rtok, r * dim + d, raw[j]);
+            const f32x4* src = reinterpret_cast<const f32x4*>((fresh ? lg : rlg) + r * dim + d);
+            const f32x4 lo = src[0], hi = src[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { a[j][e] = lo[e]; a[j][4 + e] = hi[e]; }
+        }
+    }
+    // one per-channel reduction over the token lanes: red[lane][64] -> stat[64]
+    auto reduce = [&](const float (&v)[8], bool is_max, float (&out)[8]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[lane * SD + ch * 8 + e] = v[e];
+        __syncthreads();
+        if (tid < SD) {
+            float r = red[tid];
+            for (int l = 1; l < LANES; ++l) r = is_max ? fmaxf(r, red[l * SD + tid]) : r + red[l * SD + tid];
+            stat[tid] = r;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = stat[ch * 8 + e];
+        __syncthreads();
+    };
+    float mx[8], sum[8], v[8], loc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        loc[e] = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < TPL; ++j) loc[e] = fmaxf(loc[e], a[j][e]);
+    }
+    reduce(loc, true, mx);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        loc[e] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < TPL; ++j)
+            if (lane + LANES * j < m) loc[e] += expf(a[j][e] - mx[e]);
+    }
+    reduce(loc, false, sum);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) loc[e] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < TPL; ++j) {
+        if (active && lane + LANES * j < m) {
+            float x[8];
+            cmp::unpack_chunk<TOK>(raw[j], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) loc[e] = fmaf(expf(a[j][e] - mx[e]) / sum[e], x[e], loc[e]);
+        }
+    }
+    reduce(loc, false, v);
+    // wave 0: dimension d0 + tid of the slice
+    if (tid < SD) {
+        const int E = 256 / m;
+        const int64_t row =
+            (int64_t)checked(p.block_table[(int64_t)q.b * p.max_blocks + g / E], 0, p.n_blocks - 1, p.dbg, kDbgBlock) * E +
+            g % E;
+        cmp::store_slice_dim(p, ik, row, d0 + tid, stat[tid]);
+    }
+    __syncthreads();
+    (void)v;
+}
+
+template <int TOK>
+__global__ __launch_bounds__(cmp::kThreads) void compress_gated_slice_kernel(CompressArgs p) {
+    __shared__ float red[cmp::kLanes * cmp::kSliceDims];
+    __shared__ float stat[cmp::kSliceDims];
+    __shared__ int cu_lds[cmp::kSeqLds + 1], sp_lds[cmp::kSeqLds];
+    const int t = (int)blockIdx.x, s = (int)blockIdx.y;
+    const cmp::SeqChunk q = cmp::seq_of(p, t, cu_lds, sp_lds);
+    const int m = p.m;
+    const int pos = q.start + (t - (int)q.c0);
+    const int SK = (p.D + cmp::kSliceDims - 1) / cmp::kSliceDims;
+    const int SI = p.ik_data != nullptr ? (p.dI + cmp::kSliceDims - 1) / cmp::kSliceDims : 0;
+    const int g0 = q.start / m;
+    const bool race = (q.start % m) != 0 && (q.end % m) != 0 && q.end >= (g0 + 1) * m;
+    const int tail0 = max((q.end / m) * m, q.start);
+    if (s == SK + SI) {
+        cmp::write_window<TOK>(p, q, t, pos, red);
+        if (!race && pos >= tail0) write_ring_gated<TOK, cmp::kThreads>(p, q, pos);
+        return;
+    }
+    if ((pos + 1) % m == 0) {
+        const int g = pos / m;
+        if (race && g == g0) {
+            // the whole first group here (it reads ring slots the tail rewrites),
+            // then the tail
+            if (s == 0) {
+                for (int k = 0; k < SK; ++k) gated_slice<TOK>(p, q, g, false, k * cmp::kSliceDims, red, stat);
+                for (int k = 0; k < SI; ++k) gated_slice<TOK>(p, q, g, true, k * cmp::kSliceDims, red, stat);
+                for (int tt = tail0; tt < q.end; ++tt) write_ring_gated<TOK, cmp::kThreads>(p, q, tt);
+            }
+        } else {
+            const bool ik = s >= SK;
+            gated_slice<TOK>(p, q, g, ik, (ik ? s - SK : s) * cmp::kSliceDims, red, stat);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_compress_append(const CompressArgs& a, int total_new, hipStream_t stream) {
@@ -490,6 +617,16 @@ hipError_t launch_compress_append(const CompressArgs& a, int total_new, hipStrea
 
 hipError_t launch_compress_gated(const CompressArgs& a, int total_new, hipStream_t stream) {
     if (total_new <= 0) return hipSuccess;
+    if (a.m > kChunkMaxM) {
+        const int SK = (a.D + cmp::kSliceDims - 1) / cmp::kSliceDims;
+        const int SI = a.ik_data != nullptr ? (a.dI + cmp::kSliceDims - 1) / cmp::kSliceDims : 0;
+        const dim3 grid(total_new, SK + SI + 1);
+        if (a.tok_dtype == DT_F32)
+            hipLaunchKernelGGL(compress_gated_slice_kernel<DT_F32>, grid, dim3(cmp::kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL(compress_gated_slice_kernel<DT_BF16>, grid, dim3(cmp::kThreads), 0, stream, a);
+        return hipGetLastError();
+    }
     if (a.tok_dtype == DT_F32)
         hipLaunchKernelGGL(compress_gated_kernel<DT_F32>, dim3(total_new), dim3(kGatedThreads), 0, stream, a);
     else

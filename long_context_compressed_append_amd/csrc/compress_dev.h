@@ -214,6 +214,33 @@ __device__ void group_weights(int m, float a, float* w_lds, float* red) {
     __syncthreads();
 }
 
+// Encode dimension dim_i of an entry (value v) into pool row `row` of a
+// stream; called by the 64 threads of wave 0, thread i holding dimension
+// d0 + i of a 64-dimension slice (MXFP4 blocks of 32 dimensions are its two
+// half-waves; dimensions beyond the stream's take part in the exchanges
+// only).
+__device__ __forceinline__ void store_slice_dim(const CompressArgs& p, bool ik_stream, int64_t row, int dim_i,
+                                                float v) {
+    const int dim = ik_stream ? p.dI : p.D;
+    const int dt = ik_stream ? p.ik_dtype : p.kv_dtype;
+    uint8_t* data = reinterpret_cast<uint8_t*>(ik_stream ? p.ik_data : p.kv_data);
+    const bool in = dim_i < dim;
+    if (dt == DT_MXFP4) {
+        float a = in ? fabsf(v) : 0.0f;
+        for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+        const int X = mx_scale_exp(a);
+        const uint32_t c = fp4_code(ldexpf(v, -X));
+        const uint32_t c_hi = __shfl_down(c, 1);
+        if (in && (dim_i & 1) == 0) data[row * (int64_t)(dim / 2) + dim_i / 2] = (uint8_t)(c | (c_hi << 4));
+        if (in && (dim_i & 31) == 0)
+            reinterpret_cast<uint8_t*>(p.kv_scale)[row * (int64_t)(dim / 32) + dim_i / 32] = (uint8_t)(X + 127);
+    } else if (in) {
+        if (dt == DT_F32) reinterpret_cast<float*>(data)[row * dim + dim_i] = v;
+        else if (dt == DT_BF16) reinterpret_cast<uint16_t*>(data)[row * dim + dim_i] = (uint16_t)f32_to_bf16(v);
+        else data[row * (int64_t)dim + dim_i] = (uint8_t)f32_to_fp8(v);
+    }
+}
+
 // Weighted sum of dimensions [d0, d0 + 64) of the group over its tokens
 // (loaded by issue_slice, weights in w_lds), encoded into the pool.
 template <int TOK>
@@ -250,29 +277,7 @@ __device__ void reduce_slice(const CompressArgs& p, bool ik_stream, int d0, cons
         const int nl = min(m, kLanes);                         // token lanes holding tokens
         for (int l = 0; l < nl; ++l) v += red[l * kSliceDims + dd];
     }
-    // encode and store (threads < 64 hold one dimension each)
-    const int64_t row = L.row;
-    const int dt = ik_stream ? p.ik_dtype : p.kv_dtype;
-    uint8_t* data = reinterpret_cast<uint8_t*>(ik_stream ? p.ik_data : p.kv_data);
-    if (tid < kSliceDims) {
-        const int dim_i = d0 + dd;
-        const bool in = dim_i < dim;
-        if (dt == DT_MXFP4) {
-            // blocks of 32 dimensions = the two half-waves of wave 0
-            float a = in ? fabsf(v) : 0.0f;
-            for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
-            const int X = mx_scale_exp(a);
-            const uint32_t c = fp4_code(ldexpf(v, -X));
-            const uint32_t c_hi = __shfl_down(c, 1);
-            if (in && (dim_i & 1) == 0) data[row * (int64_t)(dim / 2) + dim_i / 2] = (uint8_t)(c | (c_hi << 4));
-            if (in && (dim_i & 31) == 0)
-                reinterpret_cast<uint8_t*>(p.kv_scale)[row * (int64_t)(dim / 32) + dim_i / 32] = (uint8_t)(X + 127);
-        } else if (in) {
-            if (dt == DT_F32) reinterpret_cast<float*>(data)[row * dim + dim_i] = v;
-            else if (dt == DT_BF16) reinterpret_cast<uint16_t*>(data)[row * dim + dim_i] = (uint16_t)f32_to_bf16(v);
-            else data[row * (int64_t)dim + dim_i] = (uint8_t)f32_to_fp8(v);
-        }
-    }
+    if (tid < kSliceDims) store_slice_dim(p, ik_stream, L.row, d0 + dd, v);
     __syncthreads();                                           // red is reused by the next slice
 }
 
@@ -306,6 +311,48 @@ __device__ void write_ring(const CompressArgs& p, const SeqChunk& q, int tt) {
     }
 }
 
+// New token t (position pos of its chunk) into its window slot if it is
+// among the chunk's last `capacity` tokens (FP8: a per-token scale from the
+// block-wide max; `red` holds at least 8 floats of LDS).
+template <int TOK>
+__device__ void write_window(const CompressArgs& p, const SeqChunk& q, int t, int pos, float* red) {
+    const int tid = threadIdx.x, D = p.D;
+    if (p.win_data != nullptr && pos >= q.end - p.win_cap) {
+        const int64_t slot = (int64_t)q.b * p.win_cap + pos % p.win_cap;
+        uint8_t* wd = reinterpret_cast<uint8_t*>(p.win_data);
+        const int pairs = D / 2;
+        if (p.win_dtype == DT_FP8) {
+            float x0[kMaxPairsPerThread], x1[kMaxPairsPerThread];
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kMaxPairsPerThread; ++i) {
+                const int pr = tid + i * kThreads;
+                x0[i] = x1[i] = 0.0f;
+                if (pr < pairs) load_pair<TOK>(p.kv_tok, (int64_t)t * D + 2 * pr, x0[i], x1[i]);
+                amax = fmaxf(amax, fmaxf(fabsf(x0[i]), fabsf(x1[i])));
+            }
+            amax = block_max(amax, red);
+            const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+            if (tid == 0) p.win_scale[slot] = sc;
+#pragma unroll
+            for (int i = 0; i < kMaxPairsPerThread; ++i) {
+                const int pr = tid + i * kThreads;
+                if (pr < pairs) {
+                    const uint32_t c = f32_to_fp8(x0[i] / sc) | (f32_to_fp8(x1[i] / sc) << 8);
+                    *reinterpret_cast<uint16_t*>(wd + slot * D + 2 * pr) = (uint16_t)c;
+                }
+            }
+        } else {
+            for (int pr = tid; pr < pairs; pr += kThreads) {
+                float x0, x1;
+                load_pair<TOK>(p.kv_tok, (int64_t)t * D + 2 * pr, x0, x1);
+                store_pair(p.win_dtype, wd, slot, D, pr, x0, x1);
+            }
+        }
+    }
+}
+
+
 // The whole work of grid item (new token t, slice s) on threads 0 .. 255 of
 // a workgroup (a larger workgroup's other waves must have exited).
 template <int TOK>
@@ -313,7 +360,6 @@ __device__ __forceinline__ void compress_append_body(const CompressArgs& p, int 
     __shared__ float w_lds[256];
     __shared__ float red[kLanes * kSliceDims];
     __shared__ int cu_lds[kSeqLds + 1], sp_lds[kSeqLds];
-    const int tid = threadIdx.x;
     const SeqChunk q = seq_of(p, t, cu_lds, sp_lds);
     const int pos = q.start + (t - (int)q.c0);
     const int m = p.m, D = p.D;
@@ -325,39 +371,7 @@ __device__ __forceinline__ void compress_append_body(const CompressArgs& p, int 
 
     if (s == SK + SI) {
         // (1) window ring
-        if (p.win_data != nullptr && pos >= q.end - p.win_cap) {
-            const int64_t slot = (int64_t)q.b * p.win_cap + pos % p.win_cap;
-            uint8_t* wd = reinterpret_cast<uint8_t*>(p.win_data);
-            const int pairs = D / 2;
-            if (p.win_dtype == DT_FP8) {
-                float x0[kMaxPairsPerThread], x1[kMaxPairsPerThread];
-                float amax = 0.0f;
-#pragma unroll
-                for (int i = 0; i < kMaxPairsPerThread; ++i) {
-                    const int pr = tid + i * kThreads;
-                    x0[i] = x1[i] = 0.0f;
-                    if (pr < pairs) load_pair<TOK>(p.kv_tok, (int64_t)t * D + 2 * pr, x0[i], x1[i]);
-                    amax = fmaxf(amax, fmaxf(fabsf(x0[i]), fabsf(x1[i])));
-                }
-                amax = block_max(amax, red);
-                const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
-                if (tid == 0) p.win_scale[slot] = sc;
-#pragma unroll
-                for (int i = 0; i < kMaxPairsPerThread; ++i) {
-                    const int pr = tid + i * kThreads;
-                    if (pr < pairs) {
-                        const uint32_t c = f32_to_fp8(x0[i] / sc) | (f32_to_fp8(x1[i] / sc) << 8);
-                        *reinterpret_cast<uint16_t*>(wd + slot * D + 2 * pr) = (uint16_t)c;
-                    }
-                }
-            } else {
-                for (int pr = tid; pr < pairs; pr += kThreads) {
-                    float x0, x1;
-                    load_pair<TOK>(p.kv_tok, (int64_t)t * D + 2 * pr, x0, x1);
-                    store_pair(p.win_dtype, wd, slot, D, pr, x0, x1);
-                }
-            }
-        }
+        write_window<TOK>(p, q, t, pos, red);
         // (3) remainder ring: each tail token writes itself (see the header
         // comment for `race`)
         if (!race && pos >= tail0) write_ring<TOK>(p, q, pos);

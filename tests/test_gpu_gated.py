@@ -29,6 +29,10 @@ CASES = [
     synth.shrink(S["lp_512k"], "gated_lp", (2047, 777), (100, 63), k=64),
     synth.shrink(S["tiny"], "gated_tiny", (0, 5), (100, 90), win_cap=2048),
     synth.shrink(S["hca_1m"], "gated_hca", (40959, 25600), (200, 130)),
+    synth.shrink(S["hca_1m"], "gated_hca_decode", (40959, 25599, 777), (1, 1, 1)),
+    # 16-token groups (the slice kernel) with a chunk whose first group reads
+    # ring slots its tail rewrites
+    synth.shrink(S["csa_64k"], "gated_m16", (3001, 1039), (70, 1), k=64, m=16),
 ]
 
 
