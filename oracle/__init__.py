@@ -53,6 +53,7 @@ def lib():
         L.orc_group_compress_gated.argtypes = [i32, i32, P, P, P]
         L.orc_store_rows.argtypes = [i32, P, P, i64, i64, i32, P]
         L.orc_load_rows.argtypes = [i32, P, P, i64, i64, i32, P]
+        L.orc_quantize_fp8_rows.argtypes = [P, i64, i32, P, P]
         L.orc_mx_scale_exp.argtypes = [ctypes.c_float]
         L.orc_mx_scale_exp.restype = ctypes.c_int
         for name in ("orc_bf16_encode_array", "orc_bf16_decode_array", "orc_fp8_encode_array",
@@ -102,6 +103,17 @@ def fp8_encode(x):
     out = np.empty(x.shape, np.uint8)
     lib().orc_fp8_encode_array(_p(x), x.size, _p(out))
     return out
+
+
+def quantize_fp8_rows(x):
+    """FP8 rows with a power-of-two scale: x [n][dim] float32 -> (codes uint8
+    [n][dim], X int32 [n]); x ~ decode(codes) * 2^X."""
+    x = np.ascontiguousarray(x, np.float32)
+    n, dim = x.shape
+    codes = np.empty((n, dim), np.uint8)
+    X = np.empty(n, np.int32)
+    lib().orc_quantize_fp8_rows(_p(x), n, dim, _p(codes), _p(X))
+    return codes, X
 
 
 def fp8_decode(c):

@@ -100,6 +100,32 @@ uint8_t orc_fp8_encode(float xf)
     return sign | (uint8_t)(((ev + 7) << 3) | mant);
 }
 
+/* FP8 query rows with a power-of-two scale (the low-precision indexer's
+ * quantisation of the query; the pages name FP8 indexer keys [P3 "Vykon
+ * neprinesl jeden kernel"] and give no rule for a quantised query, so the
+ * plainest one is taken, the MX block-scale rule with one block per row and
+ * the exponent lowered by one so no element saturates):
+ * X = floor(log2(max_i |x_i|)) - 7, so the largest magnitude divided by 2^X
+ * lies in [128, 256), below E4M3's 448; code_i = RNE E4M3 of x_i / 2^X.
+ * A row of zeros takes X = -127.  X is clamped to [-127, 127]. */
+void orc_quantize_fp8_rows(const float* x, int64_t nrows, int dim, uint8_t* codes, int32_t* X)
+{
+    for (int64_t r = 0; r < nrows; ++r) {
+        const float* xr = x + r * dim;
+        double amax = 0.0;
+        for (int i = 0; i < dim; ++i) if (fabs((double)xr[i]) > amax) amax = fabs((double)xr[i]);
+        int e = -127;
+        if (amax > 0.0) {
+            int ex; frexp(amax, &ex);                 /* amax in [2^(ex-1), 2^ex) */
+            e = (ex - 1) - 7;
+            if (e < -127) e = -127;
+            if (e > 127) e = 127;
+        }
+        X[r] = e;
+        for (int i = 0; i < dim; ++i) codes[r * dim + i] = orc_fp8_encode((float)ldexp((double)xr[i], -e));
+    }
+}
+
 /* E2M1 nibble: s e e m; values 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
 double orc_fp4_decode(uint8_t nib)
 {
