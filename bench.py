@@ -251,6 +251,7 @@ class Workload:
         self.rows = lcca.Rows(self.row_seq, self.row_pos, self.max_pos)
 
         self.host = None
+        self.q_ldt = lcca.BF16          # indexer query dtype (| lcca.Q_FP8: FP8 queries)
         self._init = dict(kv_data=kv_data, kv_scale=kv_scale, ik_data=ik_data, win_data=win_data,
                           win_scale=win_scale, rem_kv=rem_kv, rem_ik=rem_ik, rem_kv_logit=rem_kv_logit,
                           rem_ik_logit=rem_ik_logit)
@@ -308,7 +309,7 @@ class Workload:
             ev[0].record()
         if self.fused:
             L.decode_select(self.pages, self.rows, self.cu_new, self.start_pos, self.total_new, L.BF16, self.new_kv,
-                            self.new_kv_logit, self.new_ik, self.new_ik_logit, kv, ik, win, rem, L.BF16, self.q_idx,
+                            self.new_kv_logit, self.new_ik, self.new_ik_logit, kv, ik, win, rem, self.q_ldt, self.q_idx,
                             c.HI, self.w_idx, 1.0, self.logits, self.ld, c.k, self.topk, self.ds_ws)
             if ev is not None:
                 ev[1].record()
@@ -323,7 +324,7 @@ class Workload:
             ev[1].record()
         idx = None
         if c.HI:
-            L.index_logits(self.pages, self.rows, L.BF16, self.q_idx, c.HI, self.w_idx, 1.0, ik, self.logits,
+            L.index_logits(self.pages, self.rows, self.q_ldt, self.q_idx, c.HI, self.w_idx, 1.0, ik, self.logits,
                            self.ld)
             if ev is not None:
                 ev[2].record()
@@ -596,6 +597,20 @@ def run_workload(torch, lcca, synth, name, args, with_oracle, cpu_seconds=0.0, b
             v["parity"] = parity_summary(wl, rows, out_ref, idx_ref)
         res["bf16_out"] = v
         log(name, "bf16 outputs", json.dumps(v))
+    if not args.no_fp8q and wl.cfg.HI and wl.cfg.ik_dtype == synth.FP8 and wl.nrows < 64:
+        # the same step with FP8 queries on the FP8 indexer keys (opt-in)
+        wl.q_ldt = lcca.BF16 | lcca.Q_FP8
+        for i in range(args.warmup):
+            wl.step(i)
+        t = plain_steps(torch, wl, steps)
+        _, st8, _ = time_steps(torch, wl, steps, 0)
+        wl.q_ldt = lcca.BF16
+        sel = "decode_select" if wl.fused else "index_logits"
+        b = work[sel][0]
+        res["fp8_query"] = {"rows_per_s": round(wl.nrows / (t / 1e3), 1), "ms_per_step": round(t, 5),
+                            sel: {"ms": round(st8[sel], 5), "GB/s": round(b / st8[sel] / 1e6, 1),
+                                  "hbm_frac": round(b / st8[sel] / 1e6 / HBM_PEAK_GBS, 4)}}
+        log(name, "fp8 queries", json.dumps(res["fp8_query"]))
     if not args.no_gated:
         t = gated_leg(torch, lcca, wl, steps, args.warmup)
         b = stage_work(wl.cfg, gated=True)["compress_append"][0]
@@ -620,6 +635,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the headline workload's oracle pass for at least this long (CPU baseline)")
     ap.add_argument("--no-hot", action="store_true")
+    ap.add_argument("--no-fp8q", action="store_true",
+                    help="skip the FP8-query indexer leg of workloads with FP8 indexer keys")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the per-channel-gated compress_append leg of each workload")
     ap.add_argument("--no-bf16-variant", action="store_true",
@@ -690,7 +707,8 @@ def main():
                      "step_hbm_frac": round(v["step_hbm_frac"], 4), "step_TFLOP/s": round(v["step_TFLOP/s"], 2),
                      "hot_rows_per_s": round(v["hot_rows_per_s"], 1) if v["hot_rows_per_s"] else None,
                      "stages": v["stages"], "cold_cache_copies": v["R"], "steps": v["steps"],
-                     "parity": v.get("parity"), "gated_compress": v.get("gated_compress")}
+                     "parity": v.get("parity"), "gated_compress": v.get("gated_compress"),
+                     "fp8_query": v.get("fp8_query")}
                  for n, v in results.items() if n != head},
     }
     print(json.dumps(line), flush=True)

@@ -101,6 +101,19 @@ typedef int32_t lcca_status;
 
 typedef enum { LCCA_F32 = 0, LCCA_BF16 = 1, LCCA_FP8_E4M3 = 2, LCCA_MXFP4 = 3 } lcca_dtype;
 
+/* Flag OR-ed into the q_dtype of lcca_index_logits and lcca_decode_select
+ * (with LCCA_BF16 queries over raw FP8 E4M3 keys, fewer than 64 rows): the
+ * kernel quantises each row's query per head to FP8 E4M3 with a power-of-two
+ * scale, X = floor(log2 max_d |q_hd|) - 7 (the head's largest magnitude /
+ * 2^X lies in [128, 256), so nothing saturates; X = -127 for a zero head),
+ * q8_hd = RNE E4M3 of q_hd / 2^X, and computes q8_h . K_g * 2^X exactly on
+ * the FP8 matrix cores (fp32 accumulation).  The logits are then those of
+ * the quantised query; against the bf16 query each head's dot product moves
+ * by at most sum_d max(2^-4 |q_hd|, 2^(X-10)) |K_gd|.  [P3 "Vykon neprinesl
+ * jeden kernel": FP8 indexer keys; the query's quantisation rule is this
+ * library's.] */
+#define LCCA_Q_FP8 0x100
+
 typedef struct {
     int32_t dtype;        /* lcca_dtype of the stored entries                    */
     int32_t dim;          /* elements per entry                                  */
@@ -234,7 +247,8 @@ lcca_status lcca_compress_append_gated(void* stream, const lcca_pages* pages,
  * written.  fp32 accumulation; bf16 queries and bf16/FP8 keys use MFMA on
  * exactly upconverted keys.
  *   q_idx   device [num_rows][HI][ik->dim] of q_dtype (F32 with F32 keys;
- *           BF16 with BF16 or FP8 keys)
+ *           BF16 with BF16 or FP8 keys; BF16 | LCCA_Q_FP8 with FP8 keys
+ *           quantises the query to FP8, see LCCA_Q_FP8)
  *   w_idx   device float [num_rows][HI]
  *   logits  device float [num_rows][ld], ld >= max visible entries
  * BF16 path: HI % 32 == 0 and ik->dim % 64 == 0 (HI <= 128, dim <= 256).

@@ -73,6 +73,20 @@ __device__ inline uint32_t f32_to_fp8(float x) {
     return sign | ((uint32_t)(e + 7) << 3) | m3;
 }
 
+// The same rounding for finite |x| < 448 without branches (both encodings
+// are formed and one is selected), for code paths where lanes hold values
+// of every binade.
+__device__ __forceinline__ uint32_t f32_to_fp8_inrange(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t ua = u & 0x7fffffffu;
+    const float a = __uint_as_float(ua);
+    const uint32_t sub = (uint32_t)rintf(a * 512.0f);                   // below 2^-6: multiples of 2^-9
+    const uint32_t r = ua + 0x7ffffu + ((ua >> 20) & 1u);               // RNE to 3 mantissa bits
+    const uint32_t nor = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);  // (e + 7) << 3 | m3
+    return sign | (a < 0.015625f ? sub : nor);
+}
+
 // ---------------------------------------------------------------------------
 // OCP MXFP4: E2M1 elements, one E8M0 scale per 32 elements
 // ---------------------------------------------------------------------------

@@ -62,6 +62,59 @@ __device__ inline bf16x8 key_operand(const RawKey<KD, KS>& k, int s) {
     }
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// FP8 keys as B operands of the 32x32x64 FP8 MFMA: a lane's 32-byte k-block
+// s8 is bytes [32 s8, 32 s8 + 32) of the 64 contiguous bytes it loaded.
+template <int KS>
+__device__ inline i32x8 key_operand8(const RawKey<DT_FP8, KS>& k, int s8) {
+    return i32x8{(int)k.w[4 * s8][0],     (int)k.w[4 * s8][1],     (int)k.w[4 * s8 + 1][0], (int)k.w[4 * s8 + 1][1],
+                 (int)k.w[4 * s8 + 2][0], (int)k.w[4 * s8 + 2][1], (int)k.w[4 * s8 + 3][0], (int)k.w[4 * s8 + 3][1]};
+}
+
+// E4M3 code -> value (finite codes), without branches.
+__device__ __forceinline__ float fp8_value(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float sub = (float)m * 0x1p-9f;
+    const float nor = ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
+    const float v = e == 0 ? sub : nor;
+    return (c & 0x80u) ? -v : v;
+}
+
+// FP8 queries: each head's query row (bf16 in q_lds, rows of QROWB bytes)
+// is quantised: X = floor(log2 max |q_h|) - 7 (the row maximum / 2^X lands
+// in [128, 256), no saturation; X = -127 for a zero row), q8 = RNE E4M3 of
+// q / 2^X.  The codes go to q8_lds (rows of Q8ROWB bytes), X to x_lds[h],
+// and q_lds is overwritten with q8 * 2^X, which bf16 holds exactly.  All
+// kThreads threads: head tid / P, part tid % P of P = kThreads / heads parts
+// (adjacent lanes).
+template <int NHT, int DI, int QROWB, int Q8ROWB>
+__device__ void quantize_query_lds(uint8_t* q_lds, uint8_t* q8_lds, int* x_lds) {
+    constexpr int NH = NHT * 32, P = kThreads / NH, DP = DI / P;
+    static_assert(P >= 1 && (P & (P - 1)) == 0 && DP % 8 == 0, "query parts of whole 16-byte units");
+    const int tid = threadIdx.x, h = tid / P, part = tid % P;
+    uint16_t* row = reinterpret_cast<uint16_t*>(q_lds + h * QROWB) + part * DP;
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < DP; ++i) amax = fmaxf(amax, fabsf(bf16_to_f32(row[i])));
+#pragma unroll
+    for (int o = 1; o < P; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    int X = -127;
+    if (amax > 0.0f) {
+        int ex = 0;
+        (void)frexpf(amax, &ex);
+        X = min(max(ex - 1 - 7, -127), 127);
+    }
+    uint8_t* codes = q8_lds + h * Q8ROWB + part * DP;
+#pragma unroll
+    for (int i = 0; i < DP; ++i) {
+        const uint32_t c = f32_to_fp8_inrange(ldexpf(bf16_to_f32(row[i]), -X));   // |.| < 256
+        codes[i] = (uint8_t)c;
+        row[i] = (uint16_t)f32_to_bf16(ldexpf(fp8_value(c), X));
+    }
+    if (part == 0) x_lds[h] = X;
+}
+
 template <int N>
 struct IntC {
     static constexpr int value = N;
@@ -196,7 +249,7 @@ __device__ __forceinline__ void score_fresh(const IndexArgs& p, const FreshIn<DI
     }
 }
 
-template <int KD, int NHT, int DI>
+template <int KD, int NHT, int DI, bool Q8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void
 index_mfma_kernel(IndexArgs p) {
     constexpr int KS = DI / 16, HALF = DI / 2;
@@ -285,14 +338,41 @@ index_mfma_kernel(IndexArgs p) {
         for (int i = 0; i < PF - 1; ++i) load_key<KD, KS>(keys, row(t_begin + i, pbs[i]), g, kr[i]);
     }
     __syncthreads();
-    // query as A operands: head 32t + j, dims [g*HALF + 8s, +8)
-    bf16x8 qa[NHT][KS];
+    // FP8 queries: quantised in place (the fresh entry's score below reads
+    // the same values), their FP8 codes as A operands of the FP8 MFMA, head
+    // 32t + j, k-block s8 = dims [g*HALF + 32 s8, +32), with the head's
+    // exponent as the operand's E8M0 scale
+    constexpr int KS8 = HALF / 32;
+    constexpr int Q8ROWB = DI + 16;                              // code rows padded against bank conflicts
+    __shared__ int x_lds[NHT * 32];
+    __shared__ __attribute__((aligned(16))) uint8_t q8_lds[Q8 ? NHT * 32 * Q8ROWB : 16];
+    i32x8 qa8[Q8 ? NHT : 1][Q8 ? KS8 : 1];
+    int sa[NHT];
+    if constexpr (Q8) {
+        quantize_query_lds<NHT, DI, QROWB, Q8ROWB>(q_lds, q8_lds, x_lds);
+        __syncthreads();
 #pragma unroll
-    for (int t = 0; t < NHT; ++t)
+        for (int t = 0; t < NHT; ++t) {
+            sa[t] = x_lds[32 * t + j] + 127;
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            qa[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                      &q_lds[(32 * t + j) * QROWB + (g * HALF + 8 * s) * 2]));
+            for (int s8 = 0; s8 < KS8; ++s8) {
+                const uint8_t* src = &q8_lds[(32 * t + j) * Q8ROWB + g * HALF + 32 * s8];
+                const u32x4 lo = *reinterpret_cast<const u32x4*>(src), hi = *reinterpret_cast<const u32x4*>(src + 16);
+                qa8[t][s8] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            }
+        }
+    }
+    // bf16 queries as A operands: head 32t + j, dims [g*HALF + 8s, +8)
+    bf16x8 qa[Q8 ? 1 : NHT][Q8 ? 1 : KS];
+    if constexpr (!Q8) {
+#pragma unroll
+        for (int t = 0; t < NHT; ++t)
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                qa[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                          &q_lds[(32 * t + j) * QROWB + (g * HALF + 8 * s) * 2]));
+    }
     // head weights are read from LDS per tile, in C-layout order: head
     // 32t + 8(v/4) + 4g + v%4, four consecutive heads per 16-byte read
     const float* wrow = &w_lds[4 * g];
@@ -307,11 +387,23 @@ index_mfma_kernel(IndexArgs p) {
         f32x16 acc[NHT];
 #pragma unroll
         for (int t = 0; t < NHT; ++t) acc[t] = f32x16{};
+        if constexpr (Q8) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+            for (int s8 = 0; s8 < KS8; ++s8) {
+                const i32x8 kb = key_operand8<KS>(kc, s8);
 #pragma unroll
-            for (int t = 0; t < NHT; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t][s], key_operand<KD, KS>(kc, s), acc[t], 0, 0, 0);
+                for (int t = 0; t < NHT; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa8[t][s8], kb, acc[t], 0, 0, 0, sa[t], 0,
+                                                                            127);
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int t = 0; t < NHT; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t][s], key_operand<KD, KS>(kc, s), acc[t], 0, 0,
+                                                                    0);
+        }
         float l = 0.0f;
 #pragma unroll
         for (int t = 0; t < NHT; ++t)
@@ -524,7 +616,13 @@ hipError_t launch_mfma(IndexArgs a, int max_entries, hipStream_t stream) {
         if (tpw < 1) tpw = 1;
         a.tiles_per_wave = tpw;
         dim3 grid((max_tiles + 4 * tpw - 1) / (4 * tpw), a.num_rows);
-        hipLaunchKernelGGL((index_mfma_kernel<KD, NHT, DI>), grid, dim3(kThreads), 0, stream, a);
+        if constexpr (KD == DT_FP8) {
+            if (a.q8) {
+                hipLaunchKernelGGL((index_mfma_kernel<KD, NHT, DI, true>), grid, dim3(kThreads), 0, stream, a);
+                return hipGetLastError();
+            }
+        }
+        hipLaunchKernelGGL((index_mfma_kernel<KD, NHT, DI, false>), grid, dim3(kThreads), 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -42,6 +42,9 @@ struct IndexArgs {
     int32_t HI, dI, m;
     int32_t key_dtype; const void* keys;
     float* logits; int64_t ld;
+    // FP8 queries (q8 != 0, FP8 keys, fewer than 64 rows): each head's query
+    // quantised to E4M3 with a power-of-two scale, products on the FP8 MFMA
+    int32_t q8;
     // launch plan
     int32_t tiles_per_wave;      // 32-entry tiles per wave (decode) / per workgroup (prefill)
     // Decode launches ahead of the step's compress_append (fresh != 0, m <= 4):

@@ -271,6 +271,10 @@ lcca_status prep_index(const lcca_pages* pages, const lcca_rows* rows, int32_t q
     if (HI < 1) return fail(LCCA_ERR_INVALID_ARG, "HI=%d", HI);
     if (ik->dtype == LCCA_FP8_E4M3 && ik->scale)
         return fail(LCCA_ERR_UNSUPPORTED, "FP8 indexer keys with a scale array (raw E4M3 only)");
+    const bool q8 = (q_dtype & LCCA_Q_FP8) != 0;
+    q_dtype &= ~LCCA_Q_FP8;
+    if (q8 && (q_dtype != LCCA_BF16 || ik->dtype != LCCA_FP8_E4M3 || rows->num_rows >= 64))
+        return fail(LCCA_ERR_UNSUPPORTED, "FP8 queries (LCCA_Q_FP8): bf16 queries over FP8 keys, fewer than 64 rows");
     if (!lcca::index_supported(q_dtype, ik->dtype, HI, ik->dim))
         return fail(LCCA_ERR_UNSUPPORTED, "index_logits: q dtype %d, key dtype %d, HI=%d, dim=%d not built", q_dtype,
                     ik->dtype, HI, ik->dim);
@@ -283,7 +287,7 @@ lcca_status prep_index(const lcca_pages* pages, const lcca_rows* rows, int32_t q
     a.block_table = pages->block_table; a.max_blocks = pages->max_blocks_per_seq;
     a.row_seq = rows->row_seq; a.row_pos = rows->row_pos; a.num_rows = rows->num_rows;
     a.batch = pages->batch; a.max_pos = rows->max_pos; a.n_blocks = ik->num_blocks;
-    a.q = q_idx; a.w = w_idx; a.s_I = s_I; a.HI = HI; a.dI = ik->dim; a.m = ik->ratio_m;
+    a.q = q_idx; a.w = w_idx; a.s_I = s_I; a.HI = HI; a.dI = ik->dim; a.m = ik->ratio_m; a.q8 = q8;
     a.key_dtype = ik->dtype; a.keys = ik->data; a.logits = logits; a.ld = ld;
     return LCCA_OK;
 }
@@ -429,7 +433,7 @@ lcca_status lcca_decode_select(void* stream, const lcca_pages* pages, const lcca
     lcca::TopkArgs ta;
     int sel_entries = 0;
     if ((s = prep_topk(rows, ik->ratio_m, logits, ld, k, topk_idx, ws, ws_bytes, ta, sel_entries, empty))) return s;
-    if (q_dtype != LCCA_BF16 || rows->num_rows >= 64 || ik->ratio_m > 4 ||
+    if ((q_dtype & ~LCCA_Q_FP8) != LCCA_BF16 || rows->num_rows >= 64 || ik->ratio_m > 4 ||
         !lcca::topk_compress_supported(ta, sel_entries, tok_dtype))
         return fail(LCCA_ERR_UNSUPPORTED, "decode_select: needs bf16 queries and tokens, fewer than 64 rows, ratio_m "
                     "<= 4, 16-byte aligned logit rows, and rows of at most 32,768 entries or slices whose k "
