@@ -443,6 +443,20 @@ def cpu_baseline(wl, rows, dt, passes):
                       "%.1f s in all" % (len(rows), wl.nrows, wl.name, passes, dt, dt * passes)}
 
 
+def cpu_single_thread(wl, rows):
+    """The oracle on one thread: one pass over a few sampled rows."""
+    import oracle as O
+    n0 = O.num_threads()
+    O.set_num_threads(1)
+    try:
+        _, _, _, dt, _ = oracle_rows(wl, rows)
+    finally:
+        O.set_num_threads(n0)
+    return {"value": round(len(rows) / dt, 3), "unit": "query-rows/s", "cores": 1, "kind": "oracle",
+            "sample": "%d of %d rows of %s (compress_append of the whole step + the three row stages), one pass, "
+                      "%.2f s" % (len(rows), wl.nrows, wl.name, dt)}
+
+
 # BASELINE bounds for bf16/FP8 paths (MXFP4 pools: max-abs 5e-2)
 PARITY_BOUNDS = {"max_abs": 2e-2, "mean_abs": 2e-3, "rel_l2": 1e-2}
 
@@ -585,6 +599,7 @@ def run_workload(torch, lcca, synth, name, args, with_oracle, cpu_seconds=0.0, b
         out_ref, idx_ref, _, dt, passes = oracle_rows(wl, rows, cpu_seconds)
         res["parity"] = parity_summary(wl, rows, out_ref, idx_ref)
         baseline = cpu_baseline(wl, rows, dt, passes)
+        res["cpu_1t"] = cpu_single_thread(wl, rows[:4])
         log(name, "oracle %.2f s x %d; parity %s" % (dt, passes, json.dumps(res["parity"])))
     if bf16_variant:
         # the same step with bf16 attention outputs (fp16 split partials)
@@ -697,6 +712,7 @@ def main():
         "step_hbm_GB/s": round(r["step_GB/s"], 1), "step_hbm_frac": round(r["step_hbm_frac"], 4),
         "roofline": roof,
         "cpu_baseline": baselines.get(head),
+        "cpu_baseline_1t": r.get("cpu_1t"),
         "stages": r["stages"],
         "hot_rows_per_s": round(r["hot_rows_per_s"], 1) if r["hot_rows_per_s"] else None,
         "parity": r.get("parity"),
@@ -708,7 +724,7 @@ def main():
                      "hot_rows_per_s": round(v["hot_rows_per_s"], 1) if v["hot_rows_per_s"] else None,
                      "stages": v["stages"], "cold_cache_copies": v["R"], "steps": v["steps"],
                      "parity": v.get("parity"), "gated_compress": v.get("gated_compress"),
-                     "fp8_query": v.get("fp8_query")}
+                     "fp8_query": v.get("fp8_query"), "cpu_1t": v.get("cpu_1t")}
                  for n, v in results.items() if n != head},
     }
     print(json.dumps(line), flush=True)

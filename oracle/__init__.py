@@ -60,6 +60,7 @@ def lib():
                      "orc_fp8_decode_array", "orc_fp4_encode_array", "orc_fp4_decode_array"):
             getattr(L, name).argtypes = [P, i64, P]
         L.orc_num_threads.restype = ctypes.c_int
+        L.orc_set_num_threads.argtypes = [i32]
         _LIB = L
     return _LIB
 
@@ -78,6 +79,11 @@ def row_bytes(dtype, dim):
 
 def num_threads():
     return lib().orc_num_threads()
+
+
+def set_num_threads(n):
+    """Threads of the oracle's parallel loops from now on."""
+    lib().orc_set_num_threads(int(n))
 
 
 # --------------------------------------------------------------------------

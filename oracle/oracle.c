@@ -637,6 +637,16 @@ int orc_num_threads(void)
 #endif
 }
 
+/* Threads of the parallel loops that follow (timing only). */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* Element-wise array helpers for the codec tests                           */
 /* ------------------------------------------------------------------------ */
