@@ -700,7 +700,10 @@ def main():
     dname, d = max(r["stages"].items(), key=lambda kv: kv[1]["ms"])
     traffic = d["traffic"]
     roof = {"kernel": dname, "bound": "hbm", "achieved": d["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": d["hbm_frac"], "traffic": traffic, "algorithmic_bytes": d["bytes"]}
+            "frac": d["hbm_frac"], "traffic": traffic, "algorithmic_bytes": d["bytes"],
+            "basis": "HIP events around the stage's C-ABI call on its launch stream: for sparse_attn_fwd the "
+                     "attention kernel, the split merge and the launch gap between them (the kernel trace in "
+                     "profiles/ gives each kernel's own duration)"}
     cfg = synth.CONFIGS[head]
     line = {
         "metric": METRIC, "value": round(r["rows_per_s"], 1), "unit": "query-rows/s", "n_gpus": 1,
