@@ -54,6 +54,7 @@ def lib():
         L.orc_store_rows.argtypes = [i32, P, P, i64, i64, i32, P]
         L.orc_load_rows.argtypes = [i32, P, P, i64, i64, i32, P]
         L.orc_quantize_fp8_rows.argtypes = [P, i64, i32, P, P]
+        L.orc_rope.argtypes = [P, i64, i32, i32, i32, i32, P, dbl, P, i32, i32]
         L.orc_mx_scale_exp.argtypes = [ctypes.c_float]
         L.orc_mx_scale_exp.restype = ctypes.c_int
         for name in ("orc_bf16_encode_array", "orc_bf16_decode_array", "orc_fp8_encode_array",
@@ -109,6 +110,18 @@ def fp8_encode(x):
     out = np.empty(x.shape, np.uint8)
     lib().orc_fp8_encode_array(_p(x), x.size, _p(out))
     return out
+
+
+def rope(x, pos, off, rd, theta=10000.0, freq=None, pairing=0, inverse=False):
+    """Rotary embedding of dims [off, off + rd) of x [rows][heads][dim] (fp64
+    copy returned), row r rotated by pos[r]; pairing 0: pairs (2i, 2i+1),
+    1: (i, i + rd/2); freq: float32 [rd/2] or None for theta^(-2i/rd)."""
+    y = np.array(x, dtype=np.float64, order="C", copy=True)
+    rows, heads, dim = y.shape
+    fr = None if freq is None else np.ascontiguousarray(freq, dtype=np.float32)
+    lib().orc_rope(_p(y), rows, heads, dim, off, rd, _p(_i32(pos)), float(theta), None if fr is None else _p(fr),
+                   int(pairing), int(bool(inverse)))
+    return y
 
 
 def quantize_fp8_rows(x):

@@ -628,6 +628,40 @@ int orc_sparse_attn(
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Rotary position embedding of a slice of dimensions                        */
+/* ------------------------------------------------------------------------ */
+
+/* Rotation of the pairs of dims [off, off + rd) of every x[r][h][0..dim) by
+ * the row's position [P1 "Kako funkcionira optimizacija KV cachea?": the
+ * shared KV vectors carry RoPE dimensions and the output is rotated back].
+ * The pages fix no convention, so it is the caller's: pair i < rd/2 is
+ * (2i, 2i+1) with pairing 0 (interleaved) or (i, i + rd/2) with pairing 1
+ * (half split); its frequency is freq[i] if freq is given, else
+ * fp32(theta^(-2i/rd)); its angle is the fp32 product fp32(pos) * freq_i
+ * (the angle a float pipeline forms), and the rotation by that angle (by its
+ * negative with `inverse`) is done in fp64. */
+void orc_rope(double* x, int64_t rows, int heads, int dim, int off, int rd, const int32_t* pos, double theta,
+              const float* freq, int pairing, int inverse)
+{
+    int half = rd / 2;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int h = 0; h < heads; ++h) {
+            double* v = x + (r * heads + h) * (int64_t)dim + off;
+            for (int i = 0; i < half; ++i) {
+                float f = freq ? freq[i] : (float)pow(theta, -2.0 * i / rd);
+                float ang = (float)pos[r] * f;
+                double c = cos((double)ang), s = sin((double)ang);
+                if (inverse) s = -s;
+                int ia = pairing ? i : 2 * i, ib = pairing ? i + half : 2 * i + 1;
+                double a = v[ia], b = v[ib];
+                v[ia] = a * c - b * s;
+                v[ib] = a * s + b * c;
+            }
+        }
+    }
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP
