@@ -551,6 +551,40 @@ def gated_leg(torch, lcca, wl, steps, warmup):
     return t0.elapsed_time(t1) / steps
 
 
+def rope_leg(torch, lcca, wl, steps, warmup):
+    """Time the rotary embeddings of one step, each on a copy of its tensor:
+    the attention queries and the new tokens (64 RoPE dims at the end of the
+    shared vector), the indexer queries and keys (their first 64 dims), and
+    the inverse rotation of the attention output's last 64 dims.  Returns
+    {call: (ms, bytes)} with bytes = the slice read and written."""
+    c = wl.cfg
+    pos_rows = wl.row_pos
+    pos_tok = torch.cat([torch.arange(p, p + n, dtype=torch.int32, device="cuda")
+                         for p, n in zip(c.prior_len, c.n_new)])
+    rd = 64
+    calls = {"q": (wl.q.clone().view(torch.bfloat16).view(wl.nrows, c.H, c.D), pos_rows, c.D - rd, False),
+             "kv_tokens": (wl.new_kv.clone().view(torch.bfloat16).view(wl.total_new, 1, c.D), pos_tok, c.D - rd, False)}
+    if c.HI:
+        calls["q_idx"] = (wl.q_idx.clone().view(torch.bfloat16).view(wl.nrows, c.HI, c.dI), pos_rows, 0, False)
+        calls["ik_tokens"] = (wl.new_ik.clone().view(torch.bfloat16).view(wl.total_new, 1, c.dI), pos_tok, 0, False)
+    calls["out_inverse"] = (wl.out.clone(), pos_rows, c.dv - rd, True)
+    res = {}
+    for name, (x, pos, off, inv) in calls.items():
+        for i in range(warmup):
+            lcca.rope(x, pos, off, rd, inverse=inv)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps):
+            lcca.rope(x, pos, off, rd, inverse=inv)
+        t1.record()
+        torch.cuda.synchronize()
+        b = 2 * x.shape[0] * x.shape[1] * rd * x.element_size()
+        res[name] = (t0.elapsed_time(t1) / steps, b)
+    return res
+
+
 def run_workload(torch, lcca, synth, name, args, with_oracle, cpu_seconds=0.0, bf16_variant=False):
     log("workload", name, "building")
     wl = Workload(name, torch, lcca, synth, cold=True, out_dtype="f32")
@@ -632,6 +666,11 @@ def run_workload(torch, lcca, synth, name, args, with_oracle, cpu_seconds=0.0, b
         res["gated_compress"] = {"ms": round(t, 5), "GB/s": round(b / t / 1e6, 1),
                                  "hbm_frac": round(b / t / 1e6 / HBM_PEAK_GBS, 4), "bytes": b}
         log(name, "compress_append_gated", json.dumps(res["gated_compress"]))
+    if not args.no_rope:
+        rr = rope_leg(torch, lcca, wl, steps, args.warmup)
+        res["rope"] = {k: {"ms": round(t, 5), "GB/s": round(b / t / 1e6, 1), "bytes": b} for k, (t, b) in rr.items()}
+        res["rope"]["total_ms"] = round(sum(t for t, _ in rr.values()), 5)
+        log(name, "rope", json.dumps(res["rope"]))
     log(name, json.dumps({k: v for k, v in res.items() if k != "stages"}))
     del wl
     torch.cuda.empty_cache()
@@ -652,6 +691,7 @@ def main():
     ap.add_argument("--no-hot", action="store_true")
     ap.add_argument("--no-fp8q", action="store_true",
                     help="skip the FP8-query indexer leg of workloads with FP8 indexer keys")
+    ap.add_argument("--no-rope", action="store_true", help="skip timing the rotary embeddings of a step")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the per-channel-gated compress_append leg of each workload")
     ap.add_argument("--no-bf16-variant", action="store_true",
@@ -721,13 +761,15 @@ def main():
         "parity": r.get("parity"),
         "bf16_out": r.get("bf16_out"),
         "gated_compress": r.get("gated_compress"),
+        "rope": r.get("rope"),
         "also": {n: {"rows_per_s": round(v["rows_per_s"], 1), "ms_per_step": round(v["ms_per_step"], 5),
                      "rows": v["rows"], "step_hbm_GB/s": round(v["step_GB/s"], 1),
                      "step_hbm_frac": round(v["step_hbm_frac"], 4), "step_TFLOP/s": round(v["step_TFLOP/s"], 2),
                      "hot_rows_per_s": round(v["hot_rows_per_s"], 1) if v["hot_rows_per_s"] else None,
                      "stages": v["stages"], "cold_cache_copies": v["R"], "steps": v["steps"],
                      "parity": v.get("parity"), "gated_compress": v.get("gated_compress"),
-                     "fp8_query": v.get("fp8_query"), "cpu_1t": v.get("cpu_1t")}
+                     "fp8_query": v.get("fp8_query"), "cpu_1t": v.get("cpu_1t"),
+                     "rope": v.get("rope")}
                  for n, v in results.items() if n != head},
     }
     print(json.dumps(line), flush=True)

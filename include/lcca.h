@@ -404,6 +404,39 @@ lcca_status lcca_sparse_attn_fwd_noalloc(void* stream, const lcca_pages* pages, 
                                          const lcca_window_cache* win, int32_t out_dtype, void* out, float* lse);
 
 /*
+ * lcca_rope -- rotary position embedding of a slice of dims, in place.
+ *
+ * [P1 "Kako funkcionira optimizacija KV cachea?": the shared KV vectors are
+ * used with RoPE and the inverse rotation is applied to the output.]  The
+ * pages fix no convention, so the caller gives it.  For every row r, head h
+ * and pair i < rope_dim / 2 of the slice [rope_off, rope_off + rope_dim) of
+ * x[r][h], the pair (a, b) = dims (rope_off + 2i, rope_off + 2i + 1)
+ * (interleaved, the default) or (rope_off + i, rope_off + i + rope_dim / 2)
+ * (flag LCCA_ROPE_HALF) becomes
+ *     (a cos t - b sin t, a sin t + b cos t),   t = fp32(pos[r]) * f_i
+ * (an fp32 product; t negated with flag LCCA_ROPE_INVERSE, which undoes the
+ * forward rotation at the same positions).  f_i = inv_freq[i] if inv_freq
+ * is given (host float [rope_dim / 2], e.g. a scaled table), else
+ * fp32(theta^(-2i / rope_dim)) formed in double.  cos/sin and the rotation
+ * are fp32; BF16 results are rounded to nearest even.  Dims outside the slice
+ * are not touched.  Use: queries and new tokens before they are scored or
+ * compressed (rows = tokens, heads = 1 for the shared vectors), and the
+ * inverse on the attention output at the query positions.
+ *   dtype     LCCA_F32 or LCCA_BF16 (else LCCA_ERR_UNSUPPORTED)
+ *   x         device [rows][heads][dim] of dtype, read and written
+ *   pos       device int32 [rows] (any value)
+ *   rope_dim  even, 2..256, with rope_off >= 0 and rope_off + rope_dim <= dim
+ *   flags     LCCA_ROPE_HALF | LCCA_ROPE_INVERSE (other bits: invalid)
+ * rows == 0 launches nothing.  Vector loads are used when x is 16-byte
+ * aligned and rope_off, rope_dim and dim are multiples of 8.
+ */
+#define LCCA_ROPE_HALF    1
+#define LCCA_ROPE_INVERSE 2
+lcca_status lcca_rope(void* stream, int32_t dtype, void* x, int64_t rows, int32_t heads, int32_t dim,
+                      int32_t rope_off, int32_t rope_dim, const int32_t* pos, double theta, const float* inv_freq,
+                      int32_t flags);
+
+/*
  * lcca_debug_check -- index violations the debug library's kernels found.
  *
  * For development and for callers that cannot vouch for their device-side

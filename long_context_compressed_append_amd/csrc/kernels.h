@@ -108,6 +108,18 @@ struct AttnArgs {
     float* part_sc;    // [rows][nsplit][d_v / 16][H]
 };
 
+// Rotary embedding of dims [off, off + rd) of x [rows][heads][dim] in place
+// (rope.hip): pair i is (2i, 2i+1), or (i, i + rd/2) with half_split, rotated
+// by fp32(pos[r]) * freq[i] (negated with inverse).
+constexpr int kRopeMaxDim = 256;
+struct RopeArgs {
+    void* x; int64_t rows; int32_t heads, dim, off, rd;
+    const int32_t* pos;
+    int32_t bf16, half_split, inverse;
+    int32_t hchunk, nchunks;         // launch plan: heads per thread, head runs per row
+    float freq[kRopeMaxDim / 2];
+};
+
 hipError_t launch_compress_append(const CompressArgs& a, int total_new, hipStream_t stream);
 hipError_t launch_compress_gated(const CompressArgs& a, int total_new, hipStream_t stream);
 hipError_t launch_index_logits(const IndexArgs& a, int max_entries, hipStream_t stream);
@@ -117,6 +129,7 @@ hipError_t launch_topk_select(TopkArgs a, int max_entries, hipStream_t stream);
 bool topk_compress_supported(const TopkArgs& a, int max_entries, int tok_dtype);
 hipError_t launch_topk_compress(TopkArgs a, int max_entries, const CompressArgs& c, int total_new, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_rope(RopeArgs a, hipStream_t stream);
 
 // The device error word of debug builds on the current device (its address,
 // found once per device); nullptr in release builds.

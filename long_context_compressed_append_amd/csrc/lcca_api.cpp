@@ -197,6 +197,36 @@ lcca_status lcca_debug_check(void* stream, uint32_t* bits) {
 #endif
 }
 
+lcca_status lcca_rope(void* stream, int32_t dtype, void* x, int64_t rows, int32_t heads, int32_t dim,
+                      int32_t rope_off, int32_t rope_dim, const int32_t* pos, double theta, const float* inv_freq,
+                      int32_t flags) {
+    g_err[0] = 0;
+    if (dtype != LCCA_F32 && dtype != LCCA_BF16) return fail(LCCA_ERR_UNSUPPORTED, "rope: dtype %d (F32 or BF16)", dtype);
+    if (rows < 0 || heads < 1 || dim < 1)
+        return fail(LCCA_ERR_INVALID_ARG, "rope: rows=%lld heads=%d dim=%d", (long long)rows, heads, dim);
+    if (rope_dim < 2 || rope_dim % 2 || rope_dim > lcca::kRopeMaxDim || rope_off < 0 ||
+        (int64_t)rope_off + rope_dim > dim)
+        return fail(LCCA_ERR_INVALID_ARG, "rope: slice [%d, %d + %d) of dim %d (even width 2..%d inside the vector)",
+                    rope_off, rope_off, rope_dim, dim, lcca::kRopeMaxDim);
+    if (flags & ~(LCCA_ROPE_HALF | LCCA_ROPE_INVERSE)) return fail(LCCA_ERR_INVALID_ARG, "rope: flags 0x%x", flags);
+    if (!inv_freq && !(std::isfinite(theta) && theta > 0.0))
+        return fail(LCCA_ERR_INVALID_ARG, "rope: theta=%g (finite and > 0 without inv_freq)", theta);
+    if (mul_sat(mul_sat((size_t)rows, (size_t)heads), (size_t)dim) >= ((size_t)1 << 62))
+        return fail(LCCA_ERR_INVALID_ARG, "rope: rows x heads x dim too large");
+    if (rows == 0) return LCCA_OK;
+    if (!x || !pos) return fail(LCCA_ERR_INVALID_ARG, "rope: x=%p pos=%p", x, (const void*)pos);
+    lcca::RopeArgs a{};
+    a.x = x; a.rows = rows; a.heads = heads; a.dim = dim; a.off = rope_off; a.rd = rope_dim; a.pos = pos;
+    a.bf16 = dtype == LCCA_BF16;
+    a.half_split = (flags & LCCA_ROPE_HALF) != 0;
+    a.inverse = (flags & LCCA_ROPE_INVERSE) != 0;
+    for (int i = 0; i < rope_dim / 2; ++i) {
+        a.freq[i] = inv_freq ? inv_freq[i] : (float)std::pow(theta, -2.0 * i / rope_dim);
+        if (!std::isfinite(a.freq[i])) return fail(LCCA_ERR_INVALID_ARG, "rope: frequency %d not finite", i);
+    }
+    return hip_status(lcca::launch_rope(a, (hipStream_t)stream), "rope launch");
+}
+
 const char* lcca_status_string(lcca_status s) {
     switch (s) {
     case LCCA_OK: return "ok";

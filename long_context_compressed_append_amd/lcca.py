@@ -14,12 +14,14 @@ import os
 from dataclasses import dataclass
 from typing import Optional
 
+import numpy as np
 import torch
 
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_DEVICE_INDEX = 0, -1, -2, -3, -4, -5
 DBG_BLOCK, DBG_ROW, DBG_CHUNK = 1, 2, 4
 Q_FP8 = 0x100          # q_dtype flag: FP8 queries on the FP8 matrix cores (lcca.h, LCCA_Q_FP8)
+ROPE_HALF, ROPE_INVERSE = 1, 2
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblcca.so")
@@ -28,7 +30,7 @@ DEBUG_LIB_PATH = os.path.join(_PKG, "liblcca_debug.so")
 EXPORTED = ("lcca_compress_append", "lcca_index_logits", "lcca_topk_select", "lcca_sparse_attn_fwd",
             "lcca_sparse_attn_workspace_size", "lcca_topk_workspace_size", "lcca_status_string", "lcca_last_error",
             "lcca_version", "lcca_decode_select", "lcca_decode_select_workspace_size", "lcca_remainder_bytes",
-            "lcca_sparse_attn_fwd_noalloc", "lcca_debug_check", "lcca_compress_append_gated")
+            "lcca_sparse_attn_fwd_noalloc", "lcca_debug_check", "lcca_compress_append_gated", "lcca_rope")
 
 
 class LccaError(RuntimeError):
@@ -103,6 +105,8 @@ def lib():
                   "lcca_decode_select", "lcca_sparse_attn_fwd_noalloc", "lcca_compress_append_gated"):
             getattr(L, n).restype = i32
         L.lcca_debug_check.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
+        L.lcca_rope.argtypes = [P, i32, P, i64, i32, i32, i32, i32, P, ctypes.c_double, P, i32]
+        L.lcca_rope.restype = i32
         L.lcca_debug_check.restype = i32
         L.lcca_status_string.argtypes = [i32]
         for n in ("lcca_status_string", "lcca_last_error", "lcca_version"):
@@ -315,3 +319,20 @@ def sparse_attn_fwd_noalloc(pages: Pages, rows: Rows, q_dtype: int, q, H: int, d
                                               q_dtype, _ptr(q), H, d_v, float(sm_scale), ctypes.byref(kv.c()),
                                               _ptr(topk_idx), k, ctypes.byref(win.c()), out_dtype, _ptr(out),
                                               _ptr(lse)))
+
+
+def rope(x, pos, rope_off: int, rope_dim: int, theta: float = 10000.0, inv_freq=None, half: bool = False,
+         inverse: bool = False, stream=None):
+    """Rotary embedding of dims [rope_off, rope_off + rope_dim) of x
+    ([rows][heads][dim], float32 or bfloat16, on the device) in place; row r
+    rotated by pos[r] (int32 device).  inv_freq: host float32 [rope_dim / 2]
+    or None for theta^(-2i/rope_dim); half: pairs (i, i + rope_dim/2)
+    instead of (2i, 2i+1); inverse: rotate back."""
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(x.dtype, -1)
+    rows, heads, dim = x.shape
+    fr = None
+    if inv_freq is not None:
+        fr = np.ascontiguousarray(np.asarray(inv_freq, dtype=np.float32))
+    flags = (ROPE_HALF if half else 0) | (ROPE_INVERSE if inverse else 0)
+    _check(lib().lcca_rope(_stream(stream), dt, _ptr(x), rows, heads, dim, int(rope_off), int(rope_dim), _ptr(pos),
+                           float(theta), fr.ctypes.data if fr is not None else None, flags))

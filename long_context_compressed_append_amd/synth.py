@@ -36,6 +36,7 @@ T_KV_ENTRIES, T_IK_ENTRIES, T_WIN, T_REM_KV, T_REM_IK, T_REM_KV_LOGIT, T_REM_IK_
 T_NEW_KV, T_NEW_IK, T_NEW_KV_LOGIT, T_NEW_IK_LOGIT = 8, 9, 10, 11
 T_Q, T_Q_IDX, T_W_IDX, T_BLOCK_PERM, T_OUTLIER = 12, 13, 14, 15, 16
 T_REM_KV_GATE, T_REM_IK_GATE, T_NEW_KV_GATE, T_NEW_IK_GATE = 17, 18, 19, 20
+T_ROPE_X, T_ROPE_POS = 21, 22
 
 F32, BF16, FP8, MXFP4 = "f32", "bf16", "fp8", "mxfp4"
 
@@ -253,3 +254,17 @@ def queries(cfg: Config, b: int, nrows: int):
     qi = _values(cfg, T_Q_IDX, b, (nrows, cfg.HI, cfg.dI), cfg.dI, 1)
     w = uniform(cfg, T_W_IDX, b, (nrows, cfg.HI))
     return q, qi, w
+
+
+def rope_inputs(seed: int, rows: int, heads: int, dim: int, max_pos: int):
+    """Vectors to rotate and their positions: x float32 N(0,1) [rows][heads][dim],
+    pos int32 [rows] uniform in [0, max_pos] with position 0 in row 0 and
+    max_pos in the last row."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_ROOT, 0x40BE, T_ROPE_X, seed])))
+    x = g.standard_normal((rows, heads, dim), dtype=np.float32)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_ROOT, 0x40BE, T_ROPE_POS, seed])))
+    pos = g.integers(0, max_pos + 1, rows).astype(np.int32)
+    if rows:
+        pos[0] = 0
+        pos[-1] = max_pos
+    return x, pos

@@ -254,3 +254,25 @@ def test_noalloc_rejects_plans_beyond_its_scratch():
     st = L.lcca_sparse_attn_fwd_noalloc(None, by(pages), by(rows), lcca.BF16, None, 640, 576, 0.04, by(kv), None,
                                         0, by(win), lcca.F32, 1, None)
     assert st == lcca.ERR_INVALID_ARG
+
+
+def test_rope_arguments_checked_before_launch():
+    """lcca_rope rejects what it does not cover on the host (dummy pointers:
+    nothing is launched), and zero rows is a no-op."""
+    L = lcca.lib()
+    R = lambda dt, rows, heads, dim, off, rd, theta=10000.0, fr=None, flags=0: L.lcca_rope(
+        None, dt, 16, rows, heads, dim, off, rd, 16, theta, fr, flags)
+    assert R(lcca.FP8_E4M3, 4, 2, 64, 0, 64) == lcca.ERR_UNSUPPORTED
+    assert R(lcca.MXFP4, 4, 2, 64, 0, 64) == lcca.ERR_UNSUPPORTED
+    for args in ((4, 2, 64, 0, 63), (4, 2, 64, 0, 0), (4, 2, 64, 2, 64), (4, 2, 600, 0, 258), (4, 2, 64, -2, 32),
+                 (-1, 2, 64, 0, 64), (4, 0, 64, 0, 64), (4, 2, 0, 0, 2)):
+        assert R(lcca.F32, *args) == lcca.ERR_INVALID_ARG, args
+    assert R(lcca.F32, 4, 2, 64, 0, 64, flags=4) == lcca.ERR_INVALID_ARG
+    for th in (0.0, -1.0, float("inf"), float("nan")):
+        assert R(lcca.BF16, 4, 2, 64, 0, 64, theta=th) == lcca.ERR_INVALID_ARG, th
+    bad = (ctypes.c_float * 32)(*([1.0] * 31 + [float("inf")]))
+    assert R(lcca.F32, 4, 2, 64, 0, 64, fr=ctypes.cast(bad, ctypes.c_void_p)) == lcca.ERR_INVALID_ARG
+    assert "frequency 31" in lcca.lib().lcca_last_error().decode()
+    assert L.lcca_rope(None, lcca.F32, None, 4, 2, 64, 0, 64, None, 1e4, None, 0) == lcca.ERR_INVALID_ARG
+    assert L.lcca_rope(None, lcca.F32, None, 0, 2, 64, 0, 64, None, 1e4, None, 0) == lcca.OK
+    assert L.lcca_rope(None, lcca.BF16, None, 0, 1, 576, 512, 64, None, 0.0, None, 3) == lcca.ERR_INVALID_ARG
