@@ -252,6 +252,7 @@ class Workload:
 
         self.host = None
         self.q_ldt = lcca.BF16          # indexer query dtype (| lcca.Q_FP8: FP8 queries)
+        self.a_qdt = lcca.BF16          # attention query dtype (| lcca.Q_FP8 on MXFP4 pools)
         self._init = dict(kv_data=kv_data, kv_scale=kv_scale, ik_data=ik_data, win_data=win_data,
                           win_scale=win_scale, rem_kv=rem_kv, rem_ik=rem_ik, rem_kv_logit=rem_kv_logit,
                           rem_ik_logit=rem_ik_logit)
@@ -313,7 +314,7 @@ class Workload:
                             c.HI, self.w_idx, 1.0, self.logits, self.ld, c.k, self.topk, self.ds_ws)
             if ev is not None:
                 ev[1].record()
-            L.sparse_attn_fwd(self.pages, self.rows, L.BF16, self.q, c.H, c.dv, c.scale, kv, self.topk, c.k, win,
+            L.sparse_attn_fwd(self.pages, self.rows, self.a_qdt, self.q, c.H, c.dv, c.scale, kv, self.topk, c.k, win,
                               self.out_ldt, self.out, self.lse, self.ws)
             if ev is not None:
                 ev[4].record()
@@ -334,7 +335,7 @@ class Workload:
             ev[2].record()
         if ev is not None:
             ev[3].record()
-        L.sparse_attn_fwd(self.pages, self.rows, L.BF16, self.q, c.H, c.dv, c.scale, kv, idx,
+        L.sparse_attn_fwd(self.pages, self.rows, self.a_qdt, self.q, c.H, c.dv, c.scale, kv, idx,
                           c.k if idx is not None else 0, win, self.out_ldt, self.out, self.lse, self.ws)
         if ev is not None:
             ev[4].record()
@@ -647,18 +648,23 @@ def run_workload(torch, lcca, synth, name, args, with_oracle, cpu_seconds=0.0, b
         res["bf16_out"] = v
         log(name, "bf16 outputs", json.dumps(v))
     if not args.no_fp8q and wl.cfg.HI and wl.cfg.ik_dtype == synth.FP8 and wl.nrows < 64:
-        # the same step with FP8 queries on the FP8 indexer keys (opt-in)
+        # the same step with FP8 queries (opt-in): the indexer on the FP8
+        # keys, and the attention on an MXFP4 pool by the FP4 x FP8 MFMA
         wl.q_ldt = lcca.BF16 | lcca.Q_FP8
+        mx = wl.cfg.kv_dtype == synth.MXFP4
+        if mx:
+            wl.a_qdt = lcca.BF16 | lcca.Q_FP8
         for i in range(args.warmup):
             wl.step(i)
         t = plain_steps(torch, wl, steps)
         _, st8, _ = time_steps(torch, wl, steps, 0)
-        wl.q_ldt = lcca.BF16
+        wl.q_ldt = wl.a_qdt = lcca.BF16
         sel = "decode_select" if wl.fused else "index_logits"
-        b = work[sel][0]
-        res["fp8_query"] = {"rows_per_s": round(wl.nrows / (t / 1e3), 1), "ms_per_step": round(t, 5),
-                            sel: {"ms": round(st8[sel], 5), "GB/s": round(b / st8[sel] / 1e6, 1),
-                                  "hbm_frac": round(b / st8[sel] / 1e6 / HBM_PEAK_GBS, 4)}}
+        res["fp8_query"] = {"rows_per_s": round(wl.nrows / (t / 1e3), 1), "ms_per_step": round(t, 5)}
+        for n in [sel] + (["sparse_attn_fwd"] if mx else []):
+            b = work[n][0]
+            res["fp8_query"][n] = {"ms": round(st8[n], 5), "GB/s": round(b / st8[n] / 1e6, 1),
+                                   "hbm_frac": round(b / st8[n] / 1e6 / HBM_PEAK_GBS, 4)}
         log(name, "fp8 queries", json.dumps(res["fp8_query"]))
     if not args.no_gated:
         t = gated_leg(torch, lcca, wl, steps, args.warmup)
@@ -761,6 +767,7 @@ def main():
         "parity": r.get("parity"),
         "bf16_out": r.get("bf16_out"),
         "gated_compress": r.get("gated_compress"),
+        "fp8_query": r.get("fp8_query"),
         "rope": r.get("rope"),
         "also": {n: {"rows_per_s": round(v["rows_per_s"], 1), "ms_per_step": round(v["ms_per_step"], 5),
                      "rows": v["rows"], "step_hbm_GB/s": round(v["step_GB/s"], 1),

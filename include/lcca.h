@@ -102,15 +102,21 @@ typedef int32_t lcca_status;
 typedef enum { LCCA_F32 = 0, LCCA_BF16 = 1, LCCA_FP8_E4M3 = 2, LCCA_MXFP4 = 3 } lcca_dtype;
 
 /* Flag OR-ed into the q_dtype of lcca_index_logits and lcca_decode_select
- * (with LCCA_BF16 queries over raw FP8 E4M3 keys, fewer than 64 rows): the
+ * (with LCCA_BF16 queries over raw FP8 E4M3 keys, fewer than 64 rows) and of
+ * lcca_sparse_attn_fwd(_noalloc) (LCCA_BF16 queries, MXFP4 kv pool): the
  * kernel quantises each row's query per head to FP8 E4M3 with a power-of-two
  * scale, X = floor(log2 max_d |q_hd|) - 7 (the head's largest magnitude /
  * 2^X lies in [128, 256), so nothing saturates; X = -127 for a zero head),
  * q8_hd = RNE E4M3 of q_hd / 2^X, and computes q8_h . K_g * 2^X exactly on
  * the FP8 matrix cores (fp32 accumulation).  The logits are then those of
  * the quantised query; against the bf16 query each head's dot product moves
- * by at most sum_d max(2^-4 |q_hd|, 2^(X-10)) |K_gd|.  [P3 "Vykon neprinesl
- * jeden kernel": FP8 indexer keys; the query's quantisation rule is this
+ * by at most sum_d max(2^-4 |q_hd|, 2^(X-10)) |K_gd|.  In the attention the
+ * pool entries are scored by the scaled FP4 x FP8 matrix instructions
+ * straight from the pool's E2M1 codes and E8M0 block scales, window tokens
+ * by bf16 products with the same dequantised query q8 * 2^X, so every key
+ * of the one softmax sees the quantised query; values stay as before.
+ * [P3 "Vykon neprinesl jeden kernel": FP8 indexer keys, and a fused
+ * attention reading a 4-bit KV cache; the query's quantisation rule is this
  * library's.] */
 #define LCCA_Q_FP8 0x100
 
@@ -355,7 +361,9 @@ size_t lcca_decode_select_workspace_size(const lcca_rows* rows, int32_t ratio_m,
  * output's 8) with a power-of-two range scale per split, head and 16 value
  * dims, for F32 outputs in fp32.
  *   q        device [num_rows][H][kv->dim] of q_dtype (F32 with F32 cache;
- *            BF16 otherwise)
+ *            BF16 otherwise; BF16 | LCCA_Q_FP8 with an MXFP4 cache quantises
+ *            it to FP8, see LCCA_Q_FP8; other combinations with the flag
+ *            return LCCA_ERR_UNSUPPORTED)
  *   out      device [num_rows][H][d_v] of out_dtype (F32 or BF16)
  *   lse      device float [num_rows][H] or NULL
  *   ws       device workspace of at least lcca_sparse_attn_workspace_size()

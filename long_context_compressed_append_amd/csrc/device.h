@@ -9,6 +9,7 @@ namespace lcca {
 enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP4 = 3, DT_NONE = -1 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -85,6 +86,15 @@ __device__ __forceinline__ uint32_t f32_to_fp8_inrange(float x) {
     const uint32_t r = ua + 0x7ffffu + ((ua >> 20) & 1u);               // RNE to 3 mantissa bits
     const uint32_t nor = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);  // (e + 7) << 3 | m3
     return sign | (a < 0.015625f ? sub : nor);
+}
+
+// E4M3 code -> value (finite codes), without branches.
+__device__ __forceinline__ float fp8_value(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float sub = (float)m * 0x1p-9f;
+    const float nor = ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
+    const float v = e == 0 ? sub : nor;
+    return (c & 0x80u) ? -v : v;
 }
 
 // ---------------------------------------------------------------------------

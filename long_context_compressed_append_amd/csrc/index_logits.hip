@@ -62,23 +62,12 @@ __device__ inline bf16x8 key_operand(const RawKey<KD, KS>& k, int s) {
     }
 }
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-
 // FP8 keys as B operands of the 32x32x64 FP8 MFMA: a lane's 32-byte k-block
 // s8 is bytes [32 s8, 32 s8 + 32) of the 64 contiguous bytes it loaded.
 template <int KS>
 __device__ inline i32x8 key_operand8(const RawKey<DT_FP8, KS>& k, int s8) {
     return i32x8{(int)k.w[4 * s8][0],     (int)k.w[4 * s8][1],     (int)k.w[4 * s8 + 1][0], (int)k.w[4 * s8 + 1][1],
                  (int)k.w[4 * s8 + 2][0], (int)k.w[4 * s8 + 2][1], (int)k.w[4 * s8 + 3][0], (int)k.w[4 * s8 + 3][1]};
-}
-
-// E4M3 code -> value (finite codes), without branches.
-__device__ __forceinline__ float fp8_value(uint32_t c) {
-    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    const float sub = (float)m * 0x1p-9f;
-    const float nor = ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
-    const float v = e == 0 ? sub : nor;
-    return (c & 0x80u) ? -v : v;
 }
 
 // FP8 queries: each head's query row (bf16 in q_lds, rows of QROWB bytes)

@@ -106,6 +106,10 @@ struct AttnArgs {
     // per (split, 16 value dims, head); part_o is then unused
     uint16_t* part_h;  // [rows][nsplit][H][d_v]
     float* part_sc;    // [rows][nsplit][d_v / 16][H]
+    // FP8 queries (q8 != 0, MXFP4 pools): each head's query quantised to
+    // E4M3 with a power-of-two scale; pool tiles scored by the scaled
+    // FP4 x FP8 MFMA on the pool's own codes and scales
+    int32_t q8;
 };
 
 // Rotary embedding of dims [off, off + rd) of x [rows][heads][dim] in place

@@ -14,29 +14,34 @@
 // entry), padded with masked slots to a multiple of 32, then the window
 // tokens.  So every 32-key tile holds either pool entries or window tokens.
 //
-// bf16/MFMA path.  A workgroup = (row, range of tiles, group of 64 heads)
-// with four waves, one per SIMD: two groups of 32 heads, each over two halves
-// of the shared-KV dimension.  Pipeline per workgroup:
+// bf16/MFMA path.  A workgroup = (row, range of key tiles, group of 64
+// heads), eight waves, two per SIMD:
 //   prologue: the storage row of every selected slot of the split is resolved
 //     through the top-k list and the block table once, into LDS;
-//   loads:    each tile's raw bytes (bf16, FP8 or MXFP4 + E8M0 scales) are
-//     loaded into registers two tiles ahead of their LDS stage (two static
-//     register sets, loop unrolled by two), converted exactly to bf16 and
-//     written to one of three padded LDS stages; one barrier per tile;
-//   compute:  partial S^T = K Q^T over a half of D with MFMA 32x32x16 (A =
-//     keys from LDS, B = the wave's queries, resident in VGPRs); the two
-//     halves of a head group exchange partials through LDS and both form the
-//     same full scores; online softmax in the exp2 domain in registers; O^T +=
-//     V^T P^T over a half of the value dims with V^T read from the same LDS
-//     tile by ds_read_b64_tr_b16 (K = V) and P taken straight from the score
-//     registers as a bf16 hi + lo pair (16 significant bits); FP8 window
-//     scales multiply the scores and are folded into P.
+//   loads:    the four score waves load each tile's raw bytes (bf16, FP8 or
+//     MXFP4 + E8M0 scales) into registers two tiles ahead, convert them
+//     exactly to bf16 and write them to one of three padded LDS stages; one
+//     barrier per tile;
+//   scores:   each score wave holds 16 heads' queries over all of D and forms
+//     S^T = K Q^T for the tile with MFMA 16x16x32 (A = keys from LDS), the
+//     online softmax in the exp2 domain in registers, and P as a bf16 hi + lo
+//     pair (16 significant bits) into LDS; FP8 window scales multiply the
+//     scores and are folded into P;
+//   values:   each value wave holds the O^T accumulators of all 64 heads over
+//     a quarter of the value dims and runs O^T += V^T P^T with V^T read from
+//     the same LDS tile by ds_read_b64_tr_b16 (K = V), one tile behind the
+//     score waves.
+// FP8 queries on MXFP4 pools: each head's query is quantised to E4M3 with a
+// power-of-two scale; the loaders also keep each pool tile's E2M1 codes and
+// E8M0 scales as stored (two raw stages), and the score waves form S^T from
+// them with the scaled 16x16x128 FP4 x FP8 MFMA; window tiles use bf16 MFMAs
+// on the dequantised query.  The value side is unchanged.
 // Keys are split across workgroups when the rows alone cannot fill the GPU;
 // the partial (max, sum, O) states go to the workspace and a merge kernel
 // (one workgroup per row and head) combines them.  For fp32 outputs O stays
 // fp32; for bf16 outputs O / sum is stored as fp16 (11 significant bits,
 // eight times finer than the output's rounding) with a power-of-two range
-// scale per split, head and 32 value dims.
+// scale per split, head and 16 value dims.
 #include <type_traits>
 
 #include "device.h"
@@ -71,6 +76,18 @@ struct Geo {
                                                      // cycles per LDS-active cycle against 1.0 with 16 B)
     static constexpr int STAGE = kKeys * ROWB;
     static constexpr int U16 = D / 8;                // 16-B bf16 units per key
+};
+
+// FP8 queries on MXFP4 pool tiles: the tile's E2M1 codes and E8M0 scales as
+// the pool stores them, in a stage of their own (two stages: written one
+// step ahead, read only by the score waves in the next step).
+template <int D>
+struct Raw {
+    static constexpr int ROWB = D / 2 + 16;          // codes of a key, padded: 16 lanes' 16-B reads at
+                                                     // rows 304 B apart start 12 banks apart (no conflict)
+    static constexpr int SCB = D / 32;               // scale bytes of a key
+    static constexpr int SC0 = kKeys * ROWB;         // offset of the scale bytes
+    static constexpr int STAGE = SC0 + ((kKeys * SCB + 15) & ~15);
 };
 
 // Row-level key geometry.
@@ -196,6 +213,23 @@ struct Tiler {
         else store_parts<KVD, UPK_P, NU_P>(R, dst, sub);
     }
 
+    // FP8-query path: the E2M1 codes and E8M0 scales of a pool tile, as
+    // stored (a masked key: zero codes, scale 1).
+    __device__ __forceinline__ static void store_raw(const TileRegs<NU>& R, lds_u8* raw) {
+        static_assert(KVD == DT_MXFP4, "raw stages hold MXFP4 tiles");
+        const int tid = threadIdx.x;
+        const int key = tid / kThreadsPerKey, sub = tid % kThreadsPerKey;
+        const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < NU_P; ++i) {
+            const int part = sub + kThreadsPerKey * i;
+            if ((i + 1) * kThreadsPerKey <= UPK_P || part < UPK_P) {
+                *reinterpret_cast<lds_u32x4*>(raw + key * Raw<D>::ROWB + part * 16) = R.valid ? R.v[i] : zero;
+                raw[Raw<D>::SC0 + key * Raw<D>::SCB + part] = (uint8_t)(R.valid ? R.sc[i] : 127u);
+            }
+        }
+    }
+
     template <int SRC, int UPK, int NUS>
     __device__ __forceinline__ static void store_parts(const TileRegs<NU>& R, lds_u8* dst, int sub) {
         const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
@@ -246,19 +280,152 @@ struct Tiler {
 // and tile stores overlap the value wave's MFMAs.  One barrier per tile: in
 // step k the score waves work on tile k while the value waves finish tile
 // k - 1.
-template <int D>
+template <int D, bool Q8>
 struct ScoreWave {
     static constexpr int KS = D / 32;                        // 32-dim k-steps over D
-    bf16x8 qb[KS];
+    static constexpr int KS8 = (D + 127) / 128;              // 128-dim k-steps of the FP4 x FP8 MFMA
+    bf16x8 qb[Q8 ? 1 : KS];                                  // bf16 queries (B operands)
+    i32x8 q8[Q8 ? KS8 : 1];                                  // FP8 query codes (B operands)
+    int qx;                                                  // their power-of-two scale X
     float m_run, l_run;                                      // head (lane & 15): reference max, this lane's keys' sum
 
     __device__ __forceinline__ void init(const AttnArgs& a, int r, int head0, int lane) {
-        const int c16 = lane & 15, g = lane >> 4;
-        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + head0 + c16) * D + 8 * g;
+        if constexpr (!Q8) {
+            const int c16 = lane & 15, g = lane >> 4;
+            const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + head0 + c16) * D + 8 * g;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) qb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * s));
+            for (int s = 0; s < KS; ++s)
+                qb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * s));
+        } else {
+            // The head's query quantised to E4M3 with one power-of-two scale:
+            // X = floor(log2 max |q|) - 7 (the maximum / 2^X lands in
+            // [128, 256), no saturation; X = -127 for a zero query), codes =
+            // RNE(q / 2^X).  B operand of k-step s (scaled 16x16x128 MFMA,
+            // FP8): byte e of lane group g is dim 128 s + 16 g + e for e < 16
+            // and 128 s + 64 + 16 g + (e - 16) for e >= 16 (dims past D: 0);
+            // the four lanes of a head hold all of its dims.
+            const int c16 = lane & 15, g = lane >> 4;
+            const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + head0 + c16) * D;
+            u32x4 v[KS8][2][2];
+#pragma unroll
+            for (int s = 0; s < KS8; ++s)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        v[s][h][t] = 128 * s + 64 * h < D
+                                         ? *reinterpret_cast<const u32x4*>(qrow + 128 * s + 64 * h + 16 * g + 8 * t)
+                                         : u32x4{0u, 0u, 0u, 0u};
+            float amax = 0.0f;
+#pragma unroll
+            for (int s = 0; s < KS8; ++s)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(v[s][h][t][j] & 0xffffu)),
+                                                     fabsf(bf16_to_f32(v[s][h][t][j] >> 16))));
+            amax = fmaxf(amax, __shfl_xor(amax, 16));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            int X = -127;
+            if (amax > 0.0f) {
+                int ex = 0;
+                (void)frexpf(amax, &ex);
+                X = min(max(ex - 8, -127), 127);
+            }
+            qx = X;
+            // q / 2^X is exact (a power of two; |q / 2^X| < 256); the
+            // hardware conversion rounds to nearest even, the same codes as
+            // the library's software encoder for every bf16 value below 448
+            const float inv = ldexpf(1.0f, -X);
+#pragma unroll
+            for (int s = 0; s < KS8; ++s) {
+                uint32_t w[8];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const uint32_t u0 = v[s][h][t][2 * j], u1 = v[s][h][t][2 * j + 1];
+                            int c = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_to_f32(u0 & 0xffffu) * inv,
+                                                                    bf16_to_f32(u0 >> 16) * inv, 0, false);
+                            c = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_to_f32(u1 & 0xffffu) * inv,
+                                                                bf16_to_f32(u1 >> 16) * inv, c, true);
+                            w[4 * h + 2 * t + j] = (uint32_t)c;
+                        }
+                q8[s] = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+            }
+        }
         m_run = -INFINITY;
         l_run = 0.0f;
+    }
+
+    // S^T of a pool tile from its raw stage (FP8 queries): the scaled
+    // 16x16x128 MFMA with A = the keys' E2M1 codes, lane (key k16, g) holding
+    // MX block 4s + g (32 dims, its own E8M0 scale) and B = the FP8 query
+    // codes with the head's scale.  Same C layout as scores().
+    __device__ __forceinline__ void scores8(const lds_u8* raw, int lane, f32x4 (&sacc)[2]) const {
+        using RG = Raw<D>;
+        const int k16 = lane & 15, g = lane >> 4;
+        sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const lds_u8* kr = raw + (16 * b + k16) * RG::ROWB + 16 * g;
+            const lds_u8* ks = raw + RG::SC0 + (16 * b + k16) * RG::SCB + g;
+#pragma unroll
+            for (int s = 0; s < KS8; ++s) {
+                constexpr int kBlocks = D / 32;
+                const bool in = 4 * s + g < kBlocks;
+                u32x4 v = u32x4{0u, 0u, 0u, 0u};
+                int sa = 127;
+                if (in) {
+                    v = *reinterpret_cast<const lds_u32x4*>(kr + 64 * s);
+                    sa = ks[4 * s];
+                }
+                const i32x8 av = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+                sacc[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, q8[s], sacc[b], 4, 0, 0, sa, 0,
+                                                                          qx + 127);
+            }
+        }
+    }
+
+    // S^T of a window tile (bf16 LDS stage) with FP8 queries: bf16 MFMAs on
+    // the dequantised query code * 2^X (exact in bf16), formed from the codes
+    // per k-step, dims assigned to lanes as in the codes: k-step (s, t), lane
+    // group g takes dims 128 s + 64 (t >> 1) + 16 g + 8 (t & 1) .. +7 for
+    // both operands.
+    __device__ __forceinline__ void scores_q8win(const lds_u8* st, int lane, f32x4 (&sacc)[2]) const {
+        constexpr int ROWB = Geo<D>::ROWB;
+        const int g = lane >> 4;
+        const lds_u8* kb = st + (lane & 15) * ROWB + 32 * g;
+        const float sc = ldexpf(1.0f, qx);
+        sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS8; ++s) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if (128 * s + 64 * (t >> 1) >= D) continue;
+                uint32_t w0 = (uint32_t)q8[s][4 * (t >> 1) + 2 * (t & 1)];
+                uint32_t w1 = (uint32_t)q8[s][4 * (t >> 1) + 2 * (t & 1) + 1];
+                // formed per tile: hoisted out of the tile loop, the 72
+                // registers of the bf16 query would stay live beside the codes
+                asm volatile("" : "+v"(w0), "+v"(w1));
+                const bf16x8 qv = __builtin_bit_cast(
+                    bf16x8, u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false)),
+                                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true)),
+                                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false)),
+                                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true))});
+                const int off = 2 * (128 * s + 64 * (t >> 1) + 8 * (t & 1));
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const bf16x8 k = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(kb + 16 * b * ROWB + off));
+                    sacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qv, sacc[b], 0, 0, 0);
+                }
+            }
+        }
     }
 
     // S^T of the tile: lane (head = lane & 15, g = lane >> 4) gets keys
@@ -379,10 +546,10 @@ constexpr int kLoadThreads = 256;      // the score waves load the key tiles
 constexpr int kStages = 3;             // LDS stages of the key tiles
 constexpr int kRowsLds = 2560;         // storage rows of a split's selected slots cached in LDS (= max keys per split)
 
-template <int KVD, int WD, int D, int DV>
+template <int KVD, int WD, int D, int DV, bool Q8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(AttnArgs a) {
     using G = Geo<D>;
-    using SW = ScoreWave<D>;
+    using SW = ScoreWave<D, Q8>;
     using VW = ValueWave<D, DV>;
     using TL = Tiler<KVD, WD, D, kLoadThreads>;
     constexpr int NU = TL::NU;
@@ -393,6 +560,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __shared__ __attribute__((aligned(16))) float al_mem[2][64];                 // [step parity][head]
     __shared__ float fin_mem[2][64];                                              // [m, l][head]
     __shared__ int32_t rows_mem[kRowsLds];
+    __shared__ __attribute__((aligned(128))) uint8_t raw_mem[Q8 ? 2 * Raw<D>::STAGE : 16];
     lds_i32* const rows_lds = (lds_i32*)&rows_mem[0];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -460,6 +628,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     lds_f32* const km = (lds_f32*)&kmeta[0][0];
     lds_u8* const pm = (lds_u8*)&p_mem[0][0][0][0];
     lds_f32* const alm = (lds_f32*)&al_mem[0][0];
+    lds_u8* const rw = (lds_u8*)&raw_mem[0];
     constexpr int PPAR = 2 * 4 * 64 * 16;                    // bytes between the two P parities
     const int c16 = lane & 15, g = lane >> 4;
 
@@ -473,6 +642,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         TL::issue(a, TL::resolve(a, rk, tb, true, rows_lds, idx0), R[0]);
         TL::issue(a, TL::resolve(a, rk, tb + 1, 1 < ntl, rows_lds, idx0), R[1]);
         TL::store(rk, tb, R[0], st, km);
+        if constexpr (Q8)
+            if (tb < rk.sel_tiles) TL::store_raw(R[0], rw);
         TL::issue(a, TL::resolve(a, rk, tb + 2, 2 < ntl, rows_lds, idx0), R[0]);
         __syncthreads();
         // step k: scores, softmax and P of tile k (stage k % 3); register set
@@ -483,7 +654,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             constexpr int rs = (decltype(J)::value + 1) & 1;
             const int sc = k % kStages, sn = (k + 1) % kStages;
             f32x4 sv[2];
-            W.scores(st + sc * G::STAGE, lane, sv);
+            if constexpr (Q8) {
+                if (tb + k < rk.sel_tiles) W.scores8(rw + (k & 1) * Raw<D>::STAGE, lane, sv);
+                else W.scores_q8win(st + sc * G::STAGE, lane, sv);
+            } else {
+                W.scores(st + sc * G::STAGE, lane, sv);
+            }
             const typename TL::Src nsrc = TL::resolve(a, rk, tb + k + 3, k + 3 < ntl, rows_lds, idx0);
             u32x4 h, l;
             const float al = W.softmax(sv, km + sc * kKeys, lane, a.scale_log2, h, l);
@@ -491,7 +667,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             *reinterpret_cast<lds_u32x4*>(pw) = h;
             *reinterpret_cast<lds_u32x4*>(pw + 4096) = l;
             if (g == 0) alm[(k & 1) * 64 + 16 * hb + c16] = al;
-            if (k + 1 < ntl) TL::store(rk, tb + k + 1, R[rs], st + sn * G::STAGE, km + sn * kKeys);
+            if (k + 1 < ntl) {
+                TL::store(rk, tb + k + 1, R[rs], st + sn * G::STAGE, km + sn * kKeys);
+                if constexpr (Q8)
+                    if (tb + k + 1 < rk.sel_tiles) TL::store_raw(R[rs], rw + ((k + 1) & 1) * Raw<D>::STAGE);
+            }
             TL::issue(a, nsrc, R[rs]);
             __syncthreads();
         };
@@ -795,7 +975,13 @@ template <int KVD, int WD, int D, int DV>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
     const int64_t upx = ((int64_t)a.num_rows * a.nsplit + kXcds - 1) / kXcds;
     const dim3 grid((unsigned)(kXcds * upx * (a.H / 64)));
-    hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV>), grid, dim3(kThreads), 0, stream, a);
+    if constexpr (KVD == DT_MXFP4) {
+        if (a.q8) hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, true>), grid, dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, false>), grid, dim3(kThreads), 0, stream, a);
+    } else {
+        if (a.q8) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, false>), grid, dim3(kThreads), 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     const dim3 mgrid(a.H, a.num_rows);
