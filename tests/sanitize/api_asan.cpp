@@ -168,6 +168,26 @@ static void attn_cases() {
            LCCA_ERR_UNSUPPORTED);
     lcca_rows none{0, 0, PI, PI};
     EXPECT(call(&none, LCCA_BF16, 64, 576, 0.04f, &kv, &win, LCCA_F32, nullptr, 0), LCCA_OK);
+    // FP8 queries: an MXFP4 pool and bf16 queries only
+    EXPECT(call(&rw, LCCA_BF16 | LCCA_Q_FP8, 64, 576, 0.04f, &kv, &win, LCCA_F32, P, need), LCCA_ERR_UNSUPPORTED);
+    lcca_paged_cache mx = pool(LCCA_MXFP4, 576, 4, 4096);
+    EXPECT(call(&rw, LCCA_F32 | LCCA_Q_FP8, 64, 576, 0.04f, &mx, &win, LCCA_F32, P, need), LCCA_ERR_UNSUPPORTED);
+}
+
+static void rope_cases() {
+    auto call = [](int dt, int64_t rows, int heads, int dim, int off, int rd, double theta, const float* fr,
+                   int flags) { return lcca_rope(nullptr, dt, P, rows, heads, dim, off, rd, PI, theta, fr, flags); };
+    EXPECT(call(LCCA_FP8_E4M3, 4, 2, 64, 0, 64, 1e4, nullptr, 0), LCCA_ERR_UNSUPPORTED);
+    EXPECT(call(LCCA_F32, 4, 2, 64, 0, 63, 1e4, nullptr, 0), LCCA_ERR_INVALID_ARG);
+    EXPECT(call(LCCA_F32, 4, 2, 64, INT_MAX, 64, 1e4, nullptr, 0), LCCA_ERR_INVALID_ARG);
+    EXPECT(call(LCCA_F32, 4, 2, 600, 0, 258, 1e4, nullptr, 0), LCCA_ERR_INVALID_ARG);
+    EXPECT(call(LCCA_F32, INT64_MAX, INT_MAX, INT_MAX, 0, 64, 1e4, nullptr, 0), LCCA_ERR_INVALID_ARG);
+    EXPECT(call(LCCA_F32, -1, 2, 64, 0, 64, 1e4, nullptr, 0), LCCA_ERR_INVALID_ARG);
+    EXPECT(call(LCCA_BF16, 4, 2, 64, 0, 64, 0.0, nullptr, 0), LCCA_ERR_INVALID_ARG);
+    EXPECT(call(LCCA_BF16, 4, 2, 64, 0, 64, 1e4, nullptr, 8), LCCA_ERR_INVALID_ARG);
+    const float inf_table[2] = {1.0f, __builtin_inff()};
+    EXPECT(call(LCCA_F32, 4, 2, 64, 0, 4, 1e4, inf_table, 0), LCCA_ERR_INVALID_ARG);
+    EXPECT(call(LCCA_F32, 0, 2, 64, 0, 64, 1e4, nullptr, LCCA_ROPE_HALF | LCCA_ROPE_INVERSE), LCCA_OK);
 }
 
 // Size functions over their argument range: each returns a size (0 for an
@@ -206,6 +226,7 @@ int main() {
     index_topk_cases();
     decode_select_cases();
     attn_cases();
+    rope_cases();
     size_sweeps();
     for (int s = -6; s <= 1; ++s) (void)std::strlen(lcca_status_string(s));
     uint32_t bits = 5;

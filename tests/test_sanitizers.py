@@ -21,7 +21,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SAN = os.path.join(ROOT, "tests", "sanitize")
 CLANG = "/opt/rocm/llvm/bin/clang++"
-HIP_OBJS = ("attn_scratch", "compress_append", "index_logits", "sparse_attn", "topk_select")
+HIP_OBJS = tuple(sorted(f[:-4] for f in os.listdir(os.path.join(ROOT, "long_context_compressed_append_amd", "csrc"))
+                        if f.endswith(".hip")))
 
 ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:halt_on_error=1",
            UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1", OMP_NUM_THREADS="2", HIP_VISIBLE_DEVICES="",
