@@ -125,3 +125,43 @@ def test_rope_zero_rows_launches_nothing():
     p = torch.zeros((0,), dtype=torch.int32, device=DEV)
     lcca.rope(x, p, 0, 64)
     torch.cuda.synchronize()
+
+
+def test_rope_around_the_attention_matches_the_oracle_composition():
+    """The steps either side of the path composed with it: the new shared-KV
+    tokens rotated at their positions before compress_append, the queries at
+    the row positions before the attention, the output's RoPE dims rotated
+    back afterwards (64 RoPE dims at the end of the 576-dim vector, the
+    interleaved convention, base 10000), against the oracle doing the same
+    in fp64 (bf16 tokens and queries re-encoded after rotation).  Attention on
+    the oracle's top-k indices, at the bf16 path's bounds."""
+    import compare as C
+    from state import State
+    from gpu_state import GpuState
+    cfg = synth.shrink(synth.CONFIGS["csa_64k"], "rope_path", (4095, 2999, 6001), (1, 1, 1), k=256)
+    st = State(cfg)
+    nr = len(st.row_seq)
+    tok_pos = np.concatenate([np.arange(p, p + n) for p, n in zip(cfg.prior_len, cfg.n_new)]).astype(np.int32)
+    off, rd = cfg.D - 64, 64
+    gs = GpuState(st)                                        # device copies of the unrotated inputs
+    # oracle: rotate, re-encode, then the path
+    kv_tok = O.bf16_decode(st.new_kv).reshape(-1, 1, cfg.D)
+    st.new_kv = O.bf16_encode(O.rope(kv_tok, tok_pos, off, rd).astype(np.float32)).reshape(st.new_kv.shape)
+    q = O.bf16_decode(st.q).reshape(nr, cfg.H, cfg.D)
+    st.q = O.bf16_encode(O.rope(q, st.row_pos, off, rd).astype(np.float32)).reshape(st.q.shape)
+    st.oracle_compress_append()
+    lg = st.oracle_index(np.arange(nr))
+    idx = O.topk(st.row_pos, cfg.m, lg, cfg.k)
+    o_want, _ = st.oracle_attn(idx)
+    o_want = O.rope(o_want, st.row_pos, cfg.dv - 64, rd, inverse=True)
+    # device: the same steps through the library
+    kv_dev = gs.new_kv.view(torch.bfloat16).view(-1, 1, cfg.D)
+    lcca.rope(kv_dev, torch.from_numpy(tok_pos).to(DEV), off, rd)
+    q_dev = gs.q.view(torch.bfloat16).view(nr, cfg.H, cfg.D)
+    pos_dev = torch.from_numpy(st.row_pos).to(DEV)
+    lcca.rope(q_dev, pos_dev, off, rd)
+    gs.compress_append()
+    out, _ = gs.attn(torch.from_numpy(idx).to(DEV))
+    lcca.rope(out, pos_dev, cfg.dv - 64, rd, inverse=True)
+    torch.cuda.synchronize()
+    C.check_attention(out.cpu().numpy(), o_want, "bf16")
