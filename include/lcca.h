@@ -312,19 +312,23 @@ lcca_status lcca_topk_select(void* stream, const lcca_rows* rows, int32_t ratio_
  * these logits.  A row whose sequence does not
  * satisfy the device-side part of the contract (cu_new, start_pos) gets a
  * NaN logit for the entry its token completes.
- * Rows of more than 32,768 visible entries take three launches: the top-k
- * of each slice (as in lcca_topk_select, with the same workspace), then the
- * selection among the candidates beside compress_append.
- * With rows of up to 32,768 visible entries the indexer launch also counts,
- * per row, the logits whose order keys share each leading 12-bit digit, and
- * the selection starts from those counts instead of counting itself.
+ * The indexer launch also counts, per row, the logits whose order keys
+ * share each leading 12-bit digit.  With rows of up to 32,768 visible
+ * entries the selection starts from those counts instead of counting
+ * itself.  Longer rows take three launches: a selection in each slice of
+ * 16,384 entries, then the selection among the slices' candidates beside
+ * compress_append; from the row's counts every slice knows the row's
+ * boundary digit and how many entries the row takes from it, so it keeps
+ * only its keys above that digit and the largest of its keys in it (at most
+ * k, padded), a set that holds every entry of the row's top-k.
  * Arguments: those of the three calls, and
  *   ws   device workspace of at least lcca_decode_select_workspace_size()
- *        bytes for the same rows, ratio_m and k, 16-byte aligned.  Rows of
- *        up to 32,768 entries: the counts, uint32 [num_rows][4096], which
- *        must be all zero before the first call on this workspace; every
- *        call leaves them zero (the selection clears what it reads).  Longer
- *        rows: the slices' candidates, as for lcca_topk_select.
+ *        bytes for the same rows, ratio_m and k, 16-byte aligned: for rows
+ *        over 32,768 entries first the slices' candidates (the size of
+ *        lcca_topk_workspace_size), then the counts, uint32
+ *        [num_rows][4096], which must be all zero before the first call on
+ *        this workspace; every call leaves them zero (the selection clears
+ *        them once read).
  * Supported: BF16 queries and tokens, an indexer pool, fewer than 64 rows,
  * ratio_m <= 4, ld % 4 == 0 and 16-byte aligned logits, and rows of at most
  * 32,768 visible entries or with at most 32,768 slice candidates (16,384-entry

@@ -434,8 +434,11 @@ size_t lcca_decode_select_workspace_size(const lcca_rows* rows, int32_t ratio_m,
     if (!rows || rows->num_rows <= 0 || !valid_m(ratio_m) || k < 1 || rows->max_pos < 0) return 0;
     const int64_t nvis = max_visible(rows->max_pos, ratio_m);
     if (nvis > lcca::kTopkMaxEntries) return 0;                 // the selection itself is unsupported
-    if (lcca::topk_slices((int)nvis) > 1) return lcca_topk_workspace_size(rows, ratio_m, k);
-    return (size_t)rows->num_rows * ((size_t)1 << lcca::kTopkLeadBits) * sizeof(uint32_t);
+    // the rows' leading-digit counts, after the slices' candidates when rows
+    // are selected in two launches
+    const size_t counts = (size_t)rows->num_rows * ((size_t)1 << lcca::kTopkLeadBits) * sizeof(uint32_t);
+    if (lcca::topk_slices((int)nvis) > 1) return add_sat(lcca_topk_workspace_size(rows, ratio_m, k), counts);
+    return counts;
 }
 
 lcca_status lcca_decode_select(void* stream, const lcca_pages* pages, const lcca_rows* rows, const int32_t* cu_new,
@@ -468,16 +471,19 @@ lcca_status lcca_decode_select(void* stream, const lcca_pages* pages, const lcca
         return fail(LCCA_ERR_UNSUPPORTED, "decode_select: needs bf16 queries and tokens, fewer than 64 rows, ratio_m "
                     "<= 4, 16-byte aligned logit rows, and rows of at most 32,768 entries or slices whose k "
                     "candidates total at most 32,768");
-    if (lcca::topk_slices(sel_entries) == 1) {
-        // one-launch selections: the indexer counts the logits' leading key
-        // digits into the workspace, the selection reads and clears them
+    {
+        // the indexer counts the logits' leading key digits into the
+        // workspace; one-launch selections read and clear them, two-launch
+        // selections read them in every slice and clear them in the
+        // candidates' selection
         const size_t need = lcca_decode_select_workspace_size(rows, ik->ratio_m, k);
         if (!ws || ws_bytes < need)
             return fail(LCCA_ERR_WORKSPACE, "decode_select needs %zu workspace bytes (%zu given)", need,
                         ws ? ws_bytes : (size_t)0);
         if (reinterpret_cast<uintptr_t>(ws) & 15)
             return fail(LCCA_ERR_INVALID_ARG, "decode_select workspace not 16-byte aligned");
-        ia.lead_hist = ta.lead_hist = reinterpret_cast<uint32_t*>(ws);
+        const size_t cand = lcca::topk_slices(sel_entries) > 1 ? lcca_topk_workspace_size(rows, ik->ratio_m, k) : 0;
+        ia.lead_hist = ta.lead_hist = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + cand);
     }
     ia.fresh = 1;
     ia.cu_new = cu_new; ia.start_pos = start_pos; ia.tok_dtype = tok_dtype;

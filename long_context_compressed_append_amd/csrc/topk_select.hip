@@ -320,15 +320,22 @@ __device__ __forceinline__ void topk_body(const TopkArgs& p, int r, int by) {
         n = p.nslices * k;
         base = reinterpret_cast<const float*>(p.cand_key + c0);
     }
-    // leading-digit counts of this row from the indexer (fused decode launch)
-    // (cleared once read: the clearing store is issued only after the counts
-    // have arrived)
-    u32x4* const hist = MODE == kRow && p.lead_hist ? reinterpret_cast<u32x4*>(p.lead_hist + (int64_t)r * kLeadBins)
-                                                    : nullptr;
+    // leading-digit counts of this row from the indexer (fused decode launch).
+    // kRow: the row's own counts.  kSlice: the whole row's counts, read by
+    // every slice of the row; with them a slice keeps its keys above the
+    // row's boundary digit and, of its keys in that digit, the `need` largest
+    // (at most k entries, the rest of its slots padded), so every entry of the
+    // row's top-k survives.  kCand: the same counts again; the candidates
+    // hold every key of the row above the boundary digit and at least `need`
+    // of its keys in it, so the boundary digit and the count above it are the
+    // row's.  kRow and kCand clear the counts once read (the clearing store
+    // is issued only after the counts have arrived).
+    u32x4* const hist = p.lead_hist ? reinterpret_cast<u32x4*>(p.lead_hist + (int64_t)r * kLeadBins) : nullptr;
+    constexpr bool kClearCounts = MODE != kSlice;
     u32x4 hist_v = u32x4{0u, 0u, 0u, 0u};
     if (hist) hist_v = hist[tid];
     if (MODE == kSlice ? n <= k : n_row <= k) {
-        if (hist) {
+        if (hist && kClearCounts) {
             asm volatile("" ::"v"(hist_v[0]) : "memory");        // the counts have arrived
             hist[tid] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -361,8 +368,10 @@ __device__ __forceinline__ void topk_body(const TopkArgs& p, int r, int by) {
         // 1. the counts the indexer took (4096 bins = 1024 threads x 4)
         static_assert(kLeadBins == 4 * kThreads, "one 16-byte chunk of counts per thread");
         reinterpret_cast<u32x4*>(sm.cnt)[tid] = hist_v;
-        asm volatile("" ::"v"(hist_v[0]) : "memory");            // the counts have arrived
-        hist[tid] = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (kClearCounts) {
+            asm volatile("" ::"v"(hist_v[0]) : "memory");        // the counts have arrived
+            hist[tid] = u32x4{0u, 0u, 0u, 0u};
+        }
         if (tid == 0) sm.cand_n = 0;
         __syncthreads();
     } else {
@@ -489,8 +498,15 @@ __device__ __forceinline__ void topk_body(const TopkArgs& p, int r, int by) {
             if ((key >> kLeadShift) == lead) f(e, key);
         });
     };
-    if (fits) refine(sm, cands, kLeadShift - 1, &T, &mask, &need);
-    else refine(sm, row_bin, kLeadShift - 1, &T, &mask, &need);
+    if (MODE == kSlice && hist && nc <= need) {
+        // a slice with no more keys in the row's boundary digit than the row
+        // needs from it keeps them all
+        need = nc;
+    } else if (fits) {
+        refine(sm, cands, kLeadShift - 1, &T, &mask, &need);
+    } else {
+        refine(sm, row_bin, kLeadShift - 1, &T, &mask, &need);
+    }
 
     // 4. keys of the bin above T or equal to it join the bitmaps
     auto mark = [&](int e, uint32_t key) __attribute__((always_inline)) {
@@ -518,6 +534,18 @@ __device__ __forceinline__ void topk_body(const TopkArgs& p, int r, int by) {
             const bool take = ((g >> b) & 1u) || eq_seen < need;
             eq_seen += (g >> b) & 1u ? 0u : 1u;
             if (take) emit(pos++, e);
+        }
+    }
+    if constexpr (MODE == kSlice) {
+        if (hist) {
+            // the last thread's end position is the number kept; pad the rest
+            __syncthreads();
+            if (tid == kThreads - 1) sm.cand_n = pos;
+            __syncthreads();
+            for (int i = (int)sm.cand_n + tid; i < k; i += kThreads) {
+                p.cand_key[c0 + i] = 0u;
+                p.cand_idx[c0 + i] = -1;
+            }
         }
     }
 }

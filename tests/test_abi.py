@@ -199,6 +199,10 @@ def test_decode_select_rejects_what_it_does_not_cover():
     # their candidates (slices x k) must fit the compact selection
     big = lcca._Pages(16, 1024, 1)
     assert call(rows=lcca._Rows(16, 4 * 40000 - 1, 1, 1), ld=40000, pages=big) == lcca.ERR_WORKSPACE
+    # their workspace: the slices' candidates, then the leading-digit counts
+    rows_40k = lcca._Rows(16, 4 * 40000 - 1, 1, 1)
+    assert (L.lcca_decode_select_workspace_size(by(rows_40k), 4, 2048)
+            == L.lcca_topk_workspace_size(by(rows_40k), 4, 2048) + 16 * 4096 * 4)
     huge = lcca._Pages(16, 4096, 1)
     rows_long = lcca._Rows(16, 4 * 262143 - 1, 1, 1)
     need = L.lcca_topk_workspace_size(by(rows_long), 4, 4096)
