@@ -427,63 +427,81 @@ index_mfma_kernel(IndexArgs p) {
     }
 }
 
-// Many rows (prefill): a workgroup of eight waves covers eight rows, one per
-// wave, and a range of tiles.  Rows of one sequence read the same keys, so
-// each 32-entry key tile is staged in LDS once (rows padded by 16 bytes, a
+// Many rows (prefill): a workgroup of eight waves covers 8 RPW rows, RPW
+// per wave, and a range of tiles.  Rows of one sequence read the same keys,
+// so each 32-entry key tile is staged in LDS once (rows padded by 16 bytes, a
 // ring of three stages, the raw bytes of the next two tiles in flight in
-// registers) and every wave takes its B operands from there; the query
-// stays in VGPRs as A operands.  One barrier per tile: the stage written in
-// step t was last read in step t - 2, before the barrier of step t - 1.
-// Rows of a workgroup that belong to different sequences are handled one
-// sequence after another, the other waves only helping to stage keys.
+// registers) and every wave takes its B operands from there, once per tile
+// for all of its rows; the queries stay in VGPRs as A operands.  One barrier
+// per tile: the stage written in step t was last read in step t - 2, before
+// the barrier of step t - 1.  Rows of a workgroup that belong to different
+// sequences are handled one sequence after another, the other rows' waves
+// only helping to stage keys.
 constexpr int kRowWaves = 8;
 constexpr int kRowThreads = kRowWaves * 64;
 constexpr int kRowStages = 3;
+// Rows per wave: two, so each B operand read from LDS feeds both rows'
+// MFMAs and a tile's barrier covers twice the work (prefill_8k indexer 4.70
+// -> 4.26 ms, 40 % of the bf16 MFMA peak); one where the tile's B operands
+// alone take 64 registers (d_I = 256), as two rows' queries would then spill.
+template <int DI>
+constexpr int rows_per_wave() {
+    return DI / 16 <= 8 ? 2 : 1;
+}
 
-template <int KD, int NHT, int DI>
+template <int KD, int NHT, int DI, int RPW>
 __global__ __launch_bounds__(kRowThreads) void index_rows_kernel(IndexArgs p) {
     constexpr int KS = DI / 16, HALF = DI / 2;
     constexpr int KB = KD == DT_BF16 ? DI * 2 : DI;               // bytes of one key
     constexpr int KBP = KB + 16;                                   // padded LDS row
     constexpr int UPK = KB / 16;                                   // 16-byte units per key
     constexpr int UPT = (32 * UPK + kRowThreads - 1) / kRowThreads;   // units per thread per tile
+    constexpr int NR = kRowWaves * RPW;                            // rows per workgroup
     __shared__ __attribute__((aligned(16))) uint8_t kst[kRowStages][32 * KBP];
-    __shared__ __attribute__((aligned(16))) float w_lds[kRowWaves][NHT * 32];
-    __shared__ int seq_lds[kRowWaves], n_lds[kRowWaves];
+    __shared__ __attribute__((aligned(16))) float w_lds[NR][NHT * 32];
+    __shared__ int seq_lds[NR], n_lds[NR];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, j = lane & 31;
-    const int r = (int)blockIdx.y * kRowWaves + wave;
-    const bool row_ok = r < p.num_rows;
-    const int rr = row_ok ? r : p.num_rows - 1;
-    const int b = checked(p.row_seq[rr], 0, p.batch - 1, p.dbg, kDbgRow);
-    const int n = row_ok ? visible_entries(checked(p.row_pos[rr], 0, p.max_pos, p.dbg, kDbgRow), p.m) : 0;
+    // this wave's rows: slots RPW wave + q
+    bool row_ok[RPW];
+    int rr[RPW], b[RPW], n[RPW];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+        const int r = (int)blockIdx.y * NR + wave * RPW + q;
+        row_ok[q] = r < p.num_rows;
+        rr[q] = row_ok[q] ? r : p.num_rows - 1;
+        b[q] = checked(p.row_seq[rr[q]], 0, p.batch - 1, p.dbg, kDbgRow);
+        n[q] = row_ok[q] ? visible_entries(checked(p.row_pos[rr[q]], 0, p.max_pos, p.dbg, kDbgRow), p.m) : 0;
+    }
     const int tpb = p.tiles_per_wave;
     const int t_begin = (int)blockIdx.x * tpb;
-    if (lane == 0) { seq_lds[wave] = b; n_lds[wave] = n; }
-    for (int h = lane; h < NHT * 32; h += 64) w_lds[wave][h] = p.w[(int64_t)rr * p.HI + h] * p.s_I;
-    // query as A operands: head 32t + j, dims [g*HALF + 8s, +8)
-    bf16x8 qa[NHT][KS];
-    {
-        const uint8_t* qg = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)rr * p.HI * DI * 2;
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+        if (lane == 0) { seq_lds[wave * RPW + q] = b[q]; n_lds[wave * RPW + q] = n[q]; }
+        for (int h = lane; h < NHT * 32; h += 64) w_lds[wave * RPW + q][h] = p.w[(int64_t)rr[q] * p.HI + h] * p.s_I;
+    }
+    // queries as A operands: row q, head 32t + j, dims [g*HALF + 8s, +8)
+    bf16x8 qa[RPW][NHT][KS];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+        const uint8_t* qg = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)rr[q] * p.HI * DI * 2;
 #pragma unroll
         for (int t = 0; t < NHT; ++t)
 #pragma unroll
             for (int s2 = 0; s2 < KS; ++s2)
-                qa[t][s2] = __builtin_bit_cast(
+                qa[q][t][s2] = __builtin_bit_cast(
                     bf16x8, *reinterpret_cast<const u32x4*>(qg + ((int64_t)(32 * t + j) * DI + g * HALF + 8 * s2) * 2));
     }
     __syncthreads();
     const int sh = __builtin_ctz(256 / p.m);
     const uint8_t* keys = reinterpret_cast<const uint8_t*>(p.keys);
-    float* out = p.logits + (int64_t)rr * p.ld;
-    const float* wrow = &w_lds[wave][4 * g];
 
-    for (int i = 0; i < kRowWaves; ++i) {
+    for (int i = 0; i < NR; ++i) {
         const int sb = seq_lds[i];
         bool first = true;
         int nmax = 0;
-        for (int k = 0; k < kRowWaves; ++k) {
+        for (int k = 0; k < NR; ++k) {
             if (seq_lds[k] == sb) {
                 if (k < i) first = false;
                 nmax = max(nmax, n_lds[k]);
@@ -492,7 +510,12 @@ __global__ __launch_bounds__(kRowThreads) void index_rows_kernel(IndexArgs p) {
         if (!first) continue;
         const int t_end = min(t_begin + tpb, (nmax + 31) >> 5);
         if (t_begin >= t_end) continue;
-        const bool mine = row_ok && b == sb;
+        bool mine[RPW], any = false;
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) {
+            mine[q] = row_ok[q] && b[q] == sb;
+            any = any || mine[q];
+        }
         const int32_t* bt = p.block_table + (int64_t)sb * p.max_blocks;
         // this thread's units of a tile: key u / UPK, part u % UPK, u = tid + kRowThreads * i
         auto load = [&](int tile, u32x4 (&v)[UPT]) __attribute__((always_inline)) {
@@ -522,35 +545,44 @@ __global__ __launch_bounds__(kRowThreads) void index_rows_kernel(IndexArgs p) {
             // registers `nxt` hold tile + 1: into the next stage, then refill with tile + 3
             if (tile + 1 < t_end) store(stage == kRowStages - 1 ? 0 : stage + 1, nxt);
             load(tile + 3, nxt);
-            if (mine) {
-                f32x16 acc[NHT];
-#pragma unroll
-                for (int t = 0; t < NHT; ++t) acc[t] = f32x16{};
+            if (any) {
+                // the tile's B operands, read once for the wave's rows
                 const uint8_t* kb = &kst[stage][j * KBP];
+                bf16x8 kop[KS];
 #pragma unroll
                 for (int s2 = 0; s2 < KS; ++s2) {
-                    bf16x8 kop;
                     if constexpr (KD == DT_BF16) {
-                        kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kb + (g * HALF + 8 * s2) * 2));
+                        kop[s2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kb + (g * HALF + 8 * s2) * 2));
                     } else {
                         const u32x2 c = *reinterpret_cast<const u32x2*>(kb + g * HALF + 8 * s2);
-                        kop = __builtin_bit_cast(bf16x8, fp8x8_to_bf16(c[0], c[1]));
+                        kop[s2] = __builtin_bit_cast(bf16x8, fp8x8_to_bf16(c[0], c[1]));
                     }
-#pragma unroll
-                    for (int t = 0; t < NHT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t][s2], kop, acc[t], 0, 0, 0);
                 }
-                float l = 0.0f;
-#pragma unroll
-                for (int t = 0; t < NHT; ++t)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 32 * t + 8 * q);
-#pragma unroll
-                        for (int i4 = 0; i4 < 4; ++i4) l = fmaf(w4[i4], fmaxf(acc[t][4 * q + i4], 0.0f), l);
-                    }
-                l += __shfl_xor(l, 32);
                 const int e = tile * 32 + j;
-                if (g == 0 && e < n) out[e] = l;
+#pragma unroll
+                for (int q = 0; q < RPW; ++q) {
+                    if (!mine[q]) continue;
+                    f32x16 acc[NHT];
+#pragma unroll
+                    for (int t = 0; t < NHT; ++t) acc[t] = f32x16{};
+#pragma unroll
+                    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+                        for (int t = 0; t < NHT; ++t)
+                            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[q][t][s2], kop[s2], acc[t], 0, 0, 0);
+                    const float* wrow = &w_lds[wave * RPW + q][4 * g];
+                    float l = 0.0f;
+#pragma unroll
+                    for (int t = 0; t < NHT; ++t)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 32 * t + 8 * v);
+#pragma unroll
+                            for (int i4 = 0; i4 < 4; ++i4) l = fmaf(w4[i4], fmaxf(acc[t][4 * v + i4], 0.0f), l);
+                        }
+                    l += __shfl_xor(l, 32);
+                    if (g == 0 && e < n[q]) p.logits[(int64_t)rr[q] * p.ld + e] = l;
+                }
             }
             __syncthreads();
         };
@@ -594,8 +626,10 @@ hipError_t launch_mfma(IndexArgs a, int max_entries, hipStream_t stream) {
     if (a.num_rows >= 64) {
         constexpr int kTilesPerGroup = 64;
         a.tiles_per_wave = kTilesPerGroup;
-        dim3 grid((max_tiles + kTilesPerGroup - 1) / kTilesPerGroup, (a.num_rows + kRowWaves - 1) / kRowWaves);
-        hipLaunchKernelGGL((index_rows_kernel<KD, NHT, DI>), grid, dim3(kRowThreads), 0, stream, a);
+        constexpr int RPW = rows_per_wave<DI>();
+        dim3 grid((max_tiles + kTilesPerGroup - 1) / kTilesPerGroup,
+                  (a.num_rows + kRowWaves * RPW - 1) / (kRowWaves * RPW));
+        hipLaunchKernelGGL((index_rows_kernel<KD, NHT, DI, RPW>), grid, dim3(kRowThreads), 0, stream, a);
     } else {
         // one round of waves over the GPU (256 CUs x 4 SIMDs x waves per
         // SIMD), each streaming a contiguous tile range
