@@ -104,3 +104,28 @@ def test_fp8_query_attention_rejected_without_mxfp4_pool():
     with pytest.raises(lcca.LccaError) as e:
         gs.attn(None)
     assert e.value.status == lcca.ERR_UNSUPPORTED
+
+
+def test_fp8_query_attention_bf16_outputs_and_noalloc():
+    """The same FP8-query attention with bf16 outputs (fp16 split partials)
+    against the oracle with q~ at the bf16-output bound, and the allocation-
+    free entry point with fp32 outputs equal to the workspace call bit for
+    bit."""
+    cfg = CASES[0]
+    st = _state(cfg)
+    rows = np.arange(len(st.row_seq))
+    idx = O.topk(st.row_pos, cfg.m, st.oracle_index(rows), cfg.k)
+    gs = GpuState(st)
+    gs.q_dt = Q8
+    idx_d = torch.from_numpy(idx).to("cuda")
+    qd, _ = _quantised(st)
+    o_q8, _ = _oracle_attn(st, idx, O.F32, qd)
+    out_b, _ = gs.attn(idx_d, out_dtype=lcca.BF16)
+    out_f, lse_f = gs.attn(idx_d)
+    out_n = torch.empty_like(out_f)
+    lse_n = torch.empty_like(lse_f)
+    lcca.sparse_attn_fwd_noalloc(gs.pages, gs.rows, Q8, gs.q, cfg.H, cfg.dv, cfg.scale, gs.kv, idx_d, cfg.k, gs.win,
+                                 lcca.F32, out_n, lse_n)
+    torch.cuda.synchronize()
+    C.check_attention(out_b.float().cpu().numpy(), o_q8, "mxfp4", out_bf16=True)
+    assert torch.equal(out_n, out_f) and torch.equal(lse_n, lse_f)
