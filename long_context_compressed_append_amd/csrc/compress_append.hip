@@ -29,6 +29,7 @@ constexpr int kChunkTokens = 16;            // new tokens per workgroup
 constexpr int kChunkMaxM = 8;               // largest group the chunk kernel forms
 constexpr int kChunkMinTokens = 64;         // calls with fewer new tokens use the slice grid
 constexpr int kRoundSlots = 4;              // 8-dimension items per thread per round of loads
+constexpr int kWinSlots = 5;                // window items per thread requested with the first round
 
 // The encode of one 8-dimension chunk of an entry (v: its aggregate values)
 // into the pool; MXFP4 blocks of 32 dimensions are held by four adjacent
@@ -125,7 +126,10 @@ __global__ __launch_bounds__(cmp::kThreads) void compress_chunk_kernel(CompressA
     if (tid < kChunkTokens) amax_lds[tid] = 0u;
     __syncthreads();
     // each token: its sequence, position, and whether it completes a group
-    // or carries the sequence's remainder-ring duty
+    // or carries the sequence's remainder-ring duty.  The pool row of a group
+    // it completes is requested here and written to LDS only after the
+    // weights are formed, so nothing waits for the block table meanwhile.
+    int my_grp = -1, my_blk = 0, my_slot = 0;
     if (tid < ntok) {
         const int t = t0 + tid;
         auto cu = [&](int i) { return in_lds ? cu_lds[i] : p.cu_new[i]; };
@@ -152,14 +156,95 @@ __global__ __launch_bounds__(cmp::kThreads) void compress_chunk_kernel(CompressA
             const int k = atomicAdd(&n_grp, 1);
             grp_tok[k] = tid;
             const int g = pos / m, E = 256 / m;
-            grp_row[k] =
-                (long long)checked(p.block_table[(int64_t)lo * p.max_blocks + g / E], 0, p.n_blocks - 1, p.dbg, kDbgBlock) *
-                    E +
-                g % E;
+            my_grp = k;
+            my_blk = p.block_table[(int64_t)lo * p.max_blocks + g / E];
+            my_slot = g % E;
         }
     }
     __syncthreads();
     const int ng = n_grp;
+    // Every load of the workgroup's first round goes out before anything is
+    // formed: the window slots' tokens (bf16 / fp32 windows; kWinSlots items
+    // per thread) and the entries' token chunks, then the group weights'
+    // logits, so their latencies overlap.
+    const int nch = p.D / 8;
+    const int witems = p.win_data != nullptr ? ntok * nch : 0;
+    const bool win_pre = p.win_data != nullptr && p.win_dtype != DT_FP8;
+    cmp::RawChunk<TOK> wraw[kWinSlots];
+    const int win_cap = p.win_cap;
+    auto win_item_live = [&](int it) __attribute__((always_inline)) {
+        return it < witems && tk_pos[it / nch] >= tk_end[it / nch] - win_cap;
+    };
+    if (win_pre) {
+#pragma unroll
+        for (int j = 0; j < kWinSlots; ++j) {
+            const int it = tid + NT * j;
+            if (win_item_live(it)) cmp::load_chunk<TOK>(p.kv_tok, (int64_t)(t0 + it / nch) * p.D + 8 * (it % nch), wraw[j]);
+        }
+    }
+    // entries: items (group, stream, 8-dimension chunk), SLOTS per thread per
+    // round; a round requests all of its tokens' chunks before forming any.
+    // A group's items are padded to a multiple of four, and MXFP4 pools (kv
+    // only) have dimensions in multiples of 32, so the four chunks of an MXFP4
+    // block sit on four adjacent lanes.
+    constexpr int SLOTS = TOK == DT_F32 ? kRoundSlots / 2 : kRoundSlots;
+    const int nkv = p.D / 8, nik = p.ik_data != nullptr ? p.dI / 8 : 0;
+    const int per = nkv + ((nik + 3) & ~3);
+    const int items = ng * per;
+    cmp::RawChunk<TOK> raw[SLOTS][kChunkMaxM];
+    auto load_round = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < SLOTS; ++j) {
+            const int it = base + tid + NT * j;
+            if (it < items && it % per < nkv + nik) {
+                const int k = it / per, u = it % per, tk = grp_tok[k];
+                const bool ik = u >= nkv;
+                const int d0 = ik ? (u - nkv) * 8 : u * 8, dim = ik ? p.dI : p.D;
+                const int b = tk_b[tk], start = tk_start[tk], g = tk_pos[tk] / m;
+                const void* tok = ik ? p.ik_tok : p.kv_tok;
+                const void* rtok = ik ? p.rem_ik : p.rem_kv;
+#pragma unroll
+                for (int i = 0; i < kChunkMaxM; ++i) {
+                    if (i < m) {
+                        const int t = g * m + i;
+                        const int64_t trow = t >= start ? tk_c0[tk] + (t - start) : (int64_t)b * m + t % m;
+                        cmp::load_chunk<TOK>(t >= start ? tok : rtok, trow * dim + d0, raw[j][i]);
+                    }
+                }
+            }
+        }
+    };
+    auto form_round = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < SLOTS; ++j) {
+            const int it = base + tid + NT * j;
+            const bool active = it < items && it % per < nkv + nik;
+            const int k = active ? it / per : 0, u = active ? it % per : 0;
+            const bool ik = u >= nkv;
+            const int d0 = ik ? (u - nkv) * 8 : u * 8;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+            if (active) {
+                // the products rounded one by one, then summed in token
+                // order, as in the slice kernel
+#pragma clang fp contract(off)
+                const float* w = &w_lds[ik ? 1 : 0][k][0];
+#pragma unroll
+                for (int i = 0; i < kChunkMaxM; ++i) {
+                    if (i < m) {
+                        float x[8];
+                        cmp::unpack_chunk<TOK>(raw[j][i], x);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = v[e] + fmaf(w[i], x[e], 0.0f);
+                    }
+                }
+            }
+            // MXFP4 lane exchanges: every lane of the wave takes part
+            store_entry_chunk(p, ik, active ? grp_row[k] : 0, d0, v, active);
+        }
+    };
+    load_round(0);
     // softmax weights of each group's logits, one wave per (group, stream),
     // with the slice kernel's reductions
     const int nstream = p.ik_data != nullptr ? 2 : 1;
@@ -179,98 +264,50 @@ __global__ __launch_bounds__(cmp::kThreads) void compress_chunk_kernel(CompressA
         const float sum = wave_sum(e);
         if (lane < m) w_lds[s][k][lane] = e / sum;
     }
+    if (my_grp >= 0)
+        grp_row[my_grp] = (long long)checked(my_blk, 0, p.n_blocks - 1, p.dbg, kDbgBlock) * (256 / m) + my_slot;
     __syncthreads();
-    // entries: items (group, stream, 8-dimension chunk), SLOTS per thread per
-    // round; a round requests all of its tokens' chunks before forming any.
-    // A group's items are padded to a multiple of four, and MXFP4 pools (kv
-    // only) have dimensions in multiples of 32, so the four chunks of an MXFP4
-    // block sit on four adjacent lanes.
-    {
-        constexpr int SLOTS = TOK == DT_F32 ? kRoundSlots / 2 : kRoundSlots;
-        const int nkv = p.D / 8, nik = p.ik_data != nullptr ? p.dI / 8 : 0;
-        const int per = nkv + ((nik + 3) & ~3);
-        const int items = ng * per;
-        for (int base = 0; base < items; base += NT * SLOTS) {
-            cmp::RawChunk<TOK> raw[SLOTS][kChunkMaxM];
-#pragma unroll
-            for (int j = 0; j < SLOTS; ++j) {
-                const int it = base + tid + NT * j;
-                if (it < items && it % per < nkv + nik) {
-                    const int k = it / per, u = it % per, tk = grp_tok[k];
-                    const bool ik = u >= nkv;
-                    const int d0 = ik ? (u - nkv) * 8 : u * 8, dim = ik ? p.dI : p.D;
-                    const int b = tk_b[tk], start = tk_start[tk], g = tk_pos[tk] / m;
-                    const void* tok = ik ? p.ik_tok : p.kv_tok;
-                    const void* rtok = ik ? p.rem_ik : p.rem_kv;
-#pragma unroll
-                    for (int i = 0; i < kChunkMaxM; ++i) {
-                        if (i < m) {
-                            const int t = g * m + i;
-                            const int64_t trow = t >= start ? tk_c0[tk] + (t - start) : (int64_t)b * m + t % m;
-                            cmp::load_chunk<TOK>(t >= start ? tok : rtok, trow * dim + d0, raw[j][i]);
-                        }
-                    }
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < SLOTS; ++j) {
-                const int it = base + tid + NT * j;
-                const bool active = it < items && it % per < nkv + nik;
-                const int k = active ? it / per : 0, u = active ? it % per : 0;
-                const bool ik = u >= nkv;
-                const int d0 = ik ? (u - nkv) * 8 : u * 8;
-                float v[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = 0.0f;
-                if (active) {
-                    // the products rounded one by one, then summed in token
-                    // order, as in the slice kernel
-#pragma clang fp contract(off)
-                    const float* w = &w_lds[ik ? 1 : 0][k][0];
-#pragma unroll
-                    for (int i = 0; i < kChunkMaxM; ++i) {
-                        if (i < m) {
-                            float x[8];
-                            cmp::unpack_chunk<TOK>(raw[j][i], x);
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) v[e] = v[e] + fmaf(w[i], x[e], 0.0f);
-                        }
-                    }
-                }
-                // MXFP4 lane exchanges: every lane of the wave takes part
-                store_entry_chunk(p, ik, active ? grp_row[k] : 0, d0, v, active);
-            }
-        }
+    form_round(0);
+    for (int base = NT * SLOTS; base < items; base += NT * SLOTS) {
+        load_round(base);
+        form_round(base);
     }
     // window slots of the tokens among the last `capacity` of their chunk:
-    // items (token, 8-value chunk).  FP8 windows take each token's max first
-    // (a pass of loads and an LDS max), then encode in a second pass.
+    // items (token, 8-value chunk).  bf16 / fp32 windows: the prefetched
+    // items, then any further rounds.  FP8 windows take each token's max
+    // first (a pass of loads and an LDS max), then encode in a second pass.
+    if (win_pre) {
+#pragma unroll
+        for (int j = 0; j < kWinSlots; ++j) {
+            const int it = tid + NT * j;
+            if (!win_item_live(it)) continue;
+            const int tk = it / nch, c = it % nch;
+            float x[8];
+            cmp::unpack_chunk<TOK>(wraw[j], x);
+            store_window_chunk(p, (int64_t)tk_b[tk] * p.win_cap + tk_pos[tk] % p.win_cap, 8 * c, x, 1.0f);
+        }
+    }
     if (p.win_data != nullptr) {
-        const int nch = p.D / 8;
-        const int items = ntok * nch;
         const bool fp8 = p.win_dtype == DT_FP8;
+        const int first = win_pre ? NT * kWinSlots : 0;
         for (int pass = fp8 ? 0 : 1; pass < 2; ++pass) {
             if (pass == 1 && fp8) __syncthreads();
-            for (int base = 0; base < items; base += NT * kRoundSlots) {
-                cmp::RawChunk<TOK> raw[kRoundSlots];
+            for (int base = first; base < witems; base += NT * kRoundSlots) {
+                cmp::RawChunk<TOK> rw[kRoundSlots];
 #pragma unroll
                 for (int j = 0; j < kRoundSlots; ++j) {
                     const int it = base + tid + NT * j;
-                    if (it < items) {
-                        const int tk = it / nch, c = it % nch;
-                        if (tk_pos[tk] >= tk_end[tk] - p.win_cap)
-                            cmp::load_chunk<TOK>(p.kv_tok, (int64_t)(t0 + tk) * p.D + 8 * c, raw[j]);
-                    }
+                    if (win_item_live(it))
+                        cmp::load_chunk<TOK>(p.kv_tok, (int64_t)(t0 + it / nch) * p.D + 8 * (it % nch), rw[j]);
                 }
 #pragma unroll
                 for (int j = 0; j < kRoundSlots; ++j) {
                     const int it = base + tid + NT * j;
-                    if (it >= items) continue;
+                    if (!win_item_live(it)) continue;
                     const int tk = it / nch, c = it % nch;
                     const int pos = tk_pos[tk];
-                    if (pos < tk_end[tk] - p.win_cap) continue;
                     float x[8];
-                    cmp::unpack_chunk<TOK>(raw[j], x);
+                    cmp::unpack_chunk<TOK>(rw[j], x);
                     if (pass == 0) {
                         float a = 0.0f;
 #pragma unroll

@@ -292,7 +292,7 @@ __device__ void compress_slice(const CompressArgs& p, const SeqChunk& q, int g, 
 }
 
 template <int TOK>
-__device__ void write_ring(const CompressArgs& p, const SeqChunk& q, int tt) {
+__device__ __forceinline__ void write_ring(const CompressArgs& p, const SeqChunk& q, int tt) {
     const int m = p.m;
     const int esz = TOK == DT_F32 ? 4 : 2;
     const int64_t src = q.c0 + (tt - q.start);
