@@ -32,6 +32,10 @@ SMALL = {
     "idx32x256": synth.shrink(S["csa_64k"], "idx32x256", (4097, 3000), (1, 1), k=256, HI=32, dI=256),
     "lp_bf16win": synth.shrink(S["lp_512k"], "lp_bf16win", (6001, 3333), (1, 1), k=256, win_dtype=synth.BF16),
     "prefill_h128": synth.shrink(S["prefill_8k"], "prefill_h128", (2001,), (300,), k=128, win_cap=1024, H=128),
+    # chunked prefill of three sequences (424 rows, not a multiple of 16):
+    # indexer workgroups and waves hold rows of two sequences
+    "prefill_multi": synth.shrink(S["prefill_8k"], "prefill_multi", (3001, 1500, 777), (203, 131, 90), k=256,
+                                  win_cap=2048),
 }
 
 
