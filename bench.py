@@ -666,6 +666,24 @@ def run_workload(torch, lcca, synth, name, args, with_oracle, cpu_seconds=0.0, b
             res["fp8_query"][n] = {"ms": round(st8[n], 5), "GB/s": round(b / st8[n] / 1e6, 1),
                                    "hbm_frac": round(b / st8[n] / 1e6 / HBM_PEAK_GBS, 4)}
         log(name, "fp8 queries", json.dumps(res["fp8_query"]))
+    if not args.no_pbf16 and wl.cfg.outlier_frac == 0.0 and wl.cfg.kv_dtype != synth.F32:
+        # the same step with the softmax weights as bf16 alone in P.V (opt-in;
+        # not on csa_64k, whose 8-sigma outlier channels need the hi + lo pair)
+        wl.a_qdt = lcca.BF16 | lcca.P_BF16
+        for i in range(args.warmup):
+            wl.step(i)
+        t = plain_steps(torch, wl, steps)
+        _, stp, _ = time_steps(torch, wl, steps, 0)
+        b, f = work["sparse_attn_fwd"]
+        v = {"rows_per_s": round(wl.nrows / (t / 1e3), 1), "ms_per_step": round(t, 5),
+             "sparse_attn_fwd": {"ms": round(stp["sparse_attn_fwd"], 5),
+                                 "hbm_frac": round(b / stp["sparse_attn_fwd"] / 1e6 / HBM_PEAK_GBS, 4),
+                                 "mfma_frac": round(f / stp["sparse_attn_fwd"] / 1e9 / BF16_PEAK_TFLOPS, 4)}}
+        if with_oracle:
+            v["parity"] = parity_summary(wl, rows, out_ref, idx_ref)
+        wl.a_qdt = lcca.BF16
+        res["p_bf16"] = v
+        log(name, "bf16 weights", json.dumps(v))
     if not args.no_gated:
         t = gated_leg(torch, lcca, wl, steps, args.warmup)
         b = stage_work(wl.cfg, gated=True)["compress_append"][0]
@@ -698,6 +716,7 @@ def main():
     ap.add_argument("--no-fp8q", action="store_true",
                     help="skip the FP8-query indexer leg of workloads with FP8 indexer keys")
     ap.add_argument("--no-rope", action="store_true", help="skip timing the rotary embeddings of a step")
+    ap.add_argument("--no-pbf16", action="store_true", help="skip the step with bf16-only softmax weights in P.V")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the per-channel-gated compress_append leg of each workload")
     ap.add_argument("--no-bf16-variant", action="store_true",
@@ -768,6 +787,7 @@ def main():
         "bf16_out": r.get("bf16_out"),
         "gated_compress": r.get("gated_compress"),
         "fp8_query": r.get("fp8_query"),
+        "p_bf16": r.get("p_bf16"),
         "rope": r.get("rope"),
         "also": {n: {"rows_per_s": round(v["rows_per_s"], 1), "ms_per_step": round(v["ms_per_step"], 5),
                      "rows": v["rows"], "step_hbm_GB/s": round(v["step_GB/s"], 1),
@@ -776,7 +796,7 @@ def main():
                      "stages": v["stages"], "cold_cache_copies": v["R"], "steps": v["steps"],
                      "parity": v.get("parity"), "gated_compress": v.get("gated_compress"),
                      "fp8_query": v.get("fp8_query"), "cpu_1t": v.get("cpu_1t"),
-                     "rope": v.get("rope")}
+                     "rope": v.get("rope"), "p_bf16": v.get("p_bf16")}
                  for n, v in results.items() if n != head},
     }
     print(json.dumps(line), flush=True)

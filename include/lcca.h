@@ -120,6 +120,16 @@ typedef enum { LCCA_F32 = 0, LCCA_BF16 = 1, LCCA_FP8_E4M3 = 2, LCCA_MXFP4 = 3 } 
  * library's.] */
 #define LCCA_Q_FP8 0x100
 
+/* Flag OR-ed into the q_dtype of lcca_sparse_attn_fwd(_noalloc) (BF16 and
+ * FP8-query paths; no effect on the F32 path): the softmax weights P enter
+ * the P.V products as bf16 alone instead of a bf16 hi + lo pair (16
+ * significant bits), which halves the P.V matrix work.  Each weight then
+ * carries a relative error of at most 2^-9, so an output element moves by at
+ * most 2^-9 max_j |v_j| (its keys' largest value component) more than with
+ * the pair: within a 2e-2 bound while the values stay below 10 in magnitude
+ * (N(0,1) values), not with large outlier channels.  The caller decides. */
+#define LCCA_P_BF16 0x200
+
 typedef struct {
     int32_t dtype;        /* lcca_dtype of the stored entries                    */
     int32_t dim;          /* elements per entry                                  */
@@ -367,7 +377,7 @@ size_t lcca_decode_select_workspace_size(const lcca_rows* rows, int32_t ratio_m,
  *   q        device [num_rows][H][kv->dim] of q_dtype (F32 with F32 cache;
  *            BF16 otherwise; BF16 | LCCA_Q_FP8 with an MXFP4 cache quantises
  *            it to FP8, see LCCA_Q_FP8; other combinations with the flag
- *            return LCCA_ERR_UNSUPPORTED)
+ *            return LCCA_ERR_UNSUPPORTED; | LCCA_P_BF16: see there)
  *   out      device [num_rows][H][d_v] of out_dtype (F32 or BF16)
  *   lse      device float [num_rows][H] or NULL
  *   ws       device workspace of at least lcca_sparse_attn_workspace_size()

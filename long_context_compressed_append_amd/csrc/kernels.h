@@ -110,6 +110,8 @@ struct AttnArgs {
     // E4M3 with a power-of-two scale; pool tiles scored by the scaled
     // FP4 x FP8 MFMA on the pool's own codes and scales
     int32_t q8;
+    // P carried as a bf16 hi + lo pair (1, the default) or as bf16 alone (0)
+    int32_t p_lo;
 };
 
 // Rotary embedding of dims [off, off + rd) of x [rows][heads][dim] in place

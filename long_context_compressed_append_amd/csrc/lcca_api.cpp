@@ -527,7 +527,8 @@ lcca_status attn_call(void* stream, const lcca_pages* pages, const lcca_rows* ro
     if (out_dtype != LCCA_F32 && out_dtype != LCCA_BF16) return fail(LCCA_ERR_UNSUPPORTED, "out dtype %d", out_dtype);
     if (kv->dtype == LCCA_FP8_E4M3) return fail(LCCA_ERR_UNSUPPORTED, "FP8 kv pool (BF16, MXFP4 or F32)");
     const bool q8 = (q_dtype & LCCA_Q_FP8) != 0;
-    q_dtype &= ~LCCA_Q_FP8;
+    const bool p16 = (q_dtype & LCCA_P_BF16) != 0;
+    q_dtype &= ~(LCCA_Q_FP8 | LCCA_P_BF16);
     if (q8 && (q_dtype != LCCA_BF16 || kv->dtype != LCCA_MXFP4))
         return fail(LCCA_ERR_UNSUPPORTED, "sparse_attn: FP8 queries need BF16 q and an MXFP4 kv pool (q %d, kv %d)",
                     q_dtype, kv->dtype);
@@ -572,6 +573,7 @@ lcca_status attn_call(void* stream, const lcca_pages* pages, const lcca_rows* ro
     a.out_dtype = out_dtype; a.out = out; a.lse = lse;
     a.nsplit = plan.nsplit; a.split_tiles = plan.split_tiles;
     a.q8 = q8 ? 1 : 0;
+    a.p_lo = p16 ? 0 : 1;
     if (plan.nsplit > 1) {
         const size_t parts = (size_t)rows->num_rows * plan.nsplit * H * d_v;
         const size_t po = (parts * sizeof(float) + 255) & ~(size_t)255;

@@ -518,6 +518,7 @@ struct ValueWave {
     // read), dims 16 dt + 4 (s & 3) .. +3 of the quarter, so lane i receives
     // dim 16 dt + i for keys 4g + e and 16 + 4g + e: the A operand of a
     // 16x16x32 MFMA in the key order of the score waves' C layout.
+    template <bool LO>
     __device__ __forceinline__ void pv(const lds_u8* st, const bf16x8 (&phi)[4], const bf16x8 (&plo)[4], int lane) {
         constexpr int ROWB = Geo<D>::ROWB;
         const int g = lane >> 4, i16 = lane & 15;
@@ -533,7 +534,7 @@ struct ValueWave {
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb) {
                 o[hb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[hb], o[hb][dt], 0, 0, 0);
-                o[hb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[hb], o[hb][dt], 0, 0, 0);
+                if constexpr (LO) o[hb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[hb], o[hb][dt], 0, 0, 0);
             }
         }
     }
@@ -546,7 +547,8 @@ constexpr int kLoadThreads = 256;      // the score waves load the key tiles
 constexpr int kStages = 3;             // LDS stages of the key tiles
 constexpr int kRowsLds = 2560;         // storage rows of a split's selected slots cached in LDS (= max keys per split)
 
-template <int KVD, int WD, int D, int DV, bool Q8>
+// PLO: P enters P.V as a bf16 hi + lo pair (the default) or as bf16 alone.
+template <int KVD, int WD, int D, int DV, bool Q8, bool PLO>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(AttnArgs a) {
     using G = Geo<D>;
     using SW = ScoreWave<D, Q8>;
@@ -665,7 +667,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             const float al = W.softmax(sv, km + sc * kKeys, lane, a.scale_log2, h, l);
             lds_u8* pw = pm + (k & 1) * PPAR + hb * 1024 + lane * 16;
             *reinterpret_cast<lds_u32x4*>(pw) = h;
-            *reinterpret_cast<lds_u32x4*>(pw + 4096) = l;
+            if constexpr (PLO) *reinterpret_cast<lds_u32x4*>(pw + 4096) = l;
             if (g == 0) alm[(k & 1) * 64 + 16 * hb + c16] = al;
             if (k + 1 < ntl) {
                 TL::store(rk, tb + k + 1, R[rs], st + sn * G::STAGE, km + sn * kKeys);
@@ -714,7 +716,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb) {
                 phi[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(pr + hb * 1024));
-                plo[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(pr + 4096 + hb * 1024));
+                if constexpr (PLO)
+                    plo[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(pr + 4096 + hb * 1024));
                 al[hb] = alm[(kp & 1) * 64 + 16 * hb + c16];
             }
             if (__builtin_amdgcn_ballot_w64(al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f)) {
@@ -723,7 +726,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                     for (int dt = 0; dt < VW::NDT; ++dt) V.o[hb][dt] *= al[hb];
             }
-            V.pv(st + (kp % kStages) * G::STAGE, phi, plo, lane);
+            V.template pv<PLO>(st + (kp % kStages) * G::STAGE, phi, plo, lane);
         }
         __syncthreads();
     }
@@ -736,7 +739,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
             phi[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(pr + hb * 1024));
-            plo[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(pr + 4096 + hb * 1024));
+            if constexpr (PLO)
+                plo[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(pr + 4096 + hb * 1024));
             al[hb] = alm[(kp & 1) * 64 + 16 * hb + c16];
         }
         if (__builtin_amdgcn_ballot_w64(al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f)) {
@@ -745,7 +749,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                 for (int dt = 0; dt < VW::NDT; ++dt) V.o[hb][dt] *= al[hb];
         }
-        V.pv(st + (kp % kStages) * G::STAGE, phi, plo, lane);
+        V.template pv<PLO>(st + (kp % kStages) * G::STAGE, phi, plo, lane);
     }
     __syncthreads();                                         // matches the score waves' closing barrier
     __syncthreads();                                         // their m and l are in LDS
@@ -976,11 +980,17 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
     const int64_t upx = ((int64_t)a.num_rows * a.nsplit + kXcds - 1) / kXcds;
     const dim3 grid((unsigned)(kXcds * upx * (a.H / 64)));
     if constexpr (KVD == DT_MXFP4) {
-        if (a.q8) hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, true>), grid, dim3(kThreads), 0, stream, a);
-        else hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, false>), grid, dim3(kThreads), 0, stream, a);
+        if (a.q8) {
+            if (a.p_lo) hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, true, true>), grid, dim3(kThreads), 0, stream, a);
+            else hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, true, false>), grid, dim3(kThreads), 0, stream, a);
+        } else {
+            if (a.p_lo) hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, false, true>), grid, dim3(kThreads), 0, stream, a);
+            else hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, false, false>), grid, dim3(kThreads), 0, stream, a);
+        }
     } else {
         if (a.q8) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, false>), grid, dim3(kThreads), 0, stream, a);
+        if (a.p_lo) hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, false, true>), grid, dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((attn_mfma_kernel<KVD, WD, D, DV, false, false>), grid, dim3(kThreads), 0, stream, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;

@@ -21,6 +21,7 @@ F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_DEVICE_INDEX = 0, -1, -2, -3, -4, -5
 DBG_BLOCK, DBG_ROW, DBG_CHUNK = 1, 2, 4
 Q_FP8 = 0x100          # q_dtype flag: FP8 queries on the FP8 matrix cores (lcca.h, LCCA_Q_FP8)
+P_BF16 = 0x200         # q_dtype flag of the attention: softmax weights as bf16 alone (lcca.h, LCCA_P_BF16)
 ROPE_HALF, ROPE_INVERSE = 1, 2
 
 _PKG = os.path.dirname(os.path.abspath(__file__))

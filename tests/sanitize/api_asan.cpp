@@ -172,6 +172,12 @@ static void attn_cases() {
     EXPECT(call(&rw, LCCA_BF16 | LCCA_Q_FP8, 64, 576, 0.04f, &kv, &win, LCCA_F32, P, need), LCCA_ERR_UNSUPPORTED);
     lcca_paged_cache mx = pool(LCCA_MXFP4, 576, 4, 4096);
     EXPECT(call(&rw, LCCA_F32 | LCCA_Q_FP8, 64, 576, 0.04f, &mx, &win, LCCA_F32, P, need), LCCA_ERR_UNSUPPORTED);
+    // bf16-only weights: the flag does not lift the FP8-query rules, and other bits stay unsupported
+    EXPECT(call(&rw, LCCA_BF16 | LCCA_Q_FP8 | LCCA_P_BF16, 64, 576, 0.04f, &kv, &win, LCCA_F32, P, need),
+           LCCA_ERR_UNSUPPORTED);
+    EXPECT(call(&rw, LCCA_BF16 | LCCA_P_BF16 | 0x400, 64, 576, 0.04f, &kv, &win, LCCA_F32, P, need),
+           LCCA_ERR_UNSUPPORTED);
+    EXPECT(call(&none, LCCA_BF16 | LCCA_P_BF16, 64, 576, 0.04f, &kv, &win, LCCA_F32, nullptr, 0), LCCA_OK);
 }
 
 static void rope_cases() {
