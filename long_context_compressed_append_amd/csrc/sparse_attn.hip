@@ -148,8 +148,15 @@ struct Tiler {
         int64_t row;
         bool ok, win;
     };
+    // The LDS read of the storage row is separate (row_of, issued early;
+    // for window tiles its value is not used) from forming the source.
+    __device__ __forceinline__ static int row_of(const RowKeys& rk, int tile, bool live, const lds_i32* rows_lds,
+                                                 int idx0) {
+        const int key = (int)threadIdx.x / kThreadsPerKey;
+        return rows_lds[(live && tile < rk.sel_tiles ? tile * kKeys - idx0 : 0) + key];
+    }
     __device__ __forceinline__ static Src resolve(const AttnArgs& a, const RowKeys& rk, int tile, bool live,
-                                                  const lds_i32* rows_lds, int idx0) {
+                                                  int prow) {
         const int key = (int)threadIdx.x / kThreadsPerKey;
         Src s;
         s.win = live && tile >= rk.sel_tiles;                       // uniform over the workgroup
@@ -158,11 +165,14 @@ struct Tiler {
             s.ok = w < rk.nwin;
             s.row = (int64_t)rk.b * a.win_cap + (rk.t0 + (s.ok ? w : 0)) % a.win_cap;
         } else {
-            const int prow = rows_lds[(live ? tile * kKeys - idx0 : 0) + key];
             s.ok = live && prow >= 0;
             s.row = s.ok ? prow : 0;
         }
         return s;
+    }
+    __device__ __forceinline__ static Src resolve(const AttnArgs& a, const RowKeys& rk, int tile, bool live,
+                                                  const lds_i32* rows_lds, int idx0) {
+        return resolve(a, rk, tile, live, row_of(rk, tile, live, rows_lds, idx0));
     }
 
     // Issue the loads of a resolved key into registers.  One load sequence
@@ -430,17 +440,37 @@ struct ScoreWave {
 
     // S^T of the tile: lane (head = lane & 15, g = lane >> 4) gets keys
     // 16 b + 4g + j in sacc[b][j].
+    // The K fragments are read in batches of KB k-steps, the next batch's
+    // reads issued before the current batch's MFMAs, so LDS latency overlaps
+    // the MFMAs instead of gating each of them.
+    template <int KB>
     __device__ __forceinline__ void scores(const lds_u8* st, int lane, f32x4 (&sacc)[2]) const {
         constexpr int ROWB = Geo<D>::ROWB;
+        constexpr int NB = (KS + KB - 1) / KB;
         const lds_u8* kb = st + (lane & 15) * ROWB + 16 * (lane >> 4);
         sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 kf[2][KB][2];
+        auto fetch = [&](int buf, int s0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
+            for (int j = 0; j < KB; ++j)
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const bf16x8 k = __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(kb + 16 * b * ROWB + 64 * s));
-                sacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qb[s], sacc[b], 0, 0, 0);
-            }
+                for (int b = 0; b < 2; ++b)
+                    if (s0 + j < KS)
+                        kf[buf][j][b] = __builtin_bit_cast(
+                            bf16x8, *reinterpret_cast<const lds_u32x4*>(kb + 16 * b * ROWB + 64 * (s0 + j)));
+        };
+        fetch(0, 0);
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            if (n + 1 < NB) fetch((n + 1) & 1, (n + 1) * KB);
+            // the scheduler would otherwise sink each read next to its MFMA
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < KB; ++j)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    if (n * KB + j < KS)
+                        sacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[n & 1][j][b], qb[n * KB + j], sacc[b], 0, 0, 0);
         }
     }
 
@@ -448,14 +478,11 @@ struct ScoreWave {
     // the key's value scale (FP8 window scale, 1, or -1 for a masked key),
     // which also multiplies its score.  Returns the rescale factor of the
     // head's accumulators and P hi / lo in B-operand order.
-    __device__ __forceinline__ float softmax(f32x4 (&s)[2], const lds_f32* kmeta, int lane, float scale_log2,
-                                             u32x4& h, u32x4& l) {
-        const int g = lane >> 4;
-        f32x4 km[2];
+    __device__ __forceinline__ float softmax(f32x4 (&s)[2], const f32x4 (&km)[2], float scale_log2, u32x4& h,
+                                             u32x4& l) {
         float mx = -INFINITY;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            km[b] = *reinterpret_cast<const lds_f32x4*>(kmeta + 16 * b + 4 * g);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 s[b][j] = km[b][j] >= 0.0f ? s[b][j] * (scale_log2 * km[b][j]) : -INFINITY;
@@ -556,6 +583,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     using TL = Tiler<KVD, WD, D, kLoadThreads>;
     constexpr int NU = TL::NU;
     constexpr int NT = kThreads;
+    // k-steps of K fragments read ahead of the score MFMAs (two where the
+    // bf16 window tiles' load registers leave less room)
+    constexpr int KBatch = (KVD == DT_MXFP4 && WD == DT_BF16) ? 2 : 3;
     __shared__ __attribute__((aligned(16))) uint8_t stage[kStages][G::STAGE];
     __shared__ __attribute__((aligned(16))) float kmeta[kStages][kKeys];
     __shared__ __attribute__((aligned(16))) uint8_t p_mem[2][2][4][64 * 16];   // [step parity][hi, lo][head block][lane]
@@ -655,16 +685,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         auto step = [&](auto J, int k) __attribute__((always_inline)) {
             constexpr int rs = (decltype(J)::value + 1) & 1;
             const int sc = k % kStages, sn = (k + 1) % kStages;
+            // LDS reads whose results are needed only after the scores: the
+            // storage row of tile k + 3 and the keys' metadata
+            const int nrow = TL::row_of(rk, tb + k + 3, k + 3 < ntl, rows_lds, idx0);
+            f32x4 kmv[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) kmv[b] = *reinterpret_cast<const lds_f32x4*>(km + sc * kKeys + 16 * b + 4 * g);
             f32x4 sv[2];
             if constexpr (Q8) {
                 if (tb + k < rk.sel_tiles) W.scores8(rw + (k & 1) * Raw<D>::STAGE, lane, sv);
                 else W.scores_q8win(st + sc * G::STAGE, lane, sv);
             } else {
-                W.scores(st + sc * G::STAGE, lane, sv);
+                W.template scores<KBatch>(st + sc * G::STAGE, lane, sv);
             }
-            const typename TL::Src nsrc = TL::resolve(a, rk, tb + k + 3, k + 3 < ntl, rows_lds, idx0);
+            const typename TL::Src nsrc = TL::resolve(a, rk, tb + k + 3, k + 3 < ntl, nrow);
             u32x4 h, l;
-            const float al = W.softmax(sv, km + sc * kKeys, lane, a.scale_log2, h, l);
+            const float al = W.softmax(sv, kmv, a.scale_log2, h, l);
             lds_u8* pw = pm + (k & 1) * PPAR + hb * 1024 + lane * 16;
             *reinterpret_cast<lds_u32x4*>(pw) = h;
             if constexpr (PLO) *reinterpret_cast<lds_u32x4*>(pw + 4096) = l;
