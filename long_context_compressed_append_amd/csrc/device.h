@@ -176,6 +176,13 @@ __device__ inline float max_across_rows(float v) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// v of lane l plus v of lane l ^ 32, on the VALU (as above; the sum of the
+// two is the same whichever result holds which).
+__device__ inline float sum_halves(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
 __device__ inline int visible_entries(int pos, int m) { return (pos + 1) / m; }
 
 // ---------------------------------------------------------------------------

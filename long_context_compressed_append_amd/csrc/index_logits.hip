@@ -402,7 +402,7 @@ index_mfma_kernel(IndexArgs p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) l = fmaf(w4[i], fmaxf(acc[t][4 * q + i], 0.0f), l);
             }
-        l += __shfl_xor(l, 32);
+        l = sum_halves(l);
         const int e = tile * 32 + j;
         if (g == 0 && e < n) {
             out[e] = l;
@@ -580,7 +580,7 @@ __global__ __launch_bounds__(kRowThreads) void index_rows_kernel(IndexArgs p) {
 #pragma unroll
                             for (int i4 = 0; i4 < 4; ++i4) l = fmaf(w4[i4], fmaxf(acc[t][4 * v + i4], 0.0f), l);
                         }
-                    l += __shfl_xor(l, 32);
+                    l = sum_halves(l);
                     if (g == 0 && e < n[q]) p.logits[(int64_t)rr[q] * p.ld + e] = l;
                 }
             }

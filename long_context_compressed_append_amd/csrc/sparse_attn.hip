@@ -820,8 +820,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int dt = 0; dt < NDT; ++dt) {
                 float amax = fmaxf(fmaxf(fabsf(V.o[hb][dt][0]), fabsf(V.o[hb][dt][1])),
                                    fmaxf(fabsf(V.o[hb][dt][2]), fabsf(V.o[hb][dt][3])));
-                amax = fmaxf(amax, __shfl_xor(amax, 16));
-                amax = fmaxf(amax, __shfl_xor(amax, 32)) * inv;
+                amax = max_across_rows(amax) * inv;
                 int ex = 0;
                 (void)frexpf(amax, &ex);
                 const f32x4 v = V.o[hb][dt] * ldexpf(inv, 15 - ex);
