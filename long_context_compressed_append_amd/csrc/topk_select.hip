@@ -63,8 +63,13 @@ struct alignas(16) SmemT {
         uint32_t lead[kLeadBins * COPIES];            // step 1: [bin][copy]
         struct {
             uint32_t bits[2][WORDS];                  // [0] keys above T, [1] keys equal to T
-            uint32_t cand_key[kCandCap];
-            int32_t cand_idx[kCandCap];
+            union alignas(16) {
+                struct {
+                    uint32_t key[kCandCap];
+                    int32_t idx[kCandCap];
+                } c;                                  // the boundary digit's candidates
+                uint32_t sel[2 * kCandCap];           // later: the selected positions, in output order
+            } cs;
             uint32_t fine[2][256];                    // refinement histograms, double-buffered
         } b;
     } u;
@@ -349,16 +354,29 @@ __device__ __forceinline__ void topk_body(const TopkArgs& p, int r, int by) {
         }
         return;
     }
-    // the selected position `e` at output slot `pos`
+    // the selected position `e` at output slot `pos`.  kSlice and kCand
+    // outputs need a load per selected position (its logit, its entry): with
+    // up to kStageCap slots the positions are staged in LDS (over the
+    // candidate arrays, free by then) and translated after one barrier, all
+    // loads in flight together, instead of one dependent load per emitted
+    // position in the bit loop.
+    static constexpr int kStageCap = 2 * kCandCap;          // slots of sm.u.b.cs.sel
+    const bool staged = MODE != kRow && k <= kStageCap;
     auto emit = [&](uint32_t pos, int e) __attribute__((always_inline)) {
         if (pos >= (uint32_t)k) return;                // never taken; keeps every store in the row
         if constexpr (MODE == kRow) {
             out[pos] = e;
-        } else if constexpr (MODE == kSlice) {
-            p.cand_key[c0 + pos] = order_key(base[e]);
-            p.cand_idx[c0 + pos] = s0 + e;
         } else {
-            out[pos] = p.cand_idx[c0 + e];
+            if (staged) {
+                sm.u.b.cs.sel[pos] = (uint32_t)e;
+                return;
+            }
+            if constexpr (MODE == kSlice) {
+                p.cand_key[c0 + pos] = order_key(base[e]);
+                p.cand_idx[c0 + pos] = s0 + e;
+            } else {
+                out[pos] = p.cand_idx[c0 + e];
+            }
         }
     };
     Keys<R, Half, Vec, MODE == kCand> K;
@@ -449,8 +467,8 @@ __device__ __forceinline__ void topk_body(const TopkArgs& p, int r, int by) {
     };
     auto put = [&](uint32_t c, int e, uint32_t key) __attribute__((always_inline)) {
         if (c < (uint32_t)kCandCap) {
-            if constexpr (Keys<R, Half, Vec, MODE == kCand>::kFull) sm.u.b.cand_key[c] = key;
-            sm.u.b.cand_idx[c] = e;
+            if constexpr (Keys<R, Half, Vec, MODE == kCand>::kFull) sm.u.b.cs.c.key[c] = key;
+            sm.u.b.cs.c.idx[c] = e;
         }
     };
     if constexpr (R > 0) {
@@ -486,12 +504,12 @@ __device__ __forceinline__ void topk_body(const TopkArgs& p, int r, int by) {
     const bool fits = nc <= (uint32_t)kCandCap;
     if constexpr (!Keys<R, Half, Vec, MODE == kCand>::kFull) {
         if (fits) {
-            for (int c = tid; c < (int)nc; c += kThreads) sm.u.b.cand_key[c] = K.full_key(sm.u.b.cand_idx[c], 0u);
+            for (int c = tid; c < (int)nc; c += kThreads) sm.u.b.cs.c.key[c] = K.full_key(sm.u.b.cs.c.idx[c], 0u);
             __syncthreads();
         }
     }
     auto cands = [&](auto f) __attribute__((always_inline)) {
-        for (int c = tid; c < (int)nc; c += kThreads) f(sm.u.b.cand_idx[c], sm.u.b.cand_key[c]);
+        for (int c = tid; c < (int)nc; c += kThreads) f(sm.u.b.cs.c.idx[c], sm.u.b.cs.c.key[c]);
     };
     auto row_bin = [&](auto f) __attribute__((always_inline)) {
         K.each_full([&](int e, uint32_t key) __attribute__((always_inline)) {
@@ -536,15 +554,32 @@ __device__ __forceinline__ void topk_body(const TopkArgs& p, int r, int by) {
             if (take) emit(pos++, e);
         }
     }
-    if constexpr (MODE == kSlice) {
-        if (hist) {
-            // the last thread's end position is the number kept; pad the rest
+    if constexpr (MODE != kRow) {
+        // the last thread's end position is the number kept
+        if (staged || (MODE == kSlice && hist)) {
             __syncthreads();
             if (tid == kThreads - 1) sm.cand_n = pos;
             __syncthreads();
-            for (int i = (int)sm.cand_n + tid; i < k; i += kThreads) {
-                p.cand_key[c0 + i] = 0u;
-                p.cand_idx[c0 + i] = -1;
+        }
+        if (staged) {
+            const uint32_t* sel = sm.u.b.cs.sel;
+            for (int i = tid; i < (int)sm.cand_n; i += kThreads) {
+                const int e = (int)sel[i];
+                if constexpr (MODE == kSlice) {
+                    p.cand_key[c0 + i] = order_key(base[e]);
+                    p.cand_idx[c0 + i] = s0 + e;
+                } else {
+                    out[i] = p.cand_idx[c0 + e];
+                }
+            }
+        }
+        if constexpr (MODE == kSlice) {
+            if (hist) {
+                // pad the slice's slots past the number kept
+                for (int i = (int)sm.cand_n + tid; i < k; i += kThreads) {
+                    p.cand_key[c0 + i] = 0u;
+                    p.cand_idx[c0 + i] = -1;
+                }
             }
         }
     }
