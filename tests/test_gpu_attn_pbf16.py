@@ -56,3 +56,37 @@ def test_bf16_weights_within_their_bound(cfg):
     if cfg.outlier_frac == 0.0:
         o_want, _ = st.oracle_attn(idx)
         C.check_attention(out_p16.cpu().numpy(), o_want, "mxfp4" if cfg.kv_dtype == synth.MXFP4 else "bf16")
+
+
+def test_bf16_weights_with_bf16_outputs_and_noalloc():
+    """The flag with bf16 outputs (fp16 split partials) within the same bound
+    plus the bf16 output rounding of the default's result, and the
+    allocation-free entry point with the flag equal to the workspace call bit
+    for bit."""
+    cfg = CASES[0]
+    st = State(cfg)
+    st.oracle_compress_append()
+    rows = np.arange(len(st.row_seq))
+    idx = O.topk(st.row_pos, cfg.m, st.oracle_index(rows), cfg.k)
+    gs = GpuState(st)
+    idx_d = torch.from_numpy(idx).to("cuda")
+    out_full, _ = gs.attn(idx_d)
+    qdt = lcca.BF16 | lcca.P_BF16
+    gs.q_dt = qdt
+    out_b, _ = gs.attn(idx_d, out_dtype=lcca.BF16)
+    out_f, lse_f = gs.attn(idx_d)
+    out_n = torch.empty_like(out_f)
+    lse_n = torch.empty_like(lse_f)
+    lcca.sparse_attn_fwd_noalloc(gs.pages, gs.rows, qdt, gs.q, cfg.H, cfg.dv, cfg.scale, gs.kv, idx_d, cfg.k, gs.win,
+                                 lcca.F32, out_n, lse_n)
+    torch.cuda.synchronize()
+    assert torch.equal(out_n, out_f) and torch.equal(lse_n, lse_f)
+    full = out_full.cpu().numpy().astype(np.float64)
+    got = out_b.float().cpu().numpy().astype(np.float64)
+    # bf16 output: half an ulp of the value (2^-9 relative) on top of the
+    # weights' bound and the fp16 partials' 2^-12 of each 16-dim tile's range
+    vmax = _max_value(st)
+    bound = 2.0 ** -9 * vmax + 2.0 ** -9 * np.abs(full) + 2.0 ** -11 * vmax + 1e-6
+    d = np.abs(got - full)
+    print("bf16 outputs: max change %.3g (max |v| %.3g)" % (d.max(), vmax), flush=True)
+    assert np.all(d <= bound)

@@ -123,3 +123,22 @@ def test_hca_ratio():
     m, n, k = 128, 8192, 512
     x = g.standard_normal((3, n)).astype(np.float32)
     _check("m=128", x, np.array([n * m - 1, n * m // 3, 5 * m]), m, k)
+
+
+@pytest.mark.parametrize("k", [8192, 8193, 12000])
+def test_long_rows_large_k(k):
+    """Rows of 64K entries (four 16K slices, then the selection among the
+    slices' candidates) with k around the 8,192 slots in which the slice and
+    candidate selections stage their chosen positions before translating
+    them: k = 8,192 takes the staged output, larger k the direct one; random,
+    tied and ReLU-like rows, ragged lengths."""
+    g = np.random.default_rng(31 + k)
+    rows, m, n = 4, 4, 65536
+    x = np.empty((rows, n), np.float32)
+    x[0] = g.standard_normal(n).astype(np.float32)
+    x[1] = np.round(g.standard_normal(n) * 4) / 4
+    x[2] = _relu_like(g, n, 0.8)
+    x[3] = g.standard_normal(n).astype(np.float32)
+    x[3, g.integers(0, n, 20000)] = 2.0
+    lens = np.array([n, n - 9, k + 5000, n // 2 + 1])
+    _check("long rows k=%d" % k, x, lens * m - 1, m, k)
