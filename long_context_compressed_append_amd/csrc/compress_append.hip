@@ -44,8 +44,8 @@ __device__ __forceinline__ void store_entry_chunk(const CompressArgs& p, bool ik
         float a = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
-        a = fmaxf(a, __shfl_xor(a, 1));
-        a = fmaxf(a, __shfl_xor(a, 2));
+        a = fmaxf(a, lane_xor<1>(a));
+        a = fmaxf(a, lane_xor<2>(a));
         const int X = mx_scale_exp(a);
         uint32_t wd = 0;
 #pragma unroll

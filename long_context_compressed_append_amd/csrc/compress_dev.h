@@ -227,10 +227,15 @@ __device__ __forceinline__ void store_slice_dim(const CompressArgs& p, bool ik_s
     const bool in = dim_i < dim;
     if (dt == DT_MXFP4) {
         float a = in ? fabsf(v) : 0.0f;
-        for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+        a = fmaxf(a, lane_xor<16>(a));
+        a = fmaxf(a, lane_xor<8>(a));
+        a = fmaxf(a, lane_xor<4>(a));
+        a = fmaxf(a, lane_xor<2>(a));
+        a = fmaxf(a, lane_xor<1>(a));
         const int X = mx_scale_exp(a);
         const uint32_t c = fp4_code(ldexpf(v, -X));
-        const uint32_t c_hi = __shfl_down(c, 1);
+        // lane i + 1's code (row_shl:1; used by even lanes, whose partner is in their row)
+        const uint32_t c_hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)c, 0x101, 0xF, 0xF, false);
         if (in && (dim_i & 1) == 0) data[row * (int64_t)(dim / 2) + dim_i / 2] = (uint8_t)(c | (c_hi << 4));
         if (in && (dim_i & 31) == 0)
             reinterpret_cast<uint8_t*>(p.kv_scale)[row * (int64_t)(dim / 32) + dim_i / 32] = (uint8_t)(X + 127);

@@ -155,13 +155,53 @@ __device__ inline u32x4 fp4x8_to_bf16(uint32_t w, int X) {
 // ---------------------------------------------------------------------------
 // wave helpers (wave64)
 // ---------------------------------------------------------------------------
+// v of lane l ^ O, on the VALU: quad permutations (O = 1, 2), row shifts
+// within 16-lane rows selected by lane bit 2 (O = 4: lane l reads l + 4 or
+// l - 4), a rotation of each row by 8 (O = 8), and the permlane swaps across
+// rows and wave halves (O = 16, 32; their two results hold lane l's and its
+// partner's values, in an order set by lane bit 4 or 5).  No LDS round trip.
+template <int O>
+__device__ __forceinline__ float lane_xor(float v) {
+    const int x = __float_as_int(v);
+    const int lane = (int)threadIdx.x & 63;
+    if constexpr (O == 1) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+    } else if constexpr (O == 2) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+    } else if constexpr (O == 4) {
+        const int up = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0xF, false);          // row_shl:4
+        const int dn = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);          // row_shr:4
+        return __int_as_float((lane & 4) ? dn : up);
+    } else if constexpr (O == 8) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false));   // row_ror:8
+    } else if constexpr (O == 16) {
+        const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+        return __uint_as_float((lane & 16) ? a[0] : a[1]);
+    } else {
+        static_assert(O == 32, "lane_xor: O is a power of two up to 32");
+        const auto a = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+        return __uint_as_float((lane & 32) ? a[0] : a[1]);
+    }
+}
+
+// Butterfly reductions over the wave (every lane gets the result), pairing
+// lanes l and l ^ o for o = 32, 16, ..., 1: each lane adds its own value and
+// its partner's, so every lane holds the same bits.
 __device__ inline float wave_max(float v) {
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    v = fmaxf(v, lane_xor<32>(v));
+    v = fmaxf(v, lane_xor<16>(v));
+    v = fmaxf(v, lane_xor<8>(v));
+    v = fmaxf(v, lane_xor<4>(v));
+    v = fmaxf(v, lane_xor<2>(v));
+    return fmaxf(v, lane_xor<1>(v));
 }
 __device__ inline float wave_sum(float v) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    v += lane_xor<32>(v);
+    v += lane_xor<16>(v);
+    v += lane_xor<8>(v);
+    v += lane_xor<4>(v);
+    v += lane_xor<2>(v);
+    return v + lane_xor<1>(v);
 }
 
 // max of v over lanes l, l ^ 16, l ^ 32 and l ^ 48, on the VALU (gfx950's

@@ -191,7 +191,7 @@ __device__ __forceinline__ void score_fresh(const IndexArgs& p, const FreshIn<DI
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if (i < m) {
-            const float w = __shfl(w_mine, i);
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_mine), i));
 #pragma unroll
             for (int j = 0; j < DPL; ++j) {
                 const float x = p.tok_dtype == DT_F32 ? __uint_as_float(in.raw[i][j]) : bf16_to_f32(in.raw[i][j]);
