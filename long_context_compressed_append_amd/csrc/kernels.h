@@ -100,11 +100,12 @@ struct AttnArgs {
     int32_t out_dtype; void* out; float* lse;
     // split plan
     int32_t nsplit, split_tiles;       // key splits per row, 32-key tiles per split
-    float* part_o;     // [rows][nsplit][H][d_v]   (nsplit > 1, fp32 partial states)
-    float* part_ml;    // [rows][nsplit][2][H]
+    // partial values by 16-dim tiles of d_v: [.. tile][head][16 dims]
+    float* part_o;     // [rows][nsplit][d_v / 16][H][16]   (nsplit > 1, fp32 partial states)
+    float* part_ml;    // [rows][nsplit][H][2]: (m, l) of each head
     // bf16 outputs: partial O / l as fp16 with a power-of-two range scale
     // per (split, 16 value dims, head); part_o is then unused
-    uint16_t* part_h;  // [rows][nsplit][H][d_v]
+    uint16_t* part_h;  // [rows][nsplit][d_v / 16][H][16]
     float* part_sc;    // [rows][nsplit][d_v / 16][H]
     // FP8 queries (q8 != 0, MXFP4 pools): each head's query quantised to
     // E4M3 with a power-of-two scale; pool tiles scored by the scaled

@@ -614,9 +614,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (tb >= rk.tiles) {
         // empty split (a row with fewer tiles than the longest): a zero state
         if (a.nsplit > 1 && tid < 64) {
-            float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H + hblk * 64 + tid;
-            ml[0] = -INFINITY;
-            ml[a.H] = 0.0f;
+            float* ml = a.part_ml + (((int64_t)r * a.nsplit + split) * a.H + hblk * 64 + tid) * 2;
+            *reinterpret_cast<float2*>(ml) = float2{-INFINITY, 0.0f};
         }
         return;
     }
@@ -728,9 +727,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             if (a.nsplit == 1) {
                 if (a.lse) a.lse[(int64_t)r * a.H + hd] = (W.m_run + log2f(l_tot)) * kLn2;
             } else {
-                float* ml = a.part_ml + ((int64_t)r * a.nsplit + split) * 2 * a.H;
-                ml[hd] = W.m_run;
-                ml[a.H + hd] = l_tot;
+                float* ml = a.part_ml + (((int64_t)r * a.nsplit + split) * a.H + hd) * 2;
+                *reinterpret_cast<float2*>(ml) = float2{W.m_run, l_tot};
             }
         }
         __syncthreads();
@@ -813,9 +811,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         } else if (a.part_h) {
             // U = O / l, a convex combination of the values, as fp16 scaled by
-            // 2^(15 - e) where max |U| over the head's 16-dim tile < 2^e
+            // 2^(15 - e) where max |U| over the head's 16-dim tile < 2^e.
+            // Partials are [row][split][16-dim tile][head][16 dims]: one store
+            // writes 16 heads' tiles contiguously.
             const int64_t su = (int64_t)r * a.nsplit + split;
-            uint16_t* ph = a.part_h + (su * a.H + hd) * DV + V.vbase + 4 * g;
+            uint16_t* ph = a.part_h + ((su * (DV / 16) + V.vbase / 16) * a.H + hd) * 16 + 4 * g;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
                 float amax = fmaxf(fmaxf(fabsf(V.o[hb][dt][0]), fabsf(V.o[hb][dt][1])),
@@ -824,30 +824,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 int ex = 0;
                 (void)frexpf(amax, &ex);
                 const f32x4 v = V.o[hb][dt] * ldexpf(inv, 15 - ex);
-                *reinterpret_cast<u32x2*>(ph + 16 * dt) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+                *reinterpret_cast<u32x2*>(ph + (int64_t)dt * a.H * 16) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
                 if (g == 0) a.part_sc[(su * (DV / 16) + V.vbase / 16 + dt) * a.H + hd] = ldexpf(1.0f, ex - 15);
             }
         } else {
             const int64_t su = (int64_t)r * a.nsplit + split;
-            float* po = a.part_o + (su * a.H + hd) * DV + V.vbase + 4 * g;
+            float* po = a.part_o + ((su * (DV / 16) + V.vbase / 16) * a.H + hd) * 16 + 4 * g;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt) = V.o[hb][dt];
+            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + (int64_t)dt * a.H * 16) = V.o[hb][dt];
         }
     }
 }
 
-// Merge the key splits of one (row, head): m* = max m_s, w_s = 2^(m_s - m*),
-// out = sum_s w_s O_s / sum_s w_s l_s, lse = (m* + log2 sum_s w_s l_s) ln 2.
-// With fp16 partials (HALF) a split stores U_s = O_s / l_s scaled by a power
-// of two per 16 value dims, so its weight in the sum becomes
-// w_s l_s times that scale.  Each thread owns 4 value dims.  The partial
-// outputs of the first MB splits (MB = 16, or 64 for more than 16 splits)
-// are requested before anything else, so they are in flight while the block
-// forms the weights (thread s owns split s and s + kMergeThreads); loads past
-// the last split are not issued.  Empty splits carry m = -inf, weight 0, and
-// their workspace bytes are never used.
-constexpr int kMergeThreads = 192;     // >= 576 / 4
-constexpr int kMaxSplits = 256;        // <= 2 * kMergeThreads
+// Merge the key splits of one (row, 16-dim tile of the values, 64 heads):
+// per head m* = max m_s, w_s = 2^(m_s - m*), out = sum_s w_s O_s /
+// sum_s w_s l_s, lse = (m* + log2 sum_s w_s l_s) ln 2.  With fp16 partials
+// (HALF) a split stores U_s = O_s / l_s scaled by a power of two per 16 value
+// dims, so its weight in the sum becomes w_s l_s times that scale.  Four
+// threads per head, four value dims each; every thread forms its own head's
+// weights from the (m, l) pairs, so the block needs no barrier.  Partials are
+// [row][split][16-dim tile][head][16 dims] (scales [row][split][tile][head]),
+// so a wave's load of one split reads 16 heads' tiles contiguously.  Splits
+// are taken in chunks of 16 whose loads are all issued at once (split indices
+// past the last split re-read the last one and are masked); with more than
+// 16 splits (MULTI) the chunks are folded in with a running maximum, the next
+// chunk's loads in flight during the current one's sums.  Empty splits carry
+// m = -inf, weight 0, and their workspace bytes are never used.
+constexpr int kMergeThreads = 256;     // 64 heads x 4 threads
+constexpr int kMergeChunk = 16;        // splits per chunk
+constexpr int kMaxSplits = 256;
 
 template <bool HALF>
 struct MergePart {
@@ -862,78 +867,74 @@ struct MergePart {
     }
 };
 
-template <bool HALF, int MB>
+template <bool HALF, bool MULTI>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
-    __shared__ float wts[kMaxSplits];
-    __shared__ float red[2][kMergeThreads / 64];
     using MP = MergePart<HALF>;
-    const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
-    const int H = a.H, DV = a.d_v, ns = a.nsplit;
-    const float* ml = a.part_ml + (int64_t)r * ns * 2 * H + h;
-    const int d = 4 * tid;
-    const bool mine = d < DV;
-    const int64_t pbase = ((int64_t)r * ns * H + h) * DV + (mine ? d : 0);
-    const int64_t sstride = (int64_t)H * DV;
-    // fp16 partials: this thread's 16-dim tile of the value dims picks the scale
-    const int64_t sc_stride = (int64_t)(DV / 16) * H;       // between splits
-    const float* scp = HALF ? a.part_sc + ((int64_t)r * ns * (DV / 16) + (mine ? d / 16 : 0)) * H + h : nullptr;
-    typename MP::raw os[MB];
-    float sc[HALF ? MB : 1];
-#pragma unroll
-    for (int j = 0; j < MB; ++j) {
-        if (j < ns) {
-            os[j] = MP::load(a, pbase + j * sstride);
-            if constexpr (HALF) sc[j] = scp[(int64_t)j * sc_stride];
-        }
-    }
-    const int s1 = tid + kMergeThreads;
-    const float m0 = tid < ns ? ml[(int64_t)tid * 2 * H] : -INFINITY;
-    const float l0 = tid < ns ? ml[(int64_t)tid * 2 * H + H] : 0.0f;
-    const float m1 = s1 < ns ? ml[(int64_t)s1 * 2 * H] : -INFINITY;
-    const float l1 = s1 < ns ? ml[(int64_t)s1 * 2 * H + H] : 0.0f;
-    float M = wave_max(fmaxf(m0, m1));
-    if ((tid & 63) == 0) red[0][tid >> 6] = M;
-    __syncthreads();
-    M = red[0][0];
-#pragma unroll
-    for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[0][i]);
-    const float w0 = m0 == -INFINITY ? 0.0f : exp2f(m0 - M);
-    const float w1 = m1 == -INFINITY ? 0.0f : exp2f(m1 - M);
-    // fp16 partials are normalised, so their weight carries l_s
-    if (tid < ns) wts[tid] = HALF ? w0 * l0 : w0;
-    if (s1 < ns) wts[s1] = HALF ? w1 * l1 : w1;
-    float L = wave_sum(w0 * l0 + w1 * l1);
-    if ((tid & 63) == 0) red[1][tid >> 6] = L;
-    __syncthreads();
-    L = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kMergeThreads / 64; ++i) L += red[1][i];
-    if (a.lse && tid == 0) a.lse[(int64_t)r * H + h] = (M + log2f(L)) * kLn2;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto add = [&](int s, int j) __attribute__((always_inline)) {
-        const float w = s < ns ? wts[s] : 0.0f;
-        const float ws = HALF ? w * sc[HALF ? j : 0] : w;
-        acc = w > 0.0f ? acc + ws * MP::value(os[j]) : acc;
+    constexpr int MC = kMergeChunk;
+    const int tile = blockIdx.x, r = blockIdx.y;
+    const int h = (int)blockIdx.z * 64 + (int)threadIdx.x / 4, q = (int)threadIdx.x % 4;
+    const int H = a.H, DV = a.d_v, ns = a.nsplit, NTL = DV / 16;
+    const int64_t su0 = (int64_t)r * ns;
+    const int64_t pstride = (int64_t)NTL * H * 16;            // partial values between splits
+    const int64_t pbase = ((su0 * NTL + tile) * H + h) * 16 + 4 * q;
+    const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + su0 * H + h;   // (m, l) of split s at s * H
+    const int64_t sstride = (int64_t)NTL * H;                 // scales between splits
+    const float* scp = HALF ? a.part_sc + (su0 * NTL + tile) * H + h : nullptr;
+    struct Chunk {
+        typename MP::raw os[MC];
+        float m[MC], l[MC], sc[HALF ? MC : 1];
     };
+    auto load = [&](Chunk& c, int s0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < MB; ++j)
-        if (j < ns) add(j, j);
-    for (int s0 = MB; s0 < ns; s0 += MB) {
+        for (int j = 0; j < MC; ++j) {
+            const int64_t sj = min(s0 + j, ns - 1);
+            c.os[j] = MP::load(a, pbase + sj * pstride);
+            const float2 p = ml[sj * H];
+            c.m[j] = p.x;
+            c.l[j] = p.y;
+            if constexpr (HALF) c.sc[j] = scp[sj * sstride];
+        }
+    };
+    float M = -INFINITY, L = 0.0f;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto fold = [&](const Chunk& c, int s0) __attribute__((always_inline)) {
+        float mc = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < MB; ++j) {
-            if (s0 + j < ns) {
-                os[j] = MP::load(a, pbase + (s0 + j) * sstride);
-                if constexpr (HALF) sc[j] = scp[(int64_t)(s0 + j) * sc_stride];
-            }
+        for (int j = 0; j < MC; ++j) mc = s0 + j < ns ? fmaxf(mc, c.m[j]) : mc;
+        if (mc > M) {
+            // a new running maximum: rescale what the earlier chunks summed
+            const float f = __builtin_amdgcn_exp2f(M - mc);
+            acc *= f;
+            L *= f;
+            M = mc;
         }
 #pragma unroll
-        for (int j = 0; j < MB; ++j)
-            if (s0 + j < ns) add(s0 + j, j);
+        for (int j = 0; j < MC; ++j) {
+            const float w = s0 + j < ns && c.m[j] != -INFINITY ? __builtin_amdgcn_exp2f(c.m[j] - M) : 0.0f;
+            L += w * c.l[j];
+            const float ws = HALF ? w * c.l[j] * c.sc[HALF ? j : 0] : w;
+            acc = w > 0.0f ? acc + ws * MP::value(c.os[j]) : acc;
+        }
+    };
+    if constexpr (!MULTI) {
+        Chunk c;
+        load(c, 0);
+        fold(c, 0);
+    } else {
+        Chunk c[2];
+        load(c[0], 0);
+        for (int s0 = 0; s0 < ns; s0 += 2 * MC) {
+            if (s0 + MC < ns) load(c[1], s0 + MC);
+            fold(c[0], s0);
+            if (s0 + MC >= ns) break;
+            if (s0 + 2 * MC < ns) load(c[0], s0 + 2 * MC);
+            fold(c[1], s0 + MC);
+        }
     }
-    if (!mine) return;
+    if (a.lse && tile == 0 && q == 0) a.lse[(int64_t)r * H + h] = (M + log2f(L)) * kLn2;
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     acc *= inv;
-    const int64_t oi = ((int64_t)r * H + h) * DV + d;
+    const int64_t oi = ((int64_t)r * H + h) * DV + tile * 16 + 4 * q;
     if (a.out_dtype == DT_F32) {
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + oi) = acc;
     } else {
@@ -1029,13 +1030,13 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
-    const dim3 mgrid(a.H, a.num_rows);
+    const dim3 mgrid(a.d_v / 16, a.num_rows, a.H / 64);
     if (a.part_h) {
-        if (a.nsplit <= 16) hipLaunchKernelGGL((attn_merge_kernel<true, 16>), mgrid, dim3(kMergeThreads), 0, stream, a);
-        else hipLaunchKernelGGL((attn_merge_kernel<true, 64>), mgrid, dim3(kMergeThreads), 0, stream, a);
+        if (a.nsplit <= kMergeChunk) hipLaunchKernelGGL((attn_merge_kernel<true, false>), mgrid, dim3(kMergeThreads), 0, stream, a);
+        else hipLaunchKernelGGL((attn_merge_kernel<true, true>), mgrid, dim3(kMergeThreads), 0, stream, a);
     } else {
-        if (a.nsplit <= 16) hipLaunchKernelGGL((attn_merge_kernel<false, 16>), mgrid, dim3(kMergeThreads), 0, stream, a);
-        else hipLaunchKernelGGL((attn_merge_kernel<false, 64>), mgrid, dim3(kMergeThreads), 0, stream, a);
+        if (a.nsplit <= kMergeChunk) hipLaunchKernelGGL((attn_merge_kernel<false, false>), mgrid, dim3(kMergeThreads), 0, stream, a);
+        else hipLaunchKernelGGL((attn_merge_kernel<false, true>), mgrid, dim3(kMergeThreads), 0, stream, a);
     }
     return hipGetLastError();
 }
