@@ -845,10 +845,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // weights from the (m, l) pairs, so the block needs no barrier.  Partials are
 // [row][split][16-dim tile][head][16 dims] (scales [row][split][tile][head]),
 // so a wave's load of one split reads 16 heads' tiles contiguously.  Splits
-// are taken in chunks of 16 whose loads are all issued at once (split indices
-// past the last split re-read the last one and are masked); with more than
-// 16 splits (MULTI) the chunks are folded in with a running maximum, the next
-// chunk's loads in flight during the current one's sums.  Empty splits carry
+// are taken in chunks of MC whose loads are all issued at once (split indices
+// past the last split re-read the last one and are masked; with at most 8
+// splits the chunk is 8, which halves the registers a thread holds).  With
+// more than 16 splits (MULTI) a workgroup covers 16 heads with four waves,
+// wave g taking the chunks g, g + 4, ...: each folds its chunks with a
+// running maximum, and wave 0 folds the other three's states from LDS.  Empty splits carry
 // m = -inf, weight 0, and their workspace bytes are never used.
 constexpr int kMergeThreads = 256;     // 64 heads x 4 threads
 constexpr int kMergeChunk = 16;        // splits per chunk
@@ -867,12 +869,14 @@ struct MergePart {
     }
 };
 
-template <bool HALF, bool MULTI>
+template <bool HALF, int MC, bool MULTI>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     using MP = MergePart<HALF>;
-    constexpr int MC = kMergeChunk;
-    const int tile = blockIdx.x, r = blockIdx.y;
-    const int h = (int)blockIdx.z * 64 + (int)threadIdx.x / 4, q = (int)threadIdx.x % 4;
+    constexpr int NG = MULTI ? 4 : 1;                          // split groups (waves)
+    const int tid = threadIdx.x, tile = blockIdx.x, r = blockIdx.y;
+    const int grp = MULTI ? tid / 64 : 0;
+    const int h = MULTI ? (int)blockIdx.z * 16 + (tid & 63) / 4 : (int)blockIdx.z * 64 + tid / 4;
+    const int q = tid % 4;
     const int H = a.H, DV = a.d_v, ns = a.nsplit, NTL = DV / 16;
     const int64_t su0 = (int64_t)r * ns;
     const int64_t pstride = (int64_t)NTL * H * 16;            // partial values between splits
@@ -916,19 +920,39 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
             acc = w > 0.0f ? acc + ws * MP::value(c.os[j]) : acc;
         }
     };
-    if constexpr (!MULTI) {
+    for (int s0 = grp * MC; s0 < ns; s0 += NG * MC) {
         Chunk c;
-        load(c, 0);
-        fold(c, 0);
-    } else {
-        Chunk c[2];
-        load(c[0], 0);
-        for (int s0 = 0; s0 < ns; s0 += 2 * MC) {
-            if (s0 + MC < ns) load(c[1], s0 + MC);
-            fold(c[0], s0);
-            if (s0 + MC >= ns) break;
-            if (s0 + 2 * MC < ns) load(c[0], s0 + 2 * MC);
-            fold(c[1], s0 + MC);
+        load(c, s0);
+        fold(c, s0);
+    }
+    if constexpr (MULTI) {
+        // waves 1..3 hand (m, l, O) of their splits to wave 0
+        __shared__ float xs[NG - 1][64][6];
+        const int t = tid & 63;
+        if (grp > 0) {
+            float* x = xs[grp - 1][t];
+            x[0] = M;
+            x[1] = L;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[2 + i] = acc[i];
+        }
+        __syncthreads();
+        if (grp > 0) return;
+#pragma unroll
+        for (int g = 0; g < NG - 1; ++g) {
+            const float* x = xs[g][t];
+            const float mg = x[0];
+            if (mg == -INFINITY) continue;
+            if (mg > M) {
+                const float f = __builtin_amdgcn_exp2f(M - mg);
+                acc *= f;
+                L *= f;
+                M = mg;
+            }
+            const float f = __builtin_amdgcn_exp2f(mg - M);
+            L += f * x[1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += f * x[2 + i];
         }
     }
     if (a.lse && tile == 0 && q == 0) a.lse[(int64_t)r * H + h] = (M + log2f(L)) * kLn2;
@@ -1030,13 +1054,15 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
-    const dim3 mgrid(a.d_v / 16, a.num_rows, a.H / 64);
+    const dim3 mgrid(a.d_v / 16, a.num_rows, a.H / 64), mgrid16(a.d_v / 16, a.num_rows, a.H / 16);
     if (a.part_h) {
-        if (a.nsplit <= kMergeChunk) hipLaunchKernelGGL((attn_merge_kernel<true, false>), mgrid, dim3(kMergeThreads), 0, stream, a);
-        else hipLaunchKernelGGL((attn_merge_kernel<true, true>), mgrid, dim3(kMergeThreads), 0, stream, a);
+        if (a.nsplit <= kMergeChunk / 2) hipLaunchKernelGGL((attn_merge_kernel<true, kMergeChunk / 2, false>), mgrid, dim3(kMergeThreads), 0, stream, a);
+        else if (a.nsplit <= kMergeChunk) hipLaunchKernelGGL((attn_merge_kernel<true, kMergeChunk, false>), mgrid, dim3(kMergeThreads), 0, stream, a);
+        else hipLaunchKernelGGL((attn_merge_kernel<true, kMergeChunk, true>), mgrid16, dim3(kMergeThreads), 0, stream, a);
     } else {
-        if (a.nsplit <= kMergeChunk) hipLaunchKernelGGL((attn_merge_kernel<false, false>), mgrid, dim3(kMergeThreads), 0, stream, a);
-        else hipLaunchKernelGGL((attn_merge_kernel<false, true>), mgrid, dim3(kMergeThreads), 0, stream, a);
+        if (a.nsplit <= kMergeChunk / 2) hipLaunchKernelGGL((attn_merge_kernel<false, kMergeChunk / 2, false>), mgrid, dim3(kMergeThreads), 0, stream, a);
+        else if (a.nsplit <= kMergeChunk) hipLaunchKernelGGL((attn_merge_kernel<false, kMergeChunk, false>), mgrid, dim3(kMergeThreads), 0, stream, a);
+        else hipLaunchKernelGGL((attn_merge_kernel<false, kMergeChunk, true>), mgrid16, dim3(kMergeThreads), 0, stream, a);
     }
     return hipGetLastError();
 }
