@@ -27,6 +27,21 @@ def _say(*a):
     print(*a, flush=True)
 
 
+# Split plans of the split merge (dense rows, m = 128): each (row, 16-dim
+# tile of the values) folds its key splits in chunks of 8 (at most 8 splits)
+# or 16, and above 16 splits four waves share them, every fourth chunk each.
+MERGE = {
+    # 40 rows of 7 .. 312 entries (5 .. 14 tiles with the window): 5 splits of
+    # 3 tiles, the short rows' last splits empty
+    "merge_few_splits": (synth.shrink(S["hca_1m"], "merge_few", tuple(1000 * (i + 1) for i in range(40)),
+                                      (1,) * 40), 2, 8),
+    # a row of 3,200 entries (104 tiles, one split each: the first three
+    # waves fold two chunks) and one of 100 (8 tiles: the other waves' splits
+    # all empty)
+    "merge_many_splits": (synth.shrink(S["hca_1m"], "merge_many", (409599, 12799), (1, 1)), 65, 256),
+}
+
+
 def _index_bound(st, rows):
     """sum_h w_h sum_d |q_hd k_d| for every visible entry of the given rows."""
     c = st.cfg
@@ -117,4 +132,33 @@ def test_score_far_above_the_first_keys():
     # the peak dominates row 0 (every head): its output is the entry's value
     assert np.abs(o_want[0] - x[0][None, : cfg.dv]).max() < 1e-6
     C.check_attention(out.cpu().numpy(), o_want, "bf16")
+    assert np.abs(lse.cpu().numpy() - l_want).max() <= 1e-3
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", list(MERGE))
+def test_split_merge_regimes(name, out_dtype):
+    cfg, ns_lo, ns_hi = MERGE[name]
+    _say("split merge", name, out_dtype)
+    st = State(cfg)
+    st.oracle_compress_append()
+    gs = GpuState(st)
+    nr = len(st.row_seq)
+    # the plan's split count, from its workspace: fp32 partial values and an
+    # (m, l) pair per (row, split, head)
+    wsb = lcca.sparse_attn_workspace_size(gs.rows, cfg.m, cfg.H, cfg.D, cfg.dv, 0, False, cfg.window)
+    ns = int(round(wsb / (nr * cfg.H * (4 * cfg.dv + 8))))
+    assert ns_lo <= ns <= ns_hi, ns
+    bf = out_dtype == "bf16"
+    out, lse = gs.attn(None, out_dtype=lcca.BF16 if bf else lcca.F32)
+    torch.cuda.synchronize()
+    o_want, l_want = st.oracle_attn(None)
+    got = out.float().cpu().numpy()
+    C.check_attention(got, o_want, "bf16", out_bf16=bf)
+    if not bf:
+        # fp32 outputs: scores of exact bf16 operands summed in fp32, P as a
+        # bf16 hi + lo pair (16 significant bits), fp32 accumulators and
+        # merge; the values are N(0,1), so every output is within 1e-4 (a
+        # split dropped or weighted wrongly moves it by ~1e-3 or more)
+        assert np.abs(got - o_want).max() <= 1e-4
     assert np.abs(lse.cpu().numpy() - l_want).max() <= 1e-3
