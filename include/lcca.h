@@ -372,7 +372,7 @@ size_t lcca_decode_select_workspace_size(const lcca_rows* rows, int32_t ratio_m,
  * with all keys in ONE softmax.  Keys are split across workgroups and the
  * partial softmax states are merged (max, rescaled sums); for BF16 outputs
  * a split's O / sum is kept as fp16 (11 significant bits against the
- * output's 8) with a power-of-two range scale per split, head and 16 value
+ * output's 8) with a power-of-two range scale per split, head and 4 value
  * dims, for F32 outputs in fp32.
  *   q        device [num_rows][H][kv->dim] of q_dtype (F32 with F32 cache;
  *            BF16 otherwise; BF16 | LCCA_Q_FP8 with an MXFP4 cache quantises

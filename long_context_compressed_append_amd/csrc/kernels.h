@@ -104,9 +104,9 @@ struct AttnArgs {
     float* part_o;     // [rows][nsplit][d_v / 16][H][16]   (nsplit > 1, fp32 partial states)
     float* part_ml;    // [rows][nsplit][H][2]: (m, l) of each head
     // bf16 outputs: partial O / l as fp16 with a power-of-two range scale
-    // per (split, 16 value dims, head); part_o is then unused
+    // per (split, head, 4 value dims); part_o is then unused
     uint16_t* part_h;  // [rows][nsplit][d_v / 16][H][16]
-    float* part_sc;    // [rows][nsplit][d_v / 16][H]
+    float* part_sc;    // [rows][nsplit][d_v / 16][H][4]
     // FP8 queries (q8 != 0, MXFP4 pools): each head's query quantised to
     // E4M3 with a power-of-two scale; pool tiles scored by the scaled
     // FP4 x FP8 MFMA on the pool's own codes and scales

@@ -580,7 +580,8 @@ lcca_status attn_call(void* stream, const lcca_pages* pages, const lcca_rows* ro
         char* base = reinterpret_cast<char*>(ws);
         a.part_ml = reinterpret_cast<float*>(base + po);
         if (out_dtype == LCCA_BF16) {
-            // fp16 partials and their scales fit in the fp32 partials' place
+            // fp16 partials (2 bytes per value) and their scales (one float
+            // per 4 values) fit in the fp32 partials' place (4 bytes per value)
             const size_t ph = (parts * sizeof(uint16_t) + 255) & ~(size_t)255;
             a.part_h = reinterpret_cast<uint16_t*>(base);
             a.part_sc = reinterpret_cast<float*>(base + ph);

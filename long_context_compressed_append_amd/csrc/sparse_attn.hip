@@ -38,10 +38,10 @@
 // on the dequantised query.  The value side is unchanged.
 // Keys are split across workgroups when the rows alone cannot fill the GPU;
 // the partial (max, sum, O) states go to the workspace and a merge kernel
-// (one workgroup per row and head) combines them.  For fp32 outputs O stays
-// fp32; for bf16 outputs O / sum is stored as fp16 (11 significant bits,
-// eight times finer than the output's rounding) with a power-of-two range
-// scale per split, head and 16 value dims.
+// (one workgroup per row and 16 value dims) combines them.  For fp32 outputs
+// O stays fp32; for bf16 outputs O / sum is stored as fp16 (11 significant
+// bits, eight times finer than the output's rounding) with a power-of-two
+// range scale per split, head and 4 value dims.
 #include <type_traits>
 
 #include "device.h"
@@ -811,7 +811,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         } else if (a.part_h) {
             // U = O / l, a convex combination of the values, as fp16 scaled by
-            // 2^(15 - e) where max |U| over the head's 16-dim tile < 2^e.
+            // 2^(15 - e) where max |U| over the lane's four dims < 2^e (no
+            // cross-lane step; the scales are [row][split][tile][head][4]).
             // Partials are [row][split][16-dim tile][head][16 dims]: one store
             // writes 16 heads' tiles contiguously.
             const int64_t su = (int64_t)r * a.nsplit + split;
@@ -820,12 +821,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int dt = 0; dt < NDT; ++dt) {
                 float amax = fmaxf(fmaxf(fabsf(V.o[hb][dt][0]), fabsf(V.o[hb][dt][1])),
                                    fmaxf(fabsf(V.o[hb][dt][2]), fabsf(V.o[hb][dt][3])));
-                amax = max_across_rows(amax) * inv;
+                amax *= inv;
                 int ex = 0;
                 (void)frexpf(amax, &ex);
                 const f32x4 v = V.o[hb][dt] * ldexpf(inv, 15 - ex);
                 *reinterpret_cast<u32x2*>(ph + (int64_t)dt * a.H * 16) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
-                if (g == 0) a.part_sc[(su * (DV / 16) + V.vbase / 16 + dt) * a.H + hd] = ldexpf(1.0f, ex - 15);
+                a.part_sc[((su * (DV / 16) + V.vbase / 16 + dt) * a.H + hd) * 4 + g] = ldexpf(1.0f, ex - 15);
             }
         } else {
             const int64_t su = (int64_t)r * a.nsplit + split;
@@ -843,7 +844,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // dims, so its weight in the sum becomes w_s l_s times that scale.  Four
 // threads per head, four value dims each; every thread forms its own head's
 // weights from the (m, l) pairs, so the block needs no barrier.  Partials are
-// [row][split][16-dim tile][head][16 dims] (scales [row][split][tile][head]),
+// [row][split][16-dim tile][head][16 dims] (scales [row][split][tile][head][4]),
 // so a wave's load of one split reads 16 heads' tiles contiguously.  Splits
 // are taken in chunks of MC whose loads are all issued at once (split indices
 // past the last split re-read the last one and are masked; with at most 8
@@ -882,8 +883,8 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     const int64_t pstride = (int64_t)NTL * H * 16;            // partial values between splits
     const int64_t pbase = ((su0 * NTL + tile) * H + h) * 16 + 4 * q;
     const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + su0 * H + h;   // (m, l) of split s at s * H
-    const int64_t sstride = (int64_t)NTL * H;                 // scales between splits
-    const float* scp = HALF ? a.part_sc + (su0 * NTL + tile) * H + h : nullptr;
+    const int64_t sstride = (int64_t)NTL * H * 4;             // scales between splits
+    const float* scp = HALF ? a.part_sc + ((su0 * NTL + tile) * H + h) * 4 + q : nullptr;
     struct Chunk {
         typename MP::raw os[MC];
         float m[MC], l[MC], sc[HALF ? MC : 1];
